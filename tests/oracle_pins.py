@@ -1,0 +1,545 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with a
+closed form, a library routine, a brute-force computation written
+independently here, or a fixture under tests/golden/. They are collected by
+test_oracle_pins.py twice: once on the clean oracle (must pass) and once per
+planted mistake (a mutant of the oracle, patched in on the CPU; the pin that
+targets it must fail).
+"""
+from __future__ import annotations
+
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from oracle import formats as F
+from oracle import moe, mxfp8
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            rows.append(line.split())
+    return rows
+
+
+# ---------------------------------------------------------------- independent scalar helpers
+def frac_bf16_round(v: Fraction) -> Fraction:
+    """Exact round-to-nearest-even of a rational to bfloat16 (finite range),
+    written independently of oracle.formats."""
+    if v == 0:
+        return Fraction(0)
+    a = abs(v)
+    e = 0
+    while a >= 2:
+        a /= 2
+        e += 1
+    while a < 1:
+        a *= 2
+        e -= 1
+    # |v| in [2^e, 2^(e+1)); 8 significant bits -> quantum 2^(e-7); subnormal floor 2^-133
+    q = Fraction(2) ** (max(e, -126) - 7)
+    n = abs(v) / q
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    r = fl * q
+    return r if v > 0 else -r
+
+
+def bf16_bits_scalar(bits: int) -> float:
+    import struct
+    return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
+
+
+def scalar_e2m1(c: int) -> Fraction:
+    # independent form: magnitude table written as halves, from the element definition
+    halves = [0, 1, 2, 3, 4, 6, 8, 12]
+    v = Fraction(halves[c & 7], 2)
+    return -v if c & 8 else v
+
+
+def scalar_e4m3(c: int) -> Fraction:
+    s, e, m = (c >> 7) & 1, (c >> 3) & 15, c & 7
+    mag = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+    return -mag if s else mag
+
+
+# ---------------------------------------------------------------- formats
+def pin_e2m1_golden():
+    for code, val in _read_golden("e2m1_values.txt"):
+        c = int(code, 16)
+        got = F.e2m1_value(c)
+        want = float(val)
+        assert got == want and math.copysign(1, got) == math.copysign(1, want), (code, got, want)
+        assert F.E2M1_TABLE[c] == want
+
+
+def pin_e4m3_golden_and_torch():
+    import torch
+    for code, val in _read_golden("e4m3_values.txt"):
+        c = int(code, 16)
+        got = F.e4m3_value(c)
+        if val == "nan":
+            assert math.isnan(got), code
+        else:
+            assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), (code, got, val)
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    lib = codes.to(torch.float32).numpy().astype(np.float64)
+    ours = F.E4M3_TABLE
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], lib[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(lib[~nan]))
+
+
+def pin_e8m0_golden_and_torch():
+    import torch
+    for code, val in _read_golden("e8m0_values.txt"):
+        c = int(code, 16)
+        got = F.e8m0_value(c)
+        if val == "nan":
+            assert math.isnan(got)
+        else:
+            assert got == float(val), (code, got, val)
+    for c in range(255):
+        assert F.E8M0_TABLE[c] == math.ldexp(1.0, c - 127)
+    if hasattr(torch, "float8_e8m0fnu"):
+        codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e8m0fnu)
+        lib = codes.to(torch.float64).numpy()
+        fin = ~np.isnan(lib)
+        assert np.array_equal(F.E8M0_TABLE[fin], lib[fin])
+
+
+def pin_bf16_rne_vs_torch():
+    """float32 -> bfloat16 rounding equals torch's conversion (a library routine)
+    on random bit patterns, ties, subnormals and overflow."""
+    import torch
+    rng = np.random.default_rng(1234)
+    bits = rng.integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    # add exact ties (low 16 bits = 0x8000) with both parities, and subnormals / near-overflow
+    ties = (rng.integers(0, 2 ** 16, size=20000, dtype=np.uint64).astype(np.uint32) << 16) | 0x8000
+    sub = rng.integers(0, 2 ** 23, size=20000, dtype=np.uint64).astype(np.uint32)
+    big = np.uint32(0x7F7F0000) + rng.integers(0, 2 ** 16, size=5000, dtype=np.uint64).astype(np.uint32)
+    allb = np.concatenate([bits, ties, sub, sub | 0x80000000, big]).astype(np.uint32)
+    f = allb.view(np.float32)
+    f = f[np.isfinite(f)]
+    lib = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ours = F.bf16_rne_bits(f.astype(np.float64))
+    assert np.array_equal(ours, lib), int(np.sum(ours != lib))
+
+
+def pin_bf16_rne_vs_fractions():
+    """float64 -> bfloat16 in one rounding (no float32 intermediate), against
+    exact rational rounding; includes values just off a midpoint, where a
+    float32 intermediate would round twice."""
+    rng = np.random.default_rng(99)
+    vals = list(rng.standard_normal(300) * 10.0 ** rng.integers(-30, 30, 300))
+    for b in rng.standard_normal(100):
+        bb = F.bf16_rne(np.array([b]))[0]
+        u = F.bf16_ulp(np.array([bb]))[0]
+        for delta in (0.0, 2.0 ** -30, -(2.0 ** -30)):
+            vals.append(bb + u / 2 + u * delta)
+            vals.append(bb - u / 2 + u * delta)
+    vals += [2.0 ** -130 * 1.37, -(2.0 ** -133) * 0.5000001, 2.0 ** -134, 3.3895313892515355e38]
+    arr = np.array(vals, dtype=np.float64)
+    ours = F.bf16_rne(arr)
+    for v, o in zip(arr, ours):
+        want = frac_bf16_round(Fraction(float(v)))
+        assert Fraction(float(o)) == want, (v, o, float(want))
+
+
+# ---------------------------------------------------------------- dequantization and layout
+def pin_worked_rows():
+    """The hand-worked NVFP4 rows of tests/golden/nvfp4_row_worked.txt."""
+    for row in _read_golden("nvfp4_row_worked.txt"):
+        _, byte, s0, s1, ts, expect = row
+        codes = np.full((1, 16), int(byte, 16), dtype=np.uint8)
+        scales = np.array([[int(s0, 16), int(s1, 16)]], dtype=np.uint8)
+        W = moe.dequant_nvfp4(codes, scales)
+        got = float(ts) * float(W.sum())
+        assert got == float(expect), (row, got)
+
+
+def pin_one_hot_columns():
+    """x = e_i selects column i of ts * W exactly; pins nibble order, scale
+    indexing and the tensor scale, against an independent scalar decode."""
+    rng = np.random.default_rng(7)
+    f, d = 8, 64
+    q = np.frombuffer(rng.bytes(f * d // 2), dtype=np.uint8).reshape(1, f, d // 2).copy()
+    s = rng.integers(0x18, 0x49, size=(1, f, d // 16), dtype=np.uint8)
+    ts = np.array([1.25], dtype=np.float32)
+    for i in (0, 1, 2, 15, 16, 17, 33, 63):
+        x = np.zeros((1, d), dtype=np.uint16)
+        x[0, i] = 0x3F80  # bfloat16 1.0
+        for n in range(f):
+            byte = int(q[0, n, i // 2])
+            code = (byte & 0xF) if i % 2 == 0 else (byte >> 4)
+            want = float(Fraction(1.25) * scalar_e2m1(code) * scalar_e4m3(int(s[0, n, i // 16])))
+            W = moe.dequant_nvfp4(q[0], s[0])
+            X = F.bf16_bits_to_f64(x)
+            got = float(ts[0]) * (X @ W.T)[0, n]
+            assert got == want, (i, n, got, want)
+
+
+def pin_constant_codes():
+    """All codes c and all scales 1.0: W = value(c) everywhere, so every output
+    of X . W^T is value(c) * sum(x)."""
+    rng = np.random.default_rng(3)
+    d, f = 64, 4
+    x = rng.standard_normal(d)
+    xb = F.bf16_rne_bits(x)
+    X = F.bf16_bits_to_f64(xb)
+    for c in range(16):
+        q = np.full((f, d // 2), c | (c << 4), dtype=np.uint8)
+        s = np.full((f, d // 16), 0x38, dtype=np.uint8)
+        W = moe.dequant_nvfp4(q, s)
+        got = X @ W.T
+        want = float(scalar_e2m1(c)) * math.fsum(X)
+        assert np.all(np.abs(got - want) <= 1e-12 * (1 + abs(want))), (c, got, want)
+
+
+# ---------------------------------------------------------------- routing and row lists
+def pin_route_brute_force():
+    """Top-k against a rank count: expert i is selected iff fewer than k
+    experts beat it, where j beats i when l_j > l_i, or l_j == l_i and j < i;
+    its output slot is that count. Includes constructed ties and signed zeros."""
+    rng = np.random.default_rng(11)
+    cases = []
+    for _ in range(60):
+        E = int(rng.integers(1, 12))
+        k = int(rng.integers(1, E + 1))
+        T = int(rng.integers(1, 5))
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+        if rng.random() < 0.5:  # inject ties and signed zeros
+            lg = np.round(lg).astype(np.float32)
+            lg[lg == 0] = np.where(rng.random(int((lg == 0).sum())) < 0.5, -0.0, 0.0)
+        cases.append((lg, k))
+    cases.append((np.array([[0.0, -0.0, 0.0, -0.0]], dtype=np.float32), 3))
+    cases.append((np.array([[1.0, 1.0, 1.0, 2.0, 2.0]], dtype=np.float32), 4))
+    for lg, k in cases:
+        ids, w = moe.route(lg, k)
+        T, E = lg.shape
+        for t in range(T):
+            want = [None] * k
+            for i in range(E):
+                beat = sum(1 for j in range(E) if lg[t, j] > lg[t, i] or (lg[t, j] == lg[t, i] and j < i))
+                if beat < k:
+                    want[beat] = i
+            assert list(ids[t]) == want, (lg[t], k, ids[t], want)
+            # weights: independent softmax over the selected logits, with fsum
+            sel = [float(lg[t, i]) for i in want]
+            m = max(sel)
+            ex = [math.exp(v - m) for v in sel]
+            tot = math.fsum(ex)
+            for j in range(k):
+                assert abs(w[t, j] - ex[j] / tot) <= 4e-16, (w[t, j], ex[j] / tot)
+            assert abs(math.fsum(w[t]) - 1.0) <= 1e-15
+
+
+def pin_route_k2_closed_form():
+    """k = 2: w_0 = 1 / (1 + e^(l_1 - l_0))."""
+    rng = np.random.default_rng(5)
+    lg = rng.standard_normal((50, 16)).astype(np.float32)
+    ids, w = moe.route(lg, 2)
+    for t in range(50):
+        l0, l1 = float(lg[t, ids[t, 0]]), float(lg[t, ids[t, 1]])
+        assert l0 >= l1
+        w0 = 1.0 / (1.0 + math.exp(l1 - l0))
+        assert abs(w[t, 0] - w0) <= 2e-16 and abs(w[t, 1] - (1.0 - w0)) <= 2e-16
+
+
+def pin_row_lists_definition():
+    """Row lists by their definition, with Python loops: for each expert in
+    order, its assignments a = t*k + j in increasing a; counts, offsets, the
+    inverse map; every assignment appears exactly once."""
+    rng = np.random.default_rng(13)
+    for _ in range(30):
+        E = int(rng.integers(1, 20))
+        k = int(rng.integers(1, min(E, 6) + 1))
+        T = int(rng.integers(1, 30))
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+        ids, _ = moe.route(lg, k)
+        rl = moe.row_lists(ids, E)
+        flat = [int(v) for v in ids.reshape(-1)]
+        lists = [[a for a in range(T * k) if flat[a] == e] for e in range(E)]
+        want_sorted = [a for lst in lists for a in lst]
+        assert list(rl.sorted_rows) == want_sorted
+        assert list(rl.counts) == [len(lst) for lst in lists]
+        off = [0]
+        for lst in lists:
+            off.append(off[-1] + len(lst))
+        assert list(rl.offsets) == off and off[-1] == T * k
+        assert sorted(want_sorted) == list(range(T * k))
+        for p, a in enumerate(want_sorted):
+            assert rl.row_of[a] == p
+
+
+# ---------------------------------------------------------------- FFN and combine
+def _single_expert_inputs(d, f, seed):
+    rng = np.random.default_rng(seed)
+    x = F.bf16_rne_bits(rng.standard_normal((1, d)))
+    ex = dict(
+        gate_q=np.frombuffer(rng.bytes(f * d // 2), dtype=np.uint8).reshape(1, f, d // 2).copy(),
+        gate_s=rng.integers(0x18, 0x49, size=(1, f, d // 16), dtype=np.uint8),
+        gate_ts=np.array([rng.uniform(0.5, 2)], dtype=np.float32),
+        up_q=np.frombuffer(rng.bytes(f * d // 2), dtype=np.uint8).reshape(1, f, d // 2).copy(),
+        up_s=rng.integers(0x18, 0x49, size=(1, f, d // 16), dtype=np.uint8),
+        up_ts=np.array([rng.uniform(0.5, 2)], dtype=np.float32),
+        down_q=np.frombuffer(rng.bytes(d * f // 2), dtype=np.uint8).reshape(1, d, f // 2).copy(),
+        down_s=rng.integers(0x18, 0x49, size=(1, d, f // 16), dtype=np.uint8),
+        down_ts=np.array([rng.uniform(0.5, 2)], dtype=np.float32),
+    )
+    return x, ex
+
+
+def _brute_nvfp4_row(codes_row, scales_row, i):
+    byte = int(codes_row[i // 2])
+    code = (byte & 0xF) if i % 2 == 0 else (byte >> 4)
+    return scalar_e2m1(code) * scalar_e4m3(int(scales_row[i // 16]))
+
+
+def pin_single_expert_brute_force():
+    """E = 1, k = 1, w = 1, d = 32, f = 16: scalar loops in exact rationals
+    (silu in float64 math) against the vectorized oracle's h bits and output."""
+    for seed in (0, 1, 2):
+        d, f = 32, 16
+        x, ex = _single_expert_inputs(d, f, seed)
+        xs = [Fraction(bf16_bits_scalar(b)) for b in x[0]]
+        H = []
+        for n in range(f):
+            g = Fraction(float(ex["gate_ts"][0])) * sum(xs[i] * _brute_nvfp4_row(ex["gate_q"][0, n], ex["gate_s"][0, n], i) for i in range(d))
+            u = Fraction(float(ex["up_ts"][0])) * sum(xs[i] * _brute_nvfp4_row(ex["up_q"][0, n], ex["up_s"][0, n], i) for i in range(d))
+            gf = float(g)
+            sig = 1.0 / (1.0 + math.exp(-gf)) if gf >= 0 else math.exp(gf) / (1.0 + math.exp(gf))
+            h = Fraction(gf * sig) * u
+            H.append(frac_bf16_round(h))
+        out = []
+        for n in range(d):
+            o = Fraction(float(ex["down_ts"][0])) * sum(H[i] * _brute_nvfp4_row(ex["down_q"][0, n], ex["down_s"][0, n], i) for i in range(f))
+            out.append(frac_bf16_round(o))
+        ids = np.zeros((1, 1), dtype=np.int32)
+        rl = moe.row_lists(ids, 1)
+        res = moe.expert_ffn(x, 1, d, f, 1, 1, ex, rl)
+        got_h = [Fraction(bf16_bits_scalar(b)) for b in res.h_bits[0]]
+        assert got_h == H, seed
+        y, ob = moe.combine(res.y_rows, rl.row_of, np.ones((1, 1)), 1, 1)
+        got = [Fraction(bf16_bits_scalar(b)) for b in ob[0]]
+        assert got == out, seed
+
+
+def _identity_experts(d):
+    q = np.zeros((1, d, d // 2), dtype=np.uint8)
+    for i in range(d):
+        q[0, i, i // 2] = 0x02 if i % 2 == 0 else 0x20    # code 2 = 1.0 on the diagonal
+    s = np.full((1, d, d // 16), 0x38, dtype=np.uint8)     # 1.0
+    one = np.ones(1, dtype=np.float32)
+    return dict(gate_q=q, gate_s=s, gate_ts=one, up_q=q.copy(), up_s=s.copy(), up_ts=one,
+                down_q=q.copy(), down_s=s.copy(), down_ts=one)
+
+
+def pin_identity_expert():
+    """W_g = W_u = W_d = I (d = f), scales 1, tensor scales 1, one expert,
+    k = 1: out = bfloat16(silu(x) * x), a closed form."""
+    d = 64
+    rng = np.random.default_rng(21)
+    T = 5
+    x = F.bf16_rne_bits(rng.standard_normal((T, d)) * 3.0)
+    ex = _identity_experts(d)
+    ids = np.zeros((T, 1), dtype=np.int32)
+    rl = moe.row_lists(ids, 1)
+    res = moe.expert_ffn(x, T, d, d, 1, 1, ex, rl)
+    _, ob = moe.combine(res.y_rows, rl.row_of, np.ones((T, 1)), T, 1)
+    for t in range(T):
+        for i in range(d):
+            xv = bf16_bits_scalar(x[t, i])
+            sig = 1.0 / (1.0 + math.exp(-xv)) if xv >= 0 else math.exp(xv) / (1.0 + math.exp(xv))
+            want = frac_bf16_round(Fraction(xv * sig) * Fraction(xv))
+            assert Fraction(bf16_bits_scalar(ob[t, i])) == want, (t, i)
+
+
+def _small_layer(seed=0, T=6, d=64, f=32, E=5, k=2):
+    import workloads
+    return workloads.make_moe(T, d, f, E, k, seed=seed, config_id=77)
+
+
+def pin_scaling_invariants():
+    """Doubling every down tensor scale, or every up block scale (E4M3 code + 8
+    adds one to the exponent), doubles the output exactly; halving every down
+    scale halves it."""
+    inp = _small_layer()
+    base = moe.moe_layer(inp)
+    yb = F.bf16_bits_to_f64(base.out_bits)
+    inp2 = _small_layer()
+    inp2.down_ts = (inp2.down_ts * 2).astype(np.float32)
+    y2 = F.bf16_bits_to_f64(moe.moe_layer(inp2).out_bits)
+    assert np.array_equal(y2, 2 * yb)
+    inp3 = _small_layer()
+    inp3.up_s = (inp3.up_s + 8).astype(np.uint8)
+    y3 = F.bf16_bits_to_f64(moe.moe_layer(inp3).out_bits)
+    assert np.array_equal(y3, 2 * yb)
+    inp4 = _small_layer()
+    inp4.down_s = (inp4.down_s - 8).astype(np.uint8)
+    y4 = F.bf16_bits_to_f64(moe.moe_layer(inp4).out_bits)
+    assert np.array_equal(y4, yb / 2)
+
+
+def pin_gate_scale_not_linear():
+    """Doubling gate scales must NOT double the output (silu is not linear):
+    guards against a gate/up swap in SwiGLU."""
+    inp = _small_layer(seed=4)
+    yb = F.bf16_bits_to_f64(moe.moe_layer(inp).out_bits)
+    inp2 = _small_layer(seed=4)
+    inp2.gate_ts = (inp2.gate_ts * 2).astype(np.float32)
+    y2 = F.bf16_bits_to_f64(moe.moe_layer(inp2).out_bits)
+    assert not np.array_equal(y2, 2 * yb)
+
+
+def pin_combine_identical_experts():
+    """If every expert is the same, each token's output is that expert's
+    output (the k weights sum to one)."""
+    inp = _small_layer(seed=2, E=4, k=3)
+    for nm in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s"):
+        a = getattr(inp, nm)
+        a[:] = a[0:1]
+    for nm in ("gate_ts", "up_ts", "down_ts"):
+        a = getattr(inp, nm)
+        a[:] = a[0]
+    res = moe.moe_layer(inp)
+    single = moe.expert_ffn(inp.x, inp.T, inp.d, inp.f, 1, 1, {n: getattr(inp, n)[:1] for n in
+                            ("gate_q", "gate_s", "gate_ts", "up_q", "up_s", "up_ts", "down_q", "down_s", "down_ts")},
+                            moe.row_lists(np.zeros((inp.T, 1), np.int32), 1))
+    want = single.y_rows
+    assert np.all(np.abs(res.y - want) <= 1e-12 * np.abs(want) + 1e-300)
+    assert np.allclose(res.w.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+
+
+def pin_token_permutation():
+    """Permuting the tokens permutes ids, weights and outputs exactly."""
+    inp = _small_layer(seed=6, T=9, E=6, k=3)
+    res = moe.moe_layer(inp)
+    perm = np.random.default_rng(0).permutation(inp.T)
+    inp2 = _small_layer(seed=6, T=9, E=6, k=3)
+    inp2.x = inp2.x[perm].copy()
+    inp2.logits = inp2.logits[perm].copy()
+    res2 = moe.moe_layer(inp2)
+    assert np.array_equal(res2.ids, res.ids[perm])
+    assert np.array_equal(res2.w, res.w[perm])
+    assert np.array_equal(res2.out_bits, res.out_bits[perm])
+
+
+def pin_subset_equals_whole():
+    """The sampled-token path returns the same bits as the whole layer."""
+    inp = _small_layer(seed=8, T=7, E=5, k=2)
+    res = moe.moe_layer(inp)
+    sub = moe.moe_tokens(inp, [0, 3, 6])
+    assert np.array_equal(sub.out_bits, res.out_bits[[0, 3, 6]])
+
+
+# ---------------------------------------------------------------- MXFP8
+def pin_mxfp8_one_hot_and_scale():
+    """x = e_i selects column i of the dequantized weight (against the scalar
+    E4M3 decode); adding one to every E8M0 code doubles y exactly."""
+    rng = np.random.default_rng(17)
+    N, K = 6, 96
+    j = rng.integers(0, 254, size=(N, K))
+    w = np.where(j < 127, j, j + 1).astype(np.uint8)
+    s = rng.integers(121, 130, size=(N, K // 32), dtype=np.uint8)
+    for i in (0, 31, 32, 95):
+        x = np.zeros((1, K), dtype=np.uint16)
+        x[0, i] = 0x3F80
+        y, _, _ = mxfp8.mxfp8_gemm(x, w, s)
+        for n in range(N):
+            want = scalar_e4m3(int(w[n, i])) * Fraction(2) ** (int(s[n, i // 32]) - 127)
+            assert y[0, n] == float(want)
+    x = F.bf16_rne_bits(rng.standard_normal((3, K)))
+    y, ob, _ = mxfp8.mxfp8_gemm(x, w, s)
+    y2, ob2, _ = mxfp8.mxfp8_gemm(x, w, (s + 1).astype(np.uint8))
+    assert np.array_equal(y2, 2 * y)
+    assert np.array_equal(F.bf16_bits_to_f64(ob2), 2 * F.bf16_bits_to_f64(ob))
+
+
+def pin_mxfp8_brute_force():
+    rng = np.random.default_rng(19)
+    M, N, K = 2, 3, 64
+    j = rng.integers(0, 254, size=(N, K))
+    w = np.where(j < 127, j, j + 1).astype(np.uint8)
+    s = rng.integers(121, 130, size=(N, K // 32), dtype=np.uint8)
+    x = F.bf16_rne_bits(rng.standard_normal((M, K)))
+    _, ob, _ = mxfp8.mxfp8_gemm(x, w, s)
+    for m in range(M):
+        for n in range(N):
+            acc = sum(Fraction(bf16_bits_scalar(x[m, i])) * scalar_e4m3(int(w[n, i])) * Fraction(2) ** (int(s[n, i // 32]) - 127) for i in range(K))
+            assert Fraction(bf16_bits_scalar(ob[m, n])) == frac_bf16_round(acc)
+
+
+ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_") and callable(v)]
+
+
+def pin_h_rounds_once():
+    """h must be rounded once, directly from its exact value. Identity expert,
+    x = 64 at element 0: silu(G) = G exactly in float64 (e^-64 is below half an
+    ulp), so h = 4096 (1 + a)(1 + b) with ts_g = 1 + a, ts_u = 1 + b,
+    a = 2^-8 - 2^-20, b = 2^-20: h = 4112 + 2^-16 - 2^-28, just above the
+    bfloat16 midpoint 4112 between 4096 and 4128, so h rounds to 4128. Rounding
+    through float32 first would land on the midpoint and then on the even
+    neighbour 4096."""
+    d = 32
+    ex = _identity_experts(d)
+    ex["gate_ts"] = np.array([1 + 2.0 ** -8 - 2.0 ** -20], dtype=np.float32)
+    ex["up_ts"] = np.array([1 + 2.0 ** -20], dtype=np.float32)
+    assert float(ex["gate_ts"][0]) == 1 + 2.0 ** -8 - 2.0 ** -20 and float(ex["up_ts"][0]) == 1 + 2.0 ** -20
+    x = np.zeros((1, d), dtype=np.uint16)
+    x[0, 0] = 0x4280                                      # bfloat16 64.0
+    assert bf16_bits_scalar(0x4280) == 64.0
+    rl = moe.row_lists(np.zeros((1, 1), np.int32), 1)
+    res = moe.expert_ffn(x, 1, d, d, 1, 1, ex, rl)
+    assert bf16_bits_scalar(res.h_bits[0, 0]) == 4128.0
+    _, ob = moe.combine(res.y_rows, rl.row_of, np.ones((1, 1)), 1, 1)
+    assert bf16_bits_scalar(ob[0, 0]) == 4128.0
+    assert np.all(ob[0, 1:] == 0)
+
+
+def pin_two_expert_combine():
+    """Two scaled identity experts, k = 2, logits (1.0, 0.5): y = w0 * H +
+    w1 * ts1 * H with H = bf16(silu(x) x) and w0 = 1 / (1 + e^-0.5); the expert
+    rows stay unrounded until the final rounding."""
+    d = 32
+    ex1 = _identity_experts(d)
+    ex = {nm: np.concatenate([v, v]) for nm, v in ex1.items()}
+    ts1 = np.float32(1.3)
+    ex["down_ts"] = np.array([1.0, ts1], dtype=np.float32)
+    rng = np.random.default_rng(31)
+    T = 3
+    x = F.bf16_rne_bits(rng.standard_normal((T, d)) * 2)
+    logits = np.tile(np.array([[1.0, 0.5]], dtype=np.float32), (T, 1))
+    ids, w = moe.route(logits, 2)
+    assert ids.tolist() == [[0, 1]] * T
+    rl = moe.row_lists(ids, 2)
+    res = moe.expert_ffn(x, T, d, d, 2, 2, ex, rl)
+    y, ob = moe.combine(res.y_rows, rl.row_of, w, T, 2)
+    w0 = 1.0 / (1.0 + math.exp(0.5 - 1.0))
+    for t in range(T):
+        for i in range(d):
+            xv = bf16_bits_scalar(x[t, i])
+            sig = 1.0 / (1.0 + math.exp(-xv)) if xv >= 0 else math.exp(xv) / (1.0 + math.exp(xv))
+            H = frac_bf16_round(Fraction(xv * sig) * Fraction(xv))
+            want = Fraction(w0) * H + Fraction(1.0 - w0) * Fraction(float(ts1)) * H
+            assert abs(Fraction(y[t, i]) - want) <= abs(want) * Fraction(1, 2 ** 50), (t, i)
+            assert Fraction(bf16_bits_scalar(ob[t, i])) == frac_bf16_round(Fraction(y[t, i]))
+            assert Fraction(bf16_bits_scalar(ob[t, i])) == frac_bf16_round(want)
+
+
+ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_") and callable(v)]

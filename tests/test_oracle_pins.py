@@ -1,0 +1,116 @@
+"""The oracle against its pins (CPU), and planted mistakes that the pins must catch."""
+import os
+import sys
+import types
+
+import pytest
+
+import oracle_pins as P
+
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=[p.__name__ for p in P.ALL_PINS])
+def test_pin(pin):
+    pin()
+
+
+# (name, file, [(old, new), ...], pins that must go red)
+MUTANTS = [
+    ("nibble_order_swapped", "formats.py",
+     [("out[..., 0::2] = lo", "out[..., 0::2] = hi"), ("out[..., 1::2] = hi", "out[..., 1::2] = lo")],
+     ["pin_one_hot_columns", "pin_worked_rows"]),
+    ("block_scale_off_by_one", "moe.py",
+     [("np.repeat(sc, 16, axis=-1)", "np.repeat(np.roll(sc, 1, axis=-1), 16, axis=-1)")],
+     ["pin_one_hot_columns", "pin_worked_rows"]),
+    ("tie_break_flipped", "moe.py",
+     [("np.lexsort((idx[t], -vals[t]))", "np.lexsort((-idx[t], -vals[t]))")],
+     ["pin_route_brute_force"]),
+    ("gate_tensor_scale_dropped", "moe.py",
+     [("G = tg * (X @ Wg.T)", "G = (X @ Wg.T)")],
+     ["pin_single_expert_brute_force", "pin_h_rounds_once"]),
+    ("down_tensor_scale_twice", "moe.py",
+     [("O = td * (H @ Wd.T)", "O = td * td * (H @ Wd.T)")],
+     ["pin_single_expert_brute_force", "pin_two_expert_combine"]),
+    ("h_not_rounded", "moe.py",
+     [("H = F.bf16_rne(h_exact)", "H = h_exact")],
+     ["pin_single_expert_brute_force"]),
+    ("h_rounded_through_fp32", "moe.py",
+     [("H = F.bf16_rne(h_exact)", "H = F.bf16_rne(h_exact.astype(np.float32).astype(np.float64))")],
+     ["pin_h_rounds_once"]),
+    ("rows_rounded_before_combine", "moe.py",
+     [("O = td * (H @ Wd.T)", "O = F.bf16_rne(td * (H @ Wd.T))")],
+     ["pin_two_expert_combine"]),
+    ("row_list_order_reversed", "moe.py",
+     [("sorted_rows = np.argsort(flat, kind=\"stable\")",
+       "sorted_rows = np.argsort(flat * flat.size - np.arange(flat.size), kind=\"stable\")")],
+     ["pin_row_lists_definition"]),
+    ("e8m0_bias_126", "formats.py",
+     [("return 2.0 ** (code - 127)", "return 2.0 ** (code - 126)")],
+     ["pin_e8m0_golden_and_torch", "pin_mxfp8_one_hot_and_scale"]),
+    ("e4m3_subnormal_exponent", "formats.py",
+     [("mag = 2.0 ** (-6) * (m / 8.0)", "mag = 2.0 ** (-7) * (m / 8.0)")],
+     ["pin_e4m3_golden_and_torch"]),
+    ("swiglu_branches_swapped", "moe.py",
+     [("h_exact = sg * U", "h_exact = silu(U) * G")],
+     ["pin_single_expert_brute_force", "pin_gate_scale_not_linear"]),
+    ("weights_not_renormalized", "moe.py",
+     [("w = ex / ex.sum(axis=1, keepdims=True)", "w = ex")],
+     ["pin_route_brute_force", "pin_route_k2_closed_form"]),
+    ("combine_wrong_slot", "moe.py",
+     [("y += w[:, j:j + 1] * y_rows[ro[:, j]]", "y += w[:, j:j + 1] * y_rows[ro[:, 0]]")],
+     ["pin_two_expert_combine"]),
+    ("bf16_ties_away", "formats.py",
+     [("np.ldexp(np.rint(scaled), q_exp)", "np.ldexp(np.sign(scaled) * np.floor(np.abs(scaled) + 0.5), q_exp)")],
+     ["pin_bf16_rne_vs_torch", "pin_bf16_rne_vs_fractions"]),
+    ("token_of_row_wrong", "moe.py",
+     [("tok = rl.sorted_rows[p].astype(np.int64) // k", "tok = rl.sorted_rows[p].astype(np.int64) % k")],
+     ["pin_token_permutation", "pin_two_expert_combine"]),
+    ("mxfp8_block_16", "mxfp8.py",
+     [("np.repeat(F.E8M0_TABLE[s], 32, axis=-1)", "np.repeat(F.E8M0_TABLE[s], 16, axis=-1)[..., : w.shape[-1]]")],
+     ["pin_mxfp8_one_hot_and_scale", "pin_mxfp8_brute_force"]),
+]
+
+
+def _exec_module(fname, edits, pkg_overrides):
+    path = os.path.join(ORACLE_DIR, fname)
+    src = open(path).read()
+    for old, new in edits:
+        assert src.count(old) >= 1, f"mutant anchor not found in {fname}: {old}"
+        src = src.replace(old, new, 1)
+    mod = types.ModuleType("oracle_mutant_" + fname[:-3])
+    mod.__package__ = "oracle"
+    mod.__file__ = path
+    sys.modules[mod.__name__] = mod
+    exec(compile(src, path, "exec"), mod.__dict__)
+    for k, v in pkg_overrides.items():
+        setattr(mod, k, v)
+    return mod
+
+
+@pytest.mark.parametrize("name,fname,edits,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(monkeypatch, name, fname, edits, pins):
+    import oracle.formats as Freal
+    import oracle.moe as moereal
+    import oracle.mxfp8 as mxreal
+    if fname == "formats.py":
+        Fm = _exec_module("formats.py", edits, {})
+        moem = _exec_module("moe.py", [], {"F": Fm})
+        mxm = _exec_module("mxfp8.py", [], {"F": Fm})
+    elif fname == "moe.py":
+        Fm = Freal
+        moem = _exec_module("moe.py", edits, {})
+        mxm = mxreal
+    else:
+        Fm, moem = Freal, moereal
+        mxm = _exec_module("mxfp8.py", edits, {})
+    monkeypatch.setattr(P, "F", Fm)
+    monkeypatch.setattr(P, "moe", moem)
+    monkeypatch.setattr(P, "mxfp8", mxm)
+    red = []
+    for pn in pins:
+        try:
+            getattr(P, pn)()
+        except Exception:
+            red.append(pn)
+    assert red, f"mutant {name} went undetected by {pins}"
