@@ -1,0 +1,145 @@
+/*
+ * moe_nvfp4.h -- C ABI of the routed NVFP4 mixture-of-experts FFN and the MXFP8
+ * block-scaled projection, for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (as described on the pages "NVIDIA FP4-Local checkpoints on DGX Spark
+ * (TP=1, TP=2): format, model and speed plan in rounds #565", §4 Round 1, and
+ * "bloomery 0.3.9" release notes, New / From our contributors):
+ *   1. moe_route_topk        route a whole batch of tokens in one run: top-k experts
+ *                            per token, renormalized softmax weights, and per-expert
+ *                            row lists so every selected expert is read once (#740, #808);
+ *   2. moe_expert_ffn_nvfp4  per routed row: gate and up products, SwiGLU, down product,
+ *                            over NVFP4 weights held as stored -- U8 bytes of two E2M1
+ *                            codes, one F8_E4M3 scale per 16-element block, one fp32
+ *                            scale per expert tensor (#489, #517, #545, #766);
+ *   3. moe_combine           the router-weighted sum of each token's expert rows (#701);
+ *   4. mxfp8_gemm            y = x . W^T for MXFP8 weights: E4M3 elements in blocks of 32
+ *                            along K with one E8M0 scale a block, as a gemv (M = 1) and a
+ *                            wide GEMM (#521).
+ *
+ * Conventions for every entry point
+ *   - Every data pointer is a DEVICE pointer, allocated and owned by the caller; the
+ *     library never allocates, frees or retains memory and keeps no global state.
+ *   - `stream` is a hipStream_t (NULL = the default stream). A call only enqueues work
+ *     on it; results are valid once the stream reaches the call.
+ *   - Arguments are checked on the host before any HIP call; a call that returns a
+ *     non-zero status has enqueued nothing, except MOE_E_LAUNCH (a launch failed; the
+ *     HIP error text is available from moe_last_error()).
+ *   - Every pointer must be 16-byte aligned (a misaligned view is refused at the call,
+ *     after the pages' practice [#565 page, §10, #520]).
+ *   - Unsafe contract (documented, not checked on the device): router logits are finite;
+ *     no E4M3 NaN codes (0x7F, 0xFF) in block scales or MXFP8 weights, no E8M0 0xFF;
+ *     tensor scales are finite; outputs do not alias inputs; calls that share a
+ *     workspace are ordered on one stream.
+ *   - Element layouts (row-major):
+ *       bf16 tensors are uint16_t bit patterns;
+ *       NVFP4 codes: byte j of a row holds element 2j in its low nibble and element 2j+1
+ *       in its high nibble; E2M1 = sign | 2 exponent bits (bias 1) | 1 mantissa bit;
+ *       E4M3 = the "fn" variant (bias 7, no inf, S.1111.111 = NaN);
+ *       E8M0 = 2^(c - 127).
+ */
+#ifndef MOE_NVFP4_H
+#define MOE_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes; moe_status_string() names them. */
+enum {
+  MOE_OK = 0,
+  MOE_E_NULL = 1,      /* a required pointer is NULL                                  */
+  MOE_E_SHAPE = 2,     /* a size is out of range (see each entry point)               */
+  MOE_E_ALIGN = 3,     /* a pointer is not 16-byte aligned                             */
+  MOE_E_WORKSPACE = 4, /* workspace NULL or smaller than the size query returns        */
+  MOE_E_LAUNCH = 5     /* a HIP launch failed; see moe_last_error()                    */
+};
+
+/* One routed NVFP4 expert stack, stacked over the E experts, bytes as stored. The
+ * struct itself lives in host memory; its members are device pointers. */
+typedef struct moe_nvfp4_experts {
+  const uint8_t* gate_q;  /* [E][f][d/2]   E2M1 pairs                                    */
+  const uint8_t* gate_s;  /* [E][f][d/16]  E4M3 block scales (block = 16 along K = d)    */
+  const float* gate_ts;   /* [E]           fp32 tensor scale of each expert's gate       */
+  const uint8_t* up_q;    /* [E][f][d/2]                                                 */
+  const uint8_t* up_s;    /* [E][f][d/16]                                                */
+  const float* up_ts;     /* [E]                                                         */
+  const uint8_t* down_q;  /* [E][d][f/2]                                                 */
+  const uint8_t* down_s;  /* [E][d][f/16]  (block = 16 along K = f)                      */
+  const float* down_ts;   /* [E]                                                         */
+} moe_nvfp4_experts;
+
+/* ---------------------------------------------------------------------------------
+ * moe_route_topk -- top-k routing of a whole batch, and the per-expert row lists.
+ *
+ * Per token t (logits[t][0..E-1], fp32): the k experts with the largest logits, ordered
+ * by (logit descending, expert index ascending; -0.0 equals +0.0) -> topk_ids[t][0..k-1];
+ * topk_w[t][j] = exp(l_j - l_0) / sum_j' exp(l_j' - l_0), a softmax over the experts
+ * renormalized to the selected k (the router normalization policy is named on
+ * "bloomery 0.3.9" release notes, Fixed (#772); this is the renormalized-softmax one).
+ *
+ * Row lists (assignment a = t*k + j, T*k assignments):
+ *   expert_offsets[E+1]: exclusive prefix sum of the per-expert counts, [E] = T*k;
+ *   sorted_rows[T*k]:   for e = 0..E-1, every a with topk_ids.flat[a] == e in increasing a
+ *                       (a stable counting sort: bit-for-bit deterministic);
+ *   row_of[T*k]:        the inverse, row_of[sorted_rows[p]] = p.
+ *
+ * Sizes: 1 <= T, 1 <= E <= 1024, 1 <= k <= min(E, 32), T*k < 2^31.
+ * Workspace: at least moe_route_topk_workspace(T, E, k) bytes of device memory
+ * (0 is valid when the query returns 0; pass NULL then).
+ */
+size_t moe_route_topk_workspace(int T, int E, int k);
+int moe_route_topk(const float* logits, int T, int E, int k,
+                   int32_t* topk_ids, float* topk_w,
+                   int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_of,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_expert_ffn_nvfp4 -- the expert FFN of every routed row, in row-list order.
+ *
+ * For row-list position p of expert e (expert_offsets[e] <= p < expert_offsets[e+1]) and
+ * token t = sorted_rows[p] / k, with W[n][i] = E2M1(code) * E4M3(scale[n][i/16]) (exact):
+ *   G = gate_ts[e] * (x[t] . W_gate[e]^T)      fp32 accumulation     [f]
+ *   U = up_ts[e]   * (x[t] . W_up[e]^T)                                [f]
+ *   H = bf16_rne(silu(G) * U)                  silu(g) = g / (1 + exp(-g))
+ *   y_rows[p] = down_ts[e] * (H . W_down[e]^T) fp32, not rounded       [d]
+ * x is bf16 [T][d]; y_rows is fp32 [T*k][d]. expert_offsets / sorted_rows are the
+ * device outputs of moe_route_topk for the same T, E, k.
+ * Sizes: 1 <= T, d and f multiples of 32 (>= 32), 1 <= E <= 1024, 1 <= k <= min(E, 32).
+ * Workspace: at least moe_expert_ffn_nvfp4_workspace(T, d, f, E, k) bytes (holds H).
+ */
+size_t moe_expert_ffn_nvfp4_workspace(int T, int d, int f, int E, int k);
+int moe_expert_ffn_nvfp4(const uint16_t* x, int T, int d, int f, int E, int k,
+                         const moe_nvfp4_experts* w,
+                         const int32_t* expert_offsets, const int32_t* sorted_rows,
+                         float* y_rows, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_combine -- out[t][c] = bf16_rne( sum_{j=0..k-1} topk_w[t][j] * y_rows[row_of[t*k+j]][c] ),
+ * summed in fp32 in j order (so the result is deterministic), rounded once.
+ * Sizes: 1 <= T, 1 <= k <= 32, d a multiple of 32 (>= 32).
+ */
+int moe_combine(const float* y_rows, const int32_t* row_of, const float* topk_w,
+                int T, int k, int d, uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * mxfp8_gemm -- y[m][n] = bf16_rne( sum_i x[m][i] * W[n][i] ), fp32 accumulation,
+ * W[n][i] = E4M3(w[n][i]) * 2^(s[n][i/32] - 127) (exact in bf16 for the scales in use).
+ * x bf16 [M][K], w E4M3 [N][K], s E8M0 [N][K/32], y bf16 [M][N].
+ * Sizes: M, N >= 1, K a multiple of 32 (>= 32).
+ */
+int mxfp8_gemm(const uint16_t* x, int M, int N, int K,
+               const uint8_t* w, const uint8_t* s, uint16_t* y, void* stream);
+
+/* Name of a status code ("MOE_OK", "MOE_E_SHAPE", ...); never NULL. */
+const char* moe_status_string(int status);
+/* Text of the last HIP error seen by a call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_NVFP4_H */

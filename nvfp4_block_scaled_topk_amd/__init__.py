@@ -1,0 +1,248 @@
+"""Routed NVFP4 mixture-of-experts FFN and MXFP8 projection for AMD Instinct MI355X.
+
+A thin Python binding over the C ABI of libmoe_nvfp4.so (include/moe_nvfp4.h):
+argument marshalling only. Every step of the layer runs in the library's HIP
+kernels; torch supplies device memory and the current stream. There is no CPU
+fallback: without the built library every call raises.
+
+    ids, w, offsets, sorted_rows, row_of = route_topk(logits, k)
+    y_rows = expert_ffn_nvfp4(x, experts, offsets, sorted_rows, k)
+    out = combine(y_rows, row_of, w)
+    y = mxfp8_gemm(x, w_e4m3, s_e8m0)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_nvfp4.so")
+
+STATUS_NAMES = {0: "MOE_OK", 1: "MOE_E_NULL", 2: "MOE_E_SHAPE", 3: "MOE_E_ALIGN",
+                4: "MOE_E_WORKSPACE", 5: "MOE_E_LAUNCH"}
+
+EXPORTED_SYMBOLS = (
+    "moe_route_topk_workspace", "moe_route_topk", "moe_expert_ffn_nvfp4_workspace",
+    "moe_expert_ffn_nvfp4", "moe_combine", "mxfp8_gemm", "moe_status_string", "moe_last_error",
+)
+
+
+class MoEError(RuntimeError):
+    """A non-zero status from the library, named."""
+
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        name = STATUS_NAMES.get(status, f"status {status}")
+        super().__init__(f"{where}: {name}" + (f" ({detail})" if detail else ""))
+
+
+class _Experts(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("gate_q", "gate_s", "gate_ts", "up_q", "up_s", "up_ts", "down_q", "down_s", "down_ts")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m nvfp4_block_scaled_topk_amd.build` (there is no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.moe_route_topk_workspace.argtypes = [i32, i32, i32]
+    L.moe_route_topk_workspace.restype = sz
+    L.moe_route_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_route_topk.restype = i32
+    L.moe_expert_ffn_nvfp4_workspace.argtypes = [i32, i32, i32, i32, i32]
+    L.moe_expert_ffn_nvfp4_workspace.restype = sz
+    L.moe_expert_ffn_nvfp4.argtypes = [vp, i32, i32, i32, i32, i32, ctypes.POINTER(_Experts), vp, vp, vp,
+                                       vp, sz, vp]
+    L.moe_expert_ffn_nvfp4.restype = i32
+    L.moe_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
+    L.moe_combine.restype = i32
+    L.mxfp8_gemm.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
+    L.mxfp8_gemm.restype = i32
+    L.moe_status_string.argtypes = [i32]
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_last_error.argtypes = []
+    L.moe_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        detail = lib().moe_last_error().decode() if status == 5 else ""
+        raise MoEError(status, where, detail)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype, name: str, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+@dataclass
+class NVFP4Experts:
+    """E routed experts as stored: uint8 codes / E4M3 scales, fp32 tensor scales.
+
+    gate_q, up_q: [E, f, d/2]; gate_s, up_s: [E, f, d/16]; down_q: [E, d, f/2];
+    down_s: [E, d, f/16]; gate_ts, up_ts, down_ts: [E] float32.
+    """
+
+    gate_q: torch.Tensor
+    gate_s: torch.Tensor
+    gate_ts: torch.Tensor
+    up_q: torch.Tensor
+    up_s: torch.Tensor
+    up_ts: torch.Tensor
+    down_q: torch.Tensor
+    down_s: torch.Tensor
+    down_ts: torch.Tensor
+
+    @property
+    def E(self):
+        return self.gate_q.shape[0]
+
+    @property
+    def f(self):
+        return self.gate_q.shape[1]
+
+    @property
+    def d(self):
+        return self.gate_q.shape[2] * 2
+
+    def check(self):
+        E, f, d = self.E, self.f, self.d
+        _dev(self.gate_q, torch.uint8, "gate_q", (E, f, d // 2))
+        _dev(self.up_q, torch.uint8, "up_q", (E, f, d // 2))
+        _dev(self.gate_s, torch.uint8, "gate_s", (E, f, d // 16))
+        _dev(self.up_s, torch.uint8, "up_s", (E, f, d // 16))
+        _dev(self.down_q, torch.uint8, "down_q", (E, d, f // 2))
+        _dev(self.down_s, torch.uint8, "down_s", (E, d, f // 16))
+        for n in ("gate_ts", "up_ts", "down_ts"):
+            _dev(getattr(self, n), torch.float32, n, (E,))
+
+    def c_struct(self) -> _Experts:
+        return _Experts(*[getattr(self, n).data_ptr() for n in
+                          ("gate_q", "gate_s", "gate_ts", "up_q", "up_s", "up_ts", "down_q", "down_s", "down_ts")])
+
+    @classmethod
+    def from_numpy(cls, inp, device="cuda"):
+        """Upload the expert arrays of a workloads.MoEInputs-like object."""
+        def t(a):
+            return torch.from_numpy(a).to(device)
+        return cls(*[t(getattr(inp, n)) for n in
+                     ("gate_q", "gate_s", "gate_ts", "up_q", "up_s", "up_ts", "down_q", "down_s", "down_ts")])
+
+
+def route_topk_workspace(T: int, E: int, k: int) -> int:
+    return int(lib().moe_route_topk_workspace(T, E, k))
+
+
+def route_topk(logits: torch.Tensor, k: int, out=None, workspace=None):
+    """Top-k routing and row lists. Returns (ids int32 [T,k], w fp32 [T,k],
+    offsets int32 [E+1], sorted_rows int32 [T*k], row_of int32 [T*k])."""
+    T, E = logits.shape
+    lp = _dev(logits, torch.float32, "logits")
+    dev = logits.device
+    if out is None:
+        out = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32, device=dev),
+               torch.empty((E + 1,), dtype=torch.int32, device=dev), torch.empty((T * k,), dtype=torch.int32, device=dev),
+               torch.empty((T * k,), dtype=torch.int32, device=dev))
+    ids, w, off, srows, rof = out
+    need = route_topk_workspace(T, E, k)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    wsp = workspace.data_ptr() if workspace is not None else None
+    wsb = workspace.numel() if workspace is not None else 0
+    st = lib().moe_route_topk(lp, T, E, k, _dev(ids, torch.int32, "ids", (T, k)), _dev(w, torch.float32, "w", (T, k)),
+                              _dev(off, torch.int32, "offsets", (E + 1,)), _dev(srows, torch.int32, "sorted_rows", (T * k,)),
+                              _dev(rof, torch.int32, "row_of", (T * k,)), wsp, wsb, _stream(logits))
+    _check(st, "moe_route_topk")
+    return ids, w, off, srows, rof
+
+
+def expert_ffn_workspace(T: int, d: int, f: int, E: int, k: int) -> int:
+    return int(lib().moe_expert_ffn_nvfp4_workspace(T, d, f, E, k))
+
+
+def expert_ffn_nvfp4(x: torch.Tensor, experts: NVFP4Experts, offsets: torch.Tensor, sorted_rows: torch.Tensor,
+                     k: int, out=None, workspace=None, check: bool = True):
+    """Expert FFN of every routed row; x is bf16 [T, d] (torch.bfloat16 or its
+    uint16/int16 bits). Returns y_rows fp32 [T*k, d] in row-list order."""
+    if x.dtype in (torch.uint16, torch.int16):
+        x = x.view(torch.bfloat16)
+    T, d = x.shape
+    E, f = experts.E, experts.f
+    if experts.d != d:
+        raise ValueError(f"x has d={d}, experts have d={experts.d}")
+    if check:
+        experts.check()
+    dev = x.device
+    if out is None:
+        out = torch.empty((T * k, d), dtype=torch.float32, device=dev)
+    need = expert_ffn_workspace(T, d, f, E, k)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    ex = experts.c_struct()
+    st = lib().moe_expert_ffn_nvfp4(_dev(x, torch.bfloat16, "x"), T, d, f, E, k, ctypes.byref(ex),
+                                    _dev(offsets, torch.int32, "offsets", (E + 1,)),
+                                    _dev(sorted_rows, torch.int32, "sorted_rows", (T * k,)),
+                                    _dev(out, torch.float32, "y_rows", (T * k, d)), workspace.data_ptr(),
+                                    workspace.numel(), _stream(x))
+    _check(st, "moe_expert_ffn_nvfp4")
+    return out
+
+
+def combine(y_rows: torch.Tensor, row_of: torch.Tensor, w: torch.Tensor, out=None):
+    """out bf16 [T, d] = bf16_rne(sum_j w[t, j] * y_rows[row_of[t*k + j]])."""
+    T, k = w.shape
+    d = y_rows.shape[1]
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.bfloat16, device=y_rows.device)
+    st = lib().moe_combine(_dev(y_rows, torch.float32, "y_rows", (T * k, d)), _dev(row_of, torch.int32, "row_of", (T * k,)),
+                           _dev(w, torch.float32, "w", (T, k)), T, k, d, _dev(out, torch.bfloat16, "out", (T, d)),
+                           _stream(y_rows))
+    _check(st, "moe_combine")
+    return out
+
+
+def moe_layer(x: torch.Tensor, logits: torch.Tensor, experts: NVFP4Experts, k: int):
+    """Route, expert FFN, combine: the whole routed MoE FFN. Returns out bf16 [T, d]."""
+    ids, w, off, srows, rof = route_topk(logits, k)
+    y_rows = expert_ffn_nvfp4(x, experts, off, srows, k)
+    return combine(y_rows, rof, w)
+
+
+def mxfp8_gemm(x: torch.Tensor, w: torch.Tensor, s: torch.Tensor, out=None):
+    """y bf16 [M, N] = x . W^T with W = E4M3(w) * 2^(s - 127) per 32-element block."""
+    if x.dtype in (torch.uint16, torch.int16):
+        x = x.view(torch.bfloat16)
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    st = lib().mxfp8_gemm(_dev(x, torch.bfloat16, "x"), M, N, K, _dev(w, torch.uint8, "w", (N, K)),
+                          _dev(s, torch.uint8, "s", (N, K // 32)), _dev(out, torch.bfloat16, "y", (M, N)),
+                          _stream(x))
+    _check(st, "mxfp8_gemm")
+    return out

@@ -1,0 +1,152 @@
+// abi.cpp -- the C ABI: argument checks on the host (no HIP call before they pass),
+// path choice, launches. See include/moe_nvfp4.h for the contract of each entry point.
+#include "../../include/moe_nvfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int launch_status(hipError_t err) {
+  if (err == hipSuccess) return MOE_OK;
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s", hipGetErrorString(err));
+  return MOE_E_LAUNCH;
+}
+
+bool route_shape_ok(int T, int E, int k) {
+  return T >= 1 && E >= 1 && E <= 1024 && k >= 1 && k <= 32 && k <= E &&
+         (long long)T * k < (1LL << 31);
+}
+
+bool ffn_shape_ok(int T, int d, int f, int E, int k) {
+  return route_shape_ok(T, E, k) && d >= 32 && f >= 32 && d % 32 == 0 && f % 32 == 0 &&
+         (long long)T * k * (long long)(d > f ? d : f) < (1LL << 40);
+}
+
+constexpr size_t kWsAlign = 256;
+size_t round_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+}  // namespace
+
+namespace moe {
+size_t ffn_workspace_bytes(int T, int d, int f, int E, int k) {
+  (void)d;
+  (void)E;
+  return round_up((size_t)T * k * f * sizeof(uint16_t));
+}
+}  // namespace moe
+
+extern "C" {
+
+size_t moe_route_topk_workspace(int T, int E, int k) {
+  if (!route_shape_ok(T, E, k)) return 0;
+  const size_t b = moe::route_workspace_bytes(T, E, k);
+  return b ? round_up(b) : 0;
+}
+
+int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
+                   int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_of, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!logits || !topk_ids || !topk_w || !expert_offsets || !sorted_rows || !row_of) return MOE_E_NULL;
+  if (!route_shape_ok(T, E, k)) return MOE_E_SHAPE;
+  if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(expert_offsets) ||
+      !aligned16(sorted_rows) || !aligned16(row_of))
+    return MOE_E_ALIGN;
+  const size_t need = moe_route_topk_workspace(T, E, k);
+  if (need) {
+    if (!workspace || workspace_bytes < need) return MOE_E_WORKSPACE;
+    if (!aligned16(workspace)) return MOE_E_ALIGN;
+  }
+  return launch_status(moe::launch_route(logits, T, E, k, topk_ids, topk_w, expert_offsets, sorted_rows,
+                                         row_of, need ? workspace : nullptr,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_expert_ffn_nvfp4_workspace(int T, int d, int f, int E, int k) {
+  if (!ffn_shape_ok(T, d, f, E, k)) return 0;
+  return moe::ffn_workspace_bytes(T, d, f, E, k);
+}
+
+int moe_expert_ffn_nvfp4(const uint16_t* x, int T, int d, int f, int E, int k, const moe_nvfp4_experts* w,
+                         const int32_t* expert_offsets, const int32_t* sorted_rows, float* y_rows,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !w || !expert_offsets || !sorted_rows || !y_rows) return MOE_E_NULL;
+  if (!w->gate_q || !w->gate_s || !w->gate_ts || !w->up_q || !w->up_s || !w->up_ts || !w->down_q ||
+      !w->down_s || !w->down_ts)
+    return MOE_E_NULL;
+  if (!ffn_shape_ok(T, d, f, E, k)) return MOE_E_SHAPE;
+  const void* ptrs[] = {x, expert_offsets, sorted_rows, y_rows, w->gate_q, w->gate_s, w->gate_ts, w->up_q,
+                        w->up_s, w->up_ts, w->down_q, w->down_s, w->down_ts};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_E_ALIGN;
+  const size_t need = moe_expert_ffn_nvfp4_workspace(T, d, f, E, k);
+  if (!workspace || workspace_bytes < need) return MOE_E_WORKSPACE;
+  if (!aligned16(workspace)) return MOE_E_ALIGN;
+  moe::FFNArgs a;
+  a.x = x;
+  a.T = T;
+  a.d = d;
+  a.f = f;
+  a.E = E;
+  a.k = k;
+  a.gate_q = w->gate_q;
+  a.gate_s = w->gate_s;
+  a.up_q = w->up_q;
+  a.up_s = w->up_s;
+  a.down_q = w->down_q;
+  a.down_s = w->down_s;
+  a.gate_ts = w->gate_ts;
+  a.up_ts = w->up_ts;
+  a.down_ts = w->down_ts;
+  a.offsets = expert_offsets;
+  a.sorted_rows = sorted_rows;
+  a.y_rows = y_rows;
+  a.h = static_cast<uint16_t*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // a token routes to k distinct experts, so an expert has at most T rows: with
+  // T <= 16 every expert's rows fit one decode tile
+  if (T <= moe::kDecodeMaxRows) return launch_status(moe::launch_ffn_decode(a, st));
+  return launch_status(moe::launch_ffn_prompt(a, st));
+}
+
+int moe_combine(const float* y_rows, const int32_t* row_of, const float* topk_w, int T, int k, int d,
+                uint16_t* out, void* stream) {
+  if (!y_rows || !row_of || !topk_w || !out) return MOE_E_NULL;
+  if (T < 1 || k < 1 || k > 32 || d < 32 || d % 32 != 0 || (long long)T * k >= (1LL << 31)) return MOE_E_SHAPE;
+  if (!aligned16(y_rows) || !aligned16(row_of) || !aligned16(topk_w) || !aligned16(out)) return MOE_E_ALIGN;
+  return launch_status(moe::launch_combine(y_rows, row_of, topk_w, T, k, d, out, static_cast<hipStream_t>(stream)));
+}
+
+int mxfp8_gemm(const uint16_t* x, int M, int N, int K, const uint8_t* w, const uint8_t* s, uint16_t* y,
+               void* stream) {
+  if (!x || !w || !s || !y) return MOE_E_NULL;
+  if (M < 1 || N < 1 || K < 32 || K % 32 != 0 || (long long)M * K >= (1LL << 40) ||
+      (long long)N * K >= (1LL << 40))
+    return MOE_E_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(s) || !aligned16(y)) return MOE_E_ALIGN;
+  return launch_status(moe::launch_mxfp8(x, M, N, K, w, s, y, static_cast<hipStream_t>(stream)));
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_E_NULL: return "MOE_E_NULL";
+    case MOE_E_SHAPE: return "MOE_E_SHAPE";
+    case MOE_E_ALIGN: return "MOE_E_ALIGN";
+    case MOE_E_WORKSPACE: return "MOE_E_WORKSPACE";
+    case MOE_E_LAUNCH: return "MOE_E_LAUNCH";
+    default: return "MOE_E_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error; }
+
+}  // extern "C"

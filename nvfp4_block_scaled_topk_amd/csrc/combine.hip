@@ -1,0 +1,52 @@
+// combine.hip -- the router-weighted sum of each token's expert rows.
+//
+// The pages fold the card sum of the expert outputs into the combine [FP4-Local
+// checkpoints on DGX Spark, §4 Round 1, #701] and keep the rows wide until that sum
+// ([same page, §4 remaining items, #914]: rows rounded to nearest even, the block's
+// sum widening them). Here the expert rows stay fp32 and are summed in fp32 in the
+// token's top-k order, then rounded once to bf16: out[t] = bf16_rne(sum_j w_tj * y[row_of[t*k+j]]).
+// Pure streaming: each thread owns 4 consecutive columns of one token (128-bit loads).
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace moe {
+
+constexpr int kCombineThreads = 256;
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+    const float* __restrict__ y_rows, const int32_t* __restrict__ row_of,
+    const float* __restrict__ w, int T, int k, int d, uint16_t* __restrict__ out) {
+  __shared__ int s_row[32];
+  __shared__ float s_w[32];
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) {
+    s_row[threadIdx.x] = row_of[(size_t)t * k + threadIdx.x];
+    s_w[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
+  }
+  __syncthreads();
+  const int c = (blockIdx.y * kCombineThreads + threadIdx.x) * 4;
+  if (c >= d) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const float4 v = *reinterpret_cast<const float4*>(y_rows + (size_t)s_row[j] * d + c);
+    const float wj = s_w[j];
+    acc.x = fmaf(wj, v.x, acc.x);
+    acc.y = fmaf(wj, v.y, acc.y);
+    acc.z = fmaf(wj, v.z, acc.z);
+    acc.w = fmaf(wj, v.w, acc.w);
+  }
+  uint2 o;
+  o.x = (uint32_t)bf16_rne(acc.x) | ((uint32_t)bf16_rne(acc.y) << 16);
+  o.y = (uint32_t)bf16_rne(acc.z) | ((uint32_t)bf16_rne(acc.w) << 16);
+  *reinterpret_cast<uint2*>(out + (size_t)t * d + c) = o;
+}
+
+hipError_t launch_combine(const float* y_rows, const int32_t* row_of, const float* w, int T, int k,
+                          int d, uint16_t* out, hipStream_t stream) {
+  dim3 grid(T, (d / 4 + kCombineThreads - 1) / kCombineThreads);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombineThreads), 0, stream, y_rows, row_of, w, T,
+                     k, d, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

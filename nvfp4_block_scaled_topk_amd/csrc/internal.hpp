@@ -1,0 +1,45 @@
+// internal.hpp -- launchers behind the C ABI (host side). Every launcher assumes its
+// arguments were validated by abi.cpp and only enqueues kernels on `stream`.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+struct moe_nvfp4_experts;
+
+namespace moe {
+
+// routing
+size_t route_workspace_bytes(int T, int E, int k);
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                        int32_t* offsets, int32_t* sorted_rows, int32_t* row_of, void* ws,
+                        hipStream_t stream);
+
+// expert FFN: H (bf16, [T*k][f]) lives in the caller's workspace
+struct FFNArgs {
+  const uint16_t* x;
+  int T, d, f, E, k;
+  const uint8_t *gate_q, *gate_s, *up_q, *up_s, *down_q, *down_s;
+  const float *gate_ts, *up_ts, *down_ts;
+  const int32_t* offsets;
+  const int32_t* sorted_rows;
+  float* y_rows;
+  uint16_t* h;
+};
+// The decode path keeps every expert's rows in one 16-row MFMA tile.
+constexpr int kDecodeMaxRows = 16;
+size_t ffn_workspace_bytes(int T, int d, int f, int E, int k);
+hipError_t launch_ffn_decode(const FFNArgs& a, hipStream_t stream);
+hipError_t launch_ffn_prompt(const FFNArgs& a, hipStream_t stream);
+
+// combine
+hipError_t launch_combine(const float* y_rows, const int32_t* row_of, const float* w, int T,
+                          int k, int d, uint16_t* out, hipStream_t stream);
+
+// MXFP8
+hipError_t launch_mxfp8(const uint16_t* x, int M, int N, int K, const uint8_t* w,
+                        const uint8_t* s, uint16_t* y, hipStream_t stream);
+
+}  // namespace moe

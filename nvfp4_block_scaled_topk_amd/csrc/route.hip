@@ -1,0 +1,226 @@
+// route.hip -- top-k routing of a whole token batch and the per-expert row lists.
+//
+// A whole batch is routed in one run so every selected expert is read once for all
+// of its rows [FP4-Local checkpoints on DGX Spark, §4 Round 1, #740 and #808]. The
+// weights are the renormalized softmax over the selected logits (the router
+// normalization policy the pages name, [bloomery 0.3.9 release notes, Fixed, #772],
+// read as softmax -> top-k -> renormalize).
+//
+// Kernel 1 (one wave per token, 64 tokens per block): the k best (logit desc, index
+// asc) by k rounds of a wave-wide argmax over the lane-held logits; the weights; then,
+// per block, each assignment's rank among the block's earlier assignments to the same
+// expert and the block's per-expert counts. Kernel 2 (one block): per-expert running
+// sums over the blocks, the exclusive scan over experts, and the stable scatter
+// p = offset[e] + (earlier blocks' count of e) + rank. No atomics: the row lists are
+// the same bits on every run. A batch of at most 64 tokens runs as one launch.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace moe {
+
+constexpr int kRouteTokensPerBlock = 64;
+constexpr int kRouteThreads = 256;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxExperts = 1024;
+
+__device__ __forceinline__ bool route_better(float a, int ia, float b, int ib) {
+  return a > b || (a == b && ia < ib);
+}
+
+// Exclusive scan of s[0..n) in LDS by one block (n <= 1024, blockDim 256 or 1024);
+// writes s_out[0..n], s_out[n] = total.
+__device__ void block_exclusive_scan(const int* s_in, int* s_out, int n, int* s_tmp) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  // chunked: each thread sums a contiguous chunk, scan of chunk sums, then expand
+  const int per = (n + nt - 1) / nt;
+  const int b0 = tid * per;
+  int sum = 0;
+  for (int i = 0; i < per; ++i) {
+    int e = b0 + i;
+    if (e < n) sum += s_in[e];
+  }
+  s_tmp[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < nt; ++i) {
+      int c = s_tmp[i];
+      s_tmp[i] = run;
+      run += c;
+    }
+    s_out[n] = run;
+  }
+  __syncthreads();
+  int run = s_tmp[tid];
+  for (int i = 0; i < per; ++i) {
+    int e = b0 + i;
+    if (e < n) {
+      s_out[e] = run;
+      run += s_in[e];
+    }
+  }
+  __syncthreads();
+}
+
+template <int EPL>
+__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ topk_ids,
+    float* __restrict__ topk_w, int32_t* __restrict__ ws_rank, int32_t* __restrict__ ws_counts,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_rows,
+    int32_t* __restrict__ row_of) {
+  __shared__ int s_ids[kRouteTokensPerBlock * kMaxTopK];
+  __shared__ int s_rank[kRouteTokensPerBlock * kMaxTopK];
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_tmp[kRouteThreads];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t_begin = blockIdx.x * kRouteTokensPerBlock;
+  const int t_end = min(T, t_begin + kRouteTokensPerBlock);
+  const int ntok = t_end - t_begin;
+
+  for (int tl = wave; tl < ntok; tl += kRouteThreads / 64) {
+    const int t = t_begin + tl;
+    const float* row = logits + (size_t)t * E;
+    float v[EPL];
+    int ix[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      v[j] = e < E ? row[e] : -__builtin_inff();
+      ix[j] = e < E ? e : 0x7FFFFFFF;
+    }
+    float my_v = 0.0f;
+    int my_i = 0;
+    for (int r = 0; r < k; ++r) {
+      float bv = v[0];
+      int bi = ix[0];
+#pragma unroll
+      for (int j = 1; j < EPL; ++j)
+        if (route_better(v[j], ix[j], bv, bi)) { bv = v[j]; bi = ix[j]; }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (route_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (ix[j] == bi) { v[j] = -__builtin_inff(); ix[j] = 0x7FFFFFFF; }
+      if (lane == r) { my_v = bv; my_i = bi; }
+    }
+    // weights: softmax over the k selected logits, max-subtracted; the rounding error
+    // of l_j - l_0 is carried into the exponential to first order
+    const float m = __shfl(my_v, 0);
+    float ex = 0.0f;
+    if (lane < k) {
+      const float s = my_v - m;
+      const float bb = s - my_v;
+      const float err = (my_v - (s - bb)) + (-m - bb);
+      const float e0 = expf(s);
+      ex = fmaf(e0, err, e0);
+    }
+    float sum = ex;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (lane < k) {
+      topk_ids[(size_t)t * k + lane] = my_i;
+      topk_w[(size_t)t * k + lane] = ex / sum;
+      s_ids[tl * k + lane] = my_i;
+    }
+  }
+  __syncthreads();
+
+  // per-expert counts and ranks of this block's assignments (stable: in assignment order)
+  const int nas = ntok * k;
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+    int c = 0;
+    for (int i = 0; i < nas; ++i)
+      if (s_ids[i] == e) s_rank[i] = c++;
+    s_cnt[e] = c;
+  }
+  __syncthreads();
+
+  if (gridDim.x == 1) {
+    // whole batch in this block: scan and scatter here
+    block_exclusive_scan(s_cnt, s_off, E, s_tmp);
+    for (int e = threadIdx.x; e <= E; e += kRouteThreads) expert_offsets[e] = s_off[e];
+    for (int a = threadIdx.x; a < nas; a += kRouteThreads) {
+      const int p = s_off[s_ids[a]] + s_rank[a];
+      sorted_rows[p] = a;
+      row_of[a] = p;
+    }
+    return;
+  }
+  const size_t a0 = (size_t)t_begin * k;
+  for (int a = threadIdx.x; a < nas; a += kRouteThreads) ws_rank[a0 + a] = s_rank[a];
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) ws_counts[(size_t)blockIdx.x * E + e] = s_cnt[e];
+}
+
+__global__ __launch_bounds__(1024) void route_scan_scatter_kernel(
+    const int32_t* __restrict__ topk_ids, int T, int E, int k, int nblocks,
+    const int32_t* __restrict__ ws_rank, int32_t* __restrict__ ws_counts,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_rows,
+    int32_t* __restrict__ row_of) {
+  __shared__ int s_tot[kMaxExperts];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_tmp[1024];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int b = 0; b < nblocks; ++b) {
+      const int c = ws_counts[(size_t)b * E + e];
+      ws_counts[(size_t)b * E + e] = run;
+      run += c;
+    }
+    s_tot[e] = run;
+  }
+  __syncthreads();
+  block_exclusive_scan(s_tot, s_off, E, s_tmp);
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) expert_offsets[e] = s_off[e];
+  const int per_block = kRouteTokensPerBlock * k;
+  const int total = T * k;
+  for (int a = threadIdx.x; a < total; a += blockDim.x) {
+    const int e = topk_ids[a];
+    const int b = a / per_block;
+    const int p = s_off[e] + ws_counts[(size_t)b * E + e] + ws_rank[a];
+    sorted_rows[p] = a;
+    row_of[a] = p;
+  }
+}
+
+size_t route_workspace_bytes(int T, int E, int k) {
+  const size_t nb = ((size_t)T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock;
+  if (nb <= 1) return 0;
+  return ((size_t)T * k + nb * (size_t)E) * sizeof(int32_t);
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                        int32_t* offsets, int32_t* sorted_rows, int32_t* row_of, void* ws,
+                        hipStream_t stream) {
+  const int nb = (T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock;
+  int32_t* ws_rank = nullptr;
+  int32_t* ws_counts = nullptr;
+  if (nb > 1) {
+    ws_rank = static_cast<int32_t*>(ws);
+    ws_counts = ws_rank + (size_t)T * k;
+  }
+  const int epl = (E + 63) / 64;
+  dim3 grid(nb), block(kRouteThreads);
+#define MOE_ROUTE_LAUNCH(N)                                                                     \
+  hipLaunchKernelGGL(route_topk_kernel<N>, grid, block, 0, stream, logits, T, E, k, ids, w,     \
+                     ws_rank, ws_counts, offsets, sorted_rows, row_of)
+  if (epl <= 1) MOE_ROUTE_LAUNCH(1);
+  else if (epl <= 2) MOE_ROUTE_LAUNCH(2);
+  else if (epl <= 4) MOE_ROUTE_LAUNCH(4);
+  else if (epl <= 8) MOE_ROUTE_LAUNCH(8);
+  else MOE_ROUTE_LAUNCH(16);
+#undef MOE_ROUTE_LAUNCH
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || nb <= 1) return err;
+  hipLaunchKernelGGL(route_scan_scatter_kernel, dim3(1), dim3(1024), 0, stream, ids, T, E, k, nb,
+                     ws_rank, ws_counts, offsets, sorted_rows, row_of);
+  return hipGetLastError();
+}
+
+}  // namespace moe

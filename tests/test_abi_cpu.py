@@ -1,0 +1,113 @@
+"""The C-ABI library loads, exports every function include/moe_nvfp4.h declares,
+and refuses bad arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_block_scaled_topk_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_nvfp4.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(M.LIB_PATH), reason="library not built")
+
+OK, NULL, SHAPE, ALIGN, WS = 0, 1, 2, 3, 4
+A = 0x10000  # a 16-byte-aligned fake address: only ever passed to calls that must refuse
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert set(names) == set(M.EXPORTED_SYMBOLS), names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(M.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = M.lib()
+    for code, name in M.STATUS_NAMES.items():
+        assert L.moe_status_string(code).decode() == name
+    assert L.moe_status_string(99).decode() == "MOE_E_UNKNOWN"
+
+
+def test_route_refusals():
+    L = M.lib()
+    f = L.moe_route_topk
+    good = dict(logits=A, T=4, E=8, k=2, ids=A, w=A, off=A, sr=A, ro=A, ws=None, wsb=0, st=None)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["logits"], a["T"], a["E"], a["k"], a["ids"], a["w"], a["off"], a["sr"], a["ro"], a["ws"], a["wsb"], a["st"])
+    assert call(logits=None) == NULL
+    assert call(ro=None) == NULL
+    assert call(T=0) == SHAPE
+    assert call(E=0) == SHAPE
+    assert call(E=1025, k=2) == SHAPE
+    assert call(k=0) == SHAPE
+    assert call(k=9) == SHAPE          # k > E
+    assert call(E=64, k=33) == SHAPE   # k > 32
+    assert call(logits=A + 4) == ALIGN
+    assert call(off=A + 8) == ALIGN
+    # more than one 64-token block needs a workspace
+    need = L.moe_route_topk_workspace(65, 8, 2)
+    assert need > 0
+    assert L.moe_route_topk_workspace(64, 8, 2) == 0
+    assert call(T=65) == WS
+    assert call(T=65, ws=A, wsb=need - 1) == WS
+    assert call(T=65, ws=A + 4, wsb=need) == ALIGN
+    assert L.moe_route_topk_workspace(0, 8, 2) == 0
+
+
+def test_ffn_refusals():
+    L = M.lib()
+    ex = M._Experts(*([A] * 9))
+    T, d, f, E, k = 4, 256, 128, 8, 2
+    need = L.moe_expert_ffn_nvfp4_workspace(T, d, f, E, k)
+    assert need >= T * k * f * 2 and need % 256 == 0
+
+    def call(x=A, T=T, d=d, f=f, E=E, k=k, ex=ex, off=A, sr=A, y=A, ws=A, wsb=need):
+        return L.moe_expert_ffn_nvfp4(x, T, d, f, E, k, ctypes.byref(ex) if ex is not None else None,
+                                      off, sr, y, ws, wsb, None)
+    assert call(x=None) == NULL
+    assert call(ex=None) == NULL
+    bad = M._Experts(*([A] * 8 + [0]))
+    assert call(ex=bad) == NULL
+    assert call(d=48) == SHAPE
+    assert call(f=16) == SHAPE
+    assert call(E=1025) == SHAPE
+    assert call(k=9) == SHAPE
+    assert call(T=0) == SHAPE
+    mis = M._Experts(*([A] * 4 + [A + 2] + [A] * 4))
+    assert call(ex=mis) == ALIGN
+    assert call(y=A + 4) == ALIGN
+    assert call(ws=None) == WS
+    assert call(wsb=need - 1) == WS
+    assert call(ws=A + 8) == ALIGN
+
+
+def test_combine_and_mxfp8_refusals():
+    L = M.lib()
+    assert L.moe_combine(None, A, A, 4, 2, 64, A, None) == NULL
+    assert L.moe_combine(A, A, A, 4, 33, 64, A, None) == SHAPE
+    assert L.moe_combine(A, A, A, 4, 2, 48, A, None) == SHAPE
+    assert L.moe_combine(A, A, A + 4, 4, 2, 64, A, None) == ALIGN
+    assert L.mxfp8_gemm(A, 1, 16, 64, None, A, A, None) == NULL
+    assert L.mxfp8_gemm(A, 1, 16, 48, A, A, A, None) == SHAPE
+    assert L.mxfp8_gemm(A, 0, 16, 64, A, A, A, None) == SHAPE
+    assert L.mxfp8_gemm(A, 1, 16, 64, A, A + 1, A, None) == ALIGN
+
+
+def test_last_error_empty_before_any_launch():
+    assert M.lib().moe_last_error().decode() == ""

@@ -1,0 +1,164 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Routing indices, offsets and row lists must match bit for bit; every bf16 output
+element must be within |gpu - oracle| <= 2e-3 + 2e-2 |oracle| (strict) or within
+the documented slack (explained), never beyond (fail)."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import band, formats as F, moe, mxfp8 as omx
+
+from gpu_util import check_layer_full, check_layer_sampled, check_routing, run_moe, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import nvfp4_block_scaled_topk_amd as M
+    M.lib()
+
+
+# ---------------------------------------------------------------- routing
+@pytest.mark.parametrize("name", ["tiny", "decode", "prompt", "long_prompt"])
+def test_route_configs(name):
+    inp = workloads.moe_config(name, experts=False)
+    say(f"route {name}: T={inp.T} E={inp.E} k={inp.k}")
+    import torch
+    import nvfp4_block_scaled_topk_amd as M
+    logits = torch.from_numpy(inp.logits).cuda()
+    ids, w, off, sr, ro = M.route_topk(logits, inp.k)
+    torch.cuda.synchronize()
+    res = dict(ids=ids.cpu().numpy(), w=w.cpu().numpy(), offsets=off.cpu().numpy(),
+               sorted_rows=sr.cpu().numpy(), row_of=ro.cpu().numpy())
+    check_routing(inp, res, name)
+
+
+ROUTE_EDGE = [(1, 1, 1), (1, 8, 8), (3, 64, 32), (64, 7, 3), (65, 7, 3), (130, 1024, 32),
+              (200, 65, 1), (129, 128, 8), (1000, 256, 8), (37, 33, 32)]
+
+
+@pytest.mark.parametrize("T,E,k", ROUTE_EDGE)
+@pytest.mark.parametrize("ties", [False, True])
+def test_route_edges(T, E, k, ties):
+    import torch
+    import nvfp4_block_scaled_topk_amd as M
+    inp = workloads.make_moe(T, 32, 32, E, k, seed=3, config_id=50, zipf=not ties, experts=False)
+    if ties:
+        lg = np.round(inp.logits * 2).astype(np.float32)
+        lg[lg == 0] = np.where(np.arange((lg == 0).sum()) % 2 == 0, -0.0, 0.0)
+        inp.logits = lg
+    say(f"route edge T={T} E={E} k={k} ties={ties}")
+    ids, w, off, sr, ro = M.route_topk(torch.from_numpy(inp.logits).cuda(), k)
+    torch.cuda.synchronize()
+    res = dict(ids=ids.cpu().numpy(), w=w.cpu().numpy(), offsets=off.cpu().numpy(),
+               sorted_rows=sr.cpu().numpy(), row_of=ro.cpu().numpy())
+    check_routing(inp, res, f"T{T}E{E}k{k}")
+
+
+# ---------------------------------------------------------------- whole layer
+def test_layer_tiny():
+    inp = workloads.moe_config("tiny")
+    say("layer tiny")
+    check_layer_full(inp, run_moe(inp), "tiny")
+
+
+def test_layer_decode():
+    inp = workloads.moe_config("decode")
+    say("layer decode (T=4, d=2048, f=768, E=128, k=8)")
+    check_layer_full(inp, run_moe(inp), "decode")
+
+
+SMALL = [
+    (1, 32, 32, 1, 1),       # single row; K tails only
+    (3, 96, 64, 5, 2),       # decode path, K tail 96
+    (16, 160, 96, 6, 3),     # decode path at its 16-row limit, ragged K
+    (17, 160, 96, 6, 3),     # prompt path just above it
+    (100, 224, 160, 12, 4),  # prompt path, ragged K and features
+    (300, 256, 128, 4, 2),   # prompt path, experts with > 128 rows
+    (40, 64, 32, 64, 8),     # many experts, few rows each
+    (8, 2048, 768, 128, 8),  # decode shape with 8 tokens
+]
+
+
+@pytest.mark.parametrize("T,d,f,E,k", SMALL)
+def test_layer_small(T, d, f, E, k):
+    inp = workloads.make_moe(T, d, f, E, k, seed=1, config_id=60, zipf=True)
+    say(f"layer small T={T} d={d} f={f} E={E} k={k}")
+    check_layer_full(inp, run_moe(inp), f"T{T}d{d}f{f}E{E}k{k}")
+
+
+def test_layer_prompt_sampled():
+    inp = workloads.moe_config("prompt")
+    say("layer prompt (T=512, d=3072, f=1536, E=128, k=8), sampled tokens")
+    res = run_moe(inp)
+    toks = np.random.default_rng(0).choice(inp.T, size=24, replace=False)
+    check_layer_sampled(inp, res, np.sort(toks), "prompt")
+
+
+def test_layer_long_prompt_sampled():
+    inp = workloads.moe_config("long_prompt")
+    say("layer long_prompt (T=4096, d=7168, f=2048, E=256, k=8), sampled tokens")
+    res = run_moe(inp)
+    toks = np.random.default_rng(1).choice(inp.T, size=4, replace=False)
+    check_layer_sampled(inp, res, np.sort(toks), "long_prompt")
+
+
+def test_layer_deterministic_and_permutation():
+    """Same inputs give the same bits twice; permuting the tokens permutes the
+    outputs bit for bit (a row's result does not depend on its neighbours)."""
+    for (T, d, f, E, k) in [(4, 256, 128, 8, 2), (60, 256, 128, 8, 2)]:
+        inp = workloads.make_moe(T, d, f, E, k, seed=9, config_id=61, zipf=True)
+        a = run_moe(inp)
+        b = run_moe(inp)
+        assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["y_rows"], b["y_rows"])
+        perm = np.random.default_rng(2).permutation(T)
+        inp2 = workloads.make_moe(T, d, f, E, k, seed=9, config_id=61, zipf=True)
+        inp2.x = inp2.x[perm].copy()
+        inp2.logits = inp2.logits[perm].copy()
+        c = run_moe(inp2)
+        assert np.array_equal(c["out"], a["out"][perm])
+        assert np.array_equal(c["ids"], a["ids"][perm])
+
+
+# ---------------------------------------------------------------- MXFP8
+def _run_mxfp8(inp):
+    import torch
+    import nvfp4_block_scaled_topk_amd as M
+    x = torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16)
+    w = torch.from_numpy(inp.w).cuda()
+    s = torch.from_numpy(inp.s).cuda()
+    y = M.mxfp8_gemm(x, w, s)
+    torch.cuda.synchronize()
+    return y.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+MX_SMALL = [(1, 16, 32), (1, 100, 96), (3, 128, 4096), (16, 48, 160), (17, 130, 96), (200, 256, 288),
+            (5, 33, 64)]
+
+
+@pytest.mark.parametrize("M_,N,K", MX_SMALL)
+def test_mxfp8_small(M_, N, K):
+    inp = workloads.make_mxfp8(M_, N, K, seed=2, config_id=70)
+    say(f"mxfp8 M={M_} N={N} K={K}")
+    got = _run_mxfp8(inp)
+    _, ref, mass = omx.mxfp8_gemm(inp.x, inp.w, inp.s)
+    rep = band.classify(got, ref, mass)
+    say(f"[mxfp8 {M_}x{N}x{K}] {rep}")
+    assert rep.ok(), str(rep)
+
+
+@pytest.mark.parametrize("M_", [1, 512])
+def test_mxfp8_config(M_):
+    inp = workloads.mxfp8_config(M_)
+    say(f"mxfp8 config M={M_} N={inp.N} K={inp.K}")
+    got = _run_mxfp8(inp)
+    rows = np.arange(M_) if M_ == 1 else np.sort(np.random.default_rng(3).choice(M_, 6, replace=False))
+    _, ref, mass = omx.mxfp8_gemm(inp.x, inp.w, inp.s, rows=rows)
+    rep = band.classify(got[rows], ref, mass)
+    say(f"[mxfp8 config M={M_}] {rep}")
+    assert rep.ok(), str(rep)
