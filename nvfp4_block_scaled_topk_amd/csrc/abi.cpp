@@ -26,9 +26,13 @@ bool route_shape_ok(int T, int E, int k) {
          (long long)T * k < (1LL << 31);
 }
 
+// The kernels address activations and one expert's weight matrix through 32-bit
+// buffer offsets: x (T*d bf16), one projection (f*d/2 bytes) and H (T*k*f bf16) must
+// each stay below 2 GiB.
 bool ffn_shape_ok(int T, int d, int f, int E, int k) {
   return route_shape_ok(T, E, k) && d >= 32 && f >= 32 && d % 32 == 0 && f % 32 == 0 &&
-         (long long)T * k * (long long)(d > f ? d : f) < (1LL << 40);
+         (long long)T * d * 2 < (1LL << 31) && (long long)f * d / 2 < (1LL << 31) &&
+         (long long)T * k * f * 2 < (1LL << 31) && (long long)T * k * d * 4 < (1LL << 40);
 }
 
 constexpr size_t kWsAlign = 256;

@@ -27,37 +27,25 @@ __device__ __forceinline__ bool route_better(float a, int ia, float b, int ib) {
   return a > b || (a == b && ia < ib);
 }
 
-// Exclusive scan of s[0..n) in LDS by one block (n <= 1024, blockDim 256 or 1024);
-// writes s_out[0..n], s_out[n] = total.
-__device__ void block_exclusive_scan(const int* s_in, int* s_out, int n, int* s_tmp) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  // chunked: each thread sums a contiguous chunk, scan of chunk sums, then expand
-  const int per = (n + nt - 1) / nt;
-  const int b0 = tid * per;
-  int sum = 0;
-  for (int i = 0; i < per; ++i) {
-    int e = b0 + i;
-    if (e < n) sum += s_in[e];
-  }
-  s_tmp[tid] = sum;
-  __syncthreads();
-  if (tid == 0) {
+// Exclusive scan of s_in[0..n) in LDS (n <= 1024) by the block's first wave, 64
+// entries a step with lane shuffles; writes s_out[0..n], s_out[n] = total.
+__device__ void block_exclusive_scan(const int* s_in, int* s_out, int n) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
     int run = 0;
-    for (int i = 0; i < nt; ++i) {
-      int c = s_tmp[i];
-      s_tmp[i] = run;
-      run += c;
+    for (int base = 0; base < n; base += 64) {
+      const int e = base + lane;
+      const int v = e < n ? s_in[e] : 0;
+      int incl = v;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      if (e < n) s_out[e] = run + incl - v;
+      run += __shfl(incl, 63);
     }
-    s_out[n] = run;
-  }
-  __syncthreads();
-  int run = s_tmp[tid];
-  for (int i = 0; i < per; ++i) {
-    int e = b0 + i;
-    if (e < n) {
-      s_out[e] = run;
-      run += s_in[e];
-    }
+    if (lane == 0) s_out[n] = run;
   }
   __syncthreads();
 }
@@ -72,7 +60,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   __shared__ int s_rank[kRouteTokensPerBlock * kMaxTopK];
   __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
-  __shared__ int s_tmp[kRouteThreads];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -144,7 +131,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
 
   if (gridDim.x == 1) {
     // whole batch in this block: scan and scatter here
-    block_exclusive_scan(s_cnt, s_off, E, s_tmp);
+    block_exclusive_scan(s_cnt, s_off, E);
     for (int e = threadIdx.x; e <= E; e += kRouteThreads) expert_offsets[e] = s_off[e];
     for (int a = threadIdx.x; a < nas; a += kRouteThreads) {
       const int p = s_off[s_ids[a]] + s_rank[a];
@@ -165,7 +152,6 @@ __global__ __launch_bounds__(1024) void route_scan_scatter_kernel(
     int32_t* __restrict__ row_of) {
   __shared__ int s_tot[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
-  __shared__ int s_tmp[1024];
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int run = 0;
     for (int b = 0; b < nblocks; ++b) {
@@ -176,7 +162,7 @@ __global__ __launch_bounds__(1024) void route_scan_scatter_kernel(
     s_tot[e] = run;
   }
   __syncthreads();
-  block_exclusive_scan(s_tot, s_off, E, s_tmp);
+  block_exclusive_scan(s_tot, s_off, E);
   for (int e = threadIdx.x; e <= E; e += blockDim.x) expert_offsets[e] = s_off[e];
   const int per_block = kRouteTokensPerBlock * k;
   const int total = T * k;
