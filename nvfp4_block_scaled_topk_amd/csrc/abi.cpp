@@ -1,6 +1,6 @@
 // abi.cpp -- the C ABI: argument checks on the host (no HIP call before they pass),
 // path choice, launches. See include/moe_nvfp4.h for the contract of each entry point.
-#include "../../include/moe_nvfp4.h"
+#include "moe_nvfp4.h"
 
 #include <hip/hip_runtime.h>
 

@@ -35,15 +35,19 @@
 
 namespace moe {
 
-constexpr int kPromptRows = 128;                      // routed rows per tile
-constexpr int kPromptKC = 64;                         // K elements per stage
-constexpr int kPromptStages = 4;
-constexpr int kPromptXBytes = kPromptRows * kPromptKC * 2;  // 16 KB
-constexpr int kPromptWBytes = 256 * (kPromptKC / 2);        // 8 KB: 256 weight rows
-constexpr int kPromptSBytes = 256 * 2 * 4;                  // 2 KB: 2 scale pairs a row, dword slots
-constexpr int kPromptStageBytes = kPromptXBytes + kPromptWBytes + kPromptSBytes;
-constexpr int kPromptLdsBytes = kPromptStages * kPromptStageBytes;
-constexpr int kPromptThreads = 256;
+constexpr int kPromptRows = 256;        // routed rows per tile
+constexpr int kPromptKC = 64;           // K elements per activation stage
+constexpr int kBlockStages = 4;         // weight / scale block = 4 stages = 256 K elements
+constexpr int kXStageBytes = 256 * 128;     // 32 KB: 256 rows x 64 bf16
+constexpr int kWBlockBytes = 256 * 128;     // 32 KB: 256 weight rows x 256 codes
+constexpr int kSBlockBytes = 256 * 32;      // 8 KB: 256 rows x 8 scale pairs (dword slots)
+constexpr int kXOff = 0;
+constexpr int kWOff = 2 * kXStageBytes;
+constexpr int kSOff = kWOff + 2 * kWBlockBytes;
+constexpr int kPromptLdsBytes = kSOff + 2 * kSBlockBytes;  // 144 KB
+constexpr int kPromptThreads = 512;     // 8 waves, two per SIMD
+constexpr int kXDma = 4;                // activation DMA instructions per wave per stage
+constexpr int kWSDma = 8;               // weight + scale DMA instructions per wave per block
 constexpr int kMaxE = 1024;
 constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every record: reads zeros
 constexpr int kXcds = 8;
@@ -54,21 +58,20 @@ __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t word4(const u32x4& v, int s) {
-  return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
-}
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
 // One buffer->LDS DMA instruction: lane l writes `size` bytes read at byte offset
-// voff of the buffer to LDS address lds_base + l * max(size, 4).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, unsigned char* lds_base, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)lds_base, 16, voff, 0, 0, 0);
+// voff + soff of the buffer to LDS address lds_base + l * max(size, 4). soff is a
+// wave-uniform offset (the K step); lanes whose voff is kOOB read zeros.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, unsigned char* lds_base, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)lds_base, 16, voff, soff, 0, 0);
 }
-__device__ __forceinline__ void dma2(__amdgpu_buffer_rsrc_t rs, unsigned char* lds_base, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)lds_base, 2, voff, 0, 0, 0);
+__device__ __forceinline__ void dma2(__amdgpu_buffer_rsrc_t rs, unsigned char* lds_base, uint32_t voff,
+                                     uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)lds_base, 2, voff, soff, 0, 0);
 }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
@@ -77,8 +80,9 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// Per-block tile table: s_pref[e] = number of 128-row tiles of experts < e.
+// Per-block tile table: s_pref[e] = number of 256-row tiles of experts < e.
 __device__ void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int* s_pref) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
@@ -118,10 +122,15 @@ __global__ __launch_bounds__(kPromptThreads, 1) void ffn_prompt_kernel(FFNArgs a
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
+  const int wcol = wave & 3;   // weight-row group of this wave
+  const int wtok = wave >> 2;  // routed-row half of this wave
   const int l32 = lane & 31, g = lane >> 5;
   const int K = MODE == 0 ? a.d : a.f;  // contraction length
   const int N = MODE == 0 ? a.f : a.d;  // weight rows per matrix
   const int nch = (K + kPromptKC - 1) / kPromptKC;
+  // DMA slot -> 16-byte segment: slot s of a 128-byte LDS row r holds logical segment
+  // s ^ (r & 7). For the 8-lanes-a-row DMA pattern, r & 7 = lane >> 3 and s = lane & 7.
+  const int dseg = (lane & 7) ^ (lane >> 3);
 
   build_tile_prefix(a.offsets, a.E, s_pref);
   const int total_tiles = s_pref[a.E] * n_col_tiles;
@@ -135,14 +144,16 @@ __global__ __launch_bounds__(kPromptThreads, 1) void ffn_prompt_kernel(FFNArgs a
     const int mt = mt_all - s_pref[e];
     const int p0 = a.offsets[e] + mt * kPromptRows;
     const int nrows = min(kPromptRows, a.offsets[e + 1] - p0);
-    const int ntf = (nrows + 31) >> 5;  // 32-row activation fragments in use
+    // 32-row activation fragments this wave uses (0..4): rows 128*wtok .. 128*wtok + 127
+    const int ntf = min(4, max(0, (nrows - 128 * wtok + 31) >> 5));
 
-    // ---- buffer descriptors (wave-uniform)
+    // ---- buffer descriptors (wave-uniform). Weight rows 0..127 of the tile are gate
+    // rows and 128..255 up rows (gate/up launch).
     __amdgpu_buffer_rsrc_t xrs, wrs, srs;
     const size_t wslab = (size_t)N * (K / 2), sslab = (size_t)N * (K / 16);
     if (MODE == 0) {
       xrs = make_rsrc(a.x, (uint32_t)((size_t)a.T * a.d * 2));
-      const bool up = wave >= 2;  // waves 0,1 stage the gate rows, waves 2,3 the up rows
+      const bool up = wave >= 4;  // waves 0-3 stage the gate rows, waves 4-7 the up rows
       wrs = make_rsrc((up ? a.up_q : a.gate_q) + (size_t)e * wslab, (uint32_t)wslab);
       srs = make_rsrc((up ? a.up_s : a.gate_s) + (size_t)e * sslab, (uint32_t)sslab);
     } else {
@@ -151,59 +162,44 @@ __global__ __launch_bounds__(kPromptThreads, 1) void ffn_prompt_kernel(FFNArgs a
       srs = make_rsrc(a.down_s + (size_t)e * sslab, (uint32_t)sslab);
     }
 
-    // ---- per-lane DMA sources for this tile (byte offsets at K0 = 0)
-    // activations: 4 instructions, slot s = wave*256 + i*64 + lane -> row s/8, slot s%8
-    uint32_t xoff[4];
-    int xseg[4];
+    // ---- per-lane DMA sources. Instruction i of wave w covers LDS rows 32w + 8i + lane/8
+    // (activation rows, and weight / scale rows of the tile), 8 lanes a row.
+    uint32_t xoff[4], woff[4], soff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int s = wave * 256 + i * 64 + lane;
-      const int r = s >> 3;
-      const int j = (s & 7) ^ (r & 7);  // logical 16-byte segment held by this slot
-      xseg[i] = j;
+      const int r = wave * 32 + i * 8 + (lane >> 3);
       if (r < nrows) {
         const uint32_t rb = MODE == 0 ? (uint32_t)(a.sorted_rows[p0 + r] / a.k) * (uint32_t)(a.d * 2)
                                       : (uint32_t)(r * a.f * 2);
-        xoff[i] = rb + j * 16;
+        xoff[i] = rb + dseg * 16;
       } else {
         xoff[i] = kOOB;
       }
-    }
-    // weights / scales: 2 instructions each, slot s = wave*128 + i*64 + lane -> row s/2, half s%2
-    uint32_t woff[2], soff[2];
-    int whalf[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int s = wave * 128 + i * 64 + lane;
-      const int row = s >> 1, h = s & 1;
-      const int n = MODE == 0 ? ct * 128 + (row & 127) : ct * 256 + row;
-      whalf[i] = h;
+      const int n = MODE == 0 ? ct * 128 + (r & 127) : ct * 256 + r;
       if (n < N) {
-        woff[i] = (uint32_t)n * (uint32_t)(K / 2) + 16 * h;
-        soff[i] = (uint32_t)n * (uint32_t)(K / 16) + 2 * h;
+        woff[i] = (uint32_t)n * (uint32_t)(K / 2) + dseg * 16;        // 16 B = 32 codes of a block
+        soff[i] = (uint32_t)n * (uint32_t)(K / 16) + (lane & 7) * 2;  // scale pair u = lane & 7
       } else {
         woff[i] = soff[i] = kOOB;
       }
     }
-
-    auto issue = [&](int c) {
+    auto issue_x = [&](int c) {
       const int K0 = c * kPromptKC;
-      unsigned char* buf = smem + (c % kPromptStages) * kPromptStageBytes;
+      unsigned char* buf = smem + kXOff + (c & 1) * kXStageBytes + wave * 32 * 128;
+      const bool tail = K0 + 8 * dseg >= K;  // only in a last, half stage (K % 64 == 32)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = xoff[i] != kOOB && K0 + 8 * xseg[i] < K;
-        dma16(xrs, buf + (wave * 256 + i * 64) * 16, ok ? xoff[i] + K0 * 2 : kOOB);
-      }
+      for (int i = 0; i < 4; ++i) dma16(xrs, buf + i * 1024, tail ? kOOB : xoff[i], K0 * 2);
+    };
+    auto issue_ws = [&](int b) {
+      const int K0 = b * kBlockStages * kPromptKC;
+      unsigned char* wbuf = smem + kWOff + (b & 1) * kWBlockBytes + wave * 32 * 128;
+      unsigned char* sbuf = smem + kSOff + (b & 1) * kSBlockBytes + wave * 32 * 32;
+      const bool wtail = K0 + 32 * dseg >= K;
+      const bool stail = K0 + 32 * (lane & 7) >= K;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const bool ok = woff[i] != kOOB && K0 + 32 * whalf[i] < K;
-        dma16(wrs, buf + kPromptXBytes + (wave * 128 + i * 64) * 16, ok ? woff[i] + K0 / 2 : kOOB);
-      }
+      for (int i = 0; i < 4; ++i) dma16(wrs, wbuf + i * 1024, wtail ? kOOB : woff[i], K0 / 2);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const bool ok = soff[i] != kOOB && K0 + 32 * whalf[i] < K;
-        dma2(srs, buf + kPromptXBytes + kPromptWBytes + (wave * 128 + i * 64) * 4, ok ? soff[i] + K0 / 16 : kOOB);
-      }
+      for (int i = 0; i < 4; ++i) dma2(srs, sbuf + i * 256, stail ? kOOB : soff[i], K0 / 16);
     };
 
     floatx16 acc[2][4];
@@ -217,82 +213,100 @@ __global__ __launch_bounds__(kPromptThreads, 1) void ffn_prompt_kernel(FFNArgs a
     // this wave's weight rows inside the staged 256-row weight tile
     int wrow[2];
     if (MODE == 0) {
-      wrow[0] = wave * 32 + l32;        // gate features ct*128 + wave*32 + l32
-      wrow[1] = 128 + wave * 32 + l32;  // up rows of the same features
+      wrow[0] = wcol * 32 + l32;        // gate features ct*128 + wcol*32 + l32
+      wrow[1] = 128 + wcol * 32 + l32;  // up rows of the same features
     } else {
-      wrow[0] = wave * 64 + l32;
-      wrow[1] = wave * 64 + 32 + l32;
+      wrow[0] = wcol * 64 + l32;
+      wrow[1] = wcol * 64 + 32 + l32;
     }
-    const bool fvalid[2] = {MODE == 0 ? ct * 128 + wave * 32 < N : ct * 256 + wave * 64 < N,
-                            MODE == 0 ? ct * 128 + wave * 32 < N : ct * 256 + wave * 64 + 32 < N};
+    const int fbase = MODE == 0 ? ct * 128 + wcol * 32 : ct * 256 + wcol * 64;
+    const bool fvalid[2] = {fbase < N, MODE == 0 ? fbase < N : fbase + 32 < N};
+    const int nblk = (nch + kBlockStages - 1) / kBlockStages;
 
-    // previous tile: stores drained and every wave done with the stage buffers
+    // previous tile: stores drained and every wave done with the LDS buffers
     wait_vm<0>();
+    wait_lgkm0();
     __builtin_amdgcn_s_barrier();
-#pragma unroll
-    for (int c = 0; c < kPromptStages - 1; ++c)
-      if (c < nch) issue(c);
+    issue_ws(0);
+    issue_x(0);
 
     // The K loop, specialised on the number of 32-row activation fragments in use so
     // the MFMA sequence is branch-free (rows past nrows are zeros; weight rows past N
-    // decode to zeros and are not stored).
+    // decode to zeros and are not stored). Stage c: wait for its activations (and, at a
+    // block start, its weight block: issued earlier, so complete too), barrier, issue the
+    // next stage's activations and, at a block start, the next weight / scale block;
+    // then decode + MFMA. The MFMA step s + 1 operands are read and decoded alongside
+    // step s's MFMAs (ping-pong registers).
     auto k_loop = [&](auto ntf_c) {
       constexpr int NTF = decltype(ntf_c)::value;
       for (int c = 0; c < nch; ++c) {
-        // stages issued after c still in flight: min(kPromptStages - 2, nch - 1 - c)
-        const int after = min(kPromptStages - 2, nch - 1 - c);
-        if (after >= 2) wait_vm<16>();
-        else if (after == 1) wait_vm<8>();
+        // loads issued after stage c's activations: the block issued in stage c - 1
+        const bool blk_after = c >= 1 && ((c - 1) % kBlockStages) == 0 && (c - 1) / kBlockStages + 1 < nblk;
+        if (blk_after) wait_vm<kWSDma>();
         else wait_vm<0>();
+        wait_lgkm0();
         __builtin_amdgcn_s_barrier();
-        if (c + kPromptStages - 1 < nch) issue(c + kPromptStages - 1);
+        if (c + 1 < nch) issue_x(c + 1);
+        if (c % kBlockStages == 0 && c / kBlockStages + 1 < nblk) issue_ws(c / kBlockStages + 1);
 
-        const unsigned char* buf = smem + (c % kPromptStages) * kPromptStageBytes;
-        const unsigned char* xb = buf;
-        const unsigned char* wb = buf + kPromptXBytes;
-        const unsigned char* sb = buf + kPromptXBytes + kPromptWBytes;
-        // all operand reads of the stage first (weights first: their decode starts
-        // while the activation reads are in flight), then decode + MFMA
+        if (NTF == 0) continue;
+        const unsigned char* xb = smem + kXOff + (c & 1) * kXStageBytes + (128 * wtok + l32) * 128;
+        const int cs = c % kBlockStages;
+        const int blk = (c / kBlockStages) & 1;
+        const unsigned char* wb = smem + kWOff + blk * kWBlockBytes;
+        const unsigned char* sb = smem + kSOff + blk * kSBlockBytes;
+        // weights of this stage: logical 16-byte segment 2cs + g of the row's 128 bytes
         u32x4 q[2];
         uint32_t sc[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          q[i] = *reinterpret_cast<const u32x4*>(wb + wrow[i] * 32 + 16 * g);
-          sc[i] = *reinterpret_cast<const uint32_t*>(sb + (wrow[i] * 2 + g) * 4);
+          const int r = wrow[i];
+          q[i] = *reinterpret_cast<const u32x4*>(wb + r * 128 + (((2 * cs + g) ^ (r & 7)) * 16));
+          sc[i] = *reinterpret_cast<const uint32_t*>(sb + r * 32 + (2 * cs + g) * 4);
         }
-        u32x4 bq[4][NTF];
+        // activation fragment t of MFMA step s: row 32t + l32, logical segment 4g + s
+        constexpr int NB = NTF > 0 ? NTF : 1;
+        auto read_b = [&](int s, u32x4 (&bv)[NB]) {
+          const int off = ((4 * g + s) ^ (l32 & 7)) * 16;
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+          for (int t = 0; t < NTF; ++t) bv[t] = *reinterpret_cast<const u32x4*>(xb + t * 4096 + off);
+        };
+        auto mfma_step = [&](const u32x4 (&bv)[NB], const bf16x8 (&w)[2]) {
 #pragma unroll
           for (int t = 0; t < NTF; ++t) {
-            const int row = t * 32 + l32;
-            const int slot = (4 * g + s) ^ (row & 7);
-            bq[s][t] = *reinterpret_cast<const u32x4*>(xb + row * 128 + slot * 16);
+            const bf16x8 b = u32x4_as_bf16x8(bv[t]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) acc[i][t] = mfma32(w[i], b, acc[i][t]);
           }
-        // keep the reads above this point: the scheduler would otherwise sink each read
-        // next to its MFMA and expose the LDS latency once per operand
-        __builtin_amdgcn_sched_barrier(0);
+        };
+        u32x4 x0[NB], x1[NB];
+        read_b(0, x0);
         E4M3Split sp[2][2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           sp[i][0] = e4m3_split(sc[i] & 0xFFu);
           sp[i][1] = e4m3_split((sc[i] >> 8) & 0xFFu);
         }
+        bf16x8 w0[2], w1[2];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          bf16x8 wa[2];
+        for (int i = 0; i < 2; ++i) w0[i] = nvfp4x8_to_bf16(q[i].x, sp[i][0]);
+        read_b(1, x1);
 #pragma unroll
-          for (int i = 0; i < 2; ++i) wa[i] = nvfp4x8_to_bf16(word4(q[i], s), sp[i][s >> 1]);
+        for (int i = 0; i < 2; ++i) w1[i] = nvfp4x8_to_bf16(q[i].y, sp[i][0]);
+        mfma_step(x0, w0);
+        read_b(2, x0);
 #pragma unroll
-          for (int t = 0; t < NTF; ++t) {
-            const bf16x8 b = u32x4_as_bf16x8(bq[s][t]);
+        for (int i = 0; i < 2; ++i) w0[i] = nvfp4x8_to_bf16(q[i].z, sp[i][1]);
+        mfma_step(x1, w1);
+        read_b(3, x1);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) acc[i][t] = mfma32(wa[i], b, acc[i][t]);
-          }
-        }
+        for (int i = 0; i < 2; ++i) w1[i] = nvfp4x8_to_bf16(q[i].w, sp[i][1]);
+        mfma_step(x0, w0);
+        mfma_step(x1, w1);
       }
     };
     switch (ntf) {
+      case 0: k_loop(std::integral_constant<int, 0>()); break;
       case 1: k_loop(std::integral_constant<int, 1>()); break;
       case 2: k_loop(std::integral_constant<int, 2>()); break;
       case 3: k_loop(std::integral_constant<int, 3>()); break;
@@ -300,16 +314,15 @@ __global__ __launch_bounds__(kPromptThreads, 1) void ffn_prompt_kernel(FFNArgs a
     }
 
     // ---- epilogue. Accumulator r of fragment (i, t): weight row 8*(r/4) + 4*g + r%4 of
-    // the fragment, activation row t*32 + l32 of the tile.
+    // the fragment, activation row 128*wtok + 32t + l32 of the tile.
     if (MODE == 0) {
-      const int f0 = ct * 128 + wave * 32;
       if (fvalid[0]) {
         const float tg = a.gate_ts[e], tu = a.up_ts[e];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int row = t * 32 + l32;
+          const int row = 128 * wtok + t * 32 + l32;
           if (t < ntf && row < nrows) {
-            uint16_t* hp = a.h + (size_t)(p0 + row) * a.f + f0 + 4 * g;
+            uint16_t* hp = a.h + (size_t)(p0 + row) * a.f + fbase + 4 * g;
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
               uint32_t hb[4];
@@ -329,10 +342,10 @@ __global__ __launch_bounds__(kPromptThreads, 1) void ffn_prompt_kernel(FFNArgs a
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         if (!fvalid[i]) continue;
-        const int c0 = ct * 256 + wave * 64 + 32 * i;
+        const int c0 = fbase + 32 * i;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int row = t * 32 + l32;
+          const int row = 128 * wtok + t * 32 + l32;
           if (t < ntf && row < nrows) {
             float* yp = a.y_rows + (size_t)(p0 + row) * a.d + c0 + 4 * g;
 #pragma unroll
