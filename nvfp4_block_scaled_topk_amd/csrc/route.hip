@@ -6,13 +6,16 @@
 // normalization policy the pages name, [bloomery 0.3.9 release notes, Fixed, #772],
 // read as softmax -> top-k -> renormalize).
 //
-// Kernel 1 (one wave per token, 64 tokens per block): the k best (logit desc, index
-// asc) by k rounds of a wave-wide argmax over the lane-held logits; the weights; then,
-// per block, each assignment's rank among the block's earlier assignments to the same
-// expert and the block's per-expert counts. Kernel 2 (one block): per-expert running
-// sums over the blocks, the exclusive scan over experts, and the stable scatter
-// p = offset[e] + (earlier blocks' count of e) + rank. No atomics: the row lists are
-// the same bits on every run. A batch of at most 64 tokens runs as one launch.
+// Kernel 1 (64 tokens per block, 16 contiguous tokens per wave): the k best (logit
+// desc, index asc) by k rounds of a wave-wide argmax over the lane-held logits, and the
+// weights. Then each assignment's rank among the block's earlier assignments to the
+// same expert: every wave counts its own assignments 64 at a time with lane shuffles
+// (rank = earlier lanes with the same expert + the wave's running count), and the
+// block adds the counts of the waves before it. Kernel 2 (one block per token block):
+// each block sums the per-expert counts of the blocks before it and of all blocks,
+// scans over experts, and scatters p = offset[e] + (earlier blocks' count of e) + rank.
+// No atomics: the row lists are the same bits on every run. A batch of at most 64
+// tokens runs as one launch.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -25,6 +28,77 @@ constexpr int kMaxExperts = 1024;
 
 __device__ __forceinline__ bool route_better(float a, int ia, float b, int ib) {
   return a > b || (a == b && ia < ib);
+}
+
+// Lane exchange inside rows of 16 lanes (DPP, no LDS round trip): CTRL is a gfx9 DPP
+// control -- 0xB1 / 0x4E swap lanes at distance 1 / 2 inside each quad, 0x141 mirrors
+// each half row (8 lanes), 0x140 mirrors the row.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+template <int CTRL>
+__device__ __forceinline__ void row_argmax_step(float& bv, int& bi) {
+  const float ov = dpp_f<CTRL>(bv);
+  const int oi = dpp_i<CTRL>(bi);
+  if (route_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+}
+template <int CTRL>
+__device__ __forceinline__ void row_sum_step(float& s) {
+  s += dpp_f<CTRL>(s);
+}
+
+// Top-k of one token held by a 16-lane row (lane gl of the row holds experts gl + 16j,
+// j < EPL), k <= 16: k rounds of a row argmax. Lane gl < k gets the gl-th choice in
+// my_v / my_i and its renormalized softmax weight in my_w.
+template <int EPL>
+__device__ __forceinline__ void row_topk(const float* __restrict__ row, int E, int k, int gl, float& my_v,
+                                         int& my_i, float& my_w) {
+  float v[EPL];
+  int ix[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = gl + 16 * j;
+    v[j] = e < E ? row[e] : -__builtin_inff();
+    ix[j] = e < E ? e : 0x7FFFFFFF;
+  }
+  my_v = 0.0f;
+  my_i = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = v[0];
+    int bi = ix[0];
+#pragma unroll
+    for (int j = 1; j < EPL; ++j)
+      if (route_better(v[j], ix[j], bv, bi)) { bv = v[j]; bi = ix[j]; }
+    row_argmax_step<0xB1>(bv, bi);
+    row_argmax_step<0x4E>(bv, bi);
+    row_argmax_step<0x141>(bv, bi);
+    row_argmax_step<0x140>(bv, bi);
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (ix[j] == bi) { v[j] = -__builtin_inff(); ix[j] = 0x7FFFFFFF; }
+    if (gl == r) { my_v = bv; my_i = bi; }
+    if (r == 0) my_w = bv;  // the row maximum, broadcast to every lane of the row
+  }
+  const float m = my_w;
+  float ex = 0.0f;
+  if (gl < k) {
+    const float s = my_v - m;
+    const float bb = s - my_v;
+    const float err = (my_v - (s - bb)) + (-m - bb);
+    const float e0 = expf(s);
+    ex = fmaf(e0, err, e0);
+  }
+  float sum = ex;
+  row_sum_step<0xB1>(sum);
+  row_sum_step<0x4E>(sum);
+  row_sum_step<0x141>(sum);
+  row_sum_step<0x140>(sum);
+  my_w = ex / sum;
 }
 
 // Exclusive scan of s_in[0..n) in LDS (n <= 1024) by the block's first wave, 64
@@ -56,6 +130,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     float* __restrict__ topk_w, int32_t* __restrict__ ws_rank, int32_t* __restrict__ ws_counts,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_rows,
     int32_t* __restrict__ row_of) {
+  constexpr int kWaves = kRouteThreads / 64;
   __shared__ int s_ids[kRouteTokensPerBlock * kMaxTopK];
   __shared__ int s_rank[kRouteTokensPerBlock * kMaxTopK];
   __shared__ int s_cnt[kMaxExperts];
@@ -67,7 +142,25 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   const int t_end = min(T, t_begin + kRouteTokensPerBlock);
   const int ntok = t_end - t_begin;
 
-  for (int tl = wave; tl < ntok; tl += kRouteThreads / 64) {
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) s_cnt[e] = 0;
+  constexpr int kRowEpl = EPL <= 4 ? EPL * 4 : 1;  // experts a lane holds in the row path
+  if (EPL <= 4 && k <= 16) {
+    // top-k: one 16-lane row per token, 4 tokens per wave at once
+    const int gl = lane & 15;
+    for (int tl = wave * 4 + (lane >> 4); tl < ntok; tl += kWaves * 4) {
+      const int t = t_begin + tl;
+      float my_v, my_w;
+      int my_i;
+      row_topk<kRowEpl>(logits + (size_t)t * E, E, k, gl, my_v, my_i, my_w);
+      if (gl < k) {
+        topk_ids[(size_t)t * k + gl] = my_i;
+        topk_w[(size_t)t * k + gl] = my_w;
+        s_ids[tl * k + gl] = my_i;
+      }
+    }
+  } else
+  // top-k: one wave per token, tokens interleaved over the waves
+  for (int tl = wave; tl < ntok; tl += kWaves) {
     const int t = t_begin + tl;
     const float* row = logits + (size_t)t * E;
     float v[EPL];
@@ -119,13 +212,33 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   }
   __syncthreads();
 
-  // per-expert counts and ranks of this block's assignments (stable: in assignment order)
+  // ranks, by wave 0, 64 assignments at a time in assignment order: lanes holding the
+  // same expert are found with one ballot per bit of the expert index; the rank is the
+  // number of such lanes below plus the expert's running count (s_cnt), which the
+  // expert's last lane in the chunk then advances.
   const int nas = ntok * k;
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
-    int c = 0;
-    for (int i = 0; i < nas; ++i)
-      if (s_ids[i] == e) s_rank[i] = c++;
-    s_cnt[e] = c;
+  if (wave == 0) {
+    for (int base = 0; base < nas; base += 64) {
+      const int a = base + lane;
+      const int e = a < nas ? s_ids[a] : -1;
+      uint64_t same = __ballot(e >= 0);
+#pragma unroll
+      for (int bit = 0; bit < 10; ++bit) {
+        const uint64_t b1 = __ballot(e >= 0 && ((e >> bit) & 1));
+        same &= ((e >> bit) & 1) ? b1 : ~b1;
+      }
+      const uint64_t below = (1ull << lane) - 1ull;
+      const int before = __popcll(same & below);
+      const bool last = (same & ~below & ~(1ull << lane)) == 0;
+      int r = 0;
+      if (e >= 0) r = s_cnt[e] + before;
+      __builtin_amdgcn_wave_barrier();
+      if (e >= 0) {
+        s_rank[a] = r;
+        if (last) s_cnt[e] = r + 1;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
   }
   __syncthreads();
 
@@ -145,31 +258,48 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   for (int e = threadIdx.x; e < E; e += kRouteThreads) ws_counts[(size_t)blockIdx.x * E + e] = s_cnt[e];
 }
 
-__global__ __launch_bounds__(1024) void route_scan_scatter_kernel(
+// One block per token block: this block's base per expert (counts of the blocks before
+// it), every expert's total, the scan over experts, and the scatter of its own
+// assignments.
+__global__ __launch_bounds__(kRouteThreads) void route_scan_scatter_kernel(
     const int32_t* __restrict__ topk_ids, int T, int E, int k, int nblocks,
-    const int32_t* __restrict__ ws_rank, int32_t* __restrict__ ws_counts,
+    const int32_t* __restrict__ ws_rank, const int32_t* __restrict__ ws_counts,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_rows,
     int32_t* __restrict__ row_of) {
+  __shared__ int s_base[kMaxExperts];
   __shared__ int s_tot[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int run = 0;
-    for (int b = 0; b < nblocks; ++b) {
-      const int c = ws_counts[(size_t)b * E + e];
-      ws_counts[(size_t)b * E + e] = run;
-      run += c;
+  const int b = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+    int before = 0, total = 0;
+    int j = 0;
+    for (; j + 8 <= nblocks; j += 8) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = ws_counts[(size_t)(j + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        before += (j + u < b) ? c[u] : 0;
+        total += c[u];
+      }
     }
-    s_tot[e] = run;
+    for (; j < nblocks; ++j) {
+      const int c = ws_counts[(size_t)j * E + e];
+      before += (j < b) ? c : 0;
+      total += c;
+    }
+    s_base[e] = before;
+    s_tot[e] = total;
   }
   __syncthreads();
   block_exclusive_scan(s_tot, s_off, E);
-  for (int e = threadIdx.x; e <= E; e += blockDim.x) expert_offsets[e] = s_off[e];
-  const int per_block = kRouteTokensPerBlock * k;
-  const int total = T * k;
-  for (int a = threadIdx.x; a < total; a += blockDim.x) {
+  if (b == 0)
+    for (int e = threadIdx.x; e <= E; e += kRouteThreads) expert_offsets[e] = s_off[e];
+  const int a_begin = b * kRouteTokensPerBlock * k;
+  const int a_end = min(T * k, a_begin + kRouteTokensPerBlock * k);
+  for (int a = a_begin + threadIdx.x; a < a_end; a += kRouteThreads) {
     const int e = topk_ids[a];
-    const int b = a / per_block;
-    const int p = s_off[e] + ws_counts[(size_t)b * E + e] + ws_rank[a];
+    const int p = s_off[e] + s_base[e] + ws_rank[a];
     sorted_rows[p] = a;
     row_of[a] = p;
   }
@@ -204,7 +334,7 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
 #undef MOE_ROUTE_LAUNCH
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nb <= 1) return err;
-  hipLaunchKernelGGL(route_scan_scatter_kernel, dim3(1), dim3(1024), 0, stream, ids, T, E, k, nb,
+  hipLaunchKernelGGL(route_scan_scatter_kernel, dim3(nb), dim3(kRouteThreads), 0, stream, ids, T, E, k, nb,
                      ws_rank, ws_counts, offsets, sorted_rows, row_of);
   return hipGetLastError();
 }
