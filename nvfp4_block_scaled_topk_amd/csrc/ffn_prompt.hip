@@ -7,21 +7,18 @@
 // operands through a multi-stage pipeline in fixed K steps (§4 remaining items, #822).
 // Here, on gfx950:
 //
-//   tile    = (expert e, 128 routed rows of e, 128 features of f)   [gate/up launch]
-//             (expert e, 128 routed rows of e, 256 columns of d)    [down launch]
-//   waves   = 4; wave w owns two 32-row weight fragments (gate and up of the same 32
-//             features, or two 32-column slices of d) and all 128 routed rows
+//   tile    = (expert e, 256 routed rows of e, 128 features of f)   [gate/up launch:
+//             weight rows 0..127 are gate rows, 128..255 the up rows of the same features]
+//             (expert e, 256 routed rows of e, 256 columns of d)    [down launch]
+//   waves   = 8 (two per SIMD); wave w owns two 32-row weight fragments (gate and up of
+//             the same 32 features, or two 32-column slices of d) and 128 of the 256
+//             routed rows
 //   MFMA    = v_mfma_f32_32x32x16_bf16, weights as the A operand, activations as B
-//   stages  = 4 LDS stages of 64 K elements: activations (bf16), packed weight codes
-//             and block scales, each filled by buffer->LDS DMA (no register staging;
-//             out-of-range lanes read zeros, which also pads ragged rows and K tails)
-//
-// Each wave decodes its weight fragments from LDS into bf16 MFMA operands (exact, see
-// device.hpp); the activation tile is shared by the four waves. Activation rows sit in
-// LDS as 128-byte rows of eight 16-byte segments, segment j of row r stored at slot
-// j ^ (r & 7), so the MFMA operand reads (32 rows, same segment) hit distinct banks.
-// The fp32 tensor scale multiplies the accumulator in the epilogue; gate/up's
-// epilogue forms H = bf16_rne(silu(G) * U), down's writes fp32 rows.
+//   staging = buffer->LDS DMA only (no register staging; out-of-range lanes read zeros,
+//             which also pads ragged rows and K tails): activations in double-buffered
+//             stages of 64 K elements; packed weight codes and block scales in
+//             double-buffered blocks of 256 K elements (four activation stages), so one
+//             DMA instruction moves a whole 128-byte row segment of codes
 //
 // Work: one flat list of tiles (expert-major, column tile fastest) walked by a
 // persistent grid; each block derives the list from expert_offsets. Block b works on

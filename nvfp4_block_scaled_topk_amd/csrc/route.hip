@@ -6,16 +6,18 @@
 // normalization policy the pages name, [bloomery 0.3.9 release notes, Fixed, #772],
 // read as softmax -> top-k -> renormalize).
 //
-// Kernel 1 (64 tokens per block, 16 contiguous tokens per wave): the k best (logit
-// desc, index asc) by k rounds of a wave-wide argmax over the lane-held logits, and the
-// weights. Then each assignment's rank among the block's earlier assignments to the
-// same expert: every wave counts its own assignments 64 at a time with lane shuffles
-// (rank = earlier lanes with the same expert + the wave's running count), and the
-// block adds the counts of the waves before it. Kernel 2 (one block per token block):
-// each block sums the per-expert counts of the blocks before it and of all blocks,
-// scans over experts, and scatters p = offset[e] + (earlier blocks' count of e) + rank.
-// No atomics: the row lists are the same bits on every run. A batch of at most 64
-// tokens runs as one launch.
+// Kernel 1 (64 tokens per block, 256 threads): for E <= 256 and k <= 16 each token
+// owns one 16-lane row of a wave (four tokens a wave at a time) and finds its k best
+// (logit desc, index asc) by k rounds of a row argmax built from DPP lane exchanges;
+// larger E or k fall back to a wave per token and wave-wide shuffles. The weights
+// follow from the selected logits. Wave 0 then ranks every assignment among the block's
+// earlier assignments to the same expert, 64 at a time: ten ballots over the expert
+// index bits give each lane the mask of lanes with its expert, and a per-expert running
+// count in LDS carries across chunks. Kernel 2 (one block per token block): each block
+// sums the per-expert counts of the blocks before it and of all blocks, scans over
+// experts, and scatters p = offset[e] + (earlier blocks' count of e) + rank. No
+// atomics: the row lists are the same bits on every run. A batch of at most 64 tokens
+// runs as one launch (scan and scatter in the same block).
 #include "device.hpp"
 #include "internal.hpp"
 
