@@ -5,8 +5,9 @@
 A step is one pass of the whole layer over one batch of synthetic tokens: top-k
 routing with row lists, the gate/up/SwiGLU and down products over NVFP4 experts,
 and the weighted combine. The default workload is the decode layer (T=4, d=2048,
-f=768, E=128, top-8, Zipf(1.1)-skewed routing); the long-prompt layer (T=4096,
-d=7168, f=2048, E=256, top-8) is measured beside it under "also".
+f=768, E=128, top-8, Zipf(1.1)-skewed routing); the prompt layer (T=512, d=3072,
+f=1536, E=128), the long-prompt layer (T=4096, d=7168, f=2048, E=256) and the MXFP8
+projection (N=12288, K=4096, M=1 and 512) are measured beside it under "also".
 
 Timing: the K steps are enqueued behind a GPU sleep kernel so the device never
 waits for the host, and bracketed by HIP events on the stream the kernels run on
@@ -182,6 +183,58 @@ def bench_moe(name, steps, warmup, rotations, timer, seed=0):
     return res
 
 
+def bench_mxfp8(M, steps, warmup, rotations, timer, seed=0):
+    """MXFP8 projection y = x . W^T (N=12288, K=4096): `steps` calls queued behind a GPU
+    sleep, bracketed by one pair of HIP events; weights rotate through `rotations`
+    copies so repeats are not served from the Infinity Cache."""
+    import numpy as np
+    import torch
+
+    import nvfp4_block_scaled_topk_amd as M_
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    inp = workloads.mxfp8_config(M, seed=seed)
+    N, K = inp.N, inp.K
+    x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    w0 = torch.from_numpy(inp.w).to(dev)
+    s0 = torch.from_numpy(inp.s).to(dev)
+    del inp
+    ws = [(w0, s0)] + [(w0.clone(), s0.clone()) for _ in range(rotations - 1)]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    for i in range(warmup):
+        M_.mxfp8_gemm(x, *ws[i % rotations], out=y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(20):
+        M_.mxfp8_gemm(x, *ws[i % rotations], out=y)
+    torch.cuda.synchronize()
+    host_ms = (time.perf_counter() - t0) * 1e3 / 20
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    timer.queue_ahead(host_ms * steps * 1.5 + 20.0)
+    start.record()
+    for i in range(steps):
+        M_.mxfp8_gemm(x, *ws[i % rotations], out=y)
+    end.record()
+    torch.cuda.synchronize()
+    avg_ms = start.elapsed_time(end) / steps
+    nbytes = N * K + N * (K // 32) + M * K * 2 + M * N * 2
+    flops = 2.0 * M * N * K
+    res = {"M": M, "N": N, "K": K, "avg_us": avg_ms * 1e3, "rows_per_s": M / (avg_ms / 1e3),
+           "algorithmic_bytes": nbytes, "algorithmic_flop": flops, "weight_copies_rotated": rotations,
+           "hbm_gbps": nbytes / (avg_ms / 1e3) / 1e9, "tflops": flops / (avg_ms / 1e3) / 1e12}
+    if M <= 16:
+        res["roofline"] = {"bound": "hbm", "achieved": res["hbm_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": res["hbm_gbps"] / HBM_PEAK_GBPS, "kernel": "mxfp8_gemv_kernel"}
+    else:
+        res["roofline"] = {"bound": "mfma", "achieved": res["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": res["tflops"] / BF16_PEAK_TFLOPS, "kernel": "mxfp8_gemm_kernel"}
+    log(f"[bench] mxfp8 M={M}: {json.dumps(res)}")
+    del ws, w0, s0
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle (test infrastructure, untuned) on the host cores: whole decode
     layers (route, dequantize, FFN, combine) on the same seeded input, repeated
@@ -215,7 +268,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prompt", "long_prompt"])
     ap.add_argument("--rotations", type=int, default=0, help="weight copies to rotate (0: >= 1 GB)")
-    ap.add_argument("--no-also", action="store_true", help="skip the long-prompt measurement")
+    ap.add_argument("--no-also", action="store_true", help="skip the prompt, long-prompt and MXFP8 measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--also-steps", type=int, default=20)
     args = ap.parse_args(argv)
@@ -251,12 +304,25 @@ def main(argv=None):
             "layer_tflops": r["layer_tflops"],
         }
 
+    if not args.no_also and args.workload != "prompt":
+        r = bench_moe("prompt", args.also_steps, 3, 1, timer)
+        also["prompt"] = {
+            "tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"], "touched_experts": r["touched_experts"],
+            "ffn_avg_us": r["ffn_avg_us"], "ffn_hbm_gbps": r["ffn_hbm_gbps"],
+            "ffn_hbm_frac": r["ffn_hbm_gbps"] / HBM_PEAK_GBPS, "ffn_tflops": r["ffn_tflops"],
+            "ffn_mfma_frac": r["ffn_tflops"] / BF16_PEAK_TFLOPS,
+        }
+    if not args.no_also:
+        for m in (1, 512):
+            r = bench_mxfp8(m, max(args.also_steps, 50), 5, 20, timer)
+            also[f"mxfp8_M{m}"] = r
+
     decode_like = main_res["T"] <= 16
     if decode_like:
         files = ["ffn_decode.hip", "device.hpp"]
         roof = {"bound": "hbm", "achieved": main_res["ffn_hbm_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": main_res["ffn_hbm_gbps"] / HBM_PEAK_GBPS, "traffic": load_traffic(args.workload, files),
-                "kernel": "moe_expert_ffn_nvfp4 decode (ffn_decode_gateup_kernel + ffn_decode_down_kernel)",
+                "kernel": "moe_expert_ffn_nvfp4 decode (ffn_decode_kernel: gate/up/SwiGLU and down in one launch)",
                 "algorithmic_bytes": main_res["ffn_bytes"], "avg_us": main_res["ffn_avg_us"]}
     else:
         files = ["ffn_prompt.hip", "device.hpp"]

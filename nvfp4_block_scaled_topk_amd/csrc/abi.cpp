@@ -4,8 +4,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdio>
 #include <cstring>
+#include <random>
 
 #include "internal.hpp"
 
@@ -38,13 +40,28 @@ bool ffn_shape_ok(int T, int d, int f, int E, int k) {
 constexpr size_t kWsAlign = 256;
 size_t round_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
+// Tags of the decode path's H words: a different value on every call, never 0 (freshly
+// cleared memory), starting from a random point so that words a workspace still holds
+// from earlier use cannot match.
+uint32_t next_call_tag() {
+  static std::atomic<uint32_t> counter{static_cast<uint32_t>(std::random_device{}())};
+  uint32_t t = counter.fetch_add(1, std::memory_order_relaxed) + 1u;
+  if (t == 0) t = counter.fetch_add(1, std::memory_order_relaxed) + 1u;
+  return t;
+}
+
+// H: bf16 for the prompt path, bf16 + tag (4 bytes an element) for the decode path
+size_t h_bytes(int T, int d, int f, int k) {
+  const size_t elem = moe::use_decode_path(T, d, f) ? 4 : 2;
+  return round_up((size_t)T * k * f * elem);
+}
+
 }  // namespace
 
 namespace moe {
 size_t ffn_workspace_bytes(int T, int d, int f, int E, int k) {
-  (void)d;
   (void)E;
-  return round_up((size_t)T * k * f * sizeof(uint16_t));
+  return h_bytes(T, d, f, k);
 }
 }  // namespace moe
 
@@ -117,7 +134,7 @@ int moe_expert_ffn_nvfp4(const uint16_t* x, int T, int d, int f, int E, int k, c
   hipStream_t st = static_cast<hipStream_t>(stream);
   // a token routes to k distinct experts, so an expert has at most T rows: with
   // T <= 16 every expert's rows fit one decode tile
-  if (T <= moe::kDecodeMaxRows) return launch_status(moe::launch_ffn_decode(a, st));
+  if (moe::use_decode_path(T, d, f)) return launch_status(moe::launch_ffn_decode(a, next_call_tag(), st));
   return launch_status(moe::launch_ffn_prompt(a, st));
 }
 

@@ -17,7 +17,7 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
                         int32_t* offsets, int32_t* sorted_rows, int32_t* row_of, void* ws,
                         hipStream_t stream);
 
-// expert FFN: H (bf16, [T*k][f]) lives in the caller's workspace
+// expert FFN: H ([T*k][f]) lives in the caller's workspace
 struct FFNArgs {
   const uint16_t* x;
   int T, d, f, E, k;
@@ -28,10 +28,18 @@ struct FFNArgs {
   float* y_rows;
   uint16_t* h;
 };
-// The decode path keeps every expert's rows in one 16-row MFMA tile.
+// The decode path keeps every expert's rows in one 16-row MFMA tile (T <= 16).
 constexpr int kDecodeMaxRows = 16;
 size_t ffn_workspace_bytes(int T, int d, int f, int E, int k);
-hipError_t launch_ffn_decode(const FFNArgs& a, hipStream_t stream);
+// The decode path keeps H in the workspace as 64-bit words (two bf16 values and a
+// 32-bit tag that differs between calls): T * k * f * 4 bytes.
+// The decode path stages one expert's activation rows, then its H rows, in LDS.
+size_t ffn_decode_lds_bytes(int T, int d, int f);
+constexpr size_t kDecodeMaxLds = 64 * 1024;
+inline bool use_decode_path(int T, int d, int f) {
+  return T <= kDecodeMaxRows && ffn_decode_lds_bytes(T, d, f) <= kDecodeMaxLds;
+}
+hipError_t launch_ffn_decode(const FFNArgs& a, uint32_t tag, hipStream_t stream);
 hipError_t launch_ffn_prompt(const FFNArgs& a, hipStream_t stream);
 
 // combine
