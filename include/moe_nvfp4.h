@@ -19,7 +19,9 @@
  *
  * Conventions for every entry point
  *   - Every data pointer is a DEVICE pointer, allocated and owned by the caller; the
- *     library never allocates, frees or retains memory and keeps no global state.
+ *     library never allocates, frees or retains memory. Its only global state is a
+ *     per-process call counter (moe_expert_ffn_nvfp4 tags its workspace words with it)
+ *     and cached device properties.
  *   - `stream` is a hipStream_t (NULL = the default stream). A call only enqueues work
  *     on it; results are valid once the stream reaches the call.
  *   - Arguments are checked on the host before any HIP call; a call that returns a
@@ -109,7 +111,14 @@ int moe_route_topk(const float* logits, int T, int E, int k,
  * x is bf16 [T][d]; y_rows is fp32 [T*k][d]. expert_offsets / sorted_rows are the
  * device outputs of moe_route_topk for the same T, E, k.
  * Sizes: 1 <= T, d and f multiples of 32 (>= 32), 1 <= E <= 1024, 1 <= k <= min(E, 32).
- * Workspace: at least moe_expert_ffn_nvfp4_workspace(T, d, f, E, k) bytes (holds H).
+ * Workspace: at least moe_expert_ffn_nvfp4_workspace(T, d, f, E, k) bytes (holds H; no
+ * initial contents needed).
+ * Few tokens (T <= 16 and T * (max(d, f) + 8) * 2 <= 64 KiB) run as one launch whose
+ * down-product workgroups wait, with a bounded spin, for the gate/up workgroups of the
+ * same expert; the launch never has more workgroups than the GPU holds at once. If
+ * other work keeps some of them from becoming resident (for instance another such call
+ * running concurrently on a second stream), a wait can expire: the affected rows of
+ * y_rows are then NaN, and nothing hangs.
  */
 size_t moe_expert_ffn_nvfp4_workspace(int T, int d, int f, int E, int k);
 int moe_expert_ffn_nvfp4(const uint16_t* x, int T, int d, int f, int E, int k,
