@@ -138,7 +138,8 @@ int moe_combine(const float* y_rows, const int32_t* row_of, const float* topk_w,
  * mxfp8_gemm -- y[m][n] = bf16_rne( sum_i x[m][i] * W[n][i] ), fp32 accumulation,
  * W[n][i] = E4M3(w[n][i]) * 2^(s[n][i/32] - 127) (exact in bf16 for the scales in use).
  * x bf16 [M][K], w E4M3 [N][K], s E8M0 [N][K/32], y bf16 [M][N].
- * Sizes: M, N >= 1, K a multiple of 32 (>= 32).
+ * Sizes: M, N >= 1, K a multiple of 32 (>= 32), M * K * 2 < 2^31 and N * K < 2^31.
+ * M <= 16 runs as a gemv, larger M as a tiled GEMM (128 x 256 output tiles).
  */
 int mxfp8_gemm(const uint16_t* x, int M, int N, int K,
                const uint8_t* w, const uint8_t* s, uint16_t* y, void* stream);

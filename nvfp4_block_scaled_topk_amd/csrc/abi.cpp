@@ -149,8 +149,9 @@ int moe_combine(const float* y_rows, const int32_t* row_of, const float* topk_w,
 int mxfp8_gemm(const uint16_t* x, int M, int N, int K, const uint8_t* w, const uint8_t* s, uint16_t* y,
                void* stream) {
   if (!x || !w || !s || !y) return MOE_E_NULL;
-  if (M < 1 || N < 1 || K < 32 || K % 32 != 0 || (long long)M * K >= (1LL << 40) ||
-      (long long)N * K >= (1LL << 40))
+  // x (M * K bf16) and W (N * K bytes) are addressed through 32-bit buffer offsets
+  if (M < 1 || N < 1 || K < 32 || K % 32 != 0 || (long long)M * K * 2 >= (1LL << 31) ||
+      (long long)N * K >= (1LL << 31))
     return MOE_E_SHAPE;
   if (!aligned16(x) || !aligned16(w) || !aligned16(s) || !aligned16(y)) return MOE_E_ALIGN;
   return launch_status(moe::launch_mxfp8(x, M, N, K, w, s, y, static_cast<hipStream_t>(stream)));

@@ -11,17 +11,20 @@
 // gemv (M <= 16): one 16x16x32 MFMA tile covers every activation row; a wave owns 16
 //   weight rows and streams them with 128-bit loads (16 elements a lane, half of a
 //   scale block); KSPLIT waves split K and reduce in LDS in wave order.
-// GEMM: 128 weight rows x 128 activation rows per block, 32x32x16 MFMA, weights from
-//   registers (decoded in place), activations staged through LDS in 64-element steps.
+// GEMM: a tile of 128 activation rows x 256 weight rows per block of 8 waves (each wave
+//   2 x 2 32x32x16 MFMA fragments: 64 activation rows x 64 weight rows). Activations
+//   (bf16), weight codes (E4M3) and block scales (E8M0) reach LDS by buffer->LDS DMA in
+//   four stages of 64 K elements, three stages ahead of the products, with no register
+//   staging; out-of-range lanes read zeros, which also pads ragged tiles and the K
+//   tail. Both operands sit in LDS in swizzled 16-byte slots so the MFMA operand reads
+//   are free of bank conflicts. Blocks on one XCD take neighbouring tiles (same weight
+//   rows), which then share that XCD's L2.
 #include "device.hpp"
 #include "internal.hpp"
 
 namespace moe {
 
 constexpr int kMxGemvKsplit = 4;
-constexpr int kMxRows = 128;
-constexpr int kMxKC = 64;
-constexpr int kMxLdsRow = kMxKC * 2 + 16;
 
 __device__ __forceinline__ floatx4 mx_mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -113,99 +116,170 @@ __global__ __launch_bounds__(64 * KSPLIT) void mxfp8_gemv_kernel(const uint16_t*
   store_bf16x4(y + (size_t)col * N + nb, hb, N - nb, (N & 3) == 0);
 }
 
-__global__ __launch_bounds__(256) void mxfp8_gemm_kernel(const uint16_t* __restrict__ x, int M, int N,
-                                                         int K, const uint8_t* __restrict__ w,
-                                                         const uint8_t* __restrict__ s,
-                                                         uint16_t* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) unsigned char s_x[2][kMxRows * kMxLdsRow];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+constexpr int kGM = 128;                        // activation rows per tile
+constexpr int kGN = 256;                        // weight rows per tile
+constexpr int kGK = 64;                         // K elements per stage
+constexpr int kGStages = 4;
+constexpr int kGXBytes = kGM * kGK * 2;         // 16 KB: 128 rows x 128 bytes
+constexpr int kGWBytes = kGN * kGK;             // 16 KB: 256 rows x 64 bytes
+constexpr int kGSBytes = 8 * 64 * 4;            // 2 KB: a dword slot per (row, block)
+constexpr int kGStageBytes = kGXBytes + kGWBytes + kGSBytes;
+constexpr int kGLdsBytes = kGStages * kGStageBytes;  // 136 KB
+constexpr int kGThreads = 512;
+constexpr int kGOps = 5;                        // DMA instructions a wave issues per stage
+constexpr uint32_t kGOOB = 0x80000000u;         // a buffer offset past every record: reads zeros
+
+typedef __attribute__((address_space(3))) void* gemm_lds_ptr;
+typedef uint32_t gu32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+template <int N>
+__device__ __forceinline__ void gemm_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void gemm_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS layout of a stage:
+//   x: row r (128 bytes = 8 slots of 16 bytes), logical segment j in slot j ^ (r & 7);
+//   W: row r (64 bytes = 4 slots), logical segment j in slot j ^ ((r >> 1) & 3);
+//   scales: wave w's region holds rows 32w .. 32w + 31, (row, block b) in dword slot
+//   2 * (row & 31) + b.
+// MFMA K order within a stage (a permutation of K applied to both operands): lane group
+// g (lane / 32) at step 2p + h takes W bytes 8h .. 8h + 7 of segment 2p + g, i.e. K
+// elements 16 * (2p + g) + 8h .. + 7, which are activation segment 4p + 2g + h.
+__global__ __launch_bounds__(kGThreads, 1) void mxfp8_gemm_kernel(const uint16_t* __restrict__ x, int M, int N,
+                                                                  int K, const uint8_t* __restrict__ w,
+                                                                  const uint8_t* __restrict__ s,
+                                                                  uint16_t* __restrict__ y, int mtiles) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const int n0 = blockIdx.x * 128 + wave * 32;  // this wave's 32 weight rows
-  const int m0 = blockIdx.y * kMxRows;
-  const int nrows = min(kMxRows, M - m0);
-  const int ntf = (nrows + 31) >> 5;
-  const bool nvalid = n0 + l32 < N;
-  const bool wave_has_rows = n0 < N;
-  const uint8_t* wr = w + (size_t)(nvalid ? n0 + l32 : 0) * K;
-  const uint8_t* sr = s + (size_t)(nvalid ? n0 + l32 : 0) * (K / 32);
-  const int srow = threadIdx.x >> 1, shalf = threadIdx.x & 1;
-  const bool svalid = srow < nrows;
-  const uint16_t* xr = x + (size_t)(svalid ? m0 + srow : 0) * K;
-  const int nch = (K + kMxKC - 1) / kMxKC;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int mh = wave >> 2;  // 64-row half of the activation tile
+  const int nq = wave & 3;   // 64-row quarter of the weight tile
 
-  floatx16 acc[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+  // tile of this block: XCD-aware order, neighbouring tiles share weight rows
+  const int G = gridDim.x;
+  const int lid = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int nt = lid / mtiles, mt = lid - nt * mtiles;
+  const int m0 = mt * kGM, n0 = nt * kGN;
 
-  u32x4 xs[4], wq[2];
-  uint32_t sb;
-  auto load_chunk = [&](int c, u32x4 (&xr4)[4], u32x4 (&wr2)[2], uint32_t& sbr) {
-    const int K0 = c * kMxKC;
-    const bool kv = K0 + 32 * shalf < K;
+  const __amdgpu_buffer_rsrc_t xrs = gemm_rsrc(x, (uint32_t)((size_t)M * K * 2));
+  const __amdgpu_buffer_rsrc_t wrs = gemm_rsrc(w, (uint32_t)((size_t)N * K));
+  const __amdgpu_buffer_rsrc_t srs = gemm_rsrc(s, (uint32_t)((size_t)N * (K / 32)));
+
+  // per-lane DMA sources (byte offsets; the stage's K offset goes in soffset)
+  uint32_t xoff[2], woff[2];
+  int xseg[2], wseg[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xr4[j] = (svalid && kv) ? ldg_u32x4(xr + K0 + 32 * shalf + 8 * j) : zero;
-    const bool ok = nvalid && (K0 + 32 * g < K);
-    wr2[0] = ok ? ldg_u32x4(wr + K0 + 32 * g) : zero;
-    wr2[1] = ok ? ldg_u32x4(wr + K0 + 32 * g + 16) : zero;
-    sbr = ok ? (uint32_t)sr[K0 / 32 + g] : 127u;
+  for (int i = 0; i < 2; ++i) {
+    const int ins = wave * 2 + i;
+    const int xr = ins * 8 + (lane >> 3);           // activation row in the tile
+    xseg[i] = (lane & 7) ^ (lane >> 3);              // logical segment this lane fetches
+    xoff[i] = (m0 + xr < M) ? (uint32_t)(m0 + xr) * (uint32_t)(K * 2) + xseg[i] * 16 : kGOOB;
+    const int wr = ins * 16 + (lane >> 2);           // weight row in the tile
+    wseg[i] = (lane & 3) ^ ((lane >> 3) & 3);
+    woff[i] = (n0 + wr < N) ? (uint32_t)(n0 + wr) * (uint32_t)K + wseg[i] * 16 : kGOOB;
+  }
+  const int srow = wave * 32 + (lane >> 1), sblk = lane & 1;
+  const uint32_t soff = (n0 + srow < N) ? (uint32_t)(n0 + srow) * (uint32_t)(K / 32) + sblk : kGOOB;
+  const int nst = (K + kGK - 1) / kGK;
+
+  auto issue = [&](int c) {
+    unsigned char* st = smem + (c % kGStages) * kGStageBytes;
+    const int K0 = c * kGK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bool xin = K0 + 8 * xseg[i] < K;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (gemm_lds_ptr)(st + (wave * 2 + i) * 1024), 16,
+                                               xin ? xoff[i] : kGOOB, K0 * 2, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bool win = K0 + 16 * wseg[i] < K;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (gemm_lds_ptr)(st + kGXBytes + (wave * 2 + i) * 1024), 16,
+                                               win ? woff[i] : kGOOB, K0, 0, 0);
+    }
+    const bool sin = K0 + 32 * sblk < K && lane < 64;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (gemm_lds_ptr)(st + kGXBytes + kGWBytes + wave * 256), 1,
+                                             sin ? soff : kGOOB, K0 / 32, 0, 0);
   };
-  auto store_stage = [&](int stage, const u32x4 (&xr4)[4]) {
-    unsigned char* dst = &s_x[stage][srow * kMxLdsRow + shalf * 64];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(dst + 16 * j) = xr4[j];
-  };
 
-  load_chunk(0, xs, wq, sb);
-  store_stage(0, xs);
-  __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const bool more = c + 1 < nch;
-    u32x4 wn[2];
-    uint32_t sbn;
-    if (more) load_chunk(c + 1, xs, wn, sbn);
-    const unsigned char* src = &s_x[c & 1][0];
-    const float p2 = e8m0_pow2(sb);
-    if (wave_has_rows) {
+  floatx16 acc[2][2];
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const u32x4& wv = wq[st >> 1];
-        const uint32_t lo = (st & 1) ? wv.z : wv.x;
-        const uint32_t hi = (st & 1) ? wv.w : wv.y;
-        const bf16x8 a = mxfp8x8_to_bf16(lo, hi, p2);
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if (t < ntf) {
-            const u32x4 bv = *reinterpret_cast<const u32x4*>(src + (t * 32 + l32) * kMxLdsRow + 64 * g + 16 * st);
-            acc[t] = mx_mfma32(a, u32x4_as_bf16x8(bv), acc[t]);
-          }
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][t][r] = 0.0f;
+
+  for (int c = 0; c < kGStages - 1 && c < nst; ++c) issue(c);
+  for (int c = 0; c < nst; ++c) {
+    // stage c's loads are the oldest in flight; later stages may still be outstanding
+    if (c + 2 < nst) gemm_wait_vm<2 * kGOps>();
+    else if (c + 1 < nst) gemm_wait_vm<kGOps>();
+    else gemm_wait_vm<0>();
+    gemm_barrier();  // every wave's part of stage c is in LDS; stage c - 1 is consumed
+    if (c + kGStages - 1 < nst) issue(c + kGStages - 1);
+
+    const unsigned char* st = smem + (c % kGStages) * kGStageBytes;
+    const unsigned char* xs = st;
+    const unsigned char* ws = st + kGXBytes;
+    const unsigned char* ss = st + kGXBytes + kGWBytes;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      gu32x4v wv[2];
+      float p2[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = nq * 64 + i * 32 + l32;
+        const int slot = (2 * p + g) ^ ((r >> 1) & 3);
+        wv[i] = *reinterpret_cast<const gu32x4v*>(ws + r * 64 + slot * 16);
+        const uint32_t code = *(ss + (r >> 5) * 256 + ((r & 31) * 2 + p) * 4);
+        p2[i] = e8m0_pow2(code);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 a[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) a[i] = mxfp8x8_to_bf16(wv[i][2 * h], wv[i][2 * h + 1], p2[i]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int r = mh * 64 + t * 32 + l32;
+          const int j = 4 * p + 2 * g + h;
+          const gu32x4v bv = *reinterpret_cast<const gu32x4v*>(xs + r * 128 + ((j ^ (r & 7)) * 16));
+          const bf16x8 b = __builtin_bit_cast(bf16x8, bv);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) acc[i][t] = mx_mfma32(a[i], b, acc[i][t]);
         }
       }
     }
-    if (more) store_stage((c + 1) & 1, xs);
-    __syncthreads();
-    if (more) {
-      wq[0] = wn[0];
-      wq[1] = wn[1];
-      sb = sbn;
-    }
   }
-  if (!wave_has_rows) return;
-  // accumulator r of fragment t: weight row n0 + 8*(r/4) + 4*g + r%4, activation row t*32 + l32
+
+  // accumulator r of fragment (i, t): weight row 8 * (r / 4) + 4 * g + r % 4 of the
+  // fragment, activation row l32 of the fragment
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int m = t * 32 + l32;
-    if (t < ntf && m < nrows) {
+  for (int t = 0; t < 2; ++t) {
+    const int m = m0 + mh * 64 + t * 32 + l32;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
-        const int nb = n0 + 8 * qd + 4 * g;
+        const int nb = n0 + nq * 64 + i * 32 + 8 * qd + 4 * g;
         if (nb < N) {
           uint32_t hb[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) hb[r] = bf16_rne(acc[t][4 * qd + r]);
-          store_bf16x4(y + (size_t)(m0 + m) * N + nb, hb, N - nb, (N & 3) == 0);
+          for (int r = 0; r < 4; ++r) hb[r] = bf16_rne(acc[i][t][4 * qd + r]);
+          store_bf16x4(y + (size_t)m * N + nb, hb, N - nb, (N & 3) == 0);
         }
       }
     }
@@ -217,10 +291,18 @@ hipError_t launch_mxfp8(const uint16_t* x, int M, int N, int K, const uint8_t* w
   if (M <= 16) {
     hipLaunchKernelGGL(mxfp8_gemv_kernel<kMxGemvKsplit>, dim3((N + 15) / 16), dim3(64 * kMxGemvKsplit), 0,
                        stream, x, M, N, K, w, s, y);
-  } else {
-    hipLaunchKernelGGL(mxfp8_gemm_kernel, dim3((N + 127) / 128, (M + kMxRows - 1) / kMxRows), dim3(256), 0,
-                       stream, x, M, N, K, w, s, y);
+    return hipGetLastError();
   }
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mxfp8_gemm_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kGLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int mtiles = (M + kGM - 1) / kGM, ntiles = (N + kGN - 1) / kGN;
+  hipLaunchKernelGGL(mxfp8_gemm_kernel, dim3(mtiles * ntiles), dim3(kGThreads), kGLdsBytes, stream, x, M, N, K, w,
+                     s, y, mtiles);
   return hipGetLastError();
 }
 

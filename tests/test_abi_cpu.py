@@ -107,6 +107,9 @@ def test_combine_and_mxfp8_refusals():
     assert L.mxfp8_gemm(A, 1, 16, 48, A, A, A, None) == SHAPE
     assert L.mxfp8_gemm(A, 0, 16, 64, A, A, A, None) == SHAPE
     assert L.mxfp8_gemm(A, 1, 16, 64, A, A + 1, A, None) == ALIGN
+    # 32-bit buffer offsets: N * K and M * K * 2 must stay below 2^31
+    assert L.mxfp8_gemm(A, 1, 1 << 20, 1 << 11, A, A, A, None) == SHAPE
+    assert L.mxfp8_gemm(A, 1 << 19, 16, 1 << 11, A, A, A, None) == SHAPE
 
 
 def test_last_error_empty_before_any_launch():
