@@ -101,4 +101,12 @@ __device__ __forceinline__ u32x4 ldg_u32x4(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t word_of(const u32x4& v, int s) {
+  return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
+}
+
 }  // namespace moe

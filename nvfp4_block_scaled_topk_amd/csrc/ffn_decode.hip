@@ -82,94 +82,6 @@ __device__ __forceinline__ unsigned long long h_word(uint32_t lo, uint32_t hi, u
   return (unsigned long long)(lo | (hi << 16)) | ((unsigned long long)tag << 32);
 }
 
-__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t word_of(const u32x4& v, int s) {
-  return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
-}
-
-// Accumulates NW weight matrices (rows wrow[i], K = K elements) against one activation
-// row per lane column, over 128-element chunks [c_begin, c_end) and, when `tail`, the
-// 32-element chunks past the last full 128 chunk.
-template <int NW>
-__device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW],
-                                                  const uint8_t* const (&wsc)[NW],
-                                                  const uint16_t* __restrict__ act, bool valid,
-                                                  int K, int c_begin, int c_end, bool tail,
-                                                  floatx4 (&acc)[NW]) {
-  const int grp = (threadIdx.x & 63) >> 4;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  int c = c_begin;
-  // two chunks in flight per iteration
-  for (; c + 1 < c_end; c += 2) {
-    u32x4 q[2][NW];
-    uint32_t sc[2][NW];
-    u32x4 xv[2][4];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int K0 = (c + h) * 128;
-#pragma unroll
-      for (int i = 0; i < NW; ++i) {
-        q[h][i] = ldg_u32x4(wq[i] + K0 / 2 + 16 * grp);
-        sc[h][i] = *reinterpret_cast<const uint16_t*>(wsc[i] + K0 / 16 + 2 * grp);
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) xv[h][s] = valid ? ldg_u32x4(act + K0 + 32 * grp + 8 * s) : zero;
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int i = 0; i < NW; ++i) {
-        const E4M3Split s0 = e4m3_split(sc[h][i] & 0xFFu);
-        const E4M3Split s1 = e4m3_split(sc[h][i] >> 8);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 wv = nvfp4x8_to_bf16(word_of(q[h][i], s), s < 2 ? s0 : s1);
-          acc[i] = mfma16(wv, u32x4_as_bf16x8(xv[h][s]), acc[i]);
-        }
-      }
-    }
-  }
-  for (; c < c_end; ++c) {
-    const int K0 = c * 128;
-    u32x4 q[NW];
-    uint32_t sc[NW];
-    u32x4 xv[4];
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      q[i] = ldg_u32x4(wq[i] + K0 / 2 + 16 * grp);
-      sc[i] = *reinterpret_cast<const uint16_t*>(wsc[i] + K0 / 16 + 2 * grp);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) xv[s] = valid ? ldg_u32x4(act + K0 + 32 * grp + 8 * s) : zero;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      const E4M3Split s0 = e4m3_split(sc[i] & 0xFFu);
-      const E4M3Split s1 = e4m3_split(sc[i] >> 8);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 wv = nvfp4x8_to_bf16(word_of(q[i], s), s < 2 ? s0 : s1);
-        acc[i] = mfma16(wv, u32x4_as_bf16x8(xv[s]), acc[i]);
-      }
-    }
-  }
-  if (tail) {
-    // 32-element chunks: lane group g holds elements K0 + 8g .. K0 + 8g + 7
-    for (int K0 = (K / 128) * 128; K0 < K; K0 += 32) {
-      const u32x4 xv = valid ? ldg_u32x4(act + K0 + 8 * grp) : zero;
-#pragma unroll
-      for (int i = 0; i < NW; ++i) {
-        const uint32_t q = *reinterpret_cast<const uint32_t*>(wq[i] + K0 / 2 + 4 * grp);
-        const E4M3Split s = e4m3_split(wsc[i][K0 / 16 + (grp >> 1)]);
-        acc[i] = mfma16(nvfp4x8_to_bf16(q, s), u32x4_as_bf16x8(xv), acc[i]);
-      }
-    }
-  }
-}
-
-
 struct DownPrefetch {
   u32x4 q[kDownPrefetch];
   uint32_t sc[kDownPrefetch];

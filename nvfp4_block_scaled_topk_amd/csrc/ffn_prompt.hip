@@ -79,14 +79,17 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// Per-block tile table: s_pref[e] = number of 256-row tiles of experts < e.
+// Per-block tile table: s_pref[e] = number of 256-row tiles of experts < e (experts with
+// at most kSkinnyRows rows have none).
 __device__ void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int* s_pref) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int run = 0;
     for (int base = 0; base < E; base += 64) {
       const int e = base + lane;
-      const int v = e < E ? (offsets[e + 1] - offsets[e] + kPromptRows - 1) / kPromptRows : 0;
+      const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+      // experts with few rows go to the weight-streaming kernels instead
+      const int v = cnt > kSkinnyRows ? (cnt + kPromptRows - 1) / kPromptRows : 0;
       int incl = v;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -386,8 +389,12 @@ hipError_t launch_ffn_prompt(const FFNArgs& a, hipStream_t stream) {
   const int ncu = device_cu_count();
   const int ct_gu = (a.f + 127) / 128;
   const int grid_gu = (int)std::min<long long>(max_tiles * ct_gu, ncu);
+  hipError_t err = launch_ffn_skinny_gateup(a, stream);
+  if (err != hipSuccess) return err;
   hipLaunchKernelGGL(ffn_prompt_kernel<0>, dim3(grid_gu), dim3(kPromptThreads), kPromptLdsBytes, stream, a, ct_gu);
-  hipError_t err = hipGetLastError();
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  err = launch_ffn_skinny_down(a, stream);
   if (err != hipSuccess) return err;
   const int ct_dn = (a.d + 255) / 256;
   const int grid_dn = (int)std::min<long long>(max_tiles * ct_dn, ncu);

@@ -1,0 +1,246 @@
+// ffn_skinny.hip -- the expert FFN of the experts that receive few rows of a prompt
+// batch.
+//
+// Routing skew leaves most selected experts of a prompt batch with a handful of rows
+// (at 4096 tokens over 256 experts, top-8, the median selected expert has 9 rows), and
+// a grouped-GEMM tile of 256 rows would spend a full tile's weight decode on them. The
+// pages read each selected expert's weights once for all of its rows
+// [FP4-Local checkpoints on DGX Spark, §4 Round 1, #808]; so these experts (at most
+// kSkinnyRows rows each) take the weight-streaming form of the decode path instead:
+// one 16x16x32 bf16 MFMA tile covers all rows of an expert, each lane streams one
+// weight row's packed codes with 128-bit loads, decodes them in registers, and four
+// waves split K and add their sums in LDS in wave order. The grouped GEMM skips these
+// experts. Two launches, gate/up/SwiGLU (-> H, bf16) then down (-> fp32 rows), each a
+// grid-stride loop over (expert, 16 features or columns) items built on the device
+// from expert_offsets.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace moe {
+
+constexpr int kSkThreads = 256;  // 4 waves split K
+constexpr int kSkWaves = 4;
+constexpr int kSkMaxE = 1024;
+
+// Accumulates NW weight matrices (one row per lane column: wq / wsc) against one
+// activation row per lane column (act), over 128-element chunks [c_begin, c_end) and,
+// when `tail`, the 32-element chunks past the last full 128. Two chunks' loads are in
+// flight at a time. Lanes of missing rows (!valid) load no activations: with a few
+// rows an expert, that keeps the activation traffic far below the weight traffic.
+template <int NW>
+__device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW],
+                                                  const uint8_t* const (&wsc)[NW],
+                                                  const uint16_t* __restrict__ act, bool valid,
+                                                  int K, int c_begin, int c_end, bool tail,
+                                                  floatx4 (&acc)[NW]) {
+  const int grp = (threadIdx.x & 63) >> 4;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  int c = c_begin;
+  // two chunks in flight per iteration
+  for (; c + 1 < c_end; c += 2) {
+    u32x4 q[2][NW];
+    uint32_t sc[2][NW];
+    u32x4 xv[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int K0 = (c + h) * 128;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        q[h][i] = ldg_u32x4(wq[i] + K0 / 2 + 16 * grp);
+        sc[h][i] = *reinterpret_cast<const uint16_t*>(wsc[i] + K0 / 16 + 2 * grp);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xv[h][s] = valid ? ldg_u32x4(act + K0 + 32 * grp + 8 * s) : zero;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        const E4M3Split s0 = e4m3_split(sc[h][i] & 0xFFu);
+        const E4M3Split s1 = e4m3_split(sc[h][i] >> 8);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 wv = nvfp4x8_to_bf16(word_of(q[h][i], s), s < 2 ? s0 : s1);
+          acc[i] = mfma16(wv, u32x4_as_bf16x8(xv[h][s]), acc[i]);
+        }
+      }
+    }
+  }
+  for (; c < c_end; ++c) {
+    const int K0 = c * 128;
+    u32x4 q[NW];
+    uint32_t sc[NW];
+    u32x4 xv[4];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      q[i] = ldg_u32x4(wq[i] + K0 / 2 + 16 * grp);
+      sc[i] = *reinterpret_cast<const uint16_t*>(wsc[i] + K0 / 16 + 2 * grp);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) xv[s] = valid ? ldg_u32x4(act + K0 + 32 * grp + 8 * s) : zero;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const E4M3Split s0 = e4m3_split(sc[i] & 0xFFu);
+      const E4M3Split s1 = e4m3_split(sc[i] >> 8);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 wv = nvfp4x8_to_bf16(word_of(q[i], s), s < 2 ? s0 : s1);
+        acc[i] = mfma16(wv, u32x4_as_bf16x8(xv[s]), acc[i]);
+      }
+    }
+  }
+  if (tail) {
+    // 32-element chunks: lane group g holds elements K0 + 8g .. K0 + 8g + 7
+    for (int K0 = (K / 128) * 128; K0 < K; K0 += 32) {
+      const u32x4 xv = valid ? ldg_u32x4(act + K0 + 8 * grp) : zero;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        const uint32_t q = *reinterpret_cast<const uint32_t*>(wq[i] + K0 / 2 + 4 * grp);
+        const E4M3Split s = e4m3_split(wsc[i][K0 / 16 + (grp >> 1)]);
+        acc[i] = mfma16(nvfp4x8_to_bf16(q, s), u32x4_as_bf16x8(xv), acc[i]);
+      }
+    }
+  }
+}
+
+
+
+// Experts with 1 .. kSkinnyRows rows, in index order, into LDS; returns their number.
+__device__ int skinny_list(const int32_t* __restrict__ offsets, int E, int* s_off, int* s_e, int* s_r0,
+                           int* s_n, int* s_cnt) {
+  for (int i = threadIdx.x; i <= E; i += kSkThreads) s_off[i] = offsets[i];
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int seen = 0;
+    for (int base = 0; base < E; base += 64) {
+      const int e = base + lane;
+      int o0 = 0, c = 0;
+      if (e < E) {
+        o0 = s_off[e];
+        c = s_off[e + 1] - o0;
+      }
+      const bool pick = c >= 1 && c <= kSkinnyRows;
+      const uint64_t m = __ballot(pick);
+      if (pick) {
+        const int r = seen + __popcll(m & ((1ull << lane) - 1ull));
+        s_e[r] = e;
+        s_r0[r] = o0;
+        s_n[r] = c;
+      }
+      seen += __popcll(m);
+    }
+    if (lane == 0) *s_cnt = seen;
+  }
+  __syncthreads();
+  return *s_cnt;
+}
+
+__global__ __launch_bounds__(kSkThreads) void ffn_skinny_gateup_kernel(FFNArgs a) {
+  __shared__ int s_off[kSkMaxE + 1];
+  __shared__ int s_e[kSkMaxE], s_r0[kSkMaxE], s_n[kSkMaxE];
+  __shared__ int s_cnt;
+  __shared__ floatx4 red[kSkWaves][2][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int U = skinny_list(a.offsets, a.E, s_off, s_e, s_r0, s_n, &s_cnt);
+  const int nft = a.f / 16;
+  const int nch = a.d / 128;
+  for (int i = blockIdx.x; i < U * nft; i += gridDim.x) {
+    const int u = i / nft, ft = i - u * nft;
+    const int e = s_e[u], r0 = s_r0[u], ne = s_n[u];
+    const size_t wrow = (size_t)e * a.f + ft * 16 + col;
+    const uint8_t* const wq[2] = {a.gate_q + wrow * (a.d / 2), a.up_q + wrow * (a.d / 2)};
+    const uint8_t* const wsc[2] = {a.gate_s + wrow * (a.d / 16), a.up_s + wrow * (a.d / 16)};
+    const bool valid = col < ne;
+    const uint16_t* act = a.x + (size_t)(a.sorted_rows[r0 + (valid ? col : 0)] / a.k) * a.d;
+    floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    decode_accumulate<2>(wq, wsc, act, valid, a.d, nch * wave / kSkWaves, nch * (wave + 1) / kSkWaves,
+                         wave == kSkWaves - 1, acc);
+    red[wave][0][lane] = acc[0];
+    red[wave][1][lane] = acc[1];
+    __syncthreads();
+    if (wave == 0 && valid) {
+      floatx4 G = red[0][0][lane], Uv = red[0][1][lane];
+#pragma unroll
+      for (int w = 1; w < kSkWaves; ++w) {
+        G += red[w][0][lane];
+        Uv += red[w][1][lane];
+      }
+      const float tg = a.gate_ts[e], tu = a.up_ts[e];
+      uint32_t hb[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hb[r] = bf16_rne(silu_f32(tg * G[r]) * (tu * Uv[r]));
+      // lane holds routed row `col`, features 4*grp .. 4*grp + 3 of the tile
+      uint2 v;
+      v.x = hb[0] | (hb[1] << 16);
+      v.y = hb[2] | (hb[3] << 16);
+      *reinterpret_cast<uint2*>(a.h + (size_t)(r0 + col) * a.f + ft * 16 + 4 * grp) = v;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kSkThreads) void ffn_skinny_down_kernel(FFNArgs a) {
+  __shared__ int s_off[kSkMaxE + 1];
+  __shared__ int s_e[kSkMaxE], s_r0[kSkMaxE], s_n[kSkMaxE];
+  __shared__ int s_cnt;
+  __shared__ floatx4 red[kSkWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int U = skinny_list(a.offsets, a.E, s_off, s_e, s_r0, s_n, &s_cnt);
+  const int ndt = a.d / 16;
+  const int nch = a.f / 128;
+  for (int i = blockIdx.x; i < U * ndt; i += gridDim.x) {
+    const int u = i / ndt, dt = i - u * ndt;
+    const int e = s_e[u], r0 = s_r0[u], ne = s_n[u];
+    const size_t wrow = (size_t)e * a.d + dt * 16 + col;
+    const uint8_t* const wq[1] = {a.down_q + wrow * (a.f / 2)};
+    const uint8_t* const wsc[1] = {a.down_s + wrow * (a.f / 16)};
+    const bool valid = col < ne;
+    const uint16_t* act = a.h + (size_t)(r0 + (valid ? col : 0)) * a.f;
+    floatx4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+    decode_accumulate<1>(wq, wsc, act, valid, a.f, nch * wave / kSkWaves, nch * (wave + 1) / kSkWaves,
+                         wave == kSkWaves - 1, acc);
+    red[wave][lane] = acc[0];
+    __syncthreads();
+    if (wave == 0 && valid) {
+      floatx4 O = red[0][lane];
+#pragma unroll
+      for (int w = 1; w < kSkWaves; ++w) O += red[w][lane];
+      const float td = a.down_ts[e];
+      float4 v;
+      v.x = td * O[0];
+      v.y = td * O[1];
+      v.z = td * O[2];
+      v.w = td * O[3];
+      *reinterpret_cast<float4*>(a.y_rows + (size_t)(r0 + col) * a.d + dt * 16 + 4 * grp) = v;
+    }
+    __syncthreads();
+  }
+}
+
+static int skinny_grid() {
+  static int grid = 0;
+  if (grid == 0) {
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+      int v = 0;
+      if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ncu = v;
+    }
+    grid = 8 * ncu;
+  }
+  return grid;
+}
+
+hipError_t launch_ffn_skinny_gateup(const FFNArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(ffn_skinny_gateup_kernel, dim3(skinny_grid()), dim3(kSkThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_skinny_down(const FFNArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(ffn_skinny_down_kernel, dim3(skinny_grid()), dim3(kSkThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

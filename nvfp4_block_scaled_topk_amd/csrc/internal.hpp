@@ -41,6 +41,11 @@ inline bool use_decode_path(int T, int d, int f) {
 }
 hipError_t launch_ffn_decode(const FFNArgs& a, uint32_t tag, hipStream_t stream);
 hipError_t launch_ffn_prompt(const FFNArgs& a, hipStream_t stream);
+// Prompt batches: experts with at most kSkinnyRows rows take the weight-streaming
+// kernels (ffn_skinny.hip); the grouped GEMM takes the others.
+constexpr int kSkinnyRows = 16;
+hipError_t launch_ffn_skinny_gateup(const FFNArgs& a, hipStream_t stream);
+hipError_t launch_ffn_skinny_down(const FFNArgs& a, hipStream_t stream);
 
 // combine
 hipError_t launch_combine(const float* y_rows, const int32_t* row_of, const float* w, int T,
