@@ -11,8 +11,10 @@ projection (N=12288, K=4096, M=1 and 512) are measured beside it under "also".
 
 Timing: the K steps are enqueued behind a GPU sleep kernel so the device never
 waits for the host, and bracketed by HIP events on the stream the kernels run on
-(torch's current stream). The expert FFN of every step is bracketed by its own
-pair of events: that is the dominant work, reported against its roofline.
+(torch's current stream). The expert FFN is the dominant work and is reported
+against its roofline: its duration per call comes from a second timed loop of
+back-to-back FFN calls between one pair of events (the per-step FFN events of the
+layer loop, which include event overhead, are reported beside it).
 Decode steps rotate through distinct copies of the expert weights (>= 1 GB in
 total) so the 256 MB Infinity Cache cannot serve repeats.
 
@@ -35,6 +37,12 @@ METRIC = "MoE-layer tokens/s + HBM GB/s (decode) and MFMA TFLOP/s (prompt), 1×M
 HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 BF16_PEAK_TFLOPS = 2500.0       # MI355X published dense bf16 MFMA rate
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+# kernel sources whose hash a traffic record must match, per path
+DECODE_FILES = ["ffn_decode.hip", "device.hpp"]
+PROMPT_FILES = ["ffn_prompt.hip", "ffn_skinny.hip", "device.hpp"]
+MXFP8_FILES = ["mxfp8.hip", "device.hpp"]
+PROMPT_KERNELS = ("moe_expert_ffn_nvfp4 prompt path (ffn_prompt_kernel grouped GEMM gate/up + down; "
+                  "ffn_skinny gate/up + down for experts with <= 16 rows)")
 
 
 def log(*a):
@@ -159,7 +167,20 @@ def bench_moe(name, steps, warmup, rotations, timer, seed=0):
     total_ms = start.elapsed_time(end)
     ffn_ms = [a.elapsed_time(b) for a, b in evs]
     ms_per_step = total_ms / steps
-    ffn_avg_ms = sum(ffn_ms) / len(ffn_ms)
+    ffn_in_layer_ms = sum(ffn_ms) / len(ffn_ms)
+
+    # The expert FFN alone, back to back (same routing, rotating weight copies), between
+    # one pair of events: its average duration per call, without per-call event overhead.
+    n_ffn = max(steps, 20)
+    a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    timer.queue_ahead(host_ms_per_step * n_ffn + 20.0)
+    a_ev.record()
+    for i in range(n_ffn):
+        M.expert_ffn_nvfp4(x, copies[i % rotations], off, srows, k, out=y_rows, workspace=fws, check=False)
+    b_ev.record()
+    torch.cuda.synchronize()
+    ffn_avg_ms = a_ev.elapsed_time(b_ev) / n_ffn
 
     # algorithmic work (only what the method must move / compute)
     eb = expert_bytes(d, f)
@@ -169,7 +190,7 @@ def bench_moe(name, steps, warmup, rotations, timer, seed=0):
     res = dict(
         name=name, T=T, d=d, f=f, E=E, k=k, touched_experts=U, rotations=rotations,
         ms_per_step=ms_per_step, tokens_per_s=T / (ms_per_step / 1e3),
-        ffn_avg_us=ffn_avg_ms * 1e3, ffn_min_us=min(ffn_ms) * 1e3,
+        ffn_avg_us=ffn_avg_ms * 1e3, ffn_in_layer_us=ffn_in_layer_ms * 1e3, ffn_min_in_layer_us=min(ffn_ms) * 1e3,
         ffn_bytes=ffn_bytes, layer_bytes=layer_bytes, flops=flops,
         layer_hbm_gbps=layer_bytes / (ms_per_step / 1e3) / 1e9,
         ffn_hbm_gbps=ffn_bytes / (ffn_avg_ms / 1e3) / 1e9,
@@ -225,10 +246,12 @@ def bench_mxfp8(M, steps, warmup, rotations, timer, seed=0):
            "hbm_gbps": nbytes / (avg_ms / 1e3) / 1e9, "tflops": flops / (avg_ms / 1e3) / 1e12}
     if M <= 16:
         res["roofline"] = {"bound": "hbm", "achieved": res["hbm_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": res["hbm_gbps"] / HBM_PEAK_GBPS, "kernel": "mxfp8_gemv_kernel"}
+                           "frac": res["hbm_gbps"] / HBM_PEAK_GBPS, "kernel": "mxfp8_gemv_kernel",
+                           "algorithmic_bytes": nbytes, "avg_us": res["avg_us"]}
     else:
         res["roofline"] = {"bound": "mfma", "achieved": res["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": res["tflops"] / BF16_PEAK_TFLOPS, "kernel": "mxfp8_gemm_kernel"}
+                           "frac": res["tflops"] / BF16_PEAK_TFLOPS, "kernel": "mxfp8_gemm_kernel",
+                           "algorithmic_flop": flops, "avg_us": res["avg_us"]}
     log(f"[bench] mxfp8 M={M}: {json.dumps(res)}")
     del ws, w0, s0
     torch.cuda.empty_cache()
@@ -266,7 +289,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prompt", "long_prompt"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["tiny", "decode", "prompt", "long_prompt", "mxfp8_M1", "mxfp8_M512"])
     ap.add_argument("--rotations", type=int, default=0, help="weight copies to rotate (0: >= 1 GB)")
     ap.add_argument("--no-also", action="store_true", help="skip the prompt, long-prompt and MXFP8 measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -288,6 +312,19 @@ def main(argv=None):
     timer = Timer(torch)
     timer.calibrate_sleep()
 
+    if args.workload.startswith("mxfp8_M"):
+        # the MXFP8 projection alone (N=12288, K=4096): its own line, rows/s as the value
+        m = int(args.workload[len("mxfp8_M"):])
+        r = bench_mxfp8(m, args.steps, args.warmup, 20, timer)
+        r["roofline"]["traffic"] = load_traffic(args.workload, MXFP8_FILES)
+        print(json.dumps({
+            "metric": METRIC, "value": r["rows_per_s"], "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": r["avg_us"] / 1e3, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"MXFP8 projection: M={m} bf16 rows, W 12288x4096 E4M3 in blocks of 32 with E8M0 scales"},
+            "roofline": r["roofline"], "cpu_baseline": None}), flush=True)
+        return
+
     cid, T, d, f, E, k, zipf = workloads.MOE_CONFIGS[args.workload]
     rot = args.rotations or max(1, -(-(1 << 30) // (E * expert_bytes(d, f))))
     main_res = bench_moe(args.workload, args.steps, args.warmup, rot, timer)
@@ -298,8 +335,8 @@ def main(argv=None):
         also["long_prompt"] = {
             "tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"], "touched_experts": r["touched_experts"],
             "roofline": {"bound": "mfma", "achieved": r["ffn_tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": r["ffn_tflops"] / BF16_PEAK_TFLOPS, "traffic": load_traffic("long_prompt", ["ffn_prompt.hip", "device.hpp"]),
-                         "kernel": "moe_expert_ffn_nvfp4 grouped GEMM (ffn_prompt_kernel gate/up + down)",
+                         "frac": r["ffn_tflops"] / BF16_PEAK_TFLOPS, "traffic": load_traffic("long_prompt", PROMPT_FILES),
+                         "kernel": PROMPT_KERNELS,
                          "algorithmic_flop": r["flops"], "avg_us": r["ffn_avg_us"]},
             "layer_tflops": r["layer_tflops"],
         }
@@ -311,25 +348,29 @@ def main(argv=None):
             "ffn_avg_us": r["ffn_avg_us"], "ffn_hbm_gbps": r["ffn_hbm_gbps"],
             "ffn_hbm_frac": r["ffn_hbm_gbps"] / HBM_PEAK_GBPS, "ffn_tflops": r["ffn_tflops"],
             "ffn_mfma_frac": r["ffn_tflops"] / BF16_PEAK_TFLOPS,
+            "ffn_traffic_bytes": load_traffic("prompt", PROMPT_FILES),
         }
     if not args.no_also:
         for m in (1, 512):
             r = bench_mxfp8(m, max(args.also_steps, 50), 5, 20, timer)
+            r["roofline"]["traffic"] = load_traffic(f"mxfp8_M{m}", MXFP8_FILES)
             also[f"mxfp8_M{m}"] = r
 
     decode_like = main_res["T"] <= 16
     if decode_like:
-        files = ["ffn_decode.hip", "device.hpp"]
+        files = DECODE_FILES
         roof = {"bound": "hbm", "achieved": main_res["ffn_hbm_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": main_res["ffn_hbm_gbps"] / HBM_PEAK_GBPS, "traffic": load_traffic(args.workload, files),
                 "kernel": "moe_expert_ffn_nvfp4 decode (ffn_decode_kernel: gate/up/SwiGLU and down in one launch)",
-                "algorithmic_bytes": main_res["ffn_bytes"], "avg_us": main_res["ffn_avg_us"]}
+                "algorithmic_bytes": main_res["ffn_bytes"], "avg_us": main_res["ffn_avg_us"],
+                "avg_us_in_layer": main_res["ffn_in_layer_us"]}
     else:
-        files = ["ffn_prompt.hip", "device.hpp"]
+        files = PROMPT_FILES
         roof = {"bound": "mfma", "achieved": main_res["ffn_tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": main_res["ffn_tflops"] / BF16_PEAK_TFLOPS, "traffic": load_traffic(args.workload, files),
-                "kernel": "moe_expert_ffn_nvfp4 grouped GEMM (ffn_prompt_kernel gate/up + down)",
-                "algorithmic_flop": main_res["flops"], "avg_us": main_res["ffn_avg_us"]}
+                "kernel": PROMPT_KERNELS,
+                "algorithmic_flop": main_res["flops"], "avg_us": main_res["ffn_avg_us"],
+                "avg_us_in_layer": main_res["ffn_in_layer_us"]}
 
     cpu = None
     if not args.no_cpu_baseline:
