@@ -9,7 +9,7 @@ import pytest
 import workloads
 from oracle import band, formats as F, moe, mxfp8 as omx
 
-from gpu_util import check_layer_full, check_layer_sampled, check_routing, run_moe, say
+from gpu_util import check_layer_full, check_layer_sampled, check_routing, run_moe, say, upload_moe
 
 pytestmark = pytest.mark.gpu
 
@@ -82,6 +82,7 @@ SMALL = [
     (300, 256, 128, 4, 2),   # prompt path, experts with > 128 rows
     (40, 64, 32, 64, 8),     # many experts, few rows each
     (8, 2048, 768, 128, 8),  # decode shape with 8 tokens
+    (200, 128, 64, 32, 4),   # prompt path: experts on both sides of the 16-row split
 ]
 
 
@@ -123,6 +124,35 @@ def test_layer_deterministic_and_permutation():
         c = run_moe(inp2)
         assert np.array_equal(c["out"], a["out"][perm])
         assert np.array_equal(c["ids"], a["ids"][perm])
+
+
+def test_decode_workspace_reuse():
+    """The few-token path hands H over through tagged words in the workspace: one
+    workspace, first filled with random bytes, then shared by consecutive calls with
+    different routings and shapes (a larger call in between), each checked against the
+    oracle -- words left by an earlier call must never be taken for this call's."""
+    import torch
+    import nvfp4_block_scaled_topk_amd as M
+    from oracle import band, moe as omoe
+
+    shapes = [(4, 256, 128, 8, 2), (3, 96, 64, 5, 2), (16, 160, 96, 6, 3), (40, 128, 64, 16, 4),
+              (8, 512, 256, 16, 4), (4, 256, 128, 8, 2)]
+    need = max(M.expert_ffn_workspace(T, d, f, E, k) for (T, d, f, E, k) in shapes)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda")
+    for i, (T, d, f, E, k) in enumerate(shapes):
+        inp = workloads.make_moe(T, d, f, E, k, seed=20 + i, config_id=62, zipf=True)
+        say(f"workspace reuse call {i}: T={T} d={d} f={f} E={E} k={k}")
+        x, logits, ex = upload_moe(inp)
+        ids, w, off, srows, rof = M.route_topk(logits, k)
+        y = torch.full((T * k, d), float("nan"), dtype=torch.float32, device="cuda")
+        M.expert_ffn_nvfp4(x, ex, off, srows, k, out=y, workspace=ws)
+        out = M.combine(y, rof, w)
+        torch.cuda.synchronize()
+        ref = omoe.moe_layer(inp)
+        got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        rep = band.classify(got, ref.out_bits, ref.mass, ref.slack)
+        say(f"[reuse {i}] {rep}")
+        assert rep.ok(), f"call {i}: {rep}"
 
 
 # ---------------------------------------------------------------- MXFP8
