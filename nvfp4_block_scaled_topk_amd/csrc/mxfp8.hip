@@ -8,6 +8,7 @@
 // conversion applies the power-of-two block scale while decoding (one instruction
 // per two weights).
 //
+// gemv (M <= 4): vector ALUs, see mxfp8_gemv_valu_kernel.
 // gemv (M <= 16): one 16x16x32 MFMA tile covers every activation row; a wave owns 16
 //   weight rows and streams them with 128-bit loads (16 elements a lane, half of a
 //   scale block); KSPLIT waves split K and reduce in LDS in wave order.
@@ -114,6 +115,87 @@ __global__ __launch_bounds__(64 * KSPLIT) void mxfp8_gemv_kernel(const uint16_t*
 #pragma unroll
   for (int r = 0; r < 4; ++r) hb[r] = bf16_rne(o[r]);
   store_bf16x4(y + (size_t)col * N + nb, hb, N - nb, (N & 3) == 0);
+}
+
+// gemv for 1..4 activation rows on the vector ALUs: with so few rows the matrix cores
+// add nothing, and plain per-row reads let each wave load 1 KB contiguous runs of a weight
+// row (full cache lines, HBM bursts) instead of 64-byte pieces of 16 rows. A wave owns
+// kVRows weight rows; lane l covers bytes [1024 i + 16 l, + 16) of each row in step i,
+// decodes its 16 E4M3 codes with the scaled FP8 -> fp32 conversion (the block's E8M0
+// scale applied on the way) and accumulates x . w in fp32; the wave then sums its lanes.
+constexpr int kVRows = 4;        // weight rows a wave
+constexpr int kVThreads = 256;   // 4 waves
+
+template <int MM>
+__global__ __launch_bounds__(kVThreads) void mxfp8_gemv_valu_kernel(const uint16_t* __restrict__ x, int N, int K,
+                                                                    const uint8_t* __restrict__ w,
+                                                                    const uint8_t* __restrict__ s,
+                                                                    uint16_t* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n0 = (blockIdx.x * (kVThreads / 64) + wave) * kVRows;
+  if (n0 >= N) return;
+  float acc[kVRows][MM];
+#pragma unroll
+  for (int r = 0; r < kVRows; ++r)
+#pragma unroll
+    for (int m = 0; m < MM; ++m) acc[r][m] = 0.0f;
+  const int nstep = (K + 1023) / 1024;
+  for (int i = 0; i < nstep; ++i) {
+    const int k0 = i * 1024 + lane * 16;  // this lane's 16 codes
+    if (k0 >= K) break;                    // K is a multiple of 32: a lane's 16 codes are all in range or none
+    // activations of this lane's 16 elements, as fp32
+    float xf[MM][16];
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      const u32x4 xa = ldg_u32x4(x + (size_t)m * K + k0);
+      const u32x4 xb = ldg_u32x4(x + (size_t)m * K + k0 + 8);
+      const uint32_t wd[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        xf[m][2 * j] = bits_f32(wd[j] << 16);
+        xf[m][2 * j + 1] = bits_f32(wd[j] & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kVRows; ++r) {
+      const int n = n0 + r;
+      if (n < N) {
+        const u32x4 q = ldg_u32x4(w + (size_t)n * K + k0);
+        const float p2 = e8m0_pow2(s[(size_t)n * (K / 32) + k0 / 32]);
+        const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const floatx2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(qw[j], p2, false);
+          const floatx2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(qw[j], p2, true);
+#pragma unroll
+          for (int m = 0; m < MM; ++m) {
+            acc[r][m] = fmaf(lo.x, xf[m][4 * j + 0], acc[r][m]);
+            acc[r][m] = fmaf(lo.y, xf[m][4 * j + 1], acc[r][m]);
+            acc[r][m] = fmaf(hi.x, xf[m][4 * j + 2], acc[r][m]);
+            acc[r][m] = fmaf(hi.y, xf[m][4 * j + 3], acc[r][m]);
+          }
+        }
+      }
+    }
+  }
+  // sum over the wave's lanes (fixed order: the result is the same on every run)
+#pragma unroll
+  for (int r = 0; r < kVRows; ++r)
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      float v = acc[r][m];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+      acc[r][m] = v;
+    }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < kVRows; ++r)
+      if (n0 + r < N)
+#pragma unroll
+        for (int m = 0; m < MM; ++m) y[(size_t)m * N + n0 + r] = bf16_rne(acc[r][m]);
+  }
 }
 
 constexpr int kGM = 128;                        // activation rows per tile
@@ -288,6 +370,16 @@ __global__ __launch_bounds__(kGThreads, 1) void mxfp8_gemm_kernel(const uint16_t
 
 hipError_t launch_mxfp8(const uint16_t* x, int M, int N, int K, const uint8_t* w, const uint8_t* s,
                         uint16_t* y, hipStream_t stream) {
+  if (M <= 4) {
+    const dim3 grid((N + kVRows * (kVThreads / 64) - 1) / (kVRows * (kVThreads / 64)));
+    switch (M) {
+      case 1: hipLaunchKernelGGL(mxfp8_gemv_valu_kernel<1>, grid, dim3(kVThreads), 0, stream, x, N, K, w, s, y); break;
+      case 2: hipLaunchKernelGGL(mxfp8_gemv_valu_kernel<2>, grid, dim3(kVThreads), 0, stream, x, N, K, w, s, y); break;
+      case 3: hipLaunchKernelGGL(mxfp8_gemv_valu_kernel<3>, grid, dim3(kVThreads), 0, stream, x, N, K, w, s, y); break;
+      default: hipLaunchKernelGGL(mxfp8_gemv_valu_kernel<4>, grid, dim3(kVThreads), 0, stream, x, N, K, w, s, y); break;
+    }
+    return hipGetLastError();
+  }
   if (M <= 16) {
     hipLaunchKernelGGL(mxfp8_gemv_kernel<kMxGemvKsplit>, dim3((N + 15) / 16), dim3(64 * kMxGemvKsplit), 0,
                        stream, x, M, N, K, w, s, y);
