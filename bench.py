@@ -246,7 +246,8 @@ def bench_mxfp8(M, steps, warmup, rotations, timer, seed=0):
            "hbm_gbps": nbytes / (avg_ms / 1e3) / 1e9, "tflops": flops / (avg_ms / 1e3) / 1e12}
     if M <= 16:
         res["roofline"] = {"bound": "hbm", "achieved": res["hbm_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": res["hbm_gbps"] / HBM_PEAK_GBPS, "kernel": "mxfp8_gemv_kernel",
+                           "frac": res["hbm_gbps"] / HBM_PEAK_GBPS,
+                           "kernel": "mxfp8_gemv_valu_kernel" if M <= 4 else "mxfp8_gemv_kernel",
                            "algorithmic_bytes": nbytes, "avg_us": res["avg_us"]}
     else:
         res["roofline"] = {"bound": "mfma", "achieved": res["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
