@@ -113,9 +113,10 @@ int moe_route_topk(const float* logits, int T, int E, int k,
  * Sizes: 1 <= T, d and f multiples of 32 (>= 32), 1 <= E <= 1024, 1 <= k <= min(E, 32).
  * Workspace: at least moe_expert_ffn_nvfp4_workspace(T, d, f, E, k) bytes (holds H; no
  * initial contents needed).
- * Few tokens (T <= 16 and T * (max(d, f) + 8) * 2 <= 64 KiB) run as one launch whose
- * down-product workgroups wait, with a bounded spin, for the gate/up workgroups of the
- * same expert; the launch never has more workgroups than the GPU holds at once. If
+ * Few tokens (T <= 16, d <= 4096, f <= 1024 and T * (max(d, f) + 8) * 2 <= 64 KiB) run as
+ * one launch whose down-product workgroups wait, with a bounded spin, for the gate/up
+ * workgroups of the same expert; the launch never has more workgroups than the GPU holds
+ * at once. If
  * other work keeps some of them from becoming resident (for instance another such call
  * running concurrently on a second stream), a wait can expire: the affected rows of
  * y_rows are then NaN, and nothing hangs.

@@ -7,12 +7,16 @@
 // expert's rows (<= 16), so each weight byte is read once whatever the row count.
 //
 // MFMA mapping (per wave and 16-row weight tile): 16 weight rows (output features) x
-// up to 16 routed rows. Each lane streams one weight row's packed codes with 128-bit
-// loads (32 E2M1 codes = two scale blocks) and decodes them in registers into four
-// MFMA operands. Within a 128-element chunk, lane group g (lane / 16) holds elements
+// up to 16 routed rows. In the MFMA operand a lane holds 32 E2M1 codes of one weight
+// row: within a 128-element chunk, lane group g (lane / 16) holds elements
 // [32g, 32g + 32) and MFMA step s takes elements 32g + 8s .. 32g + 8s + 7 of every
 // group -- a permutation of the contraction index, applied identically to the
-// activation operand, so the sums are unchanged.
+// activation operand, so the sums are unchanged. The codes are not loaded in that
+// layout, which would make every load touch 64 bytes of 16 rows: a load covers a pair
+// of chunks (128 bytes, one cache line) of 8 rows, and the wave rearranges each pair
+// through its LDS scratch into the operand layout. Block scales come in whole rows too:
+// a gate/up item's 32 scale rows of each matrix (contiguous in memory) by DMA into
+// LDS, a down tile's 16 scale rows with one 16-byte load a lane.
 //
 // One launch does gate, up, SwiGLU [same page, §4 Round 1, #766] and the down product,
 // with 8-wave blocks and two kinds of work item:
@@ -23,9 +27,9 @@
 //     quarters of their half in LDS in order, form H = bf16_rne(silu(ts_g * G) *
 //     (ts_u * U)) and store it;
 //   down item (u, 128 columns of d): wave w owns a 16-column tile over all of K = f.
-//     A block loads the weight codes of its first down item into registers as soon as
-//     its last gate/up item is done (or at the start, if it has none), so those bytes
-//     are in flight while the other gate/up items finish. It then copies H's rows of u
+//     A block loads the weight codes and scales of its first down item into registers
+//     as soon as its last gate/up item is done (or at the start, if it has none), so
+//     those bytes are in flight while the other gate/up items finish. It then copies H's rows of u
 //     into LDS, waiting until all of them are there, and finishes the products with the
 //     weights already in hand.
 // H in the workspace is self-validating: every 64-bit word holds two bf16 values and
@@ -50,8 +54,9 @@ constexpr int kDecMaxAssign = kDecodeMaxRows * 32;  // T * k
 constexpr int kDecMaxTouched = kDecMaxAssign;      // min(E, T * k)
 constexpr int kGUFeat = 32;                     // features of a gate/up item
 constexpr int kDCols = 16 * kDecWaves;          // columns of d in a down item
-constexpr int kDownPrefetch = 6;                // W_down chunks (128 K) a wave holds before its wait
+constexpr int kDownPairs = 3;                   // W_down chunk pairs (2 x 128 K) a wave holds before its wait
 constexpr uint32_t kSpinLimit = 1u << 20;       // polls (each followed by s_sleep) before giving up
+constexpr int kScrWave = 4096;                  // LDS a wave uses to rearrange its weight codes
 
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
@@ -83,24 +88,34 @@ __device__ __forceinline__ unsigned long long h_word(uint32_t lo, uint32_t hi, u
 }
 
 struct DownPrefetch {
-  u32x4 q[kDownPrefetch];
-  uint32_t sc[kDownPrefetch];
+  u32x4 q[kDownPairs][2];  // [pair][rows 0-7 / 8-15], as loaded
+  u32x4 sc;                // 16 bytes of the wave's 16 scale rows (f bytes, contiguous)
 };
 
 // Dynamic LDS: the activation rows of one expert (gate/up phase; row stride
-// xstride bytes) and later its H rows (down phase; row stride (f + 8) bf16). Both
-// strides are 16 bytes past a multiple of the bank period, which staggers the banks of
-// the 16 rows an MFMA operand read touches.
+// xstride bytes) and later its H rows (down phase; row stride (f + 8) bf16), then
+// kScrWave bytes per wave for rearranging weight codes (which also hold the gate/up
+// partial sums and, at the start, the expert offsets). Both row strides are 16 bytes
+// past a multiple of the bank period, which staggers the banks of the 16 rows an MFMA
+// operand read touches.
 __device__ __forceinline__ int dec_xstride(int d) { return (d * 2 + 1023) / 1024 * 1024 + 16; }
+__host__ __device__ __forceinline__ size_t dec_row_region(int T, int d, int f) {
+  const size_t xs = (size_t)((d * 2 + 1023) / 1024 * 1024 + 16);
+  const size_t hs = (size_t)(f + 8) * sizeof(uint16_t);
+  const size_t r = (size_t)T * (xs > hs ? xs : hs);
+  return (r + 15) / 16 * 16;
+}
 
 __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, uint32_t tag) {
   extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
-  __shared__ floatx4 red[kDecWaves][2][64];  // gate/up partial sums (16 KB); the offsets before that
   __shared__ int s_tok[kDecMaxAssign];
   __shared__ int s_e[kDecMaxTouched], s_r0[kDecMaxTouched], s_n[kDecMaxTouched];
   __shared__ int s_U, s_timeout;
-  int* s_off = reinterpret_cast<int*>(&red[0][0][0]);
-  static_assert(sizeof(red) >= sizeof(int) * (kDecMaxE + 1), "offsets fit the reduction buffer");
+  unsigned char* const s_scr = s_dyn + dec_row_region(a.T, a.d, a.f);
+  unsigned char* const s_sc = s_scr + kDecWaves * kScrWave;  // a gate/up item's block scales
+  int* s_off = reinterpret_cast<int*>(s_scr);
+  static_assert(kDecWaves * kScrWave >= (int)sizeof(int) * (kDecMaxE + 1), "offsets fit the scratch");
+  static_assert(kScrWave >= 2 * 64 * (int)sizeof(floatx4), "partial sums fit a wave's scratch");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -144,23 +159,35 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
   const __amdgpu_buffer_rsrc_t xrs = dec_rsrc(a.x, (uint32_t)(a.T * a.d * 2));
   const u32x4 zero = {0u, 0u, 0u, 0u};
 
-  // ---- this wave's share of a down item: a 16-column tile over all of K = f
-  const int nchD = a.f / 128;
+  // ---- this wave's share of a down item: a 16-column tile over all of K = f. Its 16
+  // code rows are loaded a chunk pair at a time (8 rows x 128 bytes a load, as for
+  // gate/up) and its 16 scale rows (f bytes, contiguous) 16 bytes a lane.
+  const int nchD = a.f / 128, npD = (nchD + 1) / 2;
+  const int grp8 = lane >> 3, seg8 = lane & 7;
   DownPrefetch pf;
+  auto down_rsrc = [&](int e) {
+    const size_t slab = (size_t)a.d * (a.f / 2);
+    return dec_rsrc(a.down_q + (size_t)e * slab, (uint32_t)slab);
+  };
+  auto down_pair = [&](__amdgpu_buffer_rsrc_t rs, int ct, int pr, u32x4 (&dst)[2]) {
+    const int lc = 2 * pr + (seg8 >> 2) < nchD ? 2 * pr + (seg8 >> 2) : 2 * pr;  // this lane's chunk
+    const int lb = (ct * 16 + grp8) * (a.f / 2) + lc * 64 + 16 * (seg8 & 3);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rs, lb, i * 8 * (a.f / 2), 0);
+      dst[i] = u32x4{v.x, v.y, v.z, v.w};
+    }
+  };
   auto prefetch = [&](int j) {
     const int u = j / ndt;
     const int ct = (j - u * ndt) * kDecWaves + wave;
     if (ct * 16 >= a.d) return;
-    const size_t wrow = (size_t)s_e[u] * a.d + ct * 16 + col;
-    const uint8_t* wq = a.down_q + wrow * (a.f / 2);
-    const uint8_t* ws = a.down_s + wrow * (a.f / 16);
+    const int e = s_e[u];
+    const __amdgpu_buffer_rsrc_t rs = down_rsrc(e);
 #pragma unroll
-    for (int p = 0; p < kDownPrefetch; ++p) {
-      if (p < nchD) {
-        pf.q[p] = ldg_u32x4(wq + p * 64 + 16 * grp);
-        pf.sc[p] = *reinterpret_cast<const uint16_t*>(ws + p * 8 + 2 * grp);
-      }
-    }
+    for (int pr = 0; pr < kDownPairs; ++pr)
+      if (pr < npD) down_pair(rs, ct, pr, pf.q[pr]);
+    if (lane * 16 < a.f) pf.sc = ldg_u32x4(a.down_s + ((size_t)e * a.d + ct * 16) * (a.f / 16) + lane * 16);
   };
   int j = G - 1 - (int)blockIdx.x;
 
@@ -182,30 +209,48 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
                                            dec_rsrc(a.up_q + (size_t)e * slab, (uint32_t)slab)};
     const __amdgpu_buffer_rsrc_t srs[2] = {dec_rsrc(a.gate_s + (size_t)e * sslab, (uint32_t)sslab),
                                            dec_rsrc(a.up_s + (size_t)e * sslab, (uint32_t)sslab)};
+    // MFMA layout: lane (grp, col) works on weight row `frow` of the item
     const uint32_t frow = (uint32_t)(fg * kGUFeat + half * 16 + col);
-    const uint32_t qoff = frow * (uint32_t)(a.d / 2) + 16 * grp, soff = frow * (uint32_t)(a.d / 16) + 2 * grp;
+    // the item's scales in LDS: [gate / up][32 rows][d / 16 bytes]
+    const int srow = a.d / 16, sbytes = kGUFeat * srow;
+    const unsigned char* const my_sc = s_sc + (half * 16 + col) * srow;
+    // Code loads run along the rows instead: a load covers a pair of chunks (128 bytes,
+    // one cache line) of 8 rows -- lane group grp8 = lane / 8 takes row 8i + grp8 and
+    // lane lane % 8 its 16-byte segment -- rather than 64 bytes of 16 rows. The wave
+    // rearranges each pair into the MFMA layout through its LDS scratch.
+    const int grp8 = lane >> 3, seg8 = lane & 7;
+    const uint32_t qoff = (uint32_t)(fg * kGUFeat + half * 16 + grp8) * (uint32_t)(a.d / 2);
+    unsigned char* const scr = s_scr + wave * kScrWave;
     floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    u32x4 q[kB][2];
-    uint32_t sc[kB][2];
+    u32x4 lq[2][2][2];  // [pair][gate / up][rows 0-7 / 8-15], as loaded
     // A batch always issues kB chunks of loads (a chunk past the wave's range repeats
     // chunk c), so the number of loads in flight is a constant and every wait below is
-    // exact.
+    // exact. Per pair: gate codes, then up.
     auto load_batch = [&](int c) {
 #pragma unroll
-      for (int h = 0; h < kB; ++h) {
-        const int cc = c + h < kc1 ? c + h : c;
+      for (int pr = 0; pr < 2; ++pr) {
+        const int lc = c + 2 * pr + (seg8 >> 2) < kc1 ? c + 2 * pr + (seg8 >> 2) : c;  // this lane's chunk
+        const int lb = (int)qoff + lc * 64 + 16 * (seg8 & 3);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(qrs[m], (int)qoff, cc * 64, 0);
-          q[h][m] = u32x4{v.x, v.y, v.z, v.w};
-          sc[h][m] = __builtin_amdgcn_raw_buffer_load_b16(srs[m], (int)soff, cc * 8, 0);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(qrs[m], lb, i * 8 * (a.d / 2), 0);
+            lq[pr][m][i] = u32x4{v.x, v.y, v.z, v.w};
+          }
         }
-        __builtin_amdgcn_sched_barrier(0);  // keep the chunks in issue order
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
-    // the activation rows of expert u by DMA first, then the first batch of weights;
-    // waiting for all but the weight loads leaves those in flight, and each chunk is
-    // decoded as soon as its own loads have landed
+    // the item's scales (32 whole scale rows of gate and of up, contiguous in memory)
+    // and the activation rows of expert u by DMA first, then the first batch of
+    // weights; waiting for all but the weight loads leaves those in flight, and each
+    // pair of chunks is decoded as soon as its own loads have landed
+    for (int qi = (int)threadIdx.x; qi < 2 * sbytes / 16; qi += kDecThreads) {
+      const int m = qi >= sbytes / 16;
+      const uint32_t off = (uint32_t)(fg * kGUFeat) * (uint32_t)srow + (uint32_t)(qi * 16 - m * sbytes);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs[m], (lds_void_ptr)(s_sc + (qi - lane) * 16), 16, off, 0, 0, 0);
+    }
     for (int qi = wave; qi < ne * ipr; qi += kDecWaves) {
       const int r = qi / ipr, jj = qi - r * ipr;
       const int within = jj * 1024 + lane * 16;
@@ -214,7 +259,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
                                                0, 0);
     }
     load_batch(kc0);
-    wait_vm<4 * kB>();  // the DMA has landed; the weight loads may still be in flight
+    wait_vm<8>();  // the DMA has landed; the batch's 8 code loads may still be in flight
     // a bare barrier: __syncthreads() would also wait for the weight loads
     lds_barrier();
     const bool valid = col < ne;
@@ -222,23 +267,54 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
     // depends only on operand column j, and those columns are never stored.
     const unsigned char* xrow = s_dyn + col * xstride;
     auto xop = [&](int k0) -> bf16x8 { return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4v*>(xrow + k0 * 2)); };
-    auto compute_batch = [&](int c) {
+    // Rearrange a pair: piece (row r, 16-byte segment s) of matrix m sits at
+    // m * 2048 + r * 128 + ((s + r / 2) mod 8) * 16 in the wave's scratch, so the stores
+    // (two rows per 16 lanes) and the loads (a segment of 16 rows per 16 lanes) each hit
+    // 16 distinct 16-byte bank groups. LDS operations of one wave complete in order.
+    auto compute_pair = [&](int c, int pr) {
 #pragma unroll
-      for (int h = 0; h < kB; ++h) {
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = 8 * i + grp8;
+          *reinterpret_cast<u32x4v*>(scr + m * 2048 + r * 128 + ((seg8 + (r >> 1)) & 7) * 16) =
+              u32x4v{lq[pr][m][i].x, lq[pr][m][i].y, lq[pr][m][i].z, lq[pr][m][i].w};
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      u32x4 q[2][2];  // [gate / up][chunk of the pair], MFMA layout
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          // chunk j of the pair, row col: segments 4j .. 4j + 3, lane group grp takes 4j + grp
+          const u32x4v v =
+              *reinterpret_cast<const u32x4v*>(scr + m * 2048 + col * 128 + ((4 * j + grp + (col >> 1)) & 7) * 16);
+          q[m][j] = u32x4{v.x, v.y, v.z, v.w};
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int h = 2 * pr + j;
         if (c + h < kc1) {
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
-            const E4M3Split s0 = e4m3_split(sc[h][m] & 0xFFu);
-            const E4M3Split s1 = e4m3_split(sc[h][m] >> 8);
+            const uint32_t sc = *reinterpret_cast<const uint16_t*>(my_sc + m * sbytes + (c + h) * 8 + 2 * grp);
+            const E4M3Split s0 = e4m3_split(sc & 0xFFu);
+            const E4M3Split s1 = e4m3_split(sc >> 8);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-              acc[m] = mfma16(nvfp4x8_to_bf16(word_of(q[h][m], s), s < 2 ? s0 : s1),
-                              xop((c + h) * 128 + 32 * grp + 8 * s), acc[m]);
+              acc[m] = mfma16(nvfp4x8_to_bf16(word_of(q[m][j], s), s < 2 ? s0 : s1),
+                                  xop((c + h) * 128 + 32 * grp + 8 * s), acc[m]);
           }
         }
-        // chunk by chunk, so each waits only for its own loads
-        __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto compute_batch = [&](int c) {
+      compute_pair(c, 0);
+      compute_pair(c, 1);
     };
     // the first batch straight after its loads (a separate copy keeps the compiler's
     // per-load waits exact), then any further batches
@@ -255,22 +331,24 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
         for (int m = 0; m < 2; ++m) {
           const uint32_t qq = __builtin_amdgcn_raw_buffer_load_b32(qrs[m], (int)(frow * (uint32_t)(a.d / 2) + 4 * grp),
                                                                  K0 / 2, 0);
-          const uint32_t sv = __builtin_amdgcn_raw_buffer_load_b8(
-              srs[m], (int)(frow * (uint32_t)(a.d / 16) + (grp >> 1)), K0 / 16, 0);
+          const uint32_t sv = my_sc[m * sbytes + K0 / 16 + (grp >> 1)];
           acc[m] = mfma16(nvfp4x8_to_bf16(qq, e4m3_split(sv)), xv, acc[m]);
         }
       }
     }
-    red[wave][0][lane] = acc[0];
-    red[wave][1][lane] = acc[1];
+    // partial sums through the waves' scratch: [wave][gate / up][lane]
+    floatx4* const red = reinterpret_cast<floatx4*>(s_scr);
+    constexpr int kRedWave = kScrWave / (int)sizeof(floatx4);
+    red[wave * kRedWave + lane] = acc[0];
+    red[wave * kRedWave + 64 + lane] = acc[1];
     __syncthreads();
     if (kq == 0) {
       if (valid) {
-        floatx4 Gs = red[wave][0][lane], Us = red[wave][1][lane];
+        floatx4 Gs = red[wave * kRedWave + lane], Us = red[wave * kRedWave + 64 + lane];
 #pragma unroll
         for (int w = 1; w < 4; ++w) {
-          Gs += red[wave + w][0][lane];
-          Us += red[wave + w][1][lane];
+          Gs += red[(wave + w) * kRedWave + lane];
+          Us += red[(wave + w) * kRedWave + 64 + lane];
         }
         const float tg = a.gate_ts[e], tu = a.up_ts[e];
         uint32_t hb[4];
@@ -333,37 +411,59 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
     }
     const bool valid = col < ne;
     if (ct * 16 < a.d) {
-      const size_t wrow = (size_t)e * a.d + ct * 16 + col;
-      const uint8_t* const wq = a.down_q + wrow * (a.f / 2);
-      const uint8_t* const ws = a.down_s + wrow * (a.f / 16);
+      unsigned char* const scr = s_scr + wave * kScrWave;
+      unsigned char* const dsc = scr + 2048;  // the wave's scale rows: [16][f / 16]
+      const int srowD = a.f / 16;
       const uint16_t* hrow = s_h + col * hstride;
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
       // rows >= ne: stale LDS, confined to output columns that are not stored
       auto hv = [&](int k0) -> bf16x8 { return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4v*>(hrow + k0)); };
+      if (lane * 16 < a.f) *reinterpret_cast<u32x4v*>(dsc + lane * 16) = u32x4v{pf.sc.x, pf.sc.y, pf.sc.z, pf.sc.w};
+      const __amdgpu_buffer_rsrc_t rs = down_rsrc(e);
+      // a pair of chunks: rearranged through the scratch (layout as for gate/up), then
+      // two chunks of MFMAs
+      auto down_compute = [&](int pr, const u32x4 (&lq)[2]) {
 #pragma unroll
-      for (int p = 0; p < kDownPrefetch; ++p) {
-        if (p < nchD) {
-          const E4M3Split s0 = e4m3_split(pf.sc[p] & 0xFFu);
-          const E4M3Split s1 = e4m3_split(pf.sc[p] >> 8);
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            acc = mfma16(nvfp4x8_to_bf16(word_of(pf.q[p], s), s < 2 ? s0 : s1), hv(p * 128 + 32 * grp + 8 * s), acc);
+        for (int i = 0; i < 2; ++i) {
+          const int r = 8 * i + grp8;
+          *reinterpret_cast<u32x4v*>(scr + r * 128 + ((seg8 + (r >> 1)) & 7) * 16) =
+              u32x4v{lq[i].x, lq[i].y, lq[i].z, lq[i].w};
         }
-      }
-      // chunks past the prefetch depth (f > kDownPrefetch * 128)
-      for (int c = kDownPrefetch; c < nchD; ++c) {
-        const u32x4 q = ldg_u32x4(wq + c * 64 + 16 * grp);
-        const uint32_t sc = *reinterpret_cast<const uint16_t*>(ws + c * 8 + 2 * grp);
-        const E4M3Split s0 = e4m3_split(sc & 0xFFu);
-        const E4M3Split s1 = e4m3_split(sc >> 8);
+        __builtin_amdgcn_wave_barrier();
+        u32x4 q[2];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc = mfma16(nvfp4x8_to_bf16(word_of(q, s), s < 2 ? s0 : s1), hv(c * 128 + 32 * grp + 8 * s), acc);
+        for (int jj = 0; jj < 2; ++jj) {
+          const u32x4v v = *reinterpret_cast<const u32x4v*>(scr + col * 128 + ((4 * jj + grp + (col >> 1)) & 7) * 16);
+          q[jj] = u32x4{v.x, v.y, v.z, v.w};
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int c = 2 * pr + jj;
+          if (c < nchD) {
+            const uint32_t sc = *reinterpret_cast<const uint16_t*>(dsc + col * srowD + c * 8 + 2 * grp);
+            const E4M3Split s0 = e4m3_split(sc & 0xFFu);
+            const E4M3Split s1 = e4m3_split(sc >> 8);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              acc = mfma16(nvfp4x8_to_bf16(word_of(q[jj], s), s < 2 ? s0 : s1), hv(c * 128 + 32 * grp + 8 * s), acc);
+          }
+        }
+      };
+#pragma unroll
+      for (int pr = 0; pr < kDownPairs; ++pr)
+        if (pr < npD) down_compute(pr, pf.q[pr]);
+      // pairs past the prefetch depth (f > 2 * kDownPairs * 128)
+      for (int pr = kDownPairs; pr < npD; ++pr) {
+        u32x4 lq[2];
+        down_pair(rs, ct, pr, lq);
+        down_compute(pr, lq);
       }
       // the 32-element chunks past the last full 128: lane group g holds K0 + 8g .. K0 + 8g + 7
+      const uint8_t* const wq = a.down_q + ((size_t)e * a.d + ct * 16 + col) * (a.f / 2);
       for (int K0 = nchD * 128; K0 < a.f; K0 += 32) {
         const uint32_t q = *reinterpret_cast<const uint32_t*>(wq + K0 / 2 + 4 * grp);
-        const E4M3Split sp = e4m3_split(ws[K0 / 16 + (grp >> 1)]);
+        const E4M3Split sp = e4m3_split(dsc[col * srowD + K0 / 16 + (grp >> 1)]);
         acc = mfma16(nvfp4x8_to_bf16(q, sp), hv(K0 + 8 * grp), acc);
       }
       if (valid) {
@@ -382,16 +482,12 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
   }
 }
 
-size_t ffn_decode_lds_bytes(int T, int d, int f) {
-  const size_t xs = (size_t)((d * 2 + 1023) / 1024 * 1024 + 16);
-  const size_t hs = (size_t)(f + 8) * sizeof(uint16_t);
-  return (size_t)T * std::max(xs, hs);
-}
+size_t ffn_decode_lds_bytes(int T, int d, int f) { return dec_row_region(T, d, f); }
 
 hipError_t launch_ffn_decode(const FFNArgs& a, uint32_t tag, hipStream_t stream) {
   // co-resident blocks for this dynamic LDS size (cached per size)
   static int cached_lds = -1, cached_capacity = 0;
-  const int lds = (int)ffn_decode_lds_bytes(a.T, a.d, a.f);
+  const int lds = (int)(dec_row_region(a.T, a.d, a.f) + (size_t)kDecWaves * kScrWave + (size_t)4 * a.d);
   if (lds != cached_lds) {
     int dev = 0, ncu = 0, per_cu = 0;
     hipError_t err = hipGetDevice(&dev);

@@ -36,8 +36,11 @@ size_t ffn_workspace_bytes(int T, int d, int f, int E, int k);
 // The decode path stages one expert's activation rows, then its H rows, in LDS.
 size_t ffn_decode_lds_bytes(int T, int d, int f);
 constexpr size_t kDecodeMaxLds = 64 * 1024;
+constexpr int kDecodeMaxD = 4096;  // a gate/up item keeps all its block scales (4d bytes) in LDS
+constexpr int kDecodeMaxF = 1024;  // a down tile's 16 scale rows (f bytes) fit one 16-byte load a lane
 inline bool use_decode_path(int T, int d, int f) {
-  return T <= kDecodeMaxRows && ffn_decode_lds_bytes(T, d, f) <= kDecodeMaxLds;
+  return T <= kDecodeMaxRows && d <= kDecodeMaxD && f <= kDecodeMaxF &&
+         ffn_decode_lds_bytes(T, d, f) <= kDecodeMaxLds;
 }
 hipError_t launch_ffn_decode(const FFNArgs& a, uint32_t tag, hipStream_t stream);
 hipError_t launch_ffn_prompt(const FFNArgs& a, hipStream_t stream);
