@@ -27,13 +27,23 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   const int c = (blockIdx.y * kCombineThreads + threadIdx.x) * 4;
   if (c >= d) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const float4 v = *reinterpret_cast<const float4*>(y_rows + (size_t)s_row[j] * d + c);
-    const float wj = s_w[j];
-    acc.x = fmaf(wj, v.x, acc.x);
-    acc.y = fmaf(wj, v.y, acc.y);
-    acc.z = fmaf(wj, v.z, acc.z);
-    acc.w = fmaf(wj, v.w, acc.w);
+  // eight rows' loads in flight at once (a group past k repeats row k-1 and adds
+  // nothing), then the sums in top-k order
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = *reinterpret_cast<const float4*>(y_rows + (size_t)s_row[min(j0 + u, k - 1)] * d + c);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (j0 + u < k) {
+        const float wj = s_w[j0 + u];
+        acc.x = fmaf(wj, v[u].x, acc.x);
+        acc.y = fmaf(wj, v[u].y, acc.y);
+        acc.z = fmaf(wj, v[u].z, acc.z);
+        acc.w = fmaf(wj, v[u].w, acc.w);
+      }
+    }
   }
   uint2 o;
   o.x = (uint32_t)bf16_rne(acc.x) | ((uint32_t)bf16_rne(acc.y) << 16);

@@ -104,7 +104,9 @@ __device__ __forceinline__ void row_topk(const float* __restrict__ row, int E, i
 }
 
 // Exclusive scan of s_in[0..n) in LDS (n <= 1024) by the block's first wave, 64
-// entries a step with lane shuffles; writes s_out[0..n], s_out[n] = total.
+// entries a step: an inclusive scan inside each 16-lane row by four DPP row shifts
+// (lanes shifted in from outside the row add 0), then the row totals read into scalar
+// registers and added to the rows above; writes s_out[0..n], s_out[n] = total.
 __device__ void block_exclusive_scan(const int* s_in, int* s_out, int n) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
@@ -113,13 +115,16 @@ __device__ void block_exclusive_scan(const int* s_in, int* s_out, int n) {
       const int e = base + lane;
       const int v = e < n ? s_in[e] : 0;
       int incl = v;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
-      if (e < n) s_out[e] = run + incl - v;
-      run += __shfl(incl, 63);
+      incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, false);  // row_shr:1
+      incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, false);  // row_shr:2
+      incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, false);  // row_shr:4
+      incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, false);  // row_shr:8
+      const int r0 = __builtin_amdgcn_readlane(incl, 15), r1 = __builtin_amdgcn_readlane(incl, 31);
+      const int r2 = __builtin_amdgcn_readlane(incl, 47), r3 = __builtin_amdgcn_readlane(incl, 63);
+      const int row = lane >> 4;
+      const int above = (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+      if (e < n) s_out[e] = run + above + incl - v;
+      run += r0 + r1 + r2 + r3;
     }
     if (lane == 0) s_out[n] = run;
   }
