@@ -15,8 +15,9 @@ waits for the host, and bracketed by HIP events on the stream the kernels run on
 against its roofline: its duration per call comes from a second timed loop of
 back-to-back FFN calls between one pair of events (the per-step FFN events of the
 layer loop, which include event overhead, are reported beside it).
-Decode steps rotate through distinct copies of the expert weights (>= 1 GB in
-total) so the 256 MB Infinity Cache cannot serve repeats.
+Steps rotate through distinct copies of the expert weights, as many as it takes for
+the weight bytes the steps touch over one rotation to reach 1 GB (four times the
+256 MB Infinity Cache), so repeats are not served from it.
 
 Prints ONE JSON line (rank 0). --gpus N with N > 1 is refused: this build runs
 on one GPU.
@@ -117,6 +118,14 @@ def bench_moe(name, steps, warmup, rotations, timer, seed=0):
     ex0 = M.NVFP4Experts.from_numpy(inp, dev)
     ex0.check()
     del inp
+    if rotations <= 0:
+        # enough copies that the experts a step touches, over one rotation, are >= 1 GB
+        _, _, off0, _, _ = M.route_topk(logits, k)
+        touched = int((off0[1:] - off0[:-1] > 0).sum().item())
+        per_expert = sum(getattr(ex0, n).numel() * getattr(ex0, n).element_size()
+                         for n in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")) // E
+        rotations = max(1, -(-(1 << 30) // max(1, touched * per_expert)))
+        rotations = min(rotations, max(1, (48 << 30) // max(1, E * per_expert)))  # at most ~48 GB of copies
     copies = [ex0]
     for _ in range(rotations - 1):
         copies.append(M.NVFP4Experts(*[getattr(ex0, n).clone() for n in
@@ -292,7 +301,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
                     choices=["tiny", "decode", "prompt", "long_prompt", "mxfp8_M1", "mxfp8_M512"])
-    ap.add_argument("--rotations", type=int, default=0, help="weight copies to rotate (0: >= 1 GB)")
+    ap.add_argument("--rotations", type=int, default=0,
+                    help="weight copies to rotate (0: enough for the touched weights to reach 1 GB)")
     ap.add_argument("--no-also", action="store_true", help="skip the prompt, long-prompt and MXFP8 measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--also-steps", type=int, default=20)
@@ -327,12 +337,11 @@ def main(argv=None):
         return
 
     cid, T, d, f, E, k, zipf = workloads.MOE_CONFIGS[args.workload]
-    rot = args.rotations or max(1, -(-(1 << 30) // (E * expert_bytes(d, f))))
-    main_res = bench_moe(args.workload, args.steps, args.warmup, rot, timer)
+    main_res = bench_moe(args.workload, args.steps, args.warmup, args.rotations, timer)
 
     also = {}
     if not args.no_also and args.workload != "long_prompt":
-        r = bench_moe("long_prompt", args.also_steps, 3, 1, timer)
+        r = bench_moe("long_prompt", args.also_steps, 3, 0, timer)
         also["long_prompt"] = {
             "tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"], "touched_experts": r["touched_experts"],
             "roofline": {"bound": "mfma", "achieved": r["ffn_tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -343,7 +352,7 @@ def main(argv=None):
         }
 
     if not args.no_also and args.workload != "prompt":
-        r = bench_moe("prompt", args.also_steps, 3, 1, timer)
+        r = bench_moe("prompt", args.also_steps, 3, 0, timer)
         also["prompt"] = {
             "tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"], "touched_experts": r["touched_experts"],
             "ffn_avg_us": r["ffn_avg_us"], "ffn_hbm_gbps": r["ffn_hbm_gbps"],
