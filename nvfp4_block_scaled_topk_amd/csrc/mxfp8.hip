@@ -12,8 +12,9 @@
 // gemv (M <= 16): one 16x16x32 MFMA tile covers every activation row; a wave owns 16
 //   weight rows and streams them with 128-bit loads (16 elements a lane, half of a
 //   scale block); KSPLIT waves split K and reduce in LDS in wave order.
-// GEMM: a tile of 128 activation rows x 256 weight rows per block of 8 waves (each wave
-//   2 x 2 32x32x16 MFMA fragments: 64 activation rows x 64 weight rows). Activations
+// GEMM: a tile of 128 activation rows x 192 weight rows per block of 8 waves (each wave
+//   1 x 3 32x32x16 MFMA fragments: 32 activation rows x 96 weight rows; 512 x 12288 makes
+//   256 tiles, one per CU). Activations
 //   (bf16), weight codes (E4M3) and block scales (E8M0) reach LDS by buffer->LDS DMA in
 //   four stages of 64 K elements, three stages ahead of the products, with no register
 //   staging; out-of-range lanes read zeros, which also pads ragged tiles and the K
@@ -199,14 +200,14 @@ __global__ __launch_bounds__(kVThreads) void mxfp8_gemv_valu_kernel(const uint16
 }
 
 constexpr int kGM = 128;                        // activation rows per tile
-constexpr int kGN = 256;                        // weight rows per tile
+constexpr int kGN = 192;                        // weight rows per tile
 constexpr int kGK = 64;                         // K elements per stage
 constexpr int kGStages = 4;
 constexpr int kGXBytes = kGM * kGK * 2;         // 16 KB: 128 rows x 128 bytes
-constexpr int kGWBytes = kGN * kGK;             // 16 KB: 256 rows x 64 bytes
+constexpr int kGWBytes = kGN * kGK;             // 12 KB: 192 rows x 64 bytes
 constexpr int kGSBytes = 8 * 64 * 4;            // 2 KB: a dword slot per (row, block)
 constexpr int kGStageBytes = kGXBytes + kGWBytes + kGSBytes;
-constexpr int kGLdsBytes = kGStages * kGStageBytes;  // 136 KB
+constexpr int kGLdsBytes = kGStages * kGStageBytes + 1024;  // 121 KB (the last 1 KB: see issue())
 constexpr int kGThreads = 512;
 constexpr int kGOps = 5;                        // DMA instructions a wave issues per stage
 constexpr uint32_t kGOOB = 0x80000000u;         // a buffer offset past every record: reads zeros
@@ -245,8 +246,8 @@ __global__ __launch_bounds__(kGThreads, 1) void mxfp8_gemm_kernel(const uint16_t
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const int mh = wave >> 2;  // 64-row half of the activation tile
-  const int nq = wave & 3;   // 64-row quarter of the weight tile
+  const int ma = wave >> 1;  // 32-row quarter of the activation tile
+  const int nb = wave & 1;   // 96-row half of the weight tile (three 32-row fragments)
 
   // tile of this block: XCD-aware order, neighbouring tiles share weight rows
   const int G = gridDim.x;
@@ -267,12 +268,12 @@ __global__ __launch_bounds__(kGThreads, 1) void mxfp8_gemm_kernel(const uint16_t
     const int xr = ins * 8 + (lane >> 3);           // activation row in the tile
     xseg[i] = (lane & 7) ^ (lane >> 3);              // logical segment this lane fetches
     xoff[i] = (m0 + xr < M) ? (uint32_t)(m0 + xr) * (uint32_t)(K * 2) + xseg[i] * 16 : kGOOB;
-    const int wr = ins * 16 + (lane >> 2);           // weight row in the tile
+    const int wr = ins * 16 + (lane >> 2);           // weight row in the tile (past kGN: no row)
     wseg[i] = (lane & 3) ^ ((lane >> 3) & 3);
-    woff[i] = (n0 + wr < N) ? (uint32_t)(n0 + wr) * (uint32_t)K + wseg[i] * 16 : kGOOB;
+    woff[i] = (wr < kGN && n0 + wr < N) ? (uint32_t)(n0 + wr) * (uint32_t)K + wseg[i] * 16 : kGOOB;
   }
   const int srow = wave * 32 + (lane >> 1), sblk = lane & 1;
-  const uint32_t soff = (n0 + srow < N) ? (uint32_t)(n0 + srow) * (uint32_t)(K / 32) + sblk : kGOOB;
+  const uint32_t soff = (srow < kGN && n0 + srow < N) ? (uint32_t)(n0 + srow) * (uint32_t)(K / 32) + sblk : kGOOB;
   const int nst = (K + kGK - 1) / kGK;
 
   auto issue = [&](int c) {
@@ -284,24 +285,26 @@ __global__ __launch_bounds__(kGThreads, 1) void mxfp8_gemm_kernel(const uint16_t
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (gemm_lds_ptr)(st + (wave * 2 + i) * 1024), 16,
                                                xin ? xoff[i] : kGOOB, K0 * 2, 0, 0);
     }
+    // 12 weight instructions a stage; the waves past them issue theirs too (every wave
+    // has the same number of loads in flight, so the waits stay exact), reading zeros
+    // into a 1 KB sink past the stages
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      const int ins = wave * 2 + i;
       const bool win = K0 + 16 * wseg[i] < K;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (gemm_lds_ptr)(st + kGXBytes + (wave * 2 + i) * 1024), 16,
-                                               win ? woff[i] : kGOOB, K0, 0, 0);
+      unsigned char* dst = ins * 16 < kGN ? st + kGXBytes + ins * 1024 : smem + kGStages * kGStageBytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (gemm_lds_ptr)dst, 16, win ? woff[i] : kGOOB, K0, 0, 0);
     }
     const bool sin = K0 + 32 * sblk < K && lane < 64;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (gemm_lds_ptr)(st + kGXBytes + kGWBytes + wave * 256), 1,
                                              sin ? soff : kGOOB, K0 / 32, 0, 0);
   };
 
-  floatx16 acc[2][2];
+  floatx16 acc[3];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 3; ++i)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][t][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
 
   for (int c = 0; c < kGStages - 1 && c < nst; ++c) issue(c);
   for (int c = 0; c < nst; ++c) {
@@ -318,11 +321,11 @@ __global__ __launch_bounds__(kGThreads, 1) void mxfp8_gemm_kernel(const uint16_t
     const unsigned char* ss = st + kGXBytes + kGWBytes;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      gu32x4v wv[2];
-      float p2[2];
+      gu32x4v wv[3];
+      float p2[3];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = nq * 64 + i * 32 + l32;
+      for (int i = 0; i < 3; ++i) {
+        const int r = nb * 96 + i * 32 + l32;
         const int slot = (2 * p + g) ^ ((r >> 1) & 3);
         wv[i] = *reinterpret_cast<const gu32x4v*>(ws + r * 64 + slot * 16);
         const uint32_t code = *(ss + (r >> 5) * 256 + ((r & 31) * 2 + p) * 4);
@@ -330,38 +333,33 @@ __global__ __launch_bounds__(kGThreads, 1) void mxfp8_gemm_kernel(const uint16_t
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        bf16x8 a[2];
+        bf16x8 a[3];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) a[i] = mxfp8x8_to_bf16(wv[i][2 * h], wv[i][2 * h + 1], p2[i]);
+        for (int i = 0; i < 3; ++i) a[i] = mxfp8x8_to_bf16(wv[i][2 * h], wv[i][2 * h + 1], p2[i]);
+        const int r = ma * 32 + l32;
+        const int j = 4 * p + 2 * g + h;
+        const gu32x4v bv = *reinterpret_cast<const gu32x4v*>(xs + r * 128 + ((j ^ (r & 7)) * 16));
+        const bf16x8 b = __builtin_bit_cast(bf16x8, bv);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int r = mh * 64 + t * 32 + l32;
-          const int j = 4 * p + 2 * g + h;
-          const gu32x4v bv = *reinterpret_cast<const gu32x4v*>(xs + r * 128 + ((j ^ (r & 7)) * 16));
-          const bf16x8 b = __builtin_bit_cast(bf16x8, bv);
-#pragma unroll
-          for (int i = 0; i < 2; ++i) acc[i][t] = mx_mfma32(a[i], b, acc[i][t]);
-        }
+        for (int i = 0; i < 3; ++i) acc[i] = mx_mfma32(a[i], b, acc[i]);
       }
     }
   }
 
-  // accumulator r of fragment (i, t): weight row 8 * (r / 4) + 4 * g + r % 4 of the
-  // fragment, activation row l32 of the fragment
+  // accumulator r of fragment i: weight row 8 * (r / 4) + 4 * g + r % 4 of the
+  // fragment, activation row l32 of the wave's 32 rows
+  const int m = m0 + ma * 32 + l32;
+  if (m < M) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int m = m0 + mh * 64 + t * 32 + l32;
-    if (m >= M) continue;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 3; ++i) {
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
-        const int nb = n0 + nq * 64 + i * 32 + 8 * qd + 4 * g;
-        if (nb < N) {
+        const int n = n0 + nb * 96 + i * 32 + 8 * qd + 4 * g;
+        if (n < N) {
           uint32_t hb[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) hb[r] = bf16_rne(acc[i][t][4 * qd + r]);
-          store_bf16x4(y + (size_t)m * N + nb, hb, N - nb, (N & 3) == 0);
+          for (int r = 0; r < 4; ++r) hb[r] = bf16_rne(acc[i][4 * qd + r]);
+          store_bf16x4(y + (size_t)m * N + n, hb, N - n, (N & 3) == 0);
         }
       }
     }
