@@ -206,8 +206,13 @@ constexpr int kGStages = 4;
 constexpr int kGXBytes = kGM * kGK * 2;         // 16 KB: 128 rows x 128 bytes
 constexpr int kGWBytes = kGN * kGK;             // 12 KB: 192 rows x 64 bytes
 constexpr int kGSBytes = 8 * 64 * 4;            // 2 KB: a dword slot per (row, block)
-constexpr int kGStageBytes = kGXBytes + kGWBytes + kGSBytes;
-constexpr int kGLdsBytes = kGStages * kGStageBytes + 1024;  // 121 KB (the last 1 KB: see issue())
+constexpr int kGSRow = 128;                     // preloaded scale bytes a weight row (K <= 4096)
+// a stage holds activations, weight codes and (without the scale preload) scales
+template <bool PRE>
+constexpr int gemm_stage_bytes() { return kGXBytes + kGWBytes + (PRE ? 0 : kGSBytes); }
+// the stages, a 1 KB sink (see issue()) and, with the preload, the tile's scale rows
+template <bool PRE>
+constexpr int gemm_lds_bytes() { return kGStages * gemm_stage_bytes<PRE>() + 1024 + (PRE ? kGN * kGSRow : 0); }
 constexpr int kGThreads = 512;
 constexpr int kGOps = 5;                        // DMA instructions a wave issues per stage
 constexpr uint32_t kGOOB = 0x80000000u;         // a buffer offset past every record: reads zeros
@@ -234,10 +239,14 @@ __device__ __forceinline__ void gemm_barrier() {
 //   x: row r (128 bytes = 8 slots of 16 bytes), logical segment j in slot j ^ (r & 7);
 //   W: row r (64 bytes = 4 slots), logical segment j in slot j ^ ((r >> 1) & 3);
 //   scales: wave w's region holds rows 32w .. 32w + 31, (row, block b) in dword slot
-//   2 * (row & 31) + b.
+//   2 * (row & 31) + b -- or, when K is a multiple of 512 and at most 4096, all of the
+//   tile's scale rows come in once before the K loop, in whole 128-byte rows (a DMA
+//   instruction reads 8 full cache lines instead of one byte of 32 rows every stage):
+//   row r's logical 16-byte segment j in slot j ^ (r & 7) of its 128 bytes.
 // MFMA K order within a stage (a permutation of K applied to both operands): lane group
 // g (lane / 32) at step 2p + h takes W bytes 8h .. 8h + 7 of segment 2p + g, i.e. K
 // elements 16 * (2p + g) + 8h .. + 7, which are activation segment 4p + 2g + h.
+template <bool PRE>
 __global__ __launch_bounds__(kGThreads, 1) void mxfp8_gemm_kernel(const uint16_t* __restrict__ x, int M, int N,
                                                                   int K, const uint8_t* __restrict__ w,
                                                                   const uint8_t* __restrict__ s,
@@ -275,9 +284,25 @@ __global__ __launch_bounds__(kGThreads, 1) void mxfp8_gemm_kernel(const uint16_t
   const int srow = wave * 32 + (lane >> 1), sblk = lane & 1;
   const uint32_t soff = (srow < kGN && n0 + srow < N) ? (uint32_t)(n0 + srow) * (uint32_t)(K / 32) + sblk : kGOOB;
   const int nst = (K + kGK - 1) / kGK;
+  constexpr int kStage = gemm_stage_bytes<PRE>();
+  constexpr int kOps = PRE ? 4 : kGOps;  // DMA instructions a wave issues per stage
+  unsigned char* const sink = smem + kGStages * kStage;
+  unsigned char* const scl = sink + 1024;  // preloaded scale rows
+
+  if (PRE) {
+    // the tile's scale rows: 24 instructions of 8 rows x 128 bytes, 3 a wave
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int ins = wave * 3 + j;
+      const int r = ins * 8 + (lane >> 3);
+      const int seg = (lane & 7) ^ (r & 7);
+      const uint32_t off = (n0 + r < N && seg * 16 < K / 32) ? (uint32_t)(n0 + r) * (uint32_t)(K / 32) + seg * 16 : kGOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (gemm_lds_ptr)(scl + ins * 1024), 16, off, 0, 0, 0);
+    }
+  }
 
   auto issue = [&](int c) {
-    unsigned char* st = smem + (c % kGStages) * kGStageBytes;
+    unsigned char* st = smem + (c % kGStages) * kStage;
     const int K0 = c * kGK;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -292,12 +317,14 @@ __global__ __launch_bounds__(kGThreads, 1) void mxfp8_gemm_kernel(const uint16_t
     for (int i = 0; i < 2; ++i) {
       const int ins = wave * 2 + i;
       const bool win = K0 + 16 * wseg[i] < K;
-      unsigned char* dst = ins * 16 < kGN ? st + kGXBytes + ins * 1024 : smem + kGStages * kGStageBytes;
+      unsigned char* dst = ins * 16 < kGN ? st + kGXBytes + ins * 1024 : sink;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (gemm_lds_ptr)dst, 16, win ? woff[i] : kGOOB, K0, 0, 0);
     }
-    const bool sin = K0 + 32 * sblk < K && lane < 64;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (gemm_lds_ptr)(st + kGXBytes + kGWBytes + wave * 256), 1,
-                                             sin ? soff : kGOOB, K0 / 32, 0, 0);
+    if (!PRE) {
+      const bool sin = K0 + 32 * sblk < K;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (gemm_lds_ptr)(st + kGXBytes + kGWBytes + wave * 256), 1,
+                                               sin ? soff : kGOOB, K0 / 32, 0, 0);
+    }
   };
 
   floatx16 acc[3];
@@ -309,13 +336,13 @@ __global__ __launch_bounds__(kGThreads, 1) void mxfp8_gemm_kernel(const uint16_t
   for (int c = 0; c < kGStages - 1 && c < nst; ++c) issue(c);
   for (int c = 0; c < nst; ++c) {
     // stage c's loads are the oldest in flight; later stages may still be outstanding
-    if (c + 2 < nst) gemm_wait_vm<2 * kGOps>();
-    else if (c + 1 < nst) gemm_wait_vm<kGOps>();
+    if (c + 2 < nst) gemm_wait_vm<2 * kOps>();
+    else if (c + 1 < nst) gemm_wait_vm<kOps>();
     else gemm_wait_vm<0>();
     gemm_barrier();  // every wave's part of stage c is in LDS; stage c - 1 is consumed
     if (c + kGStages - 1 < nst) issue(c + kGStages - 1);
 
-    const unsigned char* st = smem + (c % kGStages) * kGStageBytes;
+    const unsigned char* st = smem + (c % kGStages) * kStage;
     const unsigned char* xs = st;
     const unsigned char* ws = st + kGXBytes;
     const unsigned char* ss = st + kGXBytes + kGWBytes;
@@ -328,7 +355,13 @@ __global__ __launch_bounds__(kGThreads, 1) void mxfp8_gemm_kernel(const uint16_t
         const int r = nb * 96 + i * 32 + l32;
         const int slot = (2 * p + g) ^ ((r >> 1) & 3);
         wv[i] = *reinterpret_cast<const gu32x4v*>(ws + r * 64 + slot * 16);
-        const uint32_t code = *(ss + (r >> 5) * 256 + ((r & 31) * 2 + p) * 4);
+        uint32_t code;
+        if (PRE) {
+          const int b = 2 * c + p;  // scale block of this half stage
+          code = *(scl + r * kGSRow + (((b >> 4) ^ (r & 7)) * 16) + (b & 15));
+        } else {
+          code = *(ss + (r >> 5) * 256 + ((r & 31) * 2 + p) * 4);
+        }
         p2[i] = e8m0_pow2(code);
       }
 #pragma unroll
@@ -385,14 +418,21 @@ hipError_t launch_mxfp8(const uint16_t* x, int M, int N, int K, const uint8_t* w
   }
   static bool attr_set = false;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mxfp8_gemm_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kGLdsBytes);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mxfp8_gemm_kernel<true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes<true>());
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mxfp8_gemm_kernel<false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes<false>());
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int mtiles = (M + kGM - 1) / kGM, ntiles = (N + kGN - 1) / kGN;
-  hipLaunchKernelGGL(mxfp8_gemm_kernel, dim3(mtiles * ntiles), dim3(kGThreads), kGLdsBytes, stream, x, M, N, K, w,
-                     s, y, mtiles);
+  if (K % 512 == 0 && K / 32 <= kGSRow)
+    hipLaunchKernelGGL(mxfp8_gemm_kernel<true>, dim3(mtiles * ntiles), dim3(kGThreads), gemm_lds_bytes<true>(),
+                       stream, x, M, N, K, w, s, y, mtiles);
+  else
+    hipLaunchKernelGGL(mxfp8_gemm_kernel<false>, dim3(mtiles * ntiles), dim3(kGThreads), gemm_lds_bytes<false>(),
+                       stream, x, M, N, K, w, s, y, mtiles);
   return hipGetLastError();
 }
 

@@ -170,7 +170,9 @@ def _run_mxfp8(inp):
 # vector-ALU gemv (M <= 4), MFMA gemv (M <= 16) and tiled GEMM shapes: ragged M and N
 # tiles, K tails of 32 (and of a 1 KB step), one stage, several tiles in each direction
 MX_SMALL = [(1, 16, 32), (1, 100, 96), (3, 128, 4096), (16, 48, 160), (17, 130, 96), (200, 256, 288),
-            (5, 33, 64), (129, 257, 64), (300, 600, 4128), (2, 70, 1056), (4, 9, 4096), (3, 1000, 32)]
+            (5, 33, 64), (129, 257, 64), (300, 600, 4128), (2, 70, 1056), (4, 9, 4096), (3, 1000, 32),
+            # GEMM with the tile's scale rows preloaded (K a multiple of 512, <= 4096): ragged tiles
+            (130, 200, 1024), (64, 193, 512), (300, 450, 2048)]
 
 
 @pytest.mark.parametrize("M_,N,K", MX_SMALL)
