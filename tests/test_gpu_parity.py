@@ -83,6 +83,8 @@ SMALL = [
     (40, 64, 32, 64, 8),     # many experts, few rows each
     (8, 2048, 768, 128, 8),  # decode shape with 8 tokens
     (200, 128, 64, 32, 4),   # prompt path: experts on both sides of the 16-row split
+    (300, 512, 256, 6, 2),   # prompt path, d and f multiples of 256, ragged tiles
+    (70, 256, 512, 3, 2),    # the same with f > d
 ]
 
 
