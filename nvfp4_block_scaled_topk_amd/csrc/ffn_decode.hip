@@ -22,8 +22,9 @@
 // with 8-wave blocks and two kinds of work item:
 //   gate/up item (touched expert u, 32 features): waves 0-3 take the gate and up tiles
 //     of features 0..15, waves 4-7 those of 16..31, each wave a quarter of K = d. A wave
-//     issues every code and scale load of its share at once, while the block copies u's
-//     activation rows into LDS by buffer->LDS DMA. Waves 0 and 4 add the four K
+//     issues every code load of its share at once, while the block copies the item's
+//     scale rows into LDS by buffer->LDS DMA (every token's activation row came into
+//     LDS the same way at the start of the launch). Waves 0 and 4 add the four K
 //     quarters of their half in LDS in order, form H = bf16_rne(silu(ts_g * G) *
 //     (ts_u * U)) and store it;
 //   down item (u, 128 columns of d): wave w owns a 16-column tile over all of K = f.
@@ -121,7 +122,19 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
 
-  // ---- touched experts and the token of every routed row (one round trip)
+  // ---- every token's activation row into LDS (row t at t * xstride; used by all of the
+  // block's gate/up items), the touched experts and the token of every routed row: one
+  // round trip
+  const __amdgpu_buffer_rsrc_t xrs = dec_rsrc(a.x, (uint32_t)(a.T * a.d * 2));
+  {
+    const int xs = dec_xstride(a.d), ipr = (a.d * 2 + 1023) / 1024;  // 1 KB DMA instructions a row
+    for (int qi = wave; qi < a.T * ipr; qi += kDecWaves) {
+      const int r = qi / ipr, jj = qi - r * ipr;
+      const int within = jj * 1024 + lane * 16;
+      const uint32_t voff = within < a.d * 2 ? (uint32_t)r * (uint32_t)(a.d * 2) + within : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void_ptr)(s_dyn + r * xs + jj * 1024), 16, voff, 0, 0, 0);
+    }
+  }
   const int nA = a.T * a.k;
   for (int i = threadIdx.x; i <= a.E; i += kDecThreads) s_off[i] = a.offsets[i];
   for (int i = threadIdx.x; i < nA; i += kDecThreads) s_tok[i] = a.sorted_rows[i] / a.k;
@@ -156,7 +169,6 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
   const int ndt = (a.d + kDCols - 1) / kDCols;    // down items per expert
   const int nGU = U * nfg, nD = U * ndt;
   unsigned long long* const hw = reinterpret_cast<unsigned long long*>(a.h);  // [T*k][f/2] tagged words
-  const __amdgpu_buffer_rsrc_t xrs = dec_rsrc(a.x, (uint32_t)(a.T * a.d * 2));
   const u32x4 zero = {0u, 0u, 0u, 0u};
 
   // ---- this wave's share of a down item: a 16-column tile over all of K = f. Its 16
@@ -197,7 +209,6 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
   const int kc0 = nchG * kq / 4, kc1 = nchG * (kq + 1) / 4;
   const bool gtail = kq == 3;
   const int xstride = dec_xstride(a.d);
-  const int ipr = (a.d * 2 + 1023) / 1024;  // 1 KB DMA instructions per activation row
   constexpr int kB = 4;                     // chunks a wave loads at once
   auto gu_item = [&](int i, bool last) {
     const int u = i / nfg, fg = i - u * nfg;
@@ -251,21 +262,15 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
       const uint32_t off = (uint32_t)(fg * kGUFeat) * (uint32_t)srow + (uint32_t)(qi * 16 - m * sbytes);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(srs[m], (lds_void_ptr)(s_sc + (qi - lane) * 16), 16, off, 0, 0, 0);
     }
-    for (int qi = wave; qi < ne * ipr; qi += kDecWaves) {
-      const int r = qi / ipr, jj = qi - r * ipr;
-      const int within = jj * 1024 + lane * 16;
-      const uint32_t voff = within < a.d * 2 ? (uint32_t)s_tok[r0 + r] * (uint32_t)(a.d * 2) + within : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void_ptr)(s_dyn + r * xstride + jj * 1024), 16, voff, 0,
-                                               0, 0);
-    }
     load_batch(kc0);
-    wait_vm<8>();  // the DMA has landed; the batch's 8 code loads may still be in flight
+    wait_vm<8>();  // the scale DMA has landed; the batch's 8 code loads may still be in flight
     // a bare barrier: __syncthreads() would also wait for the weight loads
     lds_barrier();
     const bool valid = col < ne;
     // Lanes of routed rows >= ne read whatever the LDS row holds: MFMA output column j
     // depends only on operand column j, and those columns are never stored.
-    const unsigned char* xrow = s_dyn + col * xstride;
+    // the activation row of routed row col (rows >= ne: the expert's last row's token)
+    const unsigned char* xrow = s_dyn + s_tok[r0 + min(col, ne - 1)] * xstride;
     auto xop = [&](int k0) -> bf16x8 { return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4v*>(xrow + k0 * 2)); };
     // Rearrange a pair: piece (row r, 16-byte segment s) of matrix m sits at
     // m * 2048 + r * 128 + ((s + r / 2) mod 8) * 16 in the wave's scratch, so the stores
