@@ -9,9 +9,9 @@
 // bf16 and the matrix cores see the stored weight without rounding.
 //
 // gfx950's scaled FP4/FP8 conversions apply only the exponent of their fp32 scale
-// operand. The E4M3 scale is therefore split into its power of two (given to the
-// conversion) and its significand in [1, 2) (one fp32 multiply per element); both
-// steps are exact.
+// operand. The E4M3 scale is therefore split into a power of two (given to the
+// conversion) and its significand scaled into [0.5, 1) (one fp32 multiply per
+// element); both steps are exact.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -42,23 +42,25 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return bits_f32((uint32_t)b << 16); }
 
-// An E4M3 block scale, prepared once per block: `pow2` carries its exponent (handed to
-// the hardware conversion), `mant` its signed significand (1 + m/8 for normal codes,
-// m for subnormal codes relative to 2^-9, 0 for a zero scale).
+// An E4M3 block scale v, prepared once per block: `pow2` is 2v, whose exponent (one
+// above v's own) is what the hardware conversion applies; `mant` = v / 2^(e + 1) in
+// [0.5, 1) with v's sign (0 for a zero scale), so fp4 * 2^(e + 1) * mant = fp4 * v, and
+// both products are exact (the significand of v has at most 4 bits).
 struct E4M3Split {
   float pow2;
   float mant;
 };
 
-__device__ __forceinline__ E4M3Split e4m3_split(uint32_t code) {
-  // exact decode of the E4M3 byte by the hardware conversion (no scaling)
-  float v = __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
-  uint32_t b = f32_bits(v);
+// the scale in byte SEL of `word`
+template <int SEL>
+__device__ __forceinline__ E4M3Split e4m3_split_b(uint32_t word) {
+  const float v = __builtin_amdgcn_cvt_f32_fp8((int)word, SEL);  // exact decode of the E4M3 byte
   E4M3Split s;
-  s.pow2 = bits_f32(b & 0x7F800000u);
-  s.mant = (b & 0x7FFFFFFFu) ? bits_f32((b & 0x807FFFFFu) | 0x3F800000u) : 0.0f;
+  s.pow2 = v + v;
+  s.mant = __builtin_amdgcn_frexp_mantf(v);
   return s;
 }
+__device__ __forceinline__ E4M3Split e4m3_split(uint32_t code) { return e4m3_split_b<0>(code); }
 
 // 8 E2M1 codes (one 32-bit word, element 2j in the low nibble of byte j) times one
 // E4M3 scale -> 8 bf16 values as an MFMA operand, exactly.

@@ -306,8 +306,8 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
             const uint32_t sc = *reinterpret_cast<const uint16_t*>(my_sc + m * sbytes + (c + h) * 8 + 2 * grp);
-            const E4M3Split s0 = e4m3_split(sc & 0xFFu);
-            const E4M3Split s1 = e4m3_split(sc >> 8);
+            const E4M3Split s0 = e4m3_split_b<0>(sc);
+            const E4M3Split s1 = e4m3_split_b<1>(sc);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
               acc[m] = mfma16(nvfp4x8_to_bf16(word_of(q[m][j], s), s < 2 ? s0 : s1),
@@ -447,8 +447,8 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
           const int c = 2 * pr + jj;
           if (c < nchD) {
             const uint32_t sc = *reinterpret_cast<const uint16_t*>(dsc + col * srowD + c * 8 + 2 * grp);
-            const E4M3Split s0 = e4m3_split(sc & 0xFFu);
-            const E4M3Split s1 = e4m3_split(sc >> 8);
+            const E4M3Split s0 = e4m3_split_b<0>(sc);
+            const E4M3Split s1 = e4m3_split_b<1>(sc);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
               acc = mfma16(nvfp4x8_to_bf16(word_of(q[jj], s), s < 2 ? s0 : s1), hv(c * 128 + 32 * grp + 8 * s), acc);

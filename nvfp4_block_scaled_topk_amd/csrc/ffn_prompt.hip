@@ -284,8 +284,8 @@ __global__ __launch_bounds__(kPromptThreads, 1) void ffn_prompt_kernel(FFNArgs a
         E4M3Split sp[2][2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          sp[i][0] = e4m3_split(sc[i] & 0xFFu);
-          sp[i][1] = e4m3_split((sc[i] >> 8) & 0xFFu);
+          sp[i][0] = e4m3_split_b<0>(sc[i]);
+          sp[i][1] = e4m3_split_b<1>(sc[i]);
         }
         bf16x8 w0[2], w1[2];
 #pragma unroll

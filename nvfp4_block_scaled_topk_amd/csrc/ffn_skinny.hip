@@ -97,8 +97,8 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         if (c + j >= c_begin && c + j < c_end) {
-          const E4M3Split s0 = e4m3_split(sc[i][j] & 0xFFu);
-          const E4M3Split s1 = e4m3_split(sc[i][j] >> 8);
+          const E4M3Split s0 = e4m3_split_b<0>(sc[i][j]);
+          const E4M3Split s1 = e4m3_split_b<1>(sc[i][j]);
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             const bf16x8 wv = nvfp4x8_to_bf16(word_of(q[j], s), s < 2 ? s0 : s1);
@@ -157,8 +157,8 @@ __device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&w
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
-        const E4M3Split s0 = e4m3_split(sc[h][i] & 0xFFu);
-        const E4M3Split s1 = e4m3_split(sc[h][i] >> 8);
+        const E4M3Split s0 = e4m3_split_b<0>(sc[h][i]);
+        const E4M3Split s1 = e4m3_split_b<1>(sc[h][i]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const bf16x8 wv = nvfp4x8_to_bf16(word_of(q[h][i], s), s < 2 ? s0 : s1);
@@ -181,8 +181,8 @@ __device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&w
     for (int s = 0; s < 4; ++s) xv[s] = valid ? ldg_u32x4(act + K0 + 32 * grp + 8 * s) : zero;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-      const E4M3Split s0 = e4m3_split(sc[i] & 0xFFu);
-      const E4M3Split s1 = e4m3_split(sc[i] >> 8);
+      const E4M3Split s0 = e4m3_split_b<0>(sc[i]);
+      const E4M3Split s1 = e4m3_split_b<1>(sc[i]);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const bf16x8 wv = nvfp4x8_to_bf16(word_of(q[i], s), s < 2 ? s0 : s1);

@@ -85,6 +85,7 @@ SMALL = [
     (200, 128, 64, 32, 4),   # prompt path: experts on both sides of the 16-row split
     (300, 512, 256, 6, 2),   # prompt path, d and f multiples of 256, ragged tiles
     (70, 256, 512, 3, 2),    # the same with f > d
+    (150, 352, 320, 8, 2),   # prompt path, K stage counts 6 (half last stage) and 5
 ]
 
 
