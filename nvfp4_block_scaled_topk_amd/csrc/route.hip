@@ -44,48 +44,67 @@ __device__ __forceinline__ float dpp_f(float v) {
   return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
 }
 template <int CTRL>
-__device__ __forceinline__ void row_argmax_step(float& bv, int& bi) {
-  const float ov = dpp_f<CTRL>(bv);
-  const int oi = dpp_i<CTRL>(bi);
-  if (route_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-}
-template <int CTRL>
 __device__ __forceinline__ void row_sum_step(float& s) {
   s += dpp_f<CTRL>(s);
 }
 
+// Routing key of (logit v, expert e): one unsigned 64-bit integer whose order is the
+// selection order -- v descending (its bits made order-preserving, -0.0 taken as +0.0),
+// then e ascending -- so a comparison is one 64-bit compare. Key 0 (below every real
+// key) marks a padding or already-selected slot.
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v + 0.0f);  // -0.0 + 0.0 = +0.0
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+__device__ __forceinline__ float route_key_value(uint64_t key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ int route_key_expert(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+template <int CTRL>
+__device__ __forceinline__ void row_keymax_step(uint64_t& k) {
+  const uint64_t o = ((uint64_t)(uint32_t)dpp_i<CTRL>((int)(k >> 32)) << 32) | (uint32_t)dpp_i<CTRL>((int)(uint32_t)k);
+  k = o > k ? o : k;
+}
+
 // Top-k of one token held by a 16-lane row (lane gl of the row holds experts gl + 16j,
-// j < EPL), k <= 16: k rounds of a row argmax. Lane gl < k gets the gl-th choice in
-// my_v / my_i and its renormalized softmax weight in my_w.
+// j < EPL), k <= 16: k rounds of a row maximum over routing keys. Lane gl < k gets the
+// gl-th choice in my_v / my_i and its renormalized softmax weight in my_w.
 template <int EPL>
 __device__ __forceinline__ void row_topk(const float* __restrict__ row, int E, int k, int gl, float& my_v,
                                          int& my_i, float& my_w) {
-  float v[EPL];
-  int ix[EPL];
+  uint64_t key[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = gl + 16 * j;
-    v[j] = e < E ? row[e] : -__builtin_inff();
-    ix[j] = e < E ? e : 0x7FFFFFFF;
+    key[j] = e < E ? route_key(row[e], e) : 0ull;
   }
-  my_v = 0.0f;
-  my_i = 0;
+  uint64_t mine = 0ull, top = 0ull;
   for (int r = 0; r < k; ++r) {
-    float bv = v[0];
-    int bi = ix[0];
+    // the lane's best key, by a pairwise tree (short dependency chains)
+    uint64_t t[EPL];
 #pragma unroll
-    for (int j = 1; j < EPL; ++j)
-      if (route_better(v[j], ix[j], bv, bi)) { bv = v[j]; bi = ix[j]; }
-    row_argmax_step<0xB1>(bv, bi);
-    row_argmax_step<0x4E>(bv, bi);
-    row_argmax_step<0x141>(bv, bi);
-    row_argmax_step<0x140>(bv, bi);
+    for (int j = 0; j < EPL; ++j) t[j] = key[j];
+#pragma unroll
+    for (int w = 1; w < EPL; w *= 2)
+#pragma unroll
+      for (int j = 0; j + w < EPL; j += 2 * w) t[j] = t[j + w] > t[j] ? t[j + w] : t[j];
+    uint64_t best = t[0];
+    row_keymax_step<0xB1>(best);
+    row_keymax_step<0x4E>(best);
+    row_keymax_step<0x141>(best);
+    row_keymax_step<0x140>(best);
+    // the selected slot (keys are distinct: the low word names the expert)
 #pragma unroll
     for (int j = 0; j < EPL; ++j)
-      if (ix[j] == bi) { v[j] = -__builtin_inff(); ix[j] = 0x7FFFFFFF; }
-    if (gl == r) { my_v = bv; my_i = bi; }
-    if (r == 0) my_w = bv;  // the row maximum, broadcast to every lane of the row
+      if ((uint32_t)key[j] == (uint32_t)best) key[j] = 0ull;
+    if (gl == r) mine = best;
+    if (r == 0) top = best;  // the row maximum, in every lane of the row
   }
+  my_v = route_key_value(mine);
+  my_i = route_key_expert(mine);
+  my_w = route_key_value(top);
   const float m = my_w;
   float ex = 0.0f;
   if (gl < k) {
