@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
     const int lb = (ct * 16 + grp8) * (a.f / 2) + lc * 64 + 16 * (seg8 & 3);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rs, lb, i * 8 * (a.f / 2), 0);
+      const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rs, lb, i * 8 * (a.f / 2), kWeightAux);
       dst[i] = u32x4{v.x, v.y, v.z, v.w};
     }
   };
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
 #pragma unroll
     for (int pr = 0; pr < kDownPairs; ++pr)
       if (pr < npD) down_pair(rs, ct, pr, pf.q[pr]);
-    if (lane * 16 < a.f) pf.sc = ldg_u32x4(a.down_s + ((size_t)e * a.d + ct * 16) * (a.f / 16) + lane * 16);
+    if (lane * 16 < a.f) pf.sc = ldg_nt_u32x4(a.down_s + ((size_t)e * a.d + ct * 16) * (a.f / 16) + lane * 16);
   };
   int j = G - 1 - (int)blockIdx.x;
 
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
         for (int m = 0; m < 2; ++m) {
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
-            const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(qrs[m], lb, i * 8 * (a.d / 2), 0);
+            const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(qrs[m], lb, i * 8 * (a.d / 2), kWeightAux);
             lq[pr][m][i] = u32x4{v.x, v.y, v.z, v.w};
           }
         }
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
     for (int qi = (int)threadIdx.x; qi < 2 * sbytes / 16; qi += kDecThreads) {
       const int m = qi >= sbytes / 16;
       const uint32_t off = (uint32_t)(fg * kGUFeat) * (uint32_t)srow + (uint32_t)(qi * 16 - m * sbytes);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs[m], (lds_void_ptr)(s_sc + (qi - lane) * 16), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs[m], (lds_void_ptr)(s_sc + (qi - lane) * 16), 16, off, 0, 0, kWeightAux);
     }
     load_batch(kc0);
     wait_vm<8>();  // the scale DMA has landed; the batch's 8 code loads may still be in flight
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           const uint32_t qq = __builtin_amdgcn_raw_buffer_load_b32(qrs[m], (int)(frow * (uint32_t)(a.d / 2) + 4 * grp),
-                                                                 K0 / 2, 0);
+                                                                 K0 / 2, kWeightAux);
           const uint32_t sv = my_sc[m * sbytes + K0 / 16 + (grp >> 1)];
           acc[m] = mfma16(nvfp4x8_to_bf16(qq, e4m3_split(sv)), xv, acc[m]);
         }

@@ -61,7 +61,7 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
     for (int i = 0; i < NW; ++i) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rs[i], (int)lo, (int)(8 * h * wstride), 0);
+        const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rs[i], (int)lo, (int)(8 * h * wstride), kWeightAux);
         lq[i][h] = u32x4{v.x, v.y, v.z, v.w};
       }
 #pragma unroll
@@ -147,7 +147,7 @@ __device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&w
       const int K0 = (c + h) * 128;
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
-        q[h][i] = ldg_u32x4(wq[i] + K0 / 2 + 16 * grp);
+        q[h][i] = ldg_nt_u32x4(wq[i] + K0 / 2 + 16 * grp);
         sc[h][i] = *reinterpret_cast<const uint16_t*>(wsc[i] + K0 / 16 + 2 * grp);
       }
 #pragma unroll
@@ -174,7 +174,7 @@ __device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&w
     u32x4 xv[4];
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-      q[i] = ldg_u32x4(wq[i] + K0 / 2 + 16 * grp);
+      q[i] = ldg_nt_u32x4(wq[i] + K0 / 2 + 16 * grp);
       sc[i] = *reinterpret_cast<const uint16_t*>(wsc[i] + K0 / 16 + 2 * grp);
     }
 #pragma unroll

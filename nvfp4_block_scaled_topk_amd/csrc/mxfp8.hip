@@ -73,7 +73,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void mxfp8_gemv_kernel(const uint16_t*
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int K0 = (c + h) * 64;
-      wv[h] = nvalid ? ldg_u32x4(wr + K0 + 16 * grp) : zero;
+      wv[h] = nvalid ? ldg_nt_u32x4(wr + K0 + 16 * grp) : zero;
       sb[h] = nvalid ? sr[K0 / 32 + (grp >> 1)] : 127u;
       xa[h] = mvalid ? ldg_u32x4(xr + K0 + 16 * grp) : zero;
       xb[h] = mvalid ? ldg_u32x4(xr + K0 + 16 * grp + 8) : zero;
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void mxfp8_gemv_kernel(const uint16_t*
   }
   for (; c < c1; ++c) {
     const int K0 = c * 64;
-    const u32x4 wv = nvalid ? ldg_u32x4(wr + K0 + 16 * grp) : zero;
+    const u32x4 wv = nvalid ? ldg_nt_u32x4(wr + K0 + 16 * grp) : zero;
     const uint32_t sb = nvalid ? sr[K0 / 32 + (grp >> 1)] : 127u;
     const u32x4 xa = mvalid ? ldg_u32x4(xr + K0 + 16 * grp) : zero;
     const u32x4 xb = mvalid ? ldg_u32x4(xr + K0 + 16 * grp + 8) : zero;
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kVThreads) void mxfp8_gemv_valu_kernel(const uint16
     for (int r = 0; r < kVRows; ++r) {
       const int n = n0 + r;
       if (n < N) {
-        const u32x4 q = ldg_u32x4(w + (size_t)n * K + k0);
+        const u32x4 q = ldg_nt_u32x4(w + (size_t)n * K + k0);
         const float p2 = e8m0_pow2(s[(size_t)n * (K / 32) + k0 / 32]);
         const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
