@@ -7,18 +7,19 @@
 // operands through a multi-stage pipeline in fixed K steps (§4 remaining items, #822).
 // Here, on gfx950:
 //
-//   tile    = (expert e, 256 routed rows of e, 128 features of f)   [gate/up launch:
+//   tile    = (expert e, 128 routed rows of e, 128 features of f)   [gate/up launch:
 //             weight rows 0..127 are gate rows, 128..255 the up rows of the same features]
-//             (expert e, 256 routed rows of e, 256 columns of d)    [down launch]
-//   waves   = 8 (two per SIMD); wave w owns two 32-row weight fragments (gate and up of
-//             the same 32 features, or two 32-column slices of d) and 128 of the 256
-//             routed rows
+//             (expert e, 128 routed rows of e, 256 columns of d)    [down launch]
+//   waves   = 4 (one per SIMD), two workgroups a CU (72 KB of LDS each), so the two
+//             workgroups' barriers are independent; wave w owns two 32-row weight
+//             fragments (gate and up of the same 32 features, or two 32-column slices
+//             of d) over all 128 routed rows
 //   MFMA    = v_mfma_f32_32x32x16_bf16, weights as the A operand, activations as B
 //   staging = buffer->LDS DMA only (no register staging; out-of-range lanes read zeros,
 //             which also pads ragged rows and K tails): activations in double-buffered
 //             stages of 64 K elements; packed weight codes and block scales in
-//             double-buffered blocks of 256 K elements (four activation stages), so one
-//             DMA instruction moves a whole 128-byte row segment of codes
+//             double-buffered blocks of 128 K elements (two activation stages), 64
+//             bytes of codes a weight row
 //
 // Work: one flat list of tiles (expert-major, column tile fastest) walked by a
 // persistent grid; each block derives the list from expert_offsets. Block b works on
@@ -32,17 +33,20 @@
 
 namespace moe {
 
-constexpr int kPromptRows = 256;        // routed rows per tile
+constexpr int kPromptRows = 128;        // routed rows per tile
 constexpr int kPromptKC = 64;           // K elements per activation stage
-constexpr int kBlockStages = 4;         // weight / scale block = 4 stages = 256 K elements
-constexpr int kXStageBytes = 256 * 128;     // 32 KB: 256 rows x 64 bf16
-constexpr int kWBlockBytes = 256 * 128;     // 32 KB: 256 weight rows x 256 codes
-constexpr int kSBlockBytes = 256 * 32;      // 8 KB: 256 rows x 8 scale pairs (dword slots)
+constexpr int kBlockStages = 2;         // weight / scale block = 2 stages = 128 K elements
+constexpr int kXStageBytes = 128 * 128;     // 16 KB: 128 rows x 64 bf16
+constexpr int kWRowBytes = 64;              // a weight row's codes in one block
+constexpr int kWBlockBytes = 256 * kWRowBytes;  // 16 KB: 256 weight rows x 128 codes
+constexpr int kSRowBytes = 16;              // a weight row's 4 scale pairs in one block (dword slots)
+constexpr int kSBlockBytes = 256 * kSRowBytes;  // 4 KB
 constexpr int kXOff = 0;
 constexpr int kWOff = 2 * kXStageBytes;
 constexpr int kSOff = kWOff + 2 * kWBlockBytes;
-constexpr int kPromptLdsBytes = kSOff + 2 * kSBlockBytes;  // 144 KB
-constexpr int kPromptThreads = 512;     // 8 waves, two per SIMD
+constexpr int kPromptLdsBytes = kSOff + 2 * kSBlockBytes;  // 72 KB: two workgroups a CU
+constexpr int kPromptThreads = 256;     // 4 waves, one per SIMD (two workgroups a CU)
+constexpr int kPromptBlocksPerCu = 2;
 constexpr int kXDma = 4;                // activation DMA instructions per wave per stage
 constexpr int kWSDma = 8;               // weight + scale DMA instructions per wave per block
 constexpr int kMaxE = 1024;
@@ -116,21 +120,23 @@ __device__ __forceinline__ int find_tile_expert(const int* s_pref, int E, int t)
 }
 
 template <int MODE>  // 0: gate/up/SwiGLU -> H (bf16); 1: down -> y_rows (fp32)
-__global__ __launch_bounds__(kPromptThreads, 1) void ffn_prompt_kernel(FFNArgs a, int n_col_tiles) {
+__global__ __launch_bounds__(kPromptThreads, 2) void ffn_prompt_kernel(FFNArgs a, int n_col_tiles) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int s_pref[kMaxE + 1];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
-  const int wcol = wave & 3;   // weight-row group of this wave
-  const int wtok = wave >> 2;  // routed-row half of this wave
+  const int wcol = wave;  // weight-row group of this wave (all 128 routed rows)
   const int l32 = lane & 31, g = lane >> 5;
   const int K = MODE == 0 ? a.d : a.f;  // contraction length
   const int N = MODE == 0 ? a.f : a.d;  // weight rows per matrix
   const int nch = (K + kPromptKC - 1) / kPromptKC;
-  // DMA slot -> 16-byte segment: slot s of a 128-byte LDS row r holds logical segment
-  // s ^ (r & 7). For the 8-lanes-a-row DMA pattern, r & 7 = lane >> 3 and s = lane & 7.
+  // DMA slot -> 16-byte segment: slot s of a 128-byte activation row r holds logical
+  // segment s ^ (r & 7); for the 8-lanes-a-row DMA pattern, r & 7 = lane >> 3 and
+  // s = lane & 7. Slot s of a 64-byte weight row r holds logical segment
+  // s ^ ((r >> 1) & 3); for the 4-lanes-a-row pattern, (r >> 1) & 3 = (lane >> 3) & 3.
   const int dseg = (lane & 7) ^ (lane >> 3);
+  const int wseg = (lane & 3) ^ ((lane >> 3) & 3);
 
   build_tile_prefix(a.offsets, a.E, s_pref);
   const int total_tiles = s_pref[a.E] * n_col_tiles;
@@ -144,8 +150,8 @@ __global__ __launch_bounds__(kPromptThreads, 1) void ffn_prompt_kernel(FFNArgs a
     const int mt = mt_all - s_pref[e];
     const int p0 = a.offsets[e] + mt * kPromptRows;
     const int nrows = min(kPromptRows, a.offsets[e + 1] - p0);
-    // 32-row activation fragments this wave uses (0..4): rows 128*wtok .. 128*wtok + 127
-    const int ntf = min(4, max(0, (nrows - 128 * wtok + 31) >> 5));
+    // 32-row activation fragments in use (0..4)
+    const int ntf = min(4, (nrows + 31) >> 5);
 
     // ---- buffer descriptors (wave-uniform). Weight rows 0..127 of the tile are gate
     // rows and 128..255 up rows (gate/up launch).
@@ -153,7 +159,7 @@ __global__ __launch_bounds__(kPromptThreads, 1) void ffn_prompt_kernel(FFNArgs a
     const size_t wslab = (size_t)N * (K / 2), sslab = (size_t)N * (K / 16);
     if (MODE == 0) {
       xrs = make_rsrc(a.x, (uint32_t)((size_t)a.T * a.d * 2));
-      const bool up = wave >= 4;  // waves 0-3 stage the gate rows, waves 4-7 the up rows
+      const bool up = wave >= 2;  // waves 0-1 stage the gate rows, waves 2-3 the up rows
       wrs = make_rsrc((up ? a.up_q : a.gate_q) + (size_t)e * wslab, (uint32_t)wslab);
       srs = make_rsrc((up ? a.up_s : a.gate_s) + (size_t)e * sslab, (uint32_t)sslab);
     } else {
@@ -162,8 +168,9 @@ __global__ __launch_bounds__(kPromptThreads, 1) void ffn_prompt_kernel(FFNArgs a
       srs = make_rsrc(a.down_s + (size_t)e * sslab, (uint32_t)sslab);
     }
 
-    // ---- per-lane DMA sources. Instruction i of wave w covers LDS rows 32w + 8i + lane/8
-    // (activation rows, and weight / scale rows of the tile), 8 lanes a row.
+    // ---- per-lane DMA sources. Activation instruction i of wave w covers LDS rows
+    // 32w + 8i + lane/8, 8 lanes a row; weight / scale instruction i covers tile rows
+    // 64w + 16i + lane/4, 4 lanes a row.
     uint32_t xoff[4], woff[4], soff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -175,10 +182,14 @@ __global__ __launch_bounds__(kPromptThreads, 1) void ffn_prompt_kernel(FFNArgs a
       } else {
         xoff[i] = kOOB;
       }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wave * 64 + i * 16 + (lane >> 2);
       const int n = MODE == 0 ? ct * 128 + (r & 127) : ct * 256 + r;
       if (n < N) {
-        woff[i] = (uint32_t)n * (uint32_t)(K / 2) + dseg * 16;        // 16 B = 32 codes of a block
-        soff[i] = (uint32_t)n * (uint32_t)(K / 16) + (lane & 7) * 2;  // scale pair u = lane & 7
+        woff[i] = (uint32_t)n * (uint32_t)(K / 2) + wseg * 16;        // 16 B = 32 codes of a block
+        soff[i] = (uint32_t)n * (uint32_t)(K / 16) + (lane & 3) * 2;  // scale pair u = lane & 3
       } else {
         woff[i] = soff[i] = kOOB;
       }
@@ -192,10 +203,10 @@ __global__ __launch_bounds__(kPromptThreads, 1) void ffn_prompt_kernel(FFNArgs a
     };
     auto issue_ws = [&](int b) {
       const int K0 = b * kBlockStages * kPromptKC;
-      unsigned char* wbuf = smem + kWOff + (b & 1) * kWBlockBytes + wave * 32 * 128;
-      unsigned char* sbuf = smem + kSOff + (b & 1) * kSBlockBytes + wave * 32 * 32;
-      const bool wtail = K0 + 32 * dseg >= K;
-      const bool stail = K0 + 32 * (lane & 7) >= K;
+      unsigned char* wbuf = smem + kWOff + (b & 1) * kWBlockBytes + wave * 64 * kWRowBytes;
+      unsigned char* sbuf = smem + kSOff + (b & 1) * kSBlockBytes + wave * 64 * kSRowBytes;
+      const bool wtail = K0 + 32 * wseg >= K;
+      const bool stail = K0 + 32 * (lane & 3) >= K;
 #pragma unroll
       for (int i = 0; i < 4; ++i) dma16(wrs, wbuf + i * 1024, wtail ? kOOB : woff[i], K0 / 2);
 #pragma unroll
@@ -250,19 +261,19 @@ __global__ __launch_bounds__(kPromptThreads, 1) void ffn_prompt_kernel(FFNArgs a
         if (c % kBlockStages == 0 && c / kBlockStages + 1 < nblk) issue_ws(c / kBlockStages + 1);
 
         if (NTF == 0) continue;
-        const unsigned char* xb = smem + kXOff + (c & 1) * kXStageBytes + (128 * wtok + l32) * 128;
+        const unsigned char* xb = smem + kXOff + (c & 1) * kXStageBytes + l32 * 128;
         const int cs = c % kBlockStages;
         const int blk = (c / kBlockStages) & 1;
         const unsigned char* wb = smem + kWOff + blk * kWBlockBytes;
         const unsigned char* sb = smem + kSOff + blk * kSBlockBytes;
-        // weights of this stage: logical 16-byte segment 2cs + g of the row's 128 bytes
+        // weights of this stage: logical 16-byte segment 2cs + g of the row's 64 bytes
         u32x4 q[2];
         uint32_t sc[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int r = wrow[i];
-          q[i] = *reinterpret_cast<const u32x4*>(wb + r * 128 + (((2 * cs + g) ^ (r & 7)) * 16));
-          sc[i] = *reinterpret_cast<const uint32_t*>(sb + r * 32 + (2 * cs + g) * 4);
+          q[i] = *reinterpret_cast<const u32x4*>(wb + r * kWRowBytes + (((2 * cs + g) ^ ((r >> 1) & 3)) * 16));
+          sc[i] = *reinterpret_cast<const uint32_t*>(sb + r * kSRowBytes + (2 * cs + g) * 4);
         }
         // activation fragment t of MFMA step s: row 32t + l32, logical segment 4g + s
         constexpr int NB = NTF > 0 ? NTF : 1;
@@ -314,13 +325,13 @@ __global__ __launch_bounds__(kPromptThreads, 1) void ffn_prompt_kernel(FFNArgs a
     }
 
     // ---- epilogue. Accumulator r of fragment (i, t): weight row 8*(r/4) + 4*g + r%4 of
-    // the fragment, activation row 128*wtok + 32t + l32 of the tile.
+    // the fragment, activation row 32t + l32 of the tile.
     if (MODE == 0) {
       if (fvalid[0]) {
         const float tg = a.gate_ts[e], tu = a.up_ts[e];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int row = 128 * wtok + t * 32 + l32;
+          const int row = t * 32 + l32;
           if (t < ntf && row < nrows) {
             uint16_t* hp = a.h + (size_t)(p0 + row) * a.f + fbase + 4 * g;
 #pragma unroll
@@ -345,7 +356,7 @@ __global__ __launch_bounds__(kPromptThreads, 1) void ffn_prompt_kernel(FFNArgs a
         const int c0 = fbase + 32 * i;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int row = 128 * wtok + t * 32 + l32;
+          const int row = t * 32 + l32;
           if (t < ntf && row < nrows) {
             float* yp = a.y_rows + (size_t)(p0 + row) * a.d + c0 + 4 * g;
 #pragma unroll
@@ -388,7 +399,7 @@ hipError_t launch_ffn_prompt(const FFNArgs& a, hipStream_t stream) {
   const long long max_tiles = rows / kPromptRows + std::min<long long>(a.E, rows);
   const int ncu = device_cu_count();
   const int ct_gu = (a.f + 127) / 128;
-  const int grid_gu = (int)std::min<long long>(max_tiles * ct_gu, ncu);
+  const int grid_gu = (int)std::min<long long>(max_tiles * ct_gu, (long long)kPromptBlocksPerCu * ncu);
   hipError_t err = launch_ffn_skinny_gateup(a, stream);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(ffn_prompt_kernel<0>, dim3(grid_gu), dim3(kPromptThreads), kPromptLdsBytes, stream, a, ct_gu);
@@ -397,7 +408,7 @@ hipError_t launch_ffn_prompt(const FFNArgs& a, hipStream_t stream) {
   err = launch_ffn_skinny_down(a, stream);
   if (err != hipSuccess) return err;
   const int ct_dn = (a.d + 255) / 256;
-  const int grid_dn = (int)std::min<long long>(max_tiles * ct_dn, ncu);
+  const int grid_dn = (int)std::min<long long>(max_tiles * ct_dn, (long long)kPromptBlocksPerCu * ncu);
   hipLaunchKernelGGL(ffn_prompt_kernel<1>, dim3(grid_dn), dim3(kPromptThreads), kPromptLdsBytes, stream, a, ct_dn);
   return hipGetLastError();
 }
