@@ -16,14 +16,10 @@ constexpr int kCombineThreads = 256;
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const float* __restrict__ y_rows, const int32_t* __restrict__ row_of,
     const float* __restrict__ w, int T, int k, int d, uint16_t* __restrict__ out) {
-  __shared__ int s_row[32];
-  __shared__ float s_w[32];
+  // the token's row positions and weights are the same for the whole block: scalar loads
   const int t = blockIdx.x;
-  if (threadIdx.x < k) {
-    s_row[threadIdx.x] = row_of[(size_t)t * k + threadIdx.x];
-    s_w[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
-  }
-  __syncthreads();
+  const int32_t* const ro = row_of + (size_t)t * k;
+  const float* const wt = w + (size_t)t * k;
   const int c = (blockIdx.y * kCombineThreads + threadIdx.x) * 4;
   if (c >= d) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -33,11 +29,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     float4 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      v[u] = *reinterpret_cast<const float4*>(y_rows + (size_t)s_row[min(j0 + u, k - 1)] * d + c);
+      v[u] = *reinterpret_cast<const float4*>(y_rows + (size_t)ro[min(j0 + u, k - 1)] * d + c);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (j0 + u < k) {
-        const float wj = s_w[j0 + u];
+        const float wj = wt[j0 + u];
         acc.x = fmaf(wj, v[u].x, acc.x);
         acc.y = fmaf(wj, v[u].y, acc.y);
         acc.z = fmaf(wj, v[u].z, acc.z);
