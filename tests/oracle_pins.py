@@ -18,7 +18,7 @@ import numpy as np
 
 import oracle
 from oracle import formats as F
-from oracle import moe, mxfp8
+from oracle import moe, mxfp8, router
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -540,6 +540,111 @@ def pin_two_expert_combine():
             assert abs(Fraction(y[t, i]) - want) <= abs(want) * Fraction(1, 2 ** 50), (t, i)
             assert Fraction(bf16_bits_scalar(ob[t, i])) == frac_bf16_round(Fraction(y[t, i]))
             assert Fraction(bf16_bits_scalar(ob[t, i])) == frac_bf16_round(want)
+
+
+
+# ----------------------------------------------------------------------------- router projection
+def pin_router_worked_case():
+    """A hand-computed case: x = (1, 2, -0.5, 0, ...), router rows (1, 1, 1, 0, ...) and
+    (0.5, -1, 4, 0, ...) give logits 2.5 and -3.5 (mass 3.5 and 4.5)."""
+    d = 32
+    xv = np.zeros((1, d))
+    xv[0, :3] = [1.0, 2.0, -0.5]
+    wv = np.zeros((2, d))
+    wv[0, :3] = [1.0, 1.0, 1.0]
+    wv[1, :3] = [0.5, -1.0, 4.0]
+    lg, mass = router.router_logits(F.bf16_rne_bits(xv), F.bf16_rne_bits(wv))
+    assert lg.tolist() == [[2.5, -3.5]]
+    assert mass.tolist() == [[3.5, 4.5]]
+
+
+def pin_router_scaled_identity():
+    """Router row e = 2^(e-2) at column e, zero elsewhere: logit[t, e] = 2^(e-2) x[t, e]
+    exactly (T != E != d, so a transposed or mis-indexed operand fails)."""
+    rng = np.random.default_rng(41)
+    T, d, E = 3, 64, 5
+    x = F.bf16_rne_bits(rng.standard_normal((T, d)))
+    wv = np.zeros((E, d))
+    for e in range(E):
+        wv[e, e] = 2.0 ** (e - 2)
+    lg, _ = router.router_logits(x, F.bf16_rne_bits(wv))
+    for t in range(T):
+        for e in range(E):
+            assert lg[t, e] == 2.0 ** (e - 2) * bf16_bits_scalar(x[t, e])
+
+
+def pin_router_fractions():
+    """Exact rational brute force on a small random case: the fp64 oracle is within
+    d * 2^-53 of the mass of the exact sum."""
+    rng = np.random.default_rng(43)
+    T, d, E = 3, 96, 4
+    x = F.bf16_rne_bits(rng.standard_normal((T, d)))
+    w = F.bf16_rne_bits(rng.standard_normal((E, d)) * 0.1)
+    lg, mass = router.router_logits(x, w)
+    for t in range(T):
+        for e in range(E):
+            terms = [Fraction(bf16_bits_scalar(x[t, i])) * Fraction(bf16_bits_scalar(w[e, i])) for i in range(d)]
+            exact = sum(terms)
+            m = sum(abs(v) for v in terms)
+            assert abs(Fraction(lg[t, e]) - exact) <= m * Fraction(d, 2 ** 53)
+            assert abs(Fraction(mass[t, e]) - m) <= m * Fraction(d, 2 ** 53)
+
+
+def pin_router_mass():
+    """The mass bounds the logit, and equals it when every product is non-negative
+    (and equals minus it when every product is non-positive)."""
+    rng = np.random.default_rng(47)
+    x = F.bf16_rne_bits(np.abs(rng.standard_normal((2, 64))))
+    w = F.bf16_rne_bits(np.abs(rng.standard_normal((3, 64))))
+    lg, mass = router.router_logits(x, w)
+    assert np.array_equal(lg, mass)
+    lg2, mass2 = router.router_logits(x, w ^ np.uint16(0x8000))
+    assert np.array_equal(-lg2, mass2)
+    xm = F.bf16_rne_bits(rng.standard_normal((2, 64)))
+    lg3, mass3 = router.router_logits(xm, w)
+    assert np.all(np.abs(lg3) <= mass3) and np.any(np.abs(lg3) < mass3)
+
+
+def pin_router_tolerance_covers_fp32():
+    """Float32 sums of the products in three orders (sequential, reversed, in chunks of
+    32 added to a running sum) stay inside the stated tolerance, and the tolerance is
+    not vacuous: it is below 1e-3 of the mass at d = 7168."""
+    rng = np.random.default_rng(53)
+    T, d, E = 2, 7168, 3
+    x = F.bf16_rne_bits(rng.standard_normal((T, d)))
+    w = F.bf16_rne_bits(rng.standard_normal((E, d)) / np.sqrt(d))
+    lg, mass = router.router_logits(x, w)
+    tol = router.router_tolerance(d, mass)
+    assert np.all(tol < 1e-3 * mass)
+    xf = F.bf16_bits_to_f64(x).astype(np.float32)
+    wf = F.bf16_bits_to_f64(w).astype(np.float32)
+    for t in range(T):
+        for e in range(E):
+            prods = xf[t] * wf[e]  # exact in float32 (8 + 8 significant bits)
+            seq = np.float32(0)
+            for v in prods:
+                seq = np.float32(seq + v)
+            rev = np.float32(0)
+            for v in prods[::-1]:
+                rev = np.float32(rev + v)
+            chunked = np.float32(0)
+            for c in range(0, d, 32):
+                chunked = np.float32(chunked + np.float32(np.sum(prods[c:c + 32], dtype=np.float32)))
+            for got in (seq, rev, chunked):
+                assert abs(float(got) - lg[t, e]) <= tol[t, e]
+    # adversarial: every product is 1 + 2^-6 + 2^-14 ((1 + 2^-7)^2); past a running sum
+    # of 512 each float32 addition drops the 2^-14 part, so a sequential sum of 4096 of
+    # them is low by about 0.19 -- far beyond u * mass, inside (d + 8) * u * mass
+    d = 4096
+    one = F.bf16_rne_bits(np.full((1, d), 1.0 + 2.0 ** -7))
+    lg, mass = router.router_logits(one, one)
+    assert lg[0, 0] == d * (1.0 + 2.0 ** -6 + 2.0 ** -14)
+    p = np.float32(1.0 + 2.0 ** -6 + 2.0 ** -14)
+    seq = np.float32(0)
+    for _ in range(d):
+        seq = np.float32(seq + p)
+    err = abs(float(seq) - lg[0, 0])
+    assert err > 0.15 and err <= router.router_tolerance(d, mass)[0, 0]
 
 
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_") and callable(v)]

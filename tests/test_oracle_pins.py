@@ -66,6 +66,19 @@ MUTANTS = [
     ("token_of_row_wrong", "moe.py",
      [("tok = rl.sorted_rows[p].astype(np.int64) // k", "tok = rl.sorted_rows[p].astype(np.int64) % k")],
      ["pin_token_permutation", "pin_two_expert_combine"]),
+    ("router_mass_signed", "router.py",
+     [("np.abs(x) @ np.abs(w).T", "x @ w.T")],
+     ["pin_router_worked_case", "pin_router_mass"]),
+    ("router_experts_reversed", "router.py",
+     [("return x @ w.T,", "return x @ w[::-1].T,")],
+     ["pin_router_worked_case", "pin_router_scaled_identity", "pin_router_fractions"]),
+    ("router_weights_as_fp16", "router.py",
+     [("w = F.bf16_bits_to_f64(np.asarray(wr_bits, dtype=np.uint16))",
+       "w = np.asarray(wr_bits, dtype=np.uint16).view(np.float16).astype(np.float64)")],
+     ["pin_router_worked_case", "pin_router_scaled_identity"]),
+    ("router_tolerance_too_tight", "router.py",
+     [("return (d + 8) * U32 * mass", "return U32 * mass")],
+     ["pin_router_tolerance_covers_fp32"]),
     ("mxfp8_block_16", "mxfp8.py",
      [("np.repeat(F.E8M0_TABLE[s], 32, axis=-1)", "np.repeat(F.E8M0_TABLE[s], 16, axis=-1)[..., : w.shape[-1]]")],
      ["pin_mxfp8_one_hot_and_scale", "pin_mxfp8_brute_force"]),
@@ -93,7 +106,11 @@ def test_mutant_is_caught(monkeypatch, name, fname, edits, pins):
     import oracle.formats as Freal
     import oracle.moe as moereal
     import oracle.mxfp8 as mxreal
-    if fname == "formats.py":
+    import oracle.router as rtreal
+    rtm = _exec_module("router.py", edits, {}) if fname == "router.py" else rtreal
+    if fname == "router.py":
+        Fm, moem, mxm = Freal, moereal, mxreal
+    elif fname == "formats.py":
         Fm = _exec_module("formats.py", edits, {})
         moem = _exec_module("moe.py", [], {"F": Fm})
         mxm = _exec_module("mxfp8.py", [], {"F": Fm})
@@ -107,6 +124,7 @@ def test_mutant_is_caught(monkeypatch, name, fname, edits, pins):
     monkeypatch.setattr(P, "F", Fm)
     monkeypatch.setattr(P, "moe", moem)
     monkeypatch.setattr(P, "mxfp8", mxm)
+    monkeypatch.setattr(P, "router", rtm)
     red = []
     for pn in pins:
         try:

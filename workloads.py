@@ -24,6 +24,9 @@ so these synthetic draws stand in for them):
   span [2^-4, 2^2];
 * per-expert tensor scales: float32 uniform on [0.5, 2], one per expert and
   projection;
+* router matrix W_r (bfloat16 [E, d]): float32 N(0, 1/d), converted to bfloat16 by
+  torch, so the logits of N(0,1) activations are about N(0,1); the router inputs
+  are the activations of the MoE configuration with the same name;
 * MXFP8 weights: uniform over the 254 finite E4M3 codes (0x7F and 0xFF
   excluded); E8M0 block scales uniform over codes 121..129 (2^-6 .. 2^2).
 """
@@ -39,6 +42,7 @@ _T_GQ, _T_GS, _T_GTS = 3, 4, 5
 _T_UQ, _T_US, _T_UTS = 6, 7, 8
 _T_DQ, _T_DS, _T_DTS = 9, 10, 11
 _T_MX_W, _T_MX_S = 22, 23
+_T_ROUTER_W = 24
 _T_MX_X0 = 30  # + index of the M value
 
 ZIPF_S = 1.1
@@ -63,11 +67,13 @@ def _uniform_bytes(rng: np.random.Generator, shape) -> np.ndarray:
     return np.frombuffer(rng.bytes(n), dtype=np.uint8).reshape(shape).copy()
 
 
-def bf16_bits_from_normal(rng: np.random.Generator, shape) -> np.ndarray:
-    """float32 N(0,1) draws, converted to bfloat16 by torch, as uint16 bits."""
+def bf16_bits_from_normal(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
+    """float32 N(0, std^2) draws, converted to bfloat16 by torch, as uint16 bits."""
     import torch
 
     f = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        f *= np.float32(std)
     b = torch.from_numpy(f).to(torch.bfloat16)
     return b.view(torch.int16).numpy().view(np.uint16).copy()
 
@@ -193,3 +199,27 @@ def mxfp8_config(M: int, seed: int = 0) -> MXFP8Inputs:
         raise ValueError(f"M must be one of {c['M']}")
     return make_mxfp8(M, c["N"], c["K"], seed=seed, config_id=c["config_id"], name=f"mxfp8_M{M}",
                       m_index=c["M"].index(M))
+
+
+@dataclass
+class RouterInputs:
+    """The router projection's inputs: x uint16 [T, d] and w_r uint16 [E, d], bfloat16 bits."""
+    name: str
+    T: int
+    d: int
+    E: int
+    x: np.ndarray
+    w_r: np.ndarray
+
+
+def make_router(T: int, d: int, E: int, seed: int = 0, config_id: int = 99, name: str = "custom") -> RouterInputs:
+    x = bf16_bits_from_normal(_rng(seed, config_id, _T_X), (T, d))
+    w_r = bf16_bits_from_normal(_rng(seed, config_id, _T_ROUTER_W), (E, d), std=float(1.0 / np.sqrt(d)))
+    return RouterInputs(name, T, d, E, x, w_r)
+
+
+def router_config(name: str, seed: int = 0) -> RouterInputs:
+    """The router projection of a MoE configuration: the same activations (same seed
+    stream as that configuration's x), and a router matrix of E rows of length d."""
+    cid, T, d, f, E, k, zipf = MOE_CONFIGS[name]
+    return make_router(T, d, E, seed=seed, config_id=cid, name=name)
