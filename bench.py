@@ -278,6 +278,54 @@ def bench_mxfp8(M, steps, warmup, rotations, timer, seed=0):
     return res
 
 
+def bench_router(name, steps, warmup, timer, seed=0):
+    """Router projection logits = x . W_r^T of a MoE configuration's activations:
+    `steps` calls queued behind a GPU sleep, bracketed by one pair of HIP events."""
+    import numpy as np
+    import torch
+
+    import nvfp4_block_scaled_topk_amd as M_
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    inp = workloads.router_config(name, seed=seed)
+    T, d, E = inp.T, inp.d, inp.E
+    x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    w = torch.from_numpy(inp.w_r.view(np.int16)).to(dev).view(torch.bfloat16)
+    out = torch.empty((T, E), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        M_.router_logits(x, w, out=out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(20):
+        M_.router_logits(x, w, out=out)
+    torch.cuda.synchronize()
+    host_ms = (time.perf_counter() - t0) * 1e3 / 20
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    timer.queue_ahead(host_ms * steps * 1.5 + 20.0)
+    start.record()
+    for _ in range(steps):
+        M_.router_logits(x, w, out=out)
+    end.record()
+    torch.cuda.synchronize()
+    avg_ms = start.elapsed_time(end) / steps
+    nbytes = T * d * 2 + E * d * 2 + T * E * 4
+    flops = 2.0 * T * E * d
+    res = {"T": T, "d": d, "E": E, "avg_us": avg_ms * 1e3, "tokens_per_s": T / (avg_ms / 1e3),
+           "algorithmic_bytes": nbytes, "algorithmic_flop": flops,
+           "hbm_gbps": nbytes / (avg_ms / 1e3) / 1e9, "tflops": flops / (avg_ms / 1e3) / 1e12}
+    if T <= 16:
+        res["roofline"] = {"bound": "hbm", "achieved": res["hbm_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": res["hbm_gbps"] / HBM_PEAK_GBPS, "kernel": "router_logits_kernel",
+                           "algorithmic_bytes": nbytes, "avg_us": res["avg_us"], "traffic": None}
+    else:
+        res["roofline"] = {"bound": "mfma", "achieved": res["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": res["tflops"] / BF16_PEAK_TFLOPS, "kernel": "router_logits_kernel",
+                           "algorithmic_flop": flops, "avg_us": res["avg_us"], "traffic": None}
+    log(f"[bench] router {name}: {json.dumps(res)}")
+    return res
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle (test infrastructure, untuned) on the host cores: whole decode
     layers (route, dequantize, FFN, combine) on the same seeded input, repeated
@@ -310,7 +358,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
-                    choices=["tiny", "decode", "prompt", "long_prompt", "mxfp8_M1", "mxfp8_M512"])
+                    choices=["tiny", "decode", "prompt", "long_prompt", "mxfp8_M1", "mxfp8_M512",
+                             "router_decode", "router_long_prompt"])
     ap.add_argument("--rotations", type=int, default=0,
                     help="weight copies to rotate (0: enough for the touched weights to reach 1 GB)")
     ap.add_argument("--no-also", action="store_true", help="skip the prompt, long-prompt and MXFP8 measurements")
@@ -346,6 +395,19 @@ def main(argv=None):
             "roofline": r["roofline"], "cpu_baseline": None}), flush=True)
         return
 
+    if args.workload.startswith("router_"):
+        # the router projection alone: its own line, tokens/s as the value
+        name = args.workload[len("router_"):]
+        r = bench_router(name, args.steps, args.warmup, timer)
+        print(json.dumps({
+            "metric": METRIC, "value": r["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": r["avg_us"] / 1e3, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"router projection of the {name} MoE layer: T={r['T']} bf16 rows, "
+                                   f"W_r bf16 {r['E']}x{r['d']}, fp32 logits"},
+            "roofline": r["roofline"], "cpu_baseline": None}), flush=True)
+        return
+
     cid, T, d, f, E, k, zipf = workloads.MOE_CONFIGS[args.workload]
     main_res = bench_moe(args.workload, args.steps, args.warmup, args.rotations, timer)
 
@@ -375,6 +437,10 @@ def main(argv=None):
             r = bench_mxfp8(m, max(args.also_steps, 50), 5, 20, timer)
             r["roofline"]["traffic"] = load_traffic(f"mxfp8_M{m}", MXFP8_FILES)
             also[f"mxfp8_M{m}"] = r
+
+    if not args.no_also:
+        for name in ("decode", "long_prompt"):
+            also[f"router_{name}"] = bench_router(name, max(args.also_steps, 50), 5, timer)
 
     decode_like = main_res["T"] <= 16
     if decode_like:

@@ -13,6 +13,9 @@
  *                            codes, one F8_E4M3 scale per 16-element block, one fp32
  *                            scale per expert tensor (#489, #517, #545, #766);
  *   3. moe_combine           the router-weighted sum of each token's expert rows (#701);
+ *   0. moe_router_logits     the router projection that produces the logits step 1 takes:
+ *                            activations times the router matrix kept in its stored BF16
+ *                            words, summed in fp32 (#732, #763);
  *   4. mxfp8_gemm            y = x . W^T for MXFP8 weights: E4M3 elements in blocks of 32
  *                            along K with one E8M0 scale a block, as a gemv (M = 1) and a
  *                            wide GEMM (#521).
@@ -134,6 +137,19 @@ int moe_expert_ffn_nvfp4(const uint16_t* x, int T, int d, int f, int E, int k,
  */
 int moe_combine(const float* y_rows, const int32_t* row_of, const float* topk_w,
                 int T, int k, int d, uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_router_logits -- logits[t][e] = sum_i x[t][i] * w_r[e][i], fp32 accumulation
+ * ("NVIDIA FP4-Local checkpoints on DGX Spark" page, §4 Round 1: the router read as the
+ * checkpoint's BF16 words, #732; the routers' prompt logits on a float32 tile, #763).
+ * x bf16 [T][d] (the layer's activations), w_r bf16 [E][d] (the router matrix, one row
+ * an expert), logits fp32 [T][E] -- the input of moe_route_topk.
+ * Sizes: T, E >= 1, E <= 2^20, d a multiple of 32 (>= 32), T * d * 2 < 2^31 and
+ * E * d * 2 < 2^31. The sum over i is taken in a fixed order (deterministic); it differs
+ * from the exact sum by at most (d + 8) * 2^-24 * sum_i |x[t][i] * w_r[e][i]|.
+ */
+int moe_router_logits(const uint16_t* x, const uint16_t* w_r, int T, int d, int E,
+                      float* logits, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * mxfp8_gemm -- y[m][n] = bf16_rne( sum_i x[m][i] * W[n][i] ), fp32 accumulation,

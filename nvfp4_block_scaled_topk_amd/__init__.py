@@ -5,6 +5,7 @@ argument marshalling only. Every step of the layer runs in the library's HIP
 kernels; torch supplies device memory and the current stream. There is no CPU
 fallback: without the built library every call raises.
 
+    logits = router_logits(x, w_r)
     ids, w, offsets, sorted_rows, row_of = route_topk(logits, k)
     y_rows = expert_ffn_nvfp4(x, experts, offsets, sorted_rows, k)
     out = combine(y_rows, row_of, w)
@@ -26,7 +27,8 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_E_NULL", 2: "MOE_E_SHAPE", 3: "MOE_E_ALIGN"
 
 EXPORTED_SYMBOLS = (
     "moe_route_topk_workspace", "moe_route_topk", "moe_expert_ffn_nvfp4_workspace",
-    "moe_expert_ffn_nvfp4", "moe_combine", "mxfp8_gemm", "moe_status_string", "moe_last_error",
+    "moe_expert_ffn_nvfp4", "moe_combine", "mxfp8_gemm", "moe_router_logits", "moe_status_string",
+    "moe_last_error",
 )
 
 
@@ -70,6 +72,8 @@ def lib() -> ctypes.CDLL:
     L.moe_combine.restype = i32
     L.mxfp8_gemm.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
     L.mxfp8_gemm.restype = i32
+    L.moe_router_logits.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+    L.moe_router_logits.restype = i32
     L.moe_status_string.argtypes = [i32]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_last_error.argtypes = []
@@ -245,4 +249,20 @@ def mxfp8_gemm(x: torch.Tensor, w: torch.Tensor, s: torch.Tensor, out=None):
                           _dev(s, torch.uint8, "s", (N, K // 32)), _dev(out, torch.bfloat16, "y", (M, N)),
                           _stream(x))
     _check(st, "mxfp8_gemm")
+    return out
+
+
+def router_logits(x: torch.Tensor, w_r: torch.Tensor, out=None):
+    """logits fp32 [T, E] = x . W_r^T, x bf16 [T, d], W_r bf16 [E, d] (fp32 accumulation)."""
+    if x.dtype in (torch.uint16, torch.int16):
+        x = x.view(torch.bfloat16)
+    if w_r.dtype in (torch.uint16, torch.int16):
+        w_r = w_r.view(torch.bfloat16)
+    T, d = x.shape
+    E = w_r.shape[0]
+    if out is None:
+        out = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    st = lib().moe_router_logits(_dev(x, torch.bfloat16, "x"), _dev(w_r, torch.bfloat16, "w_r", (E, d)), T, d, E,
+                                 _dev(out, torch.float32, "logits", (T, E)), _stream(x))
+    _check(st, "moe_router_logits")
     return out

@@ -146,6 +146,17 @@ int moe_combine(const float* y_rows, const int32_t* row_of, const float* topk_w,
   return launch_status(moe::launch_combine(y_rows, row_of, topk_w, T, k, d, out, static_cast<hipStream_t>(stream)));
 }
 
+int moe_router_logits(const uint16_t* x, const uint16_t* w_r, int T, int d, int E, float* logits, void* stream) {
+  if (!x || !w_r || !logits) return MOE_E_NULL;
+  // x (T * d bf16) and W_r (E * d bf16) are addressed through 32-bit buffer offsets;
+  // the grid has ceil(E / 32) rows
+  if (T < 1 || E < 1 || d < 32 || d % 32 != 0 || (long long)T * d * 2 >= (1LL << 31) ||
+      (long long)E * d * 2 >= (1LL << 31) || E > (1 << 20))
+    return MOE_E_SHAPE;
+  if (!aligned16(x) || !aligned16(w_r) || !aligned16(logits)) return MOE_E_ALIGN;
+  return launch_status(moe::launch_router_logits(x, w_r, T, d, E, logits, static_cast<hipStream_t>(stream)));
+}
+
 int mxfp8_gemm(const uint16_t* x, int M, int N, int K, const uint8_t* w, const uint8_t* s, uint16_t* y,
                void* stream) {
   if (!x || !w || !s || !y) return MOE_E_NULL;

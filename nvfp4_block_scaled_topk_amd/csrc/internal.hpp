@@ -54,6 +54,10 @@ hipError_t launch_ffn_skinny_down(const FFNArgs& a, hipStream_t stream);
 hipError_t launch_combine(const float* y_rows, const int32_t* row_of, const float* w, int T,
                           int k, int d, uint16_t* out, hipStream_t stream);
 
+// router projection
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_r, int T, int d, int E, float* logits,
+                                hipStream_t stream);
+
 // MXFP8
 hipError_t launch_mxfp8(const uint16_t* x, int M, int N, int K, const uint8_t* w,
                         const uint8_t* s, uint16_t* y, hipStream_t stream);

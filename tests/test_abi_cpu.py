@@ -114,3 +114,18 @@ def test_combine_and_mxfp8_refusals():
 
 def test_last_error_empty_before_any_launch():
     assert M.lib().moe_last_error().decode() == ""
+
+
+def test_router_logits_refusals():
+    L = M.lib()
+    assert L.moe_router_logits(None, A, 4, 64, 8, A, None) == NULL
+    assert L.moe_router_logits(A, A, 4, 64, 8, None, None) == NULL
+    assert L.moe_router_logits(A, A, 0, 64, 8, A, None) == SHAPE
+    assert L.moe_router_logits(A, A, 4, 48, 8, A, None) == SHAPE
+    assert L.moe_router_logits(A, A, 4, 64, 0, A, None) == SHAPE
+    assert L.moe_router_logits(A, A, 4, 64, (1 << 20) + 1, A, None) == SHAPE
+    # 32-bit buffer offsets: T * d * 2 and E * d * 2 must stay below 2^31
+    assert L.moe_router_logits(A, A, 1 << 16, 1 << 14, 8, A, None) == SHAPE
+    assert L.moe_router_logits(A, A, 4, 1 << 14, 1 << 16, A, None) == SHAPE
+    assert L.moe_router_logits(A, A + 2, 4, 64, 8, A, None) == ALIGN
+
