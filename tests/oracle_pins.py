@@ -647,4 +647,84 @@ def pin_router_tolerance_covers_fp32():
     assert err > 0.15 and err <= router.router_tolerance(d, mass)[0, 0]
 
 
+
+# ----------------------------------------------------------------------------- routing policies
+def _policy_logits(seed, T, E):
+    return np.random.default_rng(seed).standard_normal((T, E)).astype(np.float32)
+
+
+def pin_policy_default_is_route():
+    """Policy 0 without a bias is the layer's routing (ids equal, weights to rounding)."""
+    lg = _policy_logits(61, 7, 20)
+    ids, w = router.route_policy(lg, 5, router.SOFTMAX_RENORM)
+    ids0, w0 = moe.route(lg, 5)
+    assert np.array_equal(ids, ids0) and np.allclose(w, w0, rtol=1e-14, atol=0)
+
+
+def pin_policy_softmax_vs_scipy():
+    """Policy 1: the selected entries of scipy's softmax over all experts; with k = E
+    the weights sum to 1, with k < E to less."""
+    from scipy.special import softmax
+    lg = _policy_logits(67, 6, 12)
+    ids, w = router.route_policy(lg, 4, router.SOFTMAX)
+    full = softmax(lg.astype(np.float64), axis=1)
+    assert np.allclose(w, np.take_along_axis(full, ids.astype(np.int64), axis=1), rtol=1e-13, atol=0)
+    assert np.all(w.sum(axis=1) < 1.0)
+    _, wall = router.route_policy(lg, 12, router.SOFTMAX)
+    assert np.allclose(wall.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+
+
+def pin_policy_sigmoid_vs_scipy():
+    """Policies 2 and 3: scipy's logistic function of the selected logits, divided by
+    their sum (2) or as is (3); large logits of both signs."""
+    from scipy.special import expit
+    lg = _policy_logits(71, 5, 10) * np.float32(30)
+    ids, w3 = router.route_policy(lg, 3, router.SIGMOID)
+    _, w2 = router.route_policy(lg, 3, router.SIGMOID_RENORM)
+    sel = np.take_along_axis(lg.astype(np.float64), ids.astype(np.int64), axis=1)
+    assert np.allclose(w3, expit(sel), rtol=1e-14, atol=1e-300)
+    assert np.allclose(w2, expit(sel) / expit(sel).sum(axis=1, keepdims=True), rtol=1e-14, atol=0)
+
+
+def pin_policy_choice_property():
+    """Brute force of the choice with a bias: every chosen key beats every other key
+    ((key, -index) larger), and the chosen ids come in that order."""
+    rng = np.random.default_rng(73)
+    lg = np.round(rng.standard_normal((40, 9)) * 2).astype(np.float32)  # many ties
+    bias = np.round(rng.standard_normal(9)).astype(np.float32)
+    keys = (lg + bias).astype(np.float32)
+    for policy in (0, 1, 2, 3):
+        ids, _ = router.route_policy(lg, 4, policy, bias)
+        for t in range(lg.shape[0]):
+            chosen = [int(e) for e in ids[t]]
+            rank = [(float(keys[t, e]), -e) for e in chosen]
+            assert rank == sorted(rank, reverse=True)
+            for u in set(range(9)) - set(chosen):
+                assert all((float(keys[t, e]), -e) > (float(keys[t, u]), -u) for e in chosen)
+
+
+def pin_bias_moves_choice_only():
+    """Logits (3, 2, 1, 0), bias 10 on expert 3, k = 2: the choice is (3, 0), and the
+    weights are those of the unbiased logits: sigmoid(0) = 1/2 and sigmoid(3)."""
+    lg = np.array([[3.0, 2.0, 1.0, 0.0]], dtype=np.float32)
+    bias = np.array([0.0, 0.0, 0.0, 10.0], dtype=np.float32)
+    ids, w = router.route_policy(lg, 2, router.SIGMOID, bias)
+    assert ids.tolist() == [[3, 0]]
+    assert w[0, 0] == 0.5 and abs(w[0, 1] - 1.0 / (1.0 + math.exp(-3.0))) < 1e-16
+    _, w0 = router.route_policy(lg, 2, router.SOFTMAX_RENORM, bias)
+    assert abs(w0[0, 0] - 1.0 / (1.0 + math.exp(3.0))) < 1e-16
+
+
+def pin_bias_rounds_in_fp32():
+    """The key is the float32 sum: logits (1, 1), bias (0, 2^-25): 1 + 2^-25 rounds to 1
+    in float32, a tie, so expert 0 comes first (in exact arithmetic expert 1 would)."""
+    lg = np.array([[1.0, 1.0]], dtype=np.float32)
+    bias = np.array([0.0, 2.0 ** -25], dtype=np.float32)
+    ids, _ = router.route_policy(lg, 2, router.SOFTMAX_RENORM, bias)
+    assert ids.tolist() == [[0, 1]]
+    bias2 = np.array([0.0, 2.0 ** -23], dtype=np.float32)
+    ids2, _ = router.route_policy(lg, 2, router.SOFTMAX_RENORM, bias2)
+    assert ids2.tolist() == [[1, 0]]
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_") and callable(v)]

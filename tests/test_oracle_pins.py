@@ -79,6 +79,24 @@ MUTANTS = [
     ("router_tolerance_too_tight", "router.py",
      [("return (d + 8) * U32 * mass", "return U32 * mass")],
      ["pin_router_tolerance_covers_fp32"]),
+    ("policy_softmax_renormalized", "router.py",
+     [("w = np.exp(sel - m) / np.exp(lg - m).sum(axis=1, keepdims=True)",
+       "w = np.exp(sel - m) / np.exp(sel - m).sum(axis=1, keepdims=True)")],
+     ["pin_policy_softmax_vs_scipy"]),
+    ("policy_bias_in_weights", "router.py",
+     [("lg = np.asarray(logits, dtype=np.float32).astype(np.float64)",
+       "lg = selection_keys(logits, bias).astype(np.float64)")],
+     ["pin_bias_moves_choice_only"]),
+    ("policy_bias_fp64", "router.py",
+     [("return (lg + np.asarray(bias, dtype=np.float32)[None, :]).astype(np.float32)",
+       "return lg.astype(np.float64) + np.asarray(bias, dtype=np.float64)[None, :]")],
+     ["pin_bias_rounds_in_fp32"]),
+    ("policy_sigmoid_renorm_dropped", "router.py",
+     [("w = sg / sg.sum(axis=1, keepdims=True) if policy == SIGMOID_RENORM else sg", "w = sg")],
+     ["pin_policy_sigmoid_vs_scipy"]),
+    ("policy_tie_to_higher_index", "router.py",
+     [("ids[t] = np.lexsort((np.arange(E), -keys[t]))[:k]", "ids[t] = np.lexsort((-np.arange(E), -keys[t]))[:k]")],
+     ["pin_policy_choice_property", "pin_bias_rounds_in_fp32"]),
     ("mxfp8_block_16", "mxfp8.py",
      [("np.repeat(F.E8M0_TABLE[s], 32, axis=-1)", "np.repeat(F.E8M0_TABLE[s], 16, axis=-1)[..., : w.shape[-1]]")],
      ["pin_mxfp8_one_hot_and_scale", "pin_mxfp8_brute_force"]),
