@@ -60,7 +60,18 @@ enum {
   MOE_E_SHAPE = 2,     /* a size is out of range (see each entry point)               */
   MOE_E_ALIGN = 3,     /* a pointer is not 16-byte aligned                             */
   MOE_E_WORKSPACE = 4, /* workspace NULL or smaller than the size query returns        */
-  MOE_E_LAUNCH = 5     /* a HIP launch failed; see moe_last_error()                    */
+  MOE_E_LAUNCH = 5,    /* a HIP launch failed; see moe_last_error()                    */
+  MOE_E_POLICY = 6     /* an unknown routing policy                                   */
+};
+
+/* Routing normalization policies (moe_route_topk_policy). The pages make the router's
+ * normalization policy a named value ("bloomery 0.3.9" release notes, From our
+ * contributors, #772) without listing the values; these are the ones offered. */
+enum {
+  MOE_ROUTE_SOFTMAX_RENORM = 0, /* softmax over the selected k logits (= softmax, top k, renormalize) */
+  MOE_ROUTE_SOFTMAX = 1,        /* the selected entries of the softmax over all E logits           */
+  MOE_ROUTE_SIGMOID_RENORM = 2, /* sigmoid of each selected logit, divided by their sum            */
+  MOE_ROUTE_SIGMOID = 3         /* sigmoid of each selected logit                                  */
 };
 
 /* One routed NVFP4 expert stack, stacked over the E experts, bytes as stored. The
@@ -101,6 +112,26 @@ int moe_route_topk(const float* logits, int T, int E, int k,
                    int32_t* topk_ids, float* topk_w,
                    int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_of,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_route_topk_policy -- moe_route_topk under a named normalization policy (the
+ * MOE_ROUTE_* values above; MOE_ROUTE_SOFTMAX_RENORM with bias NULL is moe_route_topk)
+ * and an optional correction bias.
+ *
+ * bias: NULL, or fp32 [E] (16-byte aligned). With a bias the choice is made on the
+ * fp32 sums logits[t][e] + bias[e] (ordered as above); the weights always use the
+ * unbiased logits of the chosen experts:
+ *   MOE_ROUTE_SOFTMAX_RENORM  w_j = exp(l_j) / sum over the k chosen of exp(l);
+ *   MOE_ROUTE_SOFTMAX         w_j = exp(l_j) / sum over all E experts of exp(l);
+ *   MOE_ROUTE_SIGMOID_RENORM  w_j = s_j / sum over the k chosen of s, s = 1 / (1 + exp(-l));
+ *   MOE_ROUTE_SIGMOID         w_j = 1 / (1 + exp(-l_j)).
+ * Row lists, sizes and workspace as for moe_route_topk. An unknown policy returns
+ * MOE_E_POLICY. Unsafe contract: logits[t][e] + bias[e] is finite.
+ */
+int moe_route_topk_policy(const float* logits, int T, int E, int k, int policy, const float* bias,
+                          int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                          int32_t* sorted_rows, int32_t* row_of, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * moe_expert_ffn_nvfp4 -- the expert FFN of every routed row, in row-list order.

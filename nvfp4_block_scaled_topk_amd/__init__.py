@@ -23,10 +23,12 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_nvfp4.so")
 
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_E_NULL", 2: "MOE_E_SHAPE", 3: "MOE_E_ALIGN",
-                4: "MOE_E_WORKSPACE", 5: "MOE_E_LAUNCH"}
+                4: "MOE_E_WORKSPACE", 5: "MOE_E_LAUNCH", 6: "MOE_E_POLICY"}
+# routing normalization policies (MOE_ROUTE_* in the header)
+ROUTE_SOFTMAX_RENORM, ROUTE_SOFTMAX, ROUTE_SIGMOID_RENORM, ROUTE_SIGMOID = 0, 1, 2, 3
 
 EXPORTED_SYMBOLS = (
-    "moe_route_topk_workspace", "moe_route_topk", "moe_expert_ffn_nvfp4_workspace",
+    "moe_route_topk_workspace", "moe_route_topk", "moe_route_topk_policy", "moe_expert_ffn_nvfp4_workspace",
     "moe_expert_ffn_nvfp4", "moe_combine", "mxfp8_gemm", "moe_router_logits", "moe_status_string",
     "moe_last_error",
 )
@@ -63,6 +65,8 @@ def lib() -> ctypes.CDLL:
     L.moe_route_topk_workspace.restype = sz
     L.moe_route_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_route_topk.restype = i32
+    L.moe_route_topk_policy.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_route_topk_policy.restype = i32
     L.moe_expert_ffn_nvfp4_workspace.argtypes = [i32, i32, i32, i32, i32]
     L.moe_expert_ffn_nvfp4_workspace.restype = sz
     L.moe_expert_ffn_nvfp4.argtypes = [vp, i32, i32, i32, i32, i32, ctypes.POINTER(_Experts), vp, vp, vp,
@@ -162,9 +166,11 @@ def route_topk_workspace(T: int, E: int, k: int) -> int:
     return int(lib().moe_route_topk_workspace(T, E, k))
 
 
-def route_topk(logits: torch.Tensor, k: int, out=None, workspace=None):
+def route_topk(logits: torch.Tensor, k: int, out=None, workspace=None, policy: int = ROUTE_SOFTMAX_RENORM,
+               bias: torch.Tensor | None = None):
     """Top-k routing and row lists. Returns (ids int32 [T,k], w fp32 [T,k],
-    offsets int32 [E+1], sorted_rows int32 [T*k], row_of int32 [T*k])."""
+    offsets int32 [E+1], sorted_rows int32 [T*k], row_of int32 [T*k]). `policy` is a
+    ROUTE_* normalization policy; `bias` (fp32 [E]) a correction bias on the choice."""
     T, E = logits.shape
     lp = _dev(logits, torch.float32, "logits")
     dev = logits.device
@@ -178,10 +184,16 @@ def route_topk(logits: torch.Tensor, k: int, out=None, workspace=None):
         workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
     wsp = workspace.data_ptr() if workspace is not None else None
     wsb = workspace.numel() if workspace is not None else 0
-    st = lib().moe_route_topk(lp, T, E, k, _dev(ids, torch.int32, "ids", (T, k)), _dev(w, torch.float32, "w", (T, k)),
-                              _dev(off, torch.int32, "offsets", (E + 1,)), _dev(srows, torch.int32, "sorted_rows", (T * k,)),
-                              _dev(rof, torch.int32, "row_of", (T * k,)), wsp, wsb, _stream(logits))
-    _check(st, "moe_route_topk")
+    outs = (_dev(ids, torch.int32, "ids", (T, k)), _dev(w, torch.float32, "w", (T, k)),
+            _dev(off, torch.int32, "offsets", (E + 1,)), _dev(srows, torch.int32, "sorted_rows", (T * k,)),
+            _dev(rof, torch.int32, "row_of", (T * k,)))
+    if policy == ROUTE_SOFTMAX_RENORM and bias is None:
+        st = lib().moe_route_topk(lp, T, E, k, *outs, wsp, wsb, _stream(logits))
+        _check(st, "moe_route_topk")
+    else:
+        bp = _dev(bias, torch.float32, "bias", (E,)) if bias is not None else None
+        st = lib().moe_route_topk_policy(lp, T, E, k, int(policy), bp, *outs, wsp, wsb, _stream(logits))
+        _check(st, "moe_route_topk_policy")
     return ids, w, off, srows, rof
 
 

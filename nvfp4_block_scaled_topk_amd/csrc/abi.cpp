@@ -73,22 +73,30 @@ size_t moe_route_topk_workspace(int T, int E, int k) {
   return b ? round_up(b) : 0;
 }
 
-int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
-                   int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_of, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+int moe_route_topk_policy(const float* logits, int T, int E, int k, int policy, const float* bias,
+                          int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* sorted_rows,
+                          int32_t* row_of, void* workspace, size_t workspace_bytes, void* stream) {
   if (!logits || !topk_ids || !topk_w || !expert_offsets || !sorted_rows || !row_of) return MOE_E_NULL;
   if (!route_shape_ok(T, E, k)) return MOE_E_SHAPE;
+  if (policy < MOE_ROUTE_SOFTMAX_RENORM || policy > MOE_ROUTE_SIGMOID) return MOE_E_POLICY;
   if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(expert_offsets) ||
-      !aligned16(sorted_rows) || !aligned16(row_of))
+      !aligned16(sorted_rows) || !aligned16(row_of) || (bias && !aligned16(bias)))
     return MOE_E_ALIGN;
   const size_t need = moe_route_topk_workspace(T, E, k);
   if (need) {
     if (!workspace || workspace_bytes < need) return MOE_E_WORKSPACE;
     if (!aligned16(workspace)) return MOE_E_ALIGN;
   }
-  return launch_status(moe::launch_route(logits, T, E, k, topk_ids, topk_w, expert_offsets, sorted_rows,
-                                         row_of, need ? workspace : nullptr,
+  return launch_status(moe::launch_route(logits, bias, policy, T, E, k, topk_ids, topk_w, expert_offsets,
+                                         sorted_rows, row_of, need ? workspace : nullptr,
                                          static_cast<hipStream_t>(stream)));
+}
+
+int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
+                   int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_of, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return moe_route_topk_policy(logits, T, E, k, MOE_ROUTE_SOFTMAX_RENORM, nullptr, topk_ids, topk_w,
+                               expert_offsets, sorted_rows, row_of, workspace, workspace_bytes, stream);
 }
 
 size_t moe_expert_ffn_nvfp4_workspace(int T, int d, int f, int E, int k) {
@@ -176,6 +184,7 @@ const char* moe_status_string(int status) {
     case MOE_E_ALIGN: return "MOE_E_ALIGN";
     case MOE_E_WORKSPACE: return "MOE_E_WORKSPACE";
     case MOE_E_LAUNCH: return "MOE_E_LAUNCH";
+    case MOE_E_POLICY: return "MOE_E_POLICY";
     default: return "MOE_E_UNKNOWN";
   }
 }

@@ -13,7 +13,8 @@ namespace moe {
 
 // routing
 size_t route_workspace_bytes(int T, int E, int k);
-hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+hipError_t launch_route(const float* logits, const float* bias, int policy, int T, int E, int k, int32_t* ids,
+                        float* w,
                         int32_t* offsets, int32_t* sorted_rows, int32_t* row_of, void* ws,
                         hipStream_t stream);
 

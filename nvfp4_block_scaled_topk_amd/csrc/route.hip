@@ -9,8 +9,12 @@
 // Kernel 1 (64 tokens per block, 256 threads): for E <= 256 and k <= 16 each token
 // owns one 16-lane row of a wave (four tokens a wave at a time) and finds its k best
 // (logit desc, index asc) by k rounds of a row argmax built from DPP lane exchanges;
-// larger E or k fall back to a wave per token and wave-wide shuffles. The weights
-// follow from the selected logits. Wave 0 then ranks every assignment among the block's
+// larger E or k fall back to a wave per token and wave-wide shuffles. The choice is on
+// the logits, or on the float32 sums logit + bias[e] when a correction bias is given;
+// the weights follow from the unbiased logits under the router's normalization policy,
+// a named value on the pages [bloomery 0.3.9 release notes, From our contributors,
+// #772]: softmax renormalized over the selected (the default), softmax over all
+// experts, sigmoid renormalized over the selected, or sigmoid. Wave 0 then ranks every assignment among the block's
 // earlier assignments to the same expert, 64 at a time: ten ballots over the expert
 // index bits give each lane the mask of lanes with its expert, and a per-expert running
 // count in LDS carries across chunks. Kernel 2 (one block per token block): each block
@@ -68,17 +72,50 @@ __device__ __forceinline__ void row_keymax_step(uint64_t& k) {
   k = o > k ? o : k;
 }
 
+template <int CTRL>
+__device__ __forceinline__ void row_max_step(float& m) {
+  m = fmaxf(m, dpp_f<CTRL>(m));
+}
+__device__ __forceinline__ float row_sum16(float s) {
+  row_sum_step<0xB1>(s);
+  row_sum_step<0x4E>(s);
+  row_sum_step<0x141>(s);
+  row_sum_step<0x140>(s);
+  return s;
+}
+__device__ __forceinline__ float row_max16(float m) {
+  row_max_step<0xB1>(m);
+  row_max_step<0x4E>(m);
+  row_max_step<0x141>(m);
+  row_max_step<0x140>(m);
+  return m;
+}
+// e^(l - m), with the rounding error of l - m carried into the exponential to first order
+__device__ __forceinline__ float exp_diff(float l, float m) {
+  const float s = l - m;
+  const float bb = s - l;
+  const float err = (l - (s - bb)) + (-m - bb);
+  const float e0 = expf(s);
+  return fmaf(e0, err, e0);
+}
+__device__ __forceinline__ float sigmoid_f32(float l) { return 1.0f / (1.0f + expf(-l)); }
+
 // Top-k of one token held by a 16-lane row (lane gl of the row holds experts gl + 16j,
-// j < EPL), k <= 16: k rounds of a row maximum over routing keys. Lane gl < k gets the
-// gl-th choice in my_v / my_i and its renormalized softmax weight in my_w.
+// j < EPL), k <= 16: k rounds of a row maximum over routing keys -- of the logits, or of
+// the float32 sums logit + bias[e] when a correction bias is given (it moves the choice
+// only). Lane gl < k gets the gl-th choice in my_i and its weight under `policy` in
+// my_w: 0 softmax over the selected logits, 1 softmax over all E logits, 2 sigmoid
+// renormalized over the selected, 3 sigmoid.
 template <int EPL>
-__device__ __forceinline__ void row_topk(const float* __restrict__ row, int E, int k, int gl, float& my_v,
-                                         int& my_i, float& my_w) {
+__device__ __forceinline__ void row_topk(const float* __restrict__ row, const float* __restrict__ bias, int E, int k,
+                                         int gl, int policy, int& my_i, float& my_w) {
   uint64_t key[EPL];
+  float lg[EPL];  // the unbiased logits (-inf past E)
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = gl + 16 * j;
-    key[j] = e < E ? route_key(row[e], e) : 0ull;
+    lg[j] = e < E ? row[e] : -__builtin_inff();
+    key[j] = e < E ? route_key(bias ? lg[j] + bias[e] : lg[j], e) : 0ull;
   }
   uint64_t mine = 0ull, top = 0ull;
   for (int r = 0; r < k; ++r) {
@@ -100,26 +137,37 @@ __device__ __forceinline__ void row_topk(const float* __restrict__ row, int E, i
     for (int j = 0; j < EPL; ++j)
       if ((uint32_t)key[j] == (uint32_t)best) key[j] = 0ull;
     if (gl == r) mine = best;
-    if (r == 0) top = best;  // the row maximum, in every lane of the row
+    if (r == 0) top = best;  // the first choice, in every lane of the row
   }
-  my_v = route_key_value(mine);
+  const bool sel = gl < k;
   my_i = route_key_expert(mine);
-  my_w = route_key_value(top);
-  const float m = my_w;
-  float ex = 0.0f;
-  if (gl < k) {
-    const float s = my_v - m;
-    const float bb = s - my_v;
-    const float err = (my_v - (s - bb)) + (-m - bb);
-    const float e0 = expf(s);
-    ex = fmaf(e0, err, e0);
+  // the unbiased logit of this lane's choice (without a bias, the key's own value)
+  const float my_l = sel ? (bias ? row[sel ? my_i : 0] : route_key_value(mine)) : -__builtin_inff();
+  if (policy <= 1) {
+    float m, denom;
+    float ex = 0.0f;
+    if (policy == 0) {
+      // without a bias the first choice holds the largest selected logit
+      m = bias ? row_max16(my_l) : route_key_value(top);
+      if (sel) ex = exp_diff(my_l, m);
+      denom = row_sum16(ex);
+    } else {
+      float lm = lg[0];
+#pragma unroll
+      for (int j = 1; j < EPL; ++j) lm = fmaxf(lm, lg[j]);
+      m = row_max16(lm);
+      float ls = 0.0f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (gl + 16 * j < E) ls += exp_diff(lg[j], m);
+      denom = row_sum16(ls);
+      if (sel) ex = exp_diff(my_l, m);
+    }
+    my_w = ex / denom;
+  } else {
+    const float sg = sel ? sigmoid_f32(my_l) : 0.0f;
+    my_w = policy == 2 ? sg / row_sum16(sg) : sg;
   }
-  float sum = ex;
-  row_sum_step<0xB1>(sum);
-  row_sum_step<0x4E>(sum);
-  row_sum_step<0x141>(sum);
-  row_sum_step<0x140>(sum);
-  my_w = ex / sum;
 }
 
 // Exclusive scan of s_in[0..n) in LDS (n <= 1024) by the block's first wave, 64
@@ -152,7 +200,8 @@ __device__ void block_exclusive_scan(const int* s_in, int* s_out, int n) {
 
 template <int EPL>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
-    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ topk_ids,
+    const float* __restrict__ logits, const float* __restrict__ bias, int policy, int T, int E, int k,
+    int32_t* __restrict__ topk_ids,
     float* __restrict__ topk_w, int32_t* __restrict__ ws_rank, int32_t* __restrict__ ws_counts,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_rows,
     int32_t* __restrict__ row_of) {
@@ -175,9 +224,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const int gl = lane & 15;
     for (int tl = wave * 4 + (lane >> 4); tl < ntok; tl += kWaves * 4) {
       const int t = t_begin + tl;
-      float my_v, my_w;
+      float my_w;
       int my_i;
-      row_topk<kRowEpl>(logits + (size_t)t * E, E, k, gl, my_v, my_i, my_w);
+      row_topk<kRowEpl>(logits + (size_t)t * E, bias, E, k, gl, policy, my_i, my_w);
       if (gl < k) {
         topk_ids[(size_t)t * k + gl] = my_i;
         topk_w[(size_t)t * k + gl] = my_w;
@@ -191,10 +240,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const float* row = logits + (size_t)t * E;
     float v[EPL];
     int ix[EPL];
+    // selection values: the logits, or the float32 sums logit + bias[e] (-0.0 ties +0.0)
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       const int e = lane + 64 * j;
-      v[j] = e < E ? row[e] : -__builtin_inff();
+      v[j] = e < E ? (bias ? row[e] + bias[e] : row[e]) : -__builtin_inff();
       ix[j] = e < E ? e : 0x7FFFFFFF;
     }
     float my_v = 0.0f;
@@ -216,23 +266,46 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
         if (ix[j] == bi) { v[j] = -__builtin_inff(); ix[j] = 0x7FFFFFFF; }
       if (lane == r) { my_v = bv; my_i = bi; }
     }
-    // weights: softmax over the k selected logits, max-subtracted; the rounding error
-    // of l_j - l_0 is carried into the exponential to first order
-    const float m = __shfl(my_v, 0);
-    float ex = 0.0f;
-    if (lane < k) {
-      const float s = my_v - m;
-      const float bb = s - my_v;
-      const float err = (my_v - (s - bb)) + (-m - bb);
-      const float e0 = expf(s);
-      ex = fmaf(e0, err, e0);
-    }
-    float sum = ex;
+    // weights under the policy (as in the row path), from the unbiased logits
+    const bool sel = lane < k;
+    const float my_l = sel ? (bias ? row[sel ? my_i : 0] : my_v) : -__builtin_inff();
+    auto wmax = [](float m) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-    if (lane < k) {
+      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      return m;
+    };
+    auto wsum = [](float s) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+      return s;
+    };
+    float wt;
+    if (policy <= 1) {
+      float m, denom, ex = 0.0f;
+      if (policy == 0) {
+        m = bias ? wmax(my_l) : __shfl(my_v, 0);  // without a bias, the first choice
+        if (sel) ex = exp_diff(my_l, m);
+        denom = wsum(ex);
+      } else {
+        float lm = -__builtin_inff(), ls = 0.0f;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+          if (lane + 64 * j < E) lm = fmaxf(lm, row[lane + 64 * j]);
+        m = wmax(lm);
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+          if (lane + 64 * j < E) ls += exp_diff(row[lane + 64 * j], m);
+        denom = wsum(ls);
+        if (sel) ex = exp_diff(my_l, m);
+      }
+      wt = ex / denom;
+    } else {
+      const float sg = sel ? sigmoid_f32(my_l) : 0.0f;
+      wt = policy == 2 ? sg / wsum(sg) : sg;
+    }
+    if (sel) {
       topk_ids[(size_t)t * k + lane] = my_i;
-      topk_w[(size_t)t * k + lane] = ex / sum;
+      topk_w[(size_t)t * k + lane] = wt;
       s_ids[tl * k + lane] = my_i;
     }
   }
@@ -337,7 +410,8 @@ size_t route_workspace_bytes(int T, int E, int k) {
   return ((size_t)T * k + nb * (size_t)E) * sizeof(int32_t);
 }
 
-hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+hipError_t launch_route(const float* logits, const float* bias, int policy, int T, int E, int k, int32_t* ids,
+                        float* w,
                         int32_t* offsets, int32_t* sorted_rows, int32_t* row_of, void* ws,
                         hipStream_t stream) {
   const int nb = (T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock;
@@ -350,7 +424,7 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
   const int epl = (E + 63) / 64;
   dim3 grid(nb), block(kRouteThreads);
 #define MOE_ROUTE_LAUNCH(N)                                                                     \
-  hipLaunchKernelGGL(route_topk_kernel<N>, grid, block, 0, stream, logits, T, E, k, ids, w,     \
+  hipLaunchKernelGGL(route_topk_kernel<N>, grid, block, 0, stream, logits, bias, policy, T, E, k, ids, w, \
                      ws_rank, ws_counts, offsets, sorted_rows, row_of)
   if (epl <= 1) MOE_ROUTE_LAUNCH(1);
   else if (epl <= 2) MOE_ROUTE_LAUNCH(2);

@@ -129,3 +129,14 @@ def test_router_logits_refusals():
     assert L.moe_router_logits(A, A, 4, 1 << 14, 1 << 16, A, None) == SHAPE
     assert L.moe_router_logits(A, A + 2, 4, 64, 8, A, None) == ALIGN
 
+
+def test_route_policy_refusals():
+    L = M.lib()
+    ws = 0
+    assert L.moe_route_topk_policy(None, 4, 8, 2, 0, None, A, A, A, A, A, None, ws, None) == NULL
+    assert L.moe_route_topk_policy(A, 4, 8, 9, 0, None, A, A, A, A, A, None, ws, None) == SHAPE
+    for bad in (-1, 4, 99):
+        assert L.moe_route_topk_policy(A, 4, 8, 2, bad, None, A, A, A, A, A, None, ws, None) == 6
+    assert L.moe_status_string(6).decode() == "MOE_E_POLICY"
+    assert L.moe_route_topk_policy(A, 4, 8, 2, 2, A + 4, A, A, A, A, A, None, ws, None) == ALIGN
+

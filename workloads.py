@@ -42,7 +42,7 @@ _T_GQ, _T_GS, _T_GTS = 3, 4, 5
 _T_UQ, _T_US, _T_UTS = 6, 7, 8
 _T_DQ, _T_DS, _T_DTS = 9, 10, 11
 _T_MX_W, _T_MX_S = 22, 23
-_T_ROUTER_W = 24
+_T_ROUTER_W, _T_ROUTER_BIAS = 24, 25
 _T_MX_X0 = 30  # + index of the M value
 
 ZIPF_S = 1.1
@@ -223,3 +223,13 @@ def router_config(name: str, seed: int = 0) -> RouterInputs:
     stream as that configuration's x), and a router matrix of E rows of length d."""
     cid, T, d, f, E, k, zipf = MOE_CONFIGS[name]
     return make_router(T, d, E, seed=seed, config_id=cid, name=name)
+
+
+def make_route_bias(E: int, seed: int = 0, config_id: int = 99, scale: float = 1.0, ties: bool = False) -> np.ndarray:
+    """A correction bias, float32 [E]: scale * N(0,1), or with ``ties`` rounded to
+    multiples of 1/2 (so biased keys tie often)."""
+    b = _rng(seed, config_id, _T_ROUTER_BIAS).standard_normal(size=E, dtype=np.float32)
+    if ties:
+        b = np.round(b * 2) / 2
+    return (b * np.float32(scale)).astype(np.float32)
+
