@@ -42,6 +42,7 @@ TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 DECODE_FILES = ["ffn_decode.hip", "device.hpp"]
 PROMPT_FILES = ["ffn_prompt.hip", "ffn_skinny.hip", "device.hpp"]
 MXFP8_FILES = ["mxfp8.hip", "device.hpp"]
+ROUTER_FILES = ["router.hip", "device.hpp"]
 PROMPT_KERNELS = ("moe_expert_ffn_nvfp4 prompt path (ffn_prompt_kernel grouped GEMM gate/up + down; "
                   "ffn_skinny gate/up + down for experts with <= 16 rows)")
 
@@ -317,11 +318,13 @@ def bench_router(name, steps, warmup, timer, seed=0):
     if T <= 16:
         res["roofline"] = {"bound": "hbm", "achieved": res["hbm_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": res["hbm_gbps"] / HBM_PEAK_GBPS, "kernel": "router_logits_kernel",
-                           "algorithmic_bytes": nbytes, "avg_us": res["avg_us"], "traffic": None}
+                           "algorithmic_bytes": nbytes, "avg_us": res["avg_us"],
+                           "traffic": load_traffic(f"router_{name}", ROUTER_FILES)}
     else:
         res["roofline"] = {"bound": "mfma", "achieved": res["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": res["tflops"] / BF16_PEAK_TFLOPS, "kernel": "router_logits_kernel",
-                           "algorithmic_flop": flops, "avg_us": res["avg_us"], "traffic": None}
+                           "algorithmic_flop": flops, "avg_us": res["avg_us"],
+                           "traffic": load_traffic(f"router_{name}", ROUTER_FILES)}
     log(f"[bench] router {name}: {json.dumps(res)}")
     return res
 
