@@ -198,9 +198,11 @@ __device__ void block_exclusive_scan(const int* s_in, int* s_out, int n) {
   __syncthreads();
 }
 
-template <int EPL>
+// PLAIN: the default policy without a bias, compiled with both as constants (the other
+// policies' code drops out)
+template <int EPL, bool PLAIN>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
-    const float* __restrict__ logits, const float* __restrict__ bias, int policy, int T, int E, int k,
+    const float* __restrict__ logits, const float* __restrict__ bias_arg, int policy_arg, int T, int E, int k,
     int32_t* __restrict__ topk_ids,
     float* __restrict__ topk_w, int32_t* __restrict__ ws_rank, int32_t* __restrict__ ws_counts,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_rows,
@@ -211,6 +213,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
 
+  const float* const bias = PLAIN ? nullptr : bias_arg;
+  const int policy = PLAIN ? 0 : policy_arg;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t_begin = blockIdx.x * kRouteTokensPerBlock;
@@ -423,9 +427,16 @@ hipError_t launch_route(const float* logits, const float* bias, int policy, int 
   }
   const int epl = (E + 63) / 64;
   dim3 grid(nb), block(kRouteThreads);
-#define MOE_ROUTE_LAUNCH(N)                                                                     \
-  hipLaunchKernelGGL(route_topk_kernel<N>, grid, block, 0, stream, logits, bias, policy, T, E, k, ids, w, \
-                     ws_rank, ws_counts, offsets, sorted_rows, row_of)
+  const bool plain = policy == 0 && bias == nullptr;
+#define MOE_ROUTE_LAUNCH(N)                                                                                    \
+  do {                                                                                                         \
+    if (plain)                                                                                                 \
+      hipLaunchKernelGGL((route_topk_kernel<N, true>), grid, block, 0, stream, logits, bias, policy, T, E, k,  \
+                         ids, w, ws_rank, ws_counts, offsets, sorted_rows, row_of);                            \
+    else                                                                                                       \
+      hipLaunchKernelGGL((route_topk_kernel<N, false>), grid, block, 0, stream, logits, bias, policy, T, E, k, \
+                         ids, w, ws_rank, ws_counts, offsets, sorted_rows, row_of);                            \
+  } while (0)
   if (epl <= 1) MOE_ROUTE_LAUNCH(1);
   else if (epl <= 2) MOE_ROUTE_LAUNCH(2);
   else if (epl <= 4) MOE_ROUTE_LAUNCH(4);
