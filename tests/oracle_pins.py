@@ -18,7 +18,7 @@ import numpy as np
 
 import oracle
 from oracle import formats as F
-from oracle import moe, mxfp8, router
+from oracle import moe, mxfp8, router, shared
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -725,6 +725,73 @@ def pin_bias_rounds_in_fp32():
     bias2 = np.array([0.0, 2.0 ** -23], dtype=np.float32)
     ids2, _ = router.route_policy(lg, 2, router.SOFTMAX_RENORM, bias2)
     assert ids2.tolist() == [[1, 0]]
+
+
+
+# ----------------------------------------------------------------------------- shared expert
+class _Shared:
+    def __init__(self, ex, w_sg):
+        for nm, v in ex.items():
+            setattr(self, nm, v)
+        self.w_sg = w_sg
+
+
+def pin_shared_zero_expert():
+    """A shared expert with all-zero codes adds nothing: the layer's bits are the routed
+    layer's."""
+    inp = _small_layer(seed=5)
+    ex = {nm: np.zeros_like(v) if nm.endswith("_q") else v.copy()
+          for nm, v in _identity_experts(inp.d).items()}
+    ex = {nm: (v[:, :inp.f] if nm in ("gate_q", "gate_s", "up_q", "up_s") else v) for nm, v in ex.items()}
+    ex["down_q"] = np.zeros((1, inp.d, inp.f // 2), np.uint8)
+    ex["down_s"] = np.full((1, inp.d, inp.f // 16), 0x38, np.uint8)
+    sh = _Shared(ex, F.bf16_rne_bits(np.random.default_rng(3).standard_normal(inp.d)))
+    a = shared.moe_layer_shared(inp, sh)
+    b = moe.moe_layer(inp)
+    assert np.array_equal(a.out_bits, b.out_bits)
+
+
+def pin_shared_identity_closed_form():
+    """Routed experts with all-zero codes, an identity shared expert, a zero gate vector:
+    g = sigmoid(0) = 1/2, so out = bf16(h / 2) with h = bf16(silu(x) x), i.e. exactly h / 2."""
+    import workloads
+    d = 64
+    inp = workloads.make_moe(4, d, d, 3, 2, seed=9, config_id=78)
+    for nm in ("gate_q", "up_q", "down_q"):
+        setattr(inp, nm, np.zeros_like(getattr(inp, nm)))
+    sh = _Shared(_identity_experts(d), np.zeros(d, np.uint16))
+    res = shared.moe_layer_shared(inp, sh)
+    for t in range(inp.T):
+        for i in range(d):
+            xv = bf16_bits_scalar(inp.x[t, i])
+            sig = 1.0 / (1.0 + math.exp(-xv)) if xv >= 0 else math.exp(xv) / (1.0 + math.exp(xv))
+            want = frac_bf16_round(Fraction(xv * sig) * Fraction(xv)) / 2
+            assert Fraction(bf16_bits_scalar(res.out_bits[t, i])) == want, (t, i)
+
+
+def pin_shared_is_an_extra_routed_expert():
+    """The shared expert is expert E of an (E+1)-expert layer that every token routes to
+    last, with weight g_t = sigmoid(x_t . w_sg) computed here by math.fsum and math.exp:
+    the same fp64 values, the same bits."""
+    import workloads
+    inp = _small_layer(seed=7)
+    T, d, f, E, k = inp.T, inp.d, inp.f, inp.E, inp.k
+    sh = workloads.make_shared(d, f, seed=7, config_id=79)
+    res = shared.moe_layer_shared(inp, sh)
+    ids, w = moe.route(inp.logits, k)
+    g = np.empty(T)
+    for t in range(T):
+        z = math.fsum(bf16_bits_scalar(inp.x[t, i]) * bf16_bits_scalar(sh.w_sg[i]) for i in range(d))
+        g[t] = 1.0 / (1.0 + math.exp(-z)) if z >= 0 else math.exp(z) / (1.0 + math.exp(z))
+    ex = moe.experts_dict(inp)
+    ex2 = {nm: np.concatenate([ex[nm], getattr(sh, nm)]) for nm in ex}
+    ids2 = np.concatenate([ids, np.full((T, 1), E, np.int32)], axis=1)
+    w2 = np.concatenate([w, g[:, None]], axis=1)
+    rl2 = moe.row_lists(ids2, E + 1)
+    ffn2 = moe.expert_ffn(inp.x, T, d, f, E + 1, k + 1, ex2, rl2)
+    y2, ob2 = moe.combine(ffn2.y_rows, rl2.row_of, w2, T, k + 1)
+    assert np.allclose(res.y, y2, rtol=1e-13, atol=1e-300)
+    assert np.array_equal(res.out_bits, ob2)
 
 
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_") and callable(v)]

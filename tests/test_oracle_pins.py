@@ -97,6 +97,15 @@ MUTANTS = [
     ("policy_tie_to_higher_index", "router.py",
      [("ids[t] = np.lexsort((np.arange(E), -keys[t]))[:k]", "ids[t] = np.lexsort((-np.arange(E), -keys[t]))[:k]")],
      ["pin_policy_choice_property", "pin_bias_rounds_in_fp32"]),
+    ("shared_gate_not_applied", "shared.py",
+     [("y = res.y + g[:, None] * S.y_rows", "y = res.y + S.y_rows")],
+     ["pin_shared_identity_closed_form", "pin_shared_is_an_extra_routed_expert"]),
+    ("shared_gate_sign_flipped", "shared.py",
+     [("    z = x @ w\n", "    z = -(x @ w)\n")],
+     ["pin_shared_is_an_extra_routed_expert"]),
+    ("shared_row_rounded", "shared.py",
+     [("y = res.y + g[:, None] * S.y_rows", "y = res.y + g[:, None] * F.bf16_rne(S.y_rows)")],
+     ["pin_shared_is_an_extra_routed_expert"]),
     ("mxfp8_block_16", "mxfp8.py",
      [("np.repeat(F.E8M0_TABLE[s], 32, axis=-1)", "np.repeat(F.E8M0_TABLE[s], 16, axis=-1)[..., : w.shape[-1]]")],
      ["pin_mxfp8_one_hot_and_scale", "pin_mxfp8_brute_force"]),
@@ -125,8 +134,10 @@ def test_mutant_is_caught(monkeypatch, name, fname, edits, pins):
     import oracle.moe as moereal
     import oracle.mxfp8 as mxreal
     import oracle.router as rtreal
+    import oracle.shared as shreal
     rtm = _exec_module("router.py", edits, {}) if fname == "router.py" else rtreal
-    if fname == "router.py":
+    shm = _exec_module("shared.py", edits, {}) if fname == "shared.py" else shreal
+    if fname in ("router.py", "shared.py"):
         Fm, moem, mxm = Freal, moereal, mxreal
     elif fname == "formats.py":
         Fm = _exec_module("formats.py", edits, {})
@@ -143,6 +154,7 @@ def test_mutant_is_caught(monkeypatch, name, fname, edits, pins):
     monkeypatch.setattr(P, "moe", moem)
     monkeypatch.setattr(P, "mxfp8", mxm)
     monkeypatch.setattr(P, "router", rtm)
+    monkeypatch.setattr(P, "shared", shm)
     red = []
     for pn in pins:
         try:

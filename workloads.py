@@ -27,6 +27,9 @@ so these synthetic draws stand in for them):
 * router matrix W_r (bfloat16 [E, d]): float32 N(0, 1/d), converted to bfloat16 by
   torch, so the logits of N(0,1) activations are about N(0,1); the router inputs
   are the activations of the MoE configuration with the same name;
+* shared expert: one NVFP4 expert (codes, block scales and tensor scales drawn as for
+  the routed experts, from streams of its own), and a shared-gate vector bfloat16 [d]
+  drawn as float32 N(0, 1/d);
 * MXFP8 weights: uniform over the 254 finite E4M3 codes (0x7F and 0xFF
   excluded); E8M0 block scales uniform over codes 121..129 (2^-6 .. 2^2).
 """
@@ -43,6 +46,7 @@ _T_UQ, _T_US, _T_UTS = 6, 7, 8
 _T_DQ, _T_DS, _T_DTS = 9, 10, 11
 _T_MX_W, _T_MX_S = 22, 23
 _T_ROUTER_W, _T_ROUTER_BIAS = 24, 25
+_T_SH_GQ, _T_SH_GS, _T_SH_GTS, _T_SH_UQ, _T_SH_US, _T_SH_UTS, _T_SH_DQ, _T_SH_DS, _T_SH_DTS, _T_SH_GATE = range(40, 50)
 _T_MX_X0 = 30  # + index of the M value
 
 ZIPF_S = 1.1
@@ -232,4 +236,48 @@ def make_route_bias(E: int, seed: int = 0, config_id: int = 99, scale: float = 1
     if ties:
         b = np.round(b * 2) / 2
     return (b * np.float32(scale)).astype(np.float32)
+
+
+@dataclass
+class SharedInputs:
+    """A shared expert beside the routed ones: one NVFP4 expert (arrays with a leading
+    expert axis of 1, layouts as in MoEInputs) and the shared-gate vector w_sg uint16 [d]
+    (bfloat16 bits)."""
+    d: int
+    f: int
+    gate_q: np.ndarray
+    gate_s: np.ndarray
+    gate_ts: np.ndarray
+    up_q: np.ndarray
+    up_s: np.ndarray
+    up_ts: np.ndarray
+    down_q: np.ndarray
+    down_s: np.ndarray
+    down_ts: np.ndarray
+    w_sg: np.ndarray
+
+
+def make_shared(d: int, f: int, seed: int = 0, config_id: int = 99) -> SharedInputs:
+    def codes(tid, shape):
+        return _uniform_bytes(_rng(seed, config_id, tid), shape)
+
+    def scales(tid, shape):
+        return _rng(seed, config_id, tid).integers(0x18, 0x49, size=shape, dtype=np.uint8)
+
+    def tscale(tid):
+        return _rng(seed, config_id, tid).uniform(0.5, 2.0, size=(1,)).astype(np.float32)
+
+    return SharedInputs(
+        d=d, f=f,
+        gate_q=codes(_T_SH_GQ, (1, f, d // 2)), gate_s=scales(_T_SH_GS, (1, f, d // 16)), gate_ts=tscale(_T_SH_GTS),
+        up_q=codes(_T_SH_UQ, (1, f, d // 2)), up_s=scales(_T_SH_US, (1, f, d // 16)), up_ts=tscale(_T_SH_UTS),
+        down_q=codes(_T_SH_DQ, (1, d, f // 2)), down_s=scales(_T_SH_DS, (1, d, f // 16)), down_ts=tscale(_T_SH_DTS),
+        w_sg=bf16_bits_from_normal(_rng(seed, config_id, _T_SH_GATE), (d,), std=float(1.0 / np.sqrt(d))),
+    )
+
+
+def shared_config(name: str, seed: int = 0) -> SharedInputs:
+    """The shared expert of a MoE configuration (same d and f)."""
+    cid, T, d, f, E, k, zipf = MOE_CONFIGS[name]
+    return make_shared(d, f, seed=seed, config_id=cid)
 
