@@ -13,6 +13,7 @@
  *                            codes, one F8_E4M3 scale per 16-element block, one fp32
  *                            scale per expert tensor (#489, #517, #545, #766);
  *   3. moe_combine           the router-weighted sum of each token's expert rows (#701);
+ *                            moe_combine_shared adds a gated shared expert's rows (#686);
  *   0. moe_router_logits     the router projection that produces the logits step 1 takes:
  *                            activations times the router matrix kept in its stored BF16
  *                            words, summed in fp32 (#732, #763);
@@ -168,6 +169,22 @@ int moe_expert_ffn_nvfp4(const uint16_t* x, int T, int d, int f, int E, int k,
  */
 int moe_combine(const float* y_rows, const int32_t* row_of, const float* topk_w,
                 int T, int k, int d, uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_combine_shared -- moe_combine with a shared expert's rows added (the pages run a
+ * shared expert beside the routed ones, "NVIDIA FP4-Local checkpoints on DGX Spark"
+ * page, §4 Round 1, #686, and fold its add into the producing kernel, §4 remaining items):
+ *   out[t][c] = bf16_rne( sum_j topk_w[t][j] * y_rows[row_of[t*k+j]][c] + g_t * shared_rows[t][c] ),
+ *   g_t = 1 / (1 + exp(-shared_gate_logit[t])), or 1 when shared_gate_logit is NULL;
+ * the routed sum in j order, the shared term added last, one rounding.
+ * shared_rows fp32 [T][d]: the shared expert's output rows, e.g. moe_expert_ffn_nvfp4 with
+ * one expert (E = 1, k = 1, expert_offsets = {0, T}, sorted_rows[p] = p); shared_gate_logit
+ * fp32 [T] (NULL allowed), e.g. moe_router_logits with the gate vector as a one-row router.
+ * Sizes and alignment as for moe_combine; shared_rows is required (MOE_E_NULL).
+ */
+int moe_combine_shared(const float* y_rows, const int32_t* row_of, const float* topk_w,
+                       int T, int k, int d, const float* shared_rows,
+                       const float* shared_gate_logit, uint16_t* out, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * moe_router_logits -- logits[t][e] = sum_i x[t][i] * w_r[e][i], fp32 accumulation

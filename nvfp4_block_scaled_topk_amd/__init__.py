@@ -29,7 +29,7 @@ ROUTE_SOFTMAX_RENORM, ROUTE_SOFTMAX, ROUTE_SIGMOID_RENORM, ROUTE_SIGMOID = 0, 1,
 
 EXPORTED_SYMBOLS = (
     "moe_route_topk_workspace", "moe_route_topk", "moe_route_topk_policy", "moe_expert_ffn_nvfp4_workspace",
-    "moe_expert_ffn_nvfp4", "moe_combine", "mxfp8_gemm", "moe_router_logits", "moe_status_string",
+    "moe_expert_ffn_nvfp4", "moe_combine", "moe_combine_shared", "mxfp8_gemm", "moe_router_logits", "moe_status_string",
     "moe_last_error",
 )
 
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.moe_expert_ffn_nvfp4.restype = i32
     L.moe_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
     L.moe_combine.restype = i32
+    L.moe_combine_shared.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]
+    L.moe_combine_shared.restype = i32
     L.mxfp8_gemm.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
     L.mxfp8_gemm.restype = i32
     L.moe_router_logits.argtypes = [vp, vp, i32, i32, i32, vp, vp]
@@ -229,12 +231,24 @@ def expert_ffn_nvfp4(x: torch.Tensor, experts: NVFP4Experts, offsets: torch.Tens
     return out
 
 
-def combine(y_rows: torch.Tensor, row_of: torch.Tensor, w: torch.Tensor, out=None):
-    """out bf16 [T, d] = bf16_rne(sum_j w[t, j] * y_rows[row_of[t*k + j]])."""
+def combine(y_rows: torch.Tensor, row_of: torch.Tensor, w: torch.Tensor, out=None,
+            shared_rows: torch.Tensor | None = None, shared_gate_logit: torch.Tensor | None = None):
+    """out bf16 [T, d] = bf16_rne(sum_j w[t, j] * y_rows[row_of[t*k + j]] (+ g_t * shared_rows[t],
+    g_t = sigmoid(shared_gate_logit[t]) or 1))."""
     T, k = w.shape
     d = y_rows.shape[1]
     if out is None:
         out = torch.empty((T, d), dtype=torch.bfloat16, device=y_rows.device)
+    if shared_rows is not None:
+        gp = None
+        if shared_gate_logit is not None:
+            gp = _dev(shared_gate_logit.reshape(T), torch.float32, "shared_gate_logit", (T,))
+        st = lib().moe_combine_shared(_dev(y_rows, torch.float32, "y_rows", (T * k, d)),
+                                      _dev(row_of, torch.int32, "row_of", (T * k,)), _dev(w, torch.float32, "w", (T, k)),
+                                      T, k, d, _dev(shared_rows, torch.float32, "shared_rows", (T, d)), gp,
+                                      _dev(out, torch.bfloat16, "out", (T, d)), _stream(y_rows))
+        _check(st, "moe_combine_shared")
+        return out
     st = lib().moe_combine(_dev(y_rows, torch.float32, "y_rows", (T * k, d)), _dev(row_of, torch.int32, "row_of", (T * k,)),
                            _dev(w, torch.float32, "w", (T, k)), T, k, d, _dev(out, torch.bfloat16, "out", (T, d)),
                            _stream(y_rows))
@@ -278,3 +292,22 @@ def router_logits(x: torch.Tensor, w_r: torch.Tensor, out=None):
                                  _dev(out, torch.float32, "logits", (T, E)), _stream(x))
     _check(st, "moe_router_logits")
     return out
+
+
+_shared_lists = {}
+
+
+def shared_expert_nvfp4(x: torch.Tensor, shared: NVFP4Experts, out=None, workspace=None):
+    """The shared expert's rows S fp32 [T, d]: moe_expert_ffn_nvfp4 with one expert that every
+    token routes to (offsets {0, T}, row p = token p). The two index lists are constants of
+    T, built once per (T, device)."""
+    if shared.E != 1:
+        raise ValueError("a shared expert is one expert (leading axis 1)")
+    T = x.shape[0]
+    key = (T, x.device)
+    if key not in _shared_lists:
+        _shared_lists[key] = (torch.tensor([0, T], dtype=torch.int32, device=x.device),
+                              torch.arange(T, dtype=torch.int32, device=x.device))
+    off, rows = _shared_lists[key]
+    return expert_ffn_nvfp4(x, shared, off, rows, 1, out=out, workspace=workspace)
+

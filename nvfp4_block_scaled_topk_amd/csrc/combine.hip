@@ -6,6 +6,12 @@
 // sum widening them). Here the expert rows stay fp32 and are summed in fp32 in the
 // token's top-k order, then rounded once to bf16: out[t] = bf16_rne(sum_j w_tj * y[row_of[t*k+j]]).
 // Pure streaming: each thread owns 4 consecutive columns of one token (128-bit loads).
+//
+// With a shared expert beside the routed ones [same page, §4 Round 1, #686], its add
+// folds into this producer (the pages fold the shared-expert add into the kernels
+// that produce it [same page, §4 remaining items]): out[t] = bf16_rne(sum_j w_tj *
+// y[...] + g_t * S[t]), g_t = sigmoid(gate logit of t) (1 without a gate), the shared
+// row S kept fp32 and added last, before the single rounding.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -13,9 +19,11 @@ namespace moe {
 
 constexpr int kCombineThreads = 256;
 
+template <bool SHARED>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const float* __restrict__ y_rows, const int32_t* __restrict__ row_of,
-    const float* __restrict__ w, int T, int k, int d, uint16_t* __restrict__ out) {
+    const float* __restrict__ w, int T, int k, int d, const float* __restrict__ s_rows,
+    const float* __restrict__ s_gate, uint16_t* __restrict__ out) {
   // the token's row positions and weights are the same for the whole block: scalar loads
   const int t = blockIdx.x;
   const int32_t* const ro = row_of + (size_t)t * k;
@@ -23,6 +31,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   const int c = (blockIdx.y * kCombineThreads + threadIdx.x) * 4;
   if (c >= d) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 sv;
+  if constexpr (SHARED) sv = *reinterpret_cast<const float4*>(s_rows + (size_t)t * d + c);
   // eight rows' loads in flight at once (a group past k repeats row k-1 and adds
   // nothing), then the sums in top-k order
   for (int j0 = 0; j0 < k; j0 += 8) {
@@ -41,6 +51,13 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
       }
     }
   }
+  if constexpr (SHARED) {
+    const float g = s_gate ? 1.0f / (1.0f + expf(-s_gate[t])) : 1.0f;
+    acc.x = fmaf(g, sv.x, acc.x);
+    acc.y = fmaf(g, sv.y, acc.y);
+    acc.z = fmaf(g, sv.z, acc.z);
+    acc.w = fmaf(g, sv.w, acc.w);
+  }
   uint2 o;
   o.x = (uint32_t)bf16_rne(acc.x) | ((uint32_t)bf16_rne(acc.y) << 16);
   o.y = (uint32_t)bf16_rne(acc.z) | ((uint32_t)bf16_rne(acc.w) << 16);
@@ -48,10 +65,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 }
 
 hipError_t launch_combine(const float* y_rows, const int32_t* row_of, const float* w, int T, int k,
-                          int d, uint16_t* out, hipStream_t stream) {
+                          int d, const float* s_rows, const float* s_gate, uint16_t* out, hipStream_t stream) {
   dim3 grid(T, (d / 4 + kCombineThreads - 1) / kCombineThreads);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombineThreads), 0, stream, y_rows, row_of, w, T,
-                     k, d, out);
+  if (s_rows)
+    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(kCombineThreads), 0, stream, y_rows, row_of, w, T, k, d,
+                       s_rows, s_gate, out);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(kCombineThreads), 0, stream, y_rows, row_of, w, T, k, d,
+                       nullptr, nullptr, out);
   return hipGetLastError();
 }
 

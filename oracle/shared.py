@@ -49,27 +49,29 @@ def shared_gate(x_bits, w_sg_bits, tokens=None):
     return g, np.abs(x) @ np.abs(w)
 
 
-def add_shared(res: moe.MoEResult, x_bits, T, d, f, sh, tokens=None) -> moe.MoEResult:
+def add_shared(res: moe.MoEResult, x_bits, T, d, f, sh, tokens=None, gated: bool = True) -> moe.MoEResult:
     """The routed result `res` (whole layer, or the sampled `tokens` of moe_tokens) with
     the gated shared row added before the single rounding. The acceptance terms grow by
     g * mass_S and g * slack_S, plus the effect of the float32 gate logit: its error
     (at most (d + 8) 2^-24 of its mass, through sigmoid' <= 1/4) and a few ulps of the
-    float32 sigmoid, times |S|."""
+    float32 sigmoid, times |S|. Ungated (``gated=False``): g = 1."""
     S = shared_rows(x_bits, T, d, f, sh, tokens)
     g, gmass = shared_gate(x_bits, sh.w_sg, tokens)
+    if not gated:
+        g, gmass = np.ones_like(g), np.zeros_like(gmass)
     y = res.y + g[:, None] * S.y_rows
-    dg = 0.25 * (d + 8) * 2.0 ** -24 * gmass + 8 * 2.0 ** -24 * g
+    dg = 0.25 * (d + 8) * 2.0 ** -24 * gmass + (8 * 2.0 ** -24 * g if gated else 0.0)
     mass = res.mass + g[:, None] * S.mass_y
     slack = res.slack + g[:, None] * S.slack_h + dg[:, None] * np.abs(S.y_rows)
     return moe.MoEResult(res.ids, res.w, res.rl, res.ffn, y, F.bf16_rne_bits(y), mass, slack)
 
 
-def moe_layer_shared(inp, sh) -> moe.MoEResult:
+def moe_layer_shared(inp, sh, gated: bool = True) -> moe.MoEResult:
     """The whole layer with the shared expert."""
-    return add_shared(moe.moe_layer(inp), inp.x, inp.T, inp.d, inp.f, sh)
+    return add_shared(moe.moe_layer(inp), inp.x, inp.T, inp.d, inp.f, sh, gated=gated)
 
 
-def moe_tokens_shared(inp, sh, tokens) -> moe.MoEResult:
+def moe_tokens_shared(inp, sh, tokens, gated: bool = True) -> moe.MoEResult:
     """Sampled tokens of the layer with the shared expert."""
     tokens = np.asarray(tokens, dtype=np.int64)
-    return add_shared(moe.moe_tokens(inp, tokens), inp.x, inp.T, inp.d, inp.f, sh, tokens)
+    return add_shared(moe.moe_tokens(inp, tokens), inp.x, inp.T, inp.d, inp.f, sh, tokens, gated=gated)

@@ -140,3 +140,13 @@ def test_route_policy_refusals():
     assert L.moe_status_string(6).decode() == "MOE_E_POLICY"
     assert L.moe_route_topk_policy(A, 4, 8, 2, 2, A + 4, A, A, A, A, A, None, ws, None) == ALIGN
 
+
+def test_combine_shared_refusals():
+    L = M.lib()
+    assert L.moe_combine_shared(A, A, A, 4, 2, 64, None, None, A, None) == NULL
+    assert L.moe_combine_shared(None, A, A, 4, 2, 64, A, None, A, None) == NULL
+    assert L.moe_combine_shared(A, A, A, 4, 33, 64, A, None, A, None) == SHAPE
+    assert L.moe_combine_shared(A, A, A, 4, 2, 48, A, A, A, None) == SHAPE
+    assert L.moe_combine_shared(A, A, A, 4, 2, 64, A + 4, None, A, None) == ALIGN
+    assert L.moe_combine_shared(A, A, A, 4, 2, 64, A, A + 8, A, None) == ALIGN
+
