@@ -279,6 +279,87 @@ def bench_mxfp8(M, steps, warmup, rotations, timer, seed=0):
     return res
 
 
+def bench_block(name, steps, warmup, timer, seed=0):
+    """The whole MoE block of a configuration: router projection, routing, routed expert
+    FFN, the shared expert's FFN and gate logit, and the combine with the shared add, all
+    on one stream (the few-token FFN is not overlapped with other work). Routed and
+    shared weights rotate through copies as in bench_moe (touched bytes >= 1 GB a
+    rotation). Returns tokens/s and the block's algorithmic bytes and FLOP rates."""
+    import numpy as np
+    import torch
+
+    import nvfp4_block_scaled_topk_amd as M
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    inp = workloads.moe_config(name, seed=seed)
+    rin = workloads.router_config(name, seed=seed)
+    sh = workloads.shared_config(name, seed=seed)
+    T, d, f, E, k = inp.T, inp.d, inp.f, inp.E, inp.k
+    x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    w_r = torch.from_numpy(rin.w_r.view(np.int16)).to(dev).view(torch.bfloat16)
+    w_sg = torch.from_numpy(sh.w_sg.view(np.int16).reshape(1, d)).to(dev).view(torch.bfloat16)
+    ex0 = M.NVFP4Experts.from_numpy(inp, dev)
+    sx0 = M.NVFP4Experts.from_numpy(sh, dev)
+    del inp, rin, sh
+    logits = M.router_logits(x, w_r)
+    _, _, off0, _, _ = M.route_topk(logits, k)
+    U = int((off0[1:] - off0[:-1] > 0).sum().item())
+    eb = expert_bytes(d, f)
+    rotations = max(1, -(-(1 << 30) // ((U + 1) * eb)))
+    rotations = min(rotations, max(1, (48 << 30) // max(1, (E + 1) * eb)))
+    names = ("gate_q", "gate_s", "gate_ts", "up_q", "up_s", "up_ts", "down_q", "down_s", "down_ts")
+    copies = [(ex0, sx0)] + [(M.NVFP4Experts(*[getattr(ex0, n).clone() for n in names]),
+                              M.NVFP4Experts(*[getattr(sx0, n).clone() for n in names])) for _ in range(rotations - 1)]
+    rbufs = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32, device=dev),
+             torch.empty((E + 1,), dtype=torch.int32, device=dev), torch.empty((T * k,), dtype=torch.int32, device=dev),
+             torch.empty((T * k,), dtype=torch.int32, device=dev))
+    rws_n = M.route_topk_workspace(T, E, k)
+    rws = torch.empty((rws_n,), dtype=torch.uint8, device=dev) if rws_n else None
+    fws = torch.empty((max(M.expert_ffn_workspace(T, d, f, E, k), 1),), dtype=torch.uint8, device=dev)
+    sws = torch.empty((max(M.expert_ffn_workspace(T, d, f, 1, 1), 1),), dtype=torch.uint8, device=dev)
+    y_rows = torch.empty((T * k, d), dtype=torch.float32, device=dev)
+    s_rows = torch.empty((T, d), dtype=torch.float32, device=dev)
+    glog = torch.empty((T, 1), dtype=torch.float32, device=dev)
+    out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    ids, w, off, srows, rof = rbufs
+
+    def step(i):
+        ex, sx = copies[i % rotations]
+        M.router_logits(x, w_r, out=logits)
+        M.route_topk(logits, k, out=rbufs, workspace=rws)
+        M.expert_ffn_nvfp4(x, ex, off, srows, k, out=y_rows, workspace=fws, check=False)
+        M.shared_expert_nvfp4(x, sx, out=s_rows, workspace=sws)
+        M.router_logits(x, w_sg, out=glog)
+        M.combine(y_rows, rof, w, out=out, shared_rows=s_rows, shared_gate_logit=glog)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(min(steps, 20)):
+        step(i)
+    torch.cuda.synchronize()
+    host_ms = (time.perf_counter() - t0) * 1e3 / min(steps, 20)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    timer.queue_ahead(host_ms * steps * 1.5 + 20.0)
+    start.record()
+    for i in range(steps):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    nbytes = (U + 1) * eb + E * d * 2 + d * 2 + 2 * T * d * 2 + T * E * 4
+    flops = 2.0 * T * (k + 1) * 3 * d * f + 2.0 * T * (E + 1) * d
+    res = {"T": T, "d": d, "f": f, "E": E, "k": k, "touched_experts": U, "weight_copies_rotated": rotations,
+           "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "algorithmic_bytes": nbytes, "algorithmic_flop": flops,
+           "hbm_gbps": nbytes / (ms / 1e3) / 1e9, "tflops": flops / (ms / 1e3) / 1e12}
+    log(f"[bench] block {name}: {json.dumps(res)}")
+    del copies, ex0, sx0
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_router(name, steps, warmup, timer, seed=0):
     """Router projection logits = x . W_r^T of a MoE configuration's activations:
     `steps` calls queued behind a GPU sleep, bracketed by one pair of HIP events."""
@@ -362,7 +443,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
                     choices=["tiny", "decode", "prompt", "long_prompt", "mxfp8_M1", "mxfp8_M512",
-                             "router_decode", "router_long_prompt"])
+                             "router_decode", "router_long_prompt", "block_decode", "block_long_prompt"])
     ap.add_argument("--rotations", type=int, default=0,
                     help="weight copies to rotate (0: enough for the touched weights to reach 1 GB)")
     ap.add_argument("--no-also", action="store_true", help="skip the prompt, long-prompt and MXFP8 measurements")
@@ -411,6 +492,27 @@ def main(argv=None):
             "roofline": r["roofline"], "cpu_baseline": None}), flush=True)
         return
 
+    if args.workload.startswith("block_"):
+        # the whole MoE block (router, routing, routed and shared experts, combine): own line
+        name = args.workload[len("block_"):]
+        r = bench_block(name, args.steps, args.warmup, timer)
+        decode_like = r["T"] <= 16
+        roof = ({"bound": "hbm", "achieved": r["hbm_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                 "frac": r["hbm_gbps"] / HBM_PEAK_GBPS, "algorithmic_bytes": r["algorithmic_bytes"]}
+                if decode_like else
+                {"bound": "mfma", "achieved": r["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": r["tflops"] / BF16_PEAK_TFLOPS, "algorithmic_flop": r["algorithmic_flop"]})
+        roof.update({"kernel": "whole block, one step", "avg_us": r["ms_per_step"] * 1e3, "traffic": None})
+        print(json.dumps({
+            "metric": METRIC, "value": r["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"{name} MoE block: router projection, top-{r['k']} routing, {r['E']} routed NVFP4 "
+                                   f"experts and one shared NVFP4 expert (T={r['T']}, d={r['d']}, f={r['f']}), "
+                                   "gated shared add in the combine"},
+            "roofline": roof, "cpu_baseline": None}), flush=True)
+        return
+
     cid, T, d, f, E, k, zipf = workloads.MOE_CONFIGS[args.workload]
     main_res = bench_moe(args.workload, args.steps, args.warmup, args.rotations, timer)
 
@@ -444,6 +546,7 @@ def main(argv=None):
     if not args.no_also:
         for name in ("decode", "long_prompt"):
             also[f"router_{name}"] = bench_router(name, max(args.also_steps, 50), 5, timer)
+        also["block_decode"] = bench_block("decode", max(args.also_steps, 50), 5, timer)
 
     decode_like = main_res["T"] <= 16
     if decode_like:

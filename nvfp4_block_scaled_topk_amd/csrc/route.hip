@@ -6,7 +6,7 @@
 // normalization policy the pages name, [bloomery 0.3.9 release notes, Fixed, #772],
 // read as softmax -> top-k -> renormalize).
 //
-// Kernel 1 (64 tokens per block, 256 threads): for E <= 256 and k <= 16 each token
+// Kernel 1 (16 tokens per block, 256 threads): for E <= 256 and k <= 16 each token
 // owns one 16-lane row of a wave (four tokens a wave at a time) and finds its k best
 // (logit desc, index asc) by k rounds of a row argmax built from DPP lane exchanges;
 // larger E or k fall back to a wave per token and wave-wide shuffles. The choice is on
@@ -20,14 +20,14 @@
 // count in LDS carries across chunks. Kernel 2 (one block per token block): each block
 // sums the per-expert counts of the blocks before it and of all blocks, scans over
 // experts, and scatters p = offset[e] + (earlier blocks' count of e) + rank. No
-// atomics: the row lists are the same bits on every run. A batch of at most 64 tokens
+// atomics: the row lists are the same bits on every run. A batch of at most 16 tokens
 // runs as one launch (scan and scatter in the same block).
 #include "device.hpp"
 #include "internal.hpp"
 
 namespace moe {
 
-constexpr int kRouteTokensPerBlock = 64;
+constexpr int kRouteTokensPerBlock = 16;  // measured against 32 and 64: more blocks, shorter chains
 constexpr int kRouteThreads = 256;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;

@@ -60,13 +60,13 @@ def test_route_refusals():
     assert call(E=64, k=33) == SHAPE   # k > 32
     assert call(logits=A + 4) == ALIGN
     assert call(off=A + 8) == ALIGN
-    # more than one 64-token block needs a workspace
-    need = L.moe_route_topk_workspace(65, 8, 2)
+    # more than one 16-token block needs a workspace
+    need = L.moe_route_topk_workspace(17, 8, 2)
     assert need > 0
-    assert L.moe_route_topk_workspace(64, 8, 2) == 0
-    assert call(T=65) == WS
-    assert call(T=65, ws=A, wsb=need - 1) == WS
-    assert call(T=65, ws=A + 4, wsb=need) == ALIGN
+    assert L.moe_route_topk_workspace(16, 8, 2) == 0
+    assert call(T=17) == WS
+    assert call(T=17, ws=A, wsb=need - 1) == WS
+    assert call(T=17, ws=A + 4, wsb=need) == ALIGN
     assert L.moe_route_topk_workspace(0, 8, 2) == 0
 
 

@@ -38,8 +38,8 @@ def test_route_configs(name):
     check_routing(inp, res, name)
 
 
-ROUTE_EDGE = [(1, 1, 1), (1, 8, 8), (3, 64, 32), (64, 7, 3), (65, 7, 3), (130, 1024, 32),
-              (200, 65, 1), (129, 128, 8), (1000, 256, 8), (37, 33, 32)]
+ROUTE_EDGE = [(1, 1, 1), (1, 8, 8), (3, 64, 32), (16, 8, 2), (17, 8, 2), (33, 128, 8), (64, 7, 3), (65, 7, 3),
+              (130, 1024, 32), (200, 65, 1), (129, 128, 8), (1000, 256, 8), (37, 33, 32)]
 
 
 @pytest.mark.parametrize("T,E,k", ROUTE_EDGE)
