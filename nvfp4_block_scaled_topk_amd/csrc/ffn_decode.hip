@@ -392,6 +392,23 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
     // H rows of expert u -> LDS (bf16, row stride hstride), polling until every word
     // carries this call's tag
     const int npair = a.f / 4;  // pairs of H words (4 features) a row
+    {
+      // first wait on one word of each 32-feature slice of each row (one per gate/up
+      // item: 16x fewer device-scope loads while the producers finish, which eases the
+      // hot spot of many pollers on the same few KB); the full read below still
+      // validates every word. Each wait is bounded like the full poll.
+      const int nsl = a.f / 32;
+      for (int idx = threadIdx.x; idx < ne * nsl; idx += kDecThreads) {
+        const int r = idx / nsl, g = idx - r * nsl;
+        const unsigned long long* src = hw + ((size_t)(r0 + r) * a.f) / 2 + 16 * g + 15;
+        for (uint32_t it = 0; it < kSpinLimit; ++it) {
+          const unsigned long long w0 = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((uint32_t)(w0 >> 32) == tag) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      __syncthreads();
+    }
     for (uint32_t it = 0;; ++it) {
       int bad = 0;
       for (int idx = threadIdx.x; idx < ne * npair; idx += kDecThreads) {
