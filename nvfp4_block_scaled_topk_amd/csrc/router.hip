@@ -4,8 +4,9 @@
 // Spark, §4 Round 1, #732] and the logits are summed on a float32 tile [same page,
 // §4 Round 1, #763]: here bf16 x bf16 products on the 16x16x32 bf16 MFMA with fp32
 // accumulation. A block of 8 waves owns 16 NT tokens x 16 NE experts (NT x NE MFMA
-// tiles a 32-element chunk of K): 64 x 64 for batches (operand bytes fetched per
-// FLOP halve with each doubling of the tile, and they bound this kernel), 16 x 16
+// tiles a 32-element chunk of K): 64 x 64 for batches, 32 x 32 when E <= 32 (operand
+// bytes fetched per FLOP halve with each doubling of the tile, and they bound this
+// kernel), 16 x 16
 // for a few tokens (more blocks, and every load of a wave's K range in flight at
 // once); the waves split K in eight contiguous ranges and their partial tiles are
 // added in LDS in a fixed order, so the result does not depend on timing. Operands come straight from memory (no LDS staging): a lane
