@@ -142,13 +142,26 @@ def bench_moe(name, steps, warmup, rotations, timer, seed=0):
     y_rows = torch.empty((T * k, d), dtype=torch.float32, device=dev)
     out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
     ids, w, off, srows, rof = rbufs
+    # few tokens: routing runs inside the FFN launch (moe_route_expert_ffn_nvfp4) when the
+    # shape allows it; otherwise route, then FFN
+    fused = False
+    if T <= 16:
+        try:
+            M.route_expert_ffn_nvfp4(logits, x, ex0, k, route_out=rbufs, out=y_rows, workspace=fws, check=False)
+            fused = True
+        except M.MoEError:
+            fused = False
 
     def step(i, ev=None):
         ex = copies[i % rotations]
-        M.route_topk(logits, k, out=rbufs, workspace=rws)
+        if not fused:
+            M.route_topk(logits, k, out=rbufs, workspace=rws)
         if ev is not None:
             ev[0].record()
-        M.expert_ffn_nvfp4(x, ex, off, srows, k, out=y_rows, workspace=fws, check=False)
+        if fused:
+            M.route_expert_ffn_nvfp4(logits, x, ex, k, route_out=rbufs, out=y_rows, workspace=fws, check=False)
+        else:
+            M.expert_ffn_nvfp4(x, ex, off, srows, k, out=y_rows, workspace=fws, check=False)
         if ev is not None:
             ev[1].record()
         M.combine(y_rows, rof, w, out=out)
@@ -216,7 +229,7 @@ def bench_moe(name, steps, warmup, rotations, timer, seed=0):
         ffn_hbm_gbps=ffn_bytes / (ffn_avg_ms / 1e3) / 1e9,
         ffn_tflops=flops / (ffn_avg_ms / 1e3) / 1e12,
         layer_tflops=flops / (ms_per_step / 1e3) / 1e12,
-        host_ms_per_step=host_ms_per_step,
+        host_ms_per_step=host_ms_per_step, route_in_ffn_launch=fused,
     )
     log(f"[bench] {name}: {json.dumps(res)}")
     del copies, ex0
@@ -324,11 +337,22 @@ def bench_block(name, steps, warmup, timer, seed=0):
     out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
     ids, w, off, srows, rof = rbufs
 
+    fused = False
+    if T <= 16:
+        try:
+            M.route_expert_ffn_nvfp4(logits, x, ex0, k, route_out=rbufs, out=y_rows, workspace=fws, check=False)
+            fused = True
+        except M.MoEError:
+            fused = False
+
     def step(i):
         ex, sx = copies[i % rotations]
         M.router_logits(x, w_r, out=logits)
-        M.route_topk(logits, k, out=rbufs, workspace=rws)
-        M.expert_ffn_nvfp4(x, ex, off, srows, k, out=y_rows, workspace=fws, check=False)
+        if fused:
+            M.route_expert_ffn_nvfp4(logits, x, ex, k, route_out=rbufs, out=y_rows, workspace=fws, check=False)
+        else:
+            M.route_topk(logits, k, out=rbufs, workspace=rws)
+            M.expert_ffn_nvfp4(x, ex, off, srows, k, out=y_rows, workspace=fws, check=False)
         M.shared_expert_nvfp4(x, sx, out=s_rows, workspace=sws)
         M.router_logits(x, w_sg, out=glog)
         M.combine(y_rows, rof, w, out=out, shared_rows=s_rows, shared_gate_logit=glog)
@@ -352,6 +376,7 @@ def bench_block(name, steps, warmup, timer, seed=0):
     nbytes = (U + 1) * eb + E * d * 2 + d * 2 + 2 * T * d * 2 + T * E * 4
     flops = 2.0 * T * (k + 1) * 3 * d * f + 2.0 * T * (E + 1) * d
     res = {"T": T, "d": d, "f": f, "E": E, "k": k, "touched_experts": U, "weight_copies_rotated": rotations,
+           "route_in_ffn_launch": fused,
            "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "algorithmic_bytes": nbytes, "algorithmic_flop": flops,
            "hbm_gbps": nbytes / (ms / 1e3) / 1e9, "tflops": flops / (ms / 1e3) / 1e12}
     log(f"[bench] block {name}: {json.dumps(res)}")
@@ -586,6 +611,7 @@ def main(argv=None):
                                f"f={main_res['f']}, E={main_res['E']} NVFP4 experts, top-{main_res['k']}"
                                + (", Zipf(1.1) routing skew" if zipf else ""),
                    "touched_experts": main_res["touched_experts"], "weight_copies_rotated": main_res["rotations"],
+                   "route_in_ffn_launch": main_res["route_in_ffn_launch"],
                    "layer_hbm_gbps": main_res["layer_hbm_gbps"]},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -12,6 +12,7 @@
  *                            over NVFP4 weights held as stored -- U8 bytes of two E2M1
  *                            codes, one F8_E4M3 scale per 16-element block, one fp32
  *                            scale per expert tensor (#489, #517, #545, #766);
+ *   1+2. moe_route_expert_ffn_nvfp4  both in one launch for a few tokens;
  *   3. moe_combine           the router-weighted sum of each token's expert rows (#701);
  *                            moe_combine_shared adds a gated shared expert's rows (#686);
  *   0. moe_router_logits     the router projection that produces the logits step 1 takes:
@@ -161,6 +162,22 @@ int moe_expert_ffn_nvfp4(const uint16_t* x, int T, int d, int f, int E, int k,
                          const moe_nvfp4_experts* w,
                          const int32_t* expert_offsets, const int32_t* sorted_rows,
                          float* y_rows, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_route_expert_ffn_nvfp4 -- moe_route_topk (default policy, no bias) and
+ * moe_expert_ffn_nvfp4 in one launch, for few tokens: the launch routes its tokens itself
+ * (a whole batch routed in one run, "NVIDIA FP4-Local checkpoints on DGX Spark" page,
+ * §4 Round 1, #740) instead of waiting for a routing launch, and writes the same routing
+ * outputs (topk_ids, topk_w, expert_offsets, sorted_rows, row_of: bit-identical to
+ * moe_route_topk's) and y_rows (as moe_expert_ffn_nvfp4's few-token path).
+ * Sizes: those of the few-token path of moe_expert_ffn_nvfp4 (T <= 16, d <= 4096,
+ * f <= 1024, T * (max(d, f) + 8) * 2 <= 64 KiB), E <= 256, k <= 16; otherwise
+ * MOE_E_SHAPE (call the two entry points instead). Workspace: moe_expert_ffn_nvfp4_workspace.
+ */
+int moe_route_expert_ffn_nvfp4(const float* logits, const uint16_t* x, int T, int d, int f, int E, int k,
+                               const moe_nvfp4_experts* w, int32_t* topk_ids, float* topk_w,
+                               int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_of,
+                               float* y_rows, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * moe_combine -- out[t][c] = bf16_rne( sum_{j=0..k-1} topk_w[t][j] * y_rows[row_of[t*k+j]][c] ),

@@ -29,7 +29,7 @@ ROUTE_SOFTMAX_RENORM, ROUTE_SOFTMAX, ROUTE_SIGMOID_RENORM, ROUTE_SIGMOID = 0, 1,
 
 EXPORTED_SYMBOLS = (
     "moe_route_topk_workspace", "moe_route_topk", "moe_route_topk_policy", "moe_expert_ffn_nvfp4_workspace",
-    "moe_expert_ffn_nvfp4", "moe_combine", "moe_combine_shared", "mxfp8_gemm", "moe_router_logits", "moe_status_string",
+    "moe_expert_ffn_nvfp4", "moe_route_expert_ffn_nvfp4", "moe_combine", "moe_combine_shared", "mxfp8_gemm", "moe_router_logits", "moe_status_string",
     "moe_last_error",
 )
 
@@ -74,6 +74,9 @@ def lib() -> ctypes.CDLL:
     L.moe_expert_ffn_nvfp4.restype = i32
     L.moe_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
     L.moe_combine.restype = i32
+    L.moe_route_expert_ffn_nvfp4.argtypes = [vp, vp, i32, i32, i32, i32, i32, ctypes.POINTER(_Experts),
+                                             vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_route_expert_ffn_nvfp4.restype = i32
     L.moe_combine_shared.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]
     L.moe_combine_shared.restype = i32
     L.mxfp8_gemm.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
@@ -310,4 +313,37 @@ def shared_expert_nvfp4(x: torch.Tensor, shared: NVFP4Experts, out=None, workspa
                               torch.arange(T, dtype=torch.int32, device=x.device))
     off, rows = _shared_lists[key]
     return expert_ffn_nvfp4(x, shared, off, rows, 1, out=out, workspace=workspace)
+
+
+def route_expert_ffn_nvfp4(logits: torch.Tensor, x: torch.Tensor, experts: NVFP4Experts, k: int,
+                           route_out=None, out=None, workspace=None, check: bool = True):
+    """Routing and the expert FFN in one launch (few tokens: T <= 16, E <= 256, k <= 16).
+    Returns ((ids, w, offsets, sorted_rows, row_of), y_rows) as route_topk and
+    expert_ffn_nvfp4 would."""
+    if x.dtype in (torch.uint16, torch.int16):
+        x = x.view(torch.bfloat16)
+    T, E = logits.shape
+    d = x.shape[1]
+    f = experts.f
+    dev = x.device
+    if check:
+        experts.check()
+    if route_out is None:
+        route_out = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32, device=dev),
+                     torch.empty((E + 1,), dtype=torch.int32, device=dev), torch.empty((T * k,), dtype=torch.int32, device=dev),
+                     torch.empty((T * k,), dtype=torch.int32, device=dev))
+    ids, w, off, srows, rof = route_out
+    if out is None:
+        out = torch.empty((T * k, d), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty((max(expert_ffn_workspace(T, d, f, E, k), 1),), dtype=torch.uint8, device=dev)
+    cs = experts.c_struct()
+    st = lib().moe_route_expert_ffn_nvfp4(
+        _dev(logits, torch.float32, "logits", (T, E)), _dev(x, torch.bfloat16, "x", (T, d)), T, d, f, E, k,
+        ctypes.byref(cs), _dev(ids, torch.int32, "ids", (T, k)), _dev(w, torch.float32, "w", (T, k)),
+        _dev(off, torch.int32, "offsets", (E + 1,)), _dev(srows, torch.int32, "sorted_rows", (T * k,)),
+        _dev(rof, torch.int32, "row_of", (T * k,)), _dev(out, torch.float32, "y_rows", (T * k, d)),
+        workspace.data_ptr(), workspace.numel(), _stream(x))
+    _check(st, "moe_route_expert_ffn_nvfp4")
+    return route_out, out
 

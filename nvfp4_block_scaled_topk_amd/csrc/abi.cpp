@@ -104,22 +104,26 @@ size_t moe_expert_ffn_nvfp4_workspace(int T, int d, int f, int E, int k) {
   return moe::ffn_workspace_bytes(T, d, f, E, k);
 }
 
-int moe_expert_ffn_nvfp4(const uint16_t* x, int T, int d, int f, int E, int k, const moe_nvfp4_experts* w,
-                         const int32_t* expert_offsets, const int32_t* sorted_rows, float* y_rows,
-                         void* workspace, size_t workspace_bytes, void* stream) {
-  if (!x || !w || !expert_offsets || !sorted_rows || !y_rows) return MOE_E_NULL;
+}  // extern "C"
+
+namespace {
+
+// Checks and argument block shared by the two FFN entry points (routing lists given or
+// made by the launch itself); returns MOE_OK and fills `a`, or a refusal status.
+int ffn_setup(const uint16_t* x, int T, int d, int f, int E, int k, const moe_nvfp4_experts* w, float* y_rows,
+              void* workspace, size_t workspace_bytes, moe::FFNArgs& a) {
+  if (!x || !w || !y_rows) return MOE_E_NULL;
   if (!w->gate_q || !w->gate_s || !w->gate_ts || !w->up_q || !w->up_s || !w->up_ts || !w->down_q ||
       !w->down_s || !w->down_ts)
     return MOE_E_NULL;
   if (!ffn_shape_ok(T, d, f, E, k)) return MOE_E_SHAPE;
-  const void* ptrs[] = {x, expert_offsets, sorted_rows, y_rows, w->gate_q, w->gate_s, w->gate_ts, w->up_q,
-                        w->up_s, w->up_ts, w->down_q, w->down_s, w->down_ts};
+  const void* ptrs[] = {x, y_rows, w->gate_q, w->gate_s, w->gate_ts, w->up_q, w->up_s, w->up_ts, w->down_q,
+                        w->down_s, w->down_ts};
   for (const void* p : ptrs)
     if (!aligned16(p)) return MOE_E_ALIGN;
   const size_t need = moe_expert_ffn_nvfp4_workspace(T, d, f, E, k);
   if (!workspace || workspace_bytes < need) return MOE_E_WORKSPACE;
   if (!aligned16(workspace)) return MOE_E_ALIGN;
-  moe::FFNArgs a;
   a.x = x;
   a.T = T;
   a.d = d;
@@ -135,15 +139,51 @@ int moe_expert_ffn_nvfp4(const uint16_t* x, int T, int d, int f, int E, int k, c
   a.gate_ts = w->gate_ts;
   a.up_ts = w->up_ts;
   a.down_ts = w->down_ts;
-  a.offsets = expert_offsets;
-  a.sorted_rows = sorted_rows;
   a.y_rows = y_rows;
   a.h = static_cast<uint16_t*>(workspace);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_expert_ffn_nvfp4(const uint16_t* x, int T, int d, int f, int E, int k, const moe_nvfp4_experts* w,
+                         const int32_t* expert_offsets, const int32_t* sorted_rows, float* y_rows,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!expert_offsets || !sorted_rows) return MOE_E_NULL;
+  moe::FFNArgs a;
+  const int st0 = ffn_setup(x, T, d, f, E, k, w, y_rows, workspace, workspace_bytes, a);
+  if (st0 != MOE_OK) return st0;
+  if (!aligned16(expert_offsets) || !aligned16(sorted_rows)) return MOE_E_ALIGN;
+  a.offsets = expert_offsets;
+  a.sorted_rows = sorted_rows;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // a token routes to k distinct experts, so an expert has at most T rows: with
   // T <= 16 every expert's rows fit one decode tile
   if (moe::use_decode_path(T, d, f)) return launch_status(moe::launch_ffn_decode(a, next_call_tag(), st));
   return launch_status(moe::launch_ffn_prompt(a, st));
+}
+
+int moe_route_expert_ffn_nvfp4(const float* logits, const uint16_t* x, int T, int d, int f, int E, int k,
+                               const moe_nvfp4_experts* w, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                               int32_t* sorted_rows, int32_t* row_of, float* y_rows, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!logits || !topk_ids || !topk_w || !expert_offsets || !sorted_rows || !row_of) return MOE_E_NULL;
+  moe::FFNArgs a;
+  const int st0 = ffn_setup(x, T, d, f, E, k, w, y_rows, workspace, workspace_bytes, a);
+  if (st0 != MOE_OK) return st0;
+  if (!moe::use_decode_path(T, d, f) || E > moe::kFusedRouteMaxE || k > moe::kFusedRouteMaxK) return MOE_E_SHAPE;
+  if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(expert_offsets) ||
+      !aligned16(sorted_rows) || !aligned16(row_of))
+    return MOE_E_ALIGN;
+  a.logits = logits;
+  a.ids_out = topk_ids;
+  a.w_out = topk_w;
+  a.offsets_out = expert_offsets;
+  a.sorted_rows_out = sorted_rows;
+  a.row_of_out = row_of;
+  return launch_status(moe::launch_ffn_decode(a, next_call_tag(), static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine(const float* y_rows, const int32_t* row_of, const float* topk_w, int T, int k, int d,

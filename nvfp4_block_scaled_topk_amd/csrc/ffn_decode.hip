@@ -45,6 +45,7 @@
 // bounded: past kSpinLimit polls the block writes NaN rows instead of hanging.
 #include "device.hpp"
 #include "internal.hpp"
+#include "route_device.hpp"
 
 namespace moe {
 
@@ -136,8 +137,61 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
     }
   }
   const int nA = a.T * a.k;
-  for (int i = threadIdx.x; i <= a.E; i += kDecThreads) s_off[i] = a.offsets[i];
-  for (int i = threadIdx.x; i < nA; i += kDecThreads) s_tok[i] = a.sorted_rows[i] / a.k;
+  if (a.logits) {
+    // Route the tokens here (every block, redundantly: T <= 16 tokens of E <= 256 logits):
+    // the same top-k and weights as the routing kernel (one 16-lane row a token, waves
+    // 0-3), then the stable row lists -- the rank of each assignment among the earlier
+    // ones of its expert, the per-expert counts and their exclusive scan. Block 0 writes
+    // the routing outputs. Work arrays live in the waves' scratch (free until the
+    // gate/up items start): offsets at 0, counts at 1028, experts of the assignments at
+    // 1288, ranks at 1800 (ints).
+    int* const s_cnt = s_off + 1028;
+    int* const s_aid = s_off + 1288;
+    int* const s_rnk = s_off + 1800;
+    static_assert(kDecWaves * kScrWave >= (int)sizeof(int) * (1800 + kDecMaxAssign), "routing arrays fit the scratch");
+    for (int e = threadIdx.x; e < a.E; e += kDecThreads) s_cnt[e] = 0;
+    {
+      const int gl = lane & 15, t = wave * 4 + (lane >> 4);  // a 16-lane row is one token
+      if (t < a.T) {
+        float my_w;
+        int my_i;
+        if (a.E <= 128)
+          row_topk<8>(a.logits + (size_t)t * a.E, nullptr, a.E, a.k, gl, 0, my_i, my_w);
+        else
+          row_topk<16>(a.logits + (size_t)t * a.E, nullptr, a.E, a.k, gl, 0, my_i, my_w);
+        if (gl < a.k) {
+          s_aid[t * a.k + gl] = my_i;
+          if (blockIdx.x == 0) {
+            a.ids_out[t * a.k + gl] = my_i;
+            a.w_out[t * a.k + gl] = my_w;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nA; i += kDecThreads) {
+      const int e = s_aid[i];
+      int r = 0;
+      for (int j = 0; j < i; ++j) r += s_aid[j] == e;
+      s_rnk[i] = r;
+      atomicAdd(&s_cnt[e], 1);  // LDS; the final counts do not depend on the order
+    }
+    __syncthreads();
+    block_exclusive_scan(s_cnt, s_off, a.E);  // ends with a barrier
+    for (int i = threadIdx.x; i < nA; i += kDecThreads) {
+      const int p = s_off[s_aid[i]] + s_rnk[i];
+      s_tok[p] = i / a.k;
+      if (blockIdx.x == 0) {
+        a.sorted_rows_out[p] = i;
+        a.row_of_out[i] = p;
+      }
+    }
+    if (blockIdx.x == 0)
+      for (int e = threadIdx.x; e <= a.E; e += kDecThreads) a.offsets_out[e] = s_off[e];
+  } else {
+    for (int i = threadIdx.x; i <= a.E; i += kDecThreads) s_off[i] = a.offsets[i];
+    for (int i = threadIdx.x; i < nA; i += kDecThreads) s_tok[i] = a.sorted_rows[i] / a.k;
+  }
   __syncthreads();
   if (wave == 0) {
     int seen = 0;

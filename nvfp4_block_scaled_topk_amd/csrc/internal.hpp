@@ -28,7 +28,18 @@ struct FFNArgs {
   const int32_t* sorted_rows;
   float* y_rows;
   uint16_t* h;
+  // few-token path only: when `logits` is set the launch routes its tokens itself
+  // (default policy, no bias; E <= 256, k <= 16) instead of reading offsets and
+  // sorted_rows, and its first block writes the routing outputs
+  const float* logits = nullptr;
+  int32_t* ids_out = nullptr;
+  float* w_out = nullptr;
+  int32_t* offsets_out = nullptr;
+  int32_t* sorted_rows_out = nullptr;
+  int32_t* row_of_out = nullptr;
 };
+constexpr int kFusedRouteMaxE = 256;
+constexpr int kFusedRouteMaxK = 16;
 // The decode path keeps every expert's rows in one 16-row MFMA tile (T <= 16).
 constexpr int kDecodeMaxRows = 16;
 size_t ffn_workspace_bytes(int T, int d, int f, int E, int k);

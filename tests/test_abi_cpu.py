@@ -150,3 +150,24 @@ def test_combine_shared_refusals():
     assert L.moe_combine_shared(A, A, A, 4, 2, 64, A + 4, None, A, None) == ALIGN
     assert L.moe_combine_shared(A, A, A, 4, 2, 64, A, A + 8, A, None) == ALIGN
 
+
+def test_route_ffn_refusals():
+    L = M.lib()
+    ex = M._Experts(*([A] * 9))
+    T, d, f, E, k = 4, 256, 128, 8, 2
+    need = L.moe_expert_ffn_nvfp4_workspace(T, d, f, E, k)
+
+    def call(lg=A, x=A, T=T, d=d, f=f, E=E, k=k, ids=A, w=A, off=A, sr=A, ro=A, y=A, ws=A, wsb=need):
+        return L.moe_route_expert_ffn_nvfp4(lg, x, T, d, f, E, k, ctypes.byref(ex), ids, w, off, sr, ro, y, ws, wsb,
+                                            None)
+    assert call(lg=None) == NULL
+    assert call(ro=None) == NULL
+    assert call(x=None) == NULL
+    # only the few-token path, E <= 256, k <= 16
+    assert call(T=17, wsb=L.moe_expert_ffn_nvfp4_workspace(17, d, f, E, k)) == SHAPE
+    assert call(E=257, wsb=L.moe_expert_ffn_nvfp4_workspace(T, d, f, 257, k)) == SHAPE
+    assert call(E=64, k=17, wsb=L.moe_expert_ffn_nvfp4_workspace(T, d, f, 64, 17)) == SHAPE
+    assert call(lg=A + 4) == ALIGN
+    assert call(w=A + 8) == ALIGN
+    assert call(ws=None) == WS
+

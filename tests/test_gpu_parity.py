@@ -199,3 +199,28 @@ def test_mxfp8_config(M_):
     rep = band.classify(got[rows], ref, mass)
     say(f"[mxfp8 config M={M_}] {rep}")
     assert rep.ok(), str(rep)
+
+
+# ---------------------------------------------------------------- routing in the FFN launch
+@pytest.mark.parametrize("T,d,f,E,k", [(4, 2048, 768, 128, 8), (1, 32, 32, 1, 1), (3, 96, 64, 5, 2),
+                                       (16, 160, 96, 6, 3), (8, 512, 256, 256, 16), (16, 256, 128, 200, 4)])
+def test_route_ffn_fused(T, d, f, E, k):
+    """moe_route_expert_ffn_nvfp4 against the oracle (routing bit-exact, whole layer in the
+    band) and against the separate moe_route_topk + moe_expert_ffn_nvfp4 calls (same bits)."""
+    import torch
+    import nvfp4_block_scaled_topk_amd as M
+    inp = workloads.make_moe(T, d, f, E, k, seed=4, config_id=63, zipf=True)
+    say(f"fused route+FFN T={T} d={d} f={f} E={E} k={k}")
+    x, logits, ex = upload_moe(inp)
+    (ids, w, off, sr, ro), y = M.route_expert_ffn_nvfp4(logits, x, ex, k)
+    out = M.combine(y, ro, w)
+    torch.cuda.synchronize()
+    res = dict(ids=ids.cpu().numpy(), w=w.cpu().numpy(), offsets=off.cpu().numpy(), sorted_rows=sr.cpu().numpy(),
+               row_of=ro.cpu().numpy(), y_rows=y.cpu().numpy(), out=out.view(torch.int16).cpu().numpy().view(np.uint16))
+    check_layer_full(inp, res, f"fused T{T}E{E}k{k}")
+    sep = run_moe(inp)
+    for key in ("ids", "offsets", "sorted_rows", "row_of"):
+        assert np.array_equal(res[key], sep[key]), key
+    assert np.array_equal(res["w"].view(np.uint32), sep["w"].view(np.uint32))
+    assert np.array_equal(res["y_rows"].view(np.uint32), sep["y_rows"].view(np.uint32))
+
