@@ -141,7 +141,8 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
     // Route the tokens here (every block, redundantly: T <= 16 tokens of E <= 256 logits):
     // the same top-k and weights as the routing kernel (one 16-lane row a token, waves
     // 0-3), then the stable row lists -- the rank of each assignment among the earlier
-    // ones of its expert, the per-expert counts and their exclusive scan. Block 0 writes
+    // ones of its expert (ballots, as the routing kernel), the per-expert counts and
+    // their exclusive scan. Block 0 writes
     // the routing outputs. Work arrays live in the waves' scratch (free until the
     // gate/up items start): offsets at 0, counts at 1028, experts of the assignments at
     // 1288, ranks at 1800 (ints).
@@ -169,13 +170,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
       }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < nA; i += kDecThreads) {
-      const int e = s_aid[i];
-      int r = 0;
-      for (int j = 0; j < i; ++j) r += s_aid[j] == e;
-      s_rnk[i] = r;
-      atomicAdd(&s_cnt[e], 1);  // LDS; the final counts do not depend on the order
-    }
+    if (wave == 0) wave_rank_assignments(s_aid, nA, s_rnk, s_cnt, lane);
     __syncthreads();
     block_exclusive_scan(s_cnt, s_off, a.E);  // ends with a barrier
     for (int i = threadIdx.x; i < nA; i += kDecThreads) {

@@ -150,34 +150,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   }
   __syncthreads();
 
-  // ranks, by wave 0, 64 assignments at a time in assignment order: lanes holding the
-  // same expert are found with one ballot per bit of the expert index; the rank is the
-  // number of such lanes below plus the expert's running count (s_cnt), which the
-  // expert's last lane in the chunk then advances.
   const int nas = ntok * k;
-  if (wave == 0) {
-    for (int base = 0; base < nas; base += 64) {
-      const int a = base + lane;
-      const int e = a < nas ? s_ids[a] : -1;
-      uint64_t same = __ballot(e >= 0);
-#pragma unroll
-      for (int bit = 0; bit < 10; ++bit) {
-        const uint64_t b1 = __ballot(e >= 0 && ((e >> bit) & 1));
-        same &= ((e >> bit) & 1) ? b1 : ~b1;
-      }
-      const uint64_t below = (1ull << lane) - 1ull;
-      const int before = __popcll(same & below);
-      const bool last = (same & ~below & ~(1ull << lane)) == 0;
-      int r = 0;
-      if (e >= 0) r = s_cnt[e] + before;
-      __builtin_amdgcn_wave_barrier();
-      if (e >= 0) {
-        s_rank[a] = r;
-        if (last) s_cnt[e] = r + 1;
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
+  if (wave == 0) wave_rank_assignments(s_ids, nas, s_rank, s_cnt, lane);
   __syncthreads();
 
   if (gridDim.x == 1) {

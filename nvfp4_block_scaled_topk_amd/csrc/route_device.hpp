@@ -176,4 +176,33 @@ __device__ inline void block_exclusive_scan(const int* s_in, int* s_out, int n) 
   __syncthreads();
 }
 
+// Stable ranks, by one wave, 64 assignments at a time in assignment order (experts <
+// 1024): lanes holding the same expert are found with one ballot per bit of the expert
+// index; the rank is the number of such lanes below plus the expert's running count
+// (s_cnt, zero on entry), which the expert's last lane in the chunk then advances. On
+// return s_cnt holds every expert's count. The caller synchronizes before reading.
+__device__ inline void wave_rank_assignments(const int* s_ids, int nas, int* s_rank, int* s_cnt, int lane) {
+  for (int base = 0; base < nas; base += 64) {
+    const int a = base + lane;
+    const int e = a < nas ? s_ids[a] : -1;
+    uint64_t same = __ballot(e >= 0);
+#pragma unroll
+    for (int bit = 0; bit < 10; ++bit) {
+      const uint64_t b1 = __ballot(e >= 0 && ((e >> bit) & 1));
+      same &= ((e >> bit) & 1) ? b1 : ~b1;
+    }
+    const uint64_t below = (1ull << lane) - 1ull;
+    const int before = __popcll(same & below);
+    const bool last = (same & ~below & ~(1ull << lane)) == 0;
+    int r = 0;
+    if (e >= 0) r = s_cnt[e] + before;
+    __builtin_amdgcn_wave_barrier();
+    if (e >= 0) {
+      s_rank[a] = r;
+      if (last) s_cnt[e] = r + 1;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 }  // namespace moe
