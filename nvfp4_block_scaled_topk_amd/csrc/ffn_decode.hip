@@ -128,8 +128,11 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
   // round trip
   const __amdgpu_buffer_rsrc_t xrs = dec_rsrc(a.x, (uint32_t)(a.T * a.d * 2));
   {
+    // when the launch routes its tokens, waves 0-3 route (a 16-lane row a token) and their
+    // logit loads must not queue behind these copies: waves 4-7 issue them
     const int xs = dec_xstride(a.d), ipr = (a.d * 2 + 1023) / 1024;  // 1 KB DMA instructions a row
-    for (int qi = wave; qi < a.T * ipr; qi += kDecWaves) {
+    const int q0 = a.logits ? wave - kDecWaves / 2 : wave, qstep = a.logits ? kDecWaves / 2 : kDecWaves;
+    for (int qi = q0 < 0 ? a.T * ipr : q0; qi < a.T * ipr; qi += qstep) {
       const int r = qi / ipr, jj = qi - r * ipr;
       const int within = jj * 1024 + lane * 16;
       const uint32_t voff = within < a.d * 2 ? (uint32_t)r * (uint32_t)(a.d * 2) + within : kOOB;
@@ -169,9 +172,11 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
         }
       }
     }
-    __syncthreads();
+    // LDS-only barriers inside the routing (the copies and the first block's stores are
+    // covered by the full barrier that ends the prologue)
+    lds_barrier();
     if (wave == 0) wave_rank_assignments(s_aid, nA, s_rnk, s_cnt, lane);
-    __syncthreads();
+    lds_barrier();
     block_exclusive_scan(s_cnt, s_off, a.E);  // ends with a barrier
     for (int i = threadIdx.x; i < nA; i += kDecThreads) {
       const int p = s_off[s_aid[i]] + s_rnk[i];
