@@ -128,11 +128,12 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
   // round trip
   const __amdgpu_buffer_rsrc_t xrs = dec_rsrc(a.x, (uint32_t)(a.T * a.d * 2));
   {
-    // when the launch routes its tokens, waves 0-3 route (a 16-lane row a token) and their
-    // logit loads must not queue behind these copies: waves 4-7 issue them
+    // waves 0-3 load the routing inputs (or route the tokens: a 16-lane row a token) and
+    // waves 4-7 issue these copies, so that the loads the prologue waits on do not queue
+    // behind them (a wave's loads complete in order)
     const int xs = dec_xstride(a.d), ipr = (a.d * 2 + 1023) / 1024;  // 1 KB DMA instructions a row
-    const int q0 = a.logits ? wave - kDecWaves / 2 : wave, qstep = a.logits ? kDecWaves / 2 : kDecWaves;
-    for (int qi = q0 < 0 ? a.T * ipr : q0; qi < a.T * ipr; qi += qstep) {
+    for (int qi = wave - kDecWaves / 2; qi < a.T * ipr; qi += kDecWaves / 2) {
+      if (qi < 0) break;
       const int r = qi / ipr, jj = qi - r * ipr;
       const int within = jj * 1024 + lane * 16;
       const uint32_t voff = within < a.d * 2 ? (uint32_t)r * (uint32_t)(a.d * 2) + within : kOOB;
@@ -189,10 +190,15 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
     if (blockIdx.x == 0)
       for (int e = threadIdx.x; e <= a.E; e += kDecThreads) a.offsets_out[e] = s_off[e];
   } else {
-    for (int i = threadIdx.x; i <= a.E; i += kDecThreads) s_off[i] = a.offsets[i];
-    for (int i = threadIdx.x; i < nA; i += kDecThreads) s_tok[i] = a.sorted_rows[i] / a.k;
+    constexpr int kHalf = kDecThreads / 2;  // waves 0-3
+    if (threadIdx.x < kHalf) {
+      for (int i = threadIdx.x; i <= a.E; i += kHalf) s_off[i] = a.offsets[i];
+      for (int i = threadIdx.x; i < nA; i += kHalf) s_tok[i] = a.sorted_rows[i] / a.k;
+    }
   }
-  __syncthreads();
+  // LDS only: the copies (and the first block's routing stores) are covered by the full
+  // barrier that ends the prologue
+  lds_barrier();
   if (wave == 0) {
     int seen = 0;
     for (int base = 0; base < a.E; base += 64) {
