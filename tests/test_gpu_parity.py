@@ -139,16 +139,20 @@ def test_decode_workspace_reuse():
     from oracle import band, moe as omoe
 
     shapes = [(4, 256, 128, 8, 2), (3, 96, 64, 5, 2), (16, 160, 96, 6, 3), (40, 128, 64, 16, 4),
-              (8, 512, 256, 16, 4), (4, 256, 128, 8, 2)]
+              (8, 512, 256, 16, 4), (4, 256, 128, 8, 2), (4, 256, 128, 8, 2), (16, 160, 96, 6, 3)]
     need = max(M.expert_ffn_workspace(T, d, f, E, k) for (T, d, f, E, k) in shapes)
     ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda")
     for i, (T, d, f, E, k) in enumerate(shapes):
         inp = workloads.make_moe(T, d, f, E, k, seed=20 + i, config_id=62, zipf=True)
-        say(f"workspace reuse call {i}: T={T} d={d} f={f} E={E} k={k}")
+        fused = T <= 16 and i % 2 == 1  # alternate the launch that routes its own tokens
+        say(f"workspace reuse call {i}: T={T} d={d} f={f} E={E} k={k} fused={fused}")
         x, logits, ex = upload_moe(inp)
-        ids, w, off, srows, rof = M.route_topk(logits, k)
         y = torch.full((T * k, d), float("nan"), dtype=torch.float32, device="cuda")
-        M.expert_ffn_nvfp4(x, ex, off, srows, k, out=y, workspace=ws)
+        if fused:
+            (ids, w, off, srows, rof), _ = M.route_expert_ffn_nvfp4(logits, x, ex, k, out=y, workspace=ws)
+        else:
+            ids, w, off, srows, rof = M.route_topk(logits, k)
+            M.expert_ffn_nvfp4(x, ex, off, srows, k, out=y, workspace=ws)
         out = M.combine(y, rof, w)
         torch.cuda.synchronize()
         ref = omoe.moe_layer(inp)
