@@ -185,12 +185,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_scatter_kernel(
   for (int e = threadIdx.x; e < E; e += kRouteThreads) {
     int before = 0, total = 0;
     int j = 0;
-    for (; j + 8 <= nblocks; j += 8) {
-      int c[8];
+    // 32 loads in flight a thread (integer sums: the grouping does not matter)
+    for (; j + 32 <= nblocks; j += 32) {
+      int c[32];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) c[u] = ws_counts[(size_t)(j + u) * E + e];
+      for (int u = 0; u < 32; ++u) c[u] = ws_counts[(size_t)(j + u) * E + e];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 32; ++u) {
         before += (j + u < b) ? c[u] : 0;
         total += c[u];
       }
