@@ -7,11 +7,11 @@ Where the exact result sits at a bfloat16 rounding tie of h, or the output
 cancels to near zero, more than one result is correct for an fp32-accumulating
 implementation: a rounding of h that lands on the other side of a tie, or fp32
 sum-order differences of the size 2^-20 of the contraction's L1 mass. The pages
-judge such results as correct: their gates hold hardware sum orders to a band
-against an f64 oracle [bloomery 0.3.9 release notes, New, Metal tensor ops],
-and carry the kernels' exceptional range so a correct finite result is not
-judged wrong [FP4-Local checkpoints on DGX Spark, §10, #704]. Those elements
-are "explained" when
+accept such results: their checks compare hardware summation orders with an f64
+oracle inside a band [bloomery 0.3.9 release notes, New, Metal tensor ops], and
+they widen a check to the range a kernel can legitimately produce rather than
+reject a correct finite value [FP4-Local checkpoints on DGX Spark, §10, #704].
+Those elements are "explained" when
 
     |gpu - oracle| <= strict + slack_h + 2^-20 * mass + ulp_bf16(oracle)
 

@@ -49,6 +49,14 @@ def shared_gate(x_bits, w_sg_bits, tokens=None):
     return g, np.abs(x) @ np.abs(w)
 
 
+def gate_error_bound(d: int, g, gmass):
+    """Largest |g32 - g| of a float32 gate: the float32 logit is within (d + 8) 2^-24 of
+    its mass (any summation order, as for the router logits), which moves the sigmoid by
+    at most a quarter of that (sigmoid' <= 1/4), plus 8 float32 ulps of the sigmoid
+    itself (exp, add, divide)."""
+    return 0.25 * (d + 8) * 2.0 ** -24 * np.asarray(gmass) + 8 * 2.0 ** -24 * np.asarray(g)
+
+
 def add_shared(res: moe.MoEResult, x_bits, T, d, f, sh, tokens=None, gated: bool = True) -> moe.MoEResult:
     """The routed result `res` (whole layer, or the sampled `tokens` of moe_tokens) with
     the gated shared row added before the single rounding. The acceptance terms grow by
@@ -60,7 +68,7 @@ def add_shared(res: moe.MoEResult, x_bits, T, d, f, sh, tokens=None, gated: bool
     if not gated:
         g, gmass = np.ones_like(g), np.zeros_like(gmass)
     y = res.y + g[:, None] * S.y_rows
-    dg = 0.25 * (d + 8) * 2.0 ** -24 * gmass + (8 * 2.0 ** -24 * g if gated else 0.0)
+    dg = gate_error_bound(d, g, gmass) if gated else np.zeros_like(g)
     mass = res.mass + g[:, None] * S.mass_y
     slack = res.slack + g[:, None] * S.slack_h + dg[:, None] * np.abs(S.y_rows)
     return moe.MoEResult(res.ids, res.w, res.rl, res.ffn, y, F.bf16_rne_bits(y), mass, slack)

@@ -18,7 +18,7 @@ import numpy as np
 
 import oracle
 from oracle import formats as F
-from oracle import moe, mxfp8, router, shared
+from oracle import band, moe, mxfp8, router, shared
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -793,5 +793,281 @@ def pin_shared_is_an_extra_routed_expert():
     assert np.allclose(res.y, y2, rtol=1e-13, atol=1e-300)
     assert np.array_equal(res.out_bits, ob2)
 
+
+
+# ----------------------------------------------------------------------------- acceptance rule
+def _band1(fn, g, r, mass=None, slack=None):
+    """(strict, explained, fail) of one element."""
+    rep = fn(np.array([g]), np.array([r]), None if mass is None else np.array([mass], dtype=np.float64),
+             None if slack is None else np.array([slack], dtype=np.float64))
+    assert rep.n == 1
+    return rep.strict, rep.explained, rep.fail
+
+
+def pin_band_strict_by_hand():
+    """The strict band |gpu - ref| <= 2e-3 + 2e-2 |ref| on hand-placed values: at ref = 0
+    the bound is the double 0.002 itself (on it: strict; the next double above: fail);
+    at ref = 100 the bound is 2.002 and at ref = -3.5e5 it is 7000.002 (1e-4 inside:
+    strict, 1e-4 outside: fail, on both sides of ref); NaN and inf fail."""
+    C = band.classify_f32
+    assert _band1(C, 0.002, 0.0) == (1, 0, 0)
+    assert _band1(C, -0.002, 0.0) == (1, 0, 0)
+    assert _band1(C, math.nextafter(0.002, 1.0), 0.0) == (0, 0, 1)
+    assert _band1(C, 102.0019, 100.0) == (1, 0, 0)
+    assert _band1(C, 97.9981, 100.0) == (1, 0, 0)
+    assert _band1(C, 102.0021, 100.0) == (0, 0, 1)
+    assert _band1(C, 97.9979, 100.0) == (0, 0, 1)
+    assert _band1(C, -342999.9981, -3.5e5) == (1, 0, 0)
+    assert _band1(C, -342999.9979, -3.5e5) == (0, 0, 1)
+    assert _band1(C, -357000.0019, -3.5e5) == (1, 0, 0)
+    assert _band1(C, -357000.0021, -3.5e5) == (0, 0, 1)
+    for bad in (float("nan"), float("inf"), -float("inf")):
+        assert _band1(C, bad, 1.0) == (0, 0, 1)
+        assert _band1(C, bad, 1.0, mass=1e30, slack=1e30) == (0, 0, 1)
+    rep = C(np.array([102.0021, 100.0]), np.array([100.0, 100.0]))
+    assert rep.fail == 1 and abs(rep.worst_excess - 1e-4) < 1e-9
+    rep = C(np.array([101.0, 100.0]), np.array([100.0, 100.0]))
+    assert rep.fail == 0 and rep.worst_excess < 0
+
+
+def pin_band_explained_by_hand():
+    """Beyond the strict band, an element is explained only within the slack, the
+    2^-20 share of the contraction's mass and (bf16 outputs only) one bfloat16 ulp of
+    the oracle's value -- each term placed by hand on both sides of its edge."""
+    C = band.classify_f32
+    # 1e-4 beyond the strict bound 2.002 at ref 100
+    assert _band1(C, 102.0021, 100.0, slack=2e-4) == (0, 1, 0)
+    assert _band1(C, 102.0021, 100.0, slack=5e-5) == (0, 0, 1)
+    assert _band1(C, 102.0021, 100.0, mass=2e-4 * 2 ** 20) == (0, 1, 0)
+    assert _band1(C, 102.0021, 100.0, mass=5e-5 * 2 ** 20) == (0, 0, 1)
+    assert _band1(C, 102.0021, 100.0, mass=5e-5 * 2 ** 20, slack=6e-5) == (0, 1, 0)
+    # bfloat16 outputs: ref 1.0 (0x3F80), strict bound 0.022, ulp 2^-7
+    B = band.classify
+    assert _band1(B, 0x3F82, 0x3F80) == (1, 0, 0)      # 1.015625
+    assert _band1(B, 0x3F83, 0x3F80) == (0, 1, 0)      # 1.0234375: 0.0234 <= 0.022 + 0.0078
+    assert _band1(B, 0x3F84, 0x3F80) == (0, 0, 1)      # 1.03125: beyond 0.0298
+    assert _band1(C, 1.0234375, 1.0) == (0, 0, 1)      # no ulp term for fp32 rows
+    # the ulp is that of the oracle's value: ref 0.99609375 (0x3F7F, ulp 2^-8), gpu 1.0234375
+    # is 0.02734 away, beyond 0.0219 + 0.0039 (with the gpu value's ulp it would pass)
+    assert _band1(B, 0x3F83, 0x3F7F) == (0, 0, 1)
+    # signed zeros are equal; NaN bits fail
+    assert _band1(B, 0x8000, 0x0000) == (1, 0, 0)
+    assert _band1(B, 0x7FC0, 0x3F80, mass=1e30) == (0, 0, 1)
+
+
+def pin_bf16_ulp_spacing():
+    """bf16_ulp(b) equals the gap from b to the next larger bfloat16 value, for every
+    non-negative finite bfloat16 below the largest (normal, subnormal, powers of two),
+    and is symmetric in sign; between two bfloat16 values it is the quantum of the
+    binade (checked with exact rational arithmetic)."""
+    bits = np.arange(0, 0x7F7F, dtype=np.uint32)
+    b = (bits << 16).view(np.float32).astype(np.float64)
+    nxt = ((bits + 1) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(F.bf16_ulp(b), nxt - b)
+    assert np.array_equal(F.bf16_ulp(-b), nxt - b)
+    rng = np.random.default_rng(5)
+    vals = rng.standard_normal(200) * 10.0 ** rng.integers(-40, 38, 200)
+    vals = np.concatenate([vals, [2.0 ** -126, 2.0 ** -127 * 1.5, 2.0 ** -133, 3.0 * 2.0 ** -140]])
+    got = F.bf16_ulp(vals)
+    for v, u in zip(vals, got):
+        a, e = abs(Fraction(float(v))), 0
+        while a >= 2:
+            a /= 2
+            e += 1
+        while a < 1:
+            a *= 2
+            e -= 1
+        assert Fraction(float(u)) == Fraction(2) ** (max(e, -126) - 7), (v, u)
+
+
+def _midpoint_expert(tg, tu=1.0, td=1.0, d=32):
+    ex = _identity_experts(d)
+    ex["gate_ts"] = np.array([tg], dtype=np.float32)
+    ex["up_ts"] = np.array([tu], dtype=np.float32)
+    ex["down_ts"] = np.array([td], dtype=np.float32)
+    return ex
+
+
+def _one_row(ex, xvals, d=32):
+    x = np.zeros((1, d), dtype=np.uint16)
+    for i, v in xvals.items():
+        x[0, i] = F.bf16_rne_bits(np.array([v]))[0]
+        assert bf16_bits_scalar(x[0, i]) == v
+    rl = moe.row_lists(np.zeros((1, 1), np.int32), 1)
+    return moe.expert_ffn(x, 1, d, d, 1, 1, ex, rl)
+
+
+def pin_slack_h_midpoint():
+    """Identity expert, x = 64 at element 0, ts_g = 1 + 2^-8: silu(G) = G in float64, so
+    h = 4096 (1 + 2^-8) = 4112, exactly the bfloat16 midpoint between 4096 and 4128. The
+    element is ambiguous and slack_h[0] = ts_d * ulp(H) * |W_d[0, 0]| = ts_d * 32 (ts_d =
+    1 and 1.5); every other output column has no slack. With ts_g = 1, h = 4096 is a
+    bfloat16 value 16 away from either midpoint: no slack anywhere."""
+    for td in (1.0, 1.5):
+        res = _one_row(_midpoint_expert(1 + 2.0 ** -8, td=td), {0: 64.0})
+        assert bf16_bits_scalar(res.h_bits[0, 0]) == 4096.0
+        assert res.slack_h[0, 0] == 32.0 * td
+        assert np.all(res.slack_h[0, 1:] == 0)
+    res = _one_row(_midpoint_expert(1.0), {0: 64.0})
+    assert bf16_bits_scalar(res.h_bits[0, 0]) == 4096.0
+    assert np.all(res.slack_h == 0)
+
+
+def pin_slack_h_window():
+    """The width of the ambiguity window, by hand. Identity expert, x = 64 at element 0,
+    ts_g = 1 + 2^-8 - n 2^-23: h = 4112 - n/2048 exactly, and the window is
+    2^-20 (|silu'(G) U| mass_g + |silu(G)| mass_u + |h|) = 2^-20 (3 * 4096 ts_g) = 0.01176
+    (silu' = 1 and masses 64 ts_g and 64 here). n = 20 (0.00977 below the midpoint):
+    ambiguous; n = 28 (0.01367 below): not. A second row with a cancelling input checks
+    that the window uses the absolute mass: gate row 0 = e0 + e1, x = (128, -64), up row
+    0 = e0: G = 64 ts_g, mass_g = 192 ts_g, U = 128, h = 8224 - n/1024, window 2^-20 *
+    40960 ts_g = 0.0391 (with a signed mass, 0.0234): n = 32 (0.03125 below the midpoint
+    8224) is ambiguous."""
+    for n, amb in ((20, True), (28, False)):
+        tg = np.float32(1 + 2.0 ** -8 - n * 2.0 ** -23)
+        assert float(tg) == 1 + 2.0 ** -8 - n * 2.0 ** -23
+        res = _one_row(_midpoint_expert(float(tg)), {0: 64.0})
+        assert bf16_bits_scalar(res.h_bits[0, 0]) == 4096.0
+        assert (res.slack_h[0, 0] == 32.0) == amb, (n, res.slack_h[0, 0])
+    n = 32
+    tg = float(np.float32(1 + 2.0 ** -8 - n * 2.0 ** -23))
+    ex = _midpoint_expert(tg)
+    ex["gate_q"] = ex["gate_q"].copy()
+    ex["gate_q"][0, 0, 0] = 0x22                       # gate row 0: 1.0 at columns 0 and 1
+    res = _one_row(ex, {0: 128.0, 1: -64.0})
+    assert bf16_bits_scalar(res.h_bits[0, 0]) == 8192.0
+    assert res.slack_h[0, 0] == 64.0                   # ulp(8192) = 64
+
+
+def pin_mass_y_brute_force():
+    """mass_y = ts_d * sum_i |H_i| |W_d[c, i]|, against scalar loops over the oracle's own
+    H bits and an independent scalar decode of W_d (a random single expert, d = 32, f = 16)."""
+    for seed in (3, 4):
+        d, f = 32, 16
+        x, ex = _single_expert_inputs(d, f, seed)
+        rl = moe.row_lists(np.zeros((1, 1), np.int32), 1)
+        res = moe.expert_ffn(x, 1, d, f, 1, 1, ex, rl)
+        H = [abs(Fraction(bf16_bits_scalar(b))) for b in res.h_bits[0]]
+        td = Fraction(float(ex["down_ts"][0]))
+        for c in range(d):
+            want = td * sum(H[i] * abs(_brute_nvfp4_row(ex["down_q"][0, c], ex["down_s"][0, c], i)) for i in range(f))
+            assert abs(Fraction(res.mass_y[0, c]) - want) <= want * Fraction(1, 2 ** 48), (seed, c)
+        # the mass bounds the row and exceeds it where signs mix
+        assert np.all(np.abs(res.y_rows) <= res.mass_y * (1 + 2.0 ** -40))
+        assert np.any(np.abs(res.y_rows) < 0.9 * res.mass_y)
+
+
+def pin_mxfp8_mass_brute_force():
+    """The MXFP8 mass |x| . |W|^T against an exact rational brute force."""
+    rng = np.random.default_rng(23)
+    M, N, K = 2, 3, 64
+    j = rng.integers(0, 254, size=(N, K))
+    w = np.where(j < 127, j, j + 1).astype(np.uint8)
+    s = rng.integers(121, 130, size=(N, K // 32), dtype=np.uint8)
+    x = F.bf16_rne_bits(rng.standard_normal((M, K)))
+    _, _, mass = mxfp8.mxfp8_gemm(x, w, s)
+    for m in range(M):
+        for n in range(N):
+            want = sum(abs(Fraction(bf16_bits_scalar(x[m, i])) * scalar_e4m3(int(w[n, i])))
+                       * Fraction(2) ** (int(s[n, i // 32]) - 127) for i in range(K))
+            assert abs(Fraction(mass[m, n]) - want) <= want * Fraction(1, 2 ** 48)
+
+
+def pin_shared_gate_bound():
+    """The shared gate's acceptance term covers a float32 gate: float32 logits summed in
+    three orders, a float32 sigmoid, against the fp64 gate -- and an adversarial logit
+    (products that a running float32 sum rounds away, see below) shows the (d + 8) term is needed.
+    The term is not vacuous: below 2e-3 (of a gate in (0, 1)) at d = 2048 for N(0, 1/d)
+    gate vectors."""
+    import workloads
+
+    d = 2048
+    rng = np.random.default_rng(29)
+    xb = F.bf16_rne_bits(rng.standard_normal((3, d)))
+    wb = workloads.bf16_bits_from_normal(np.random.default_rng(31), (d,), std=float(1 / np.sqrt(d)))
+    g, gmass = shared.shared_gate(xb, wb)
+    dg = shared.gate_error_bound(d, g, gmass)
+    assert np.all(dg < 2e-3)
+    xf = F.bf16_bits_to_f64(xb).astype(np.float32)
+    wf = F.bf16_bits_to_f64(wb).astype(np.float32)
+    for t in range(3):
+        p = xf[t] * wf
+        orders = [np.float32(0), np.float32(0), np.float32(0)]
+        for v in p:
+            orders[0] = np.float32(orders[0] + v)
+        for v in p[::-1]:
+            orders[1] = np.float32(orders[1] + v)
+        for c in range(0, d, 64):
+            orders[2] = np.float32(orders[2] + np.float32(np.sum(p[c:c + 64], dtype=np.float32)))
+        for z in orders:
+            g32 = np.float32(1) / (np.float32(1) + np.exp(-z, dtype=np.float32))
+            assert abs(float(g32) - g[t]) <= dg[t], (t, float(g32), g[t], dg[t])
+    # adversarial: 4096 products (1 + 2^-7)^2 = 1 + 2^-6 + 2^-14, then 4096 products
+    # -(1 + 2^-6): exactly 4096 * 2^-14 = 0.25; a running float32 sum drops the 2^-14
+    # parts once it passes 1024 and ends near 0.1
+    d = 8192
+    a, b = 1.0 + 2.0 ** -7, 1.0 + 2.0 ** -6
+    xv = np.concatenate([np.full(d // 2, a), np.ones(d // 2)])[None, :]
+    wv = np.concatenate([np.full(d // 2, a), np.full(d // 2, -b)])
+    xb2, wb2 = F.bf16_rne_bits(xv), F.bf16_rne_bits(wv)
+    g, gmass = shared.shared_gate(xb2, wb2)
+    assert abs(g[0] - 1.0 / (1.0 + math.exp(-0.25))) < 1e-15
+    z = np.float32(0)
+    for i in range(d):
+        z = np.float32(z + np.float32(xv[0, i]) * np.float32(wv[i]))
+    g32 = np.float32(1) / (np.float32(1) + np.exp(-z, dtype=np.float32))
+    err = abs(float(g32) - g[0])
+    assert err > 0.005 and err <= shared.gate_error_bound(d, g, gmass)[0], (float(z), err)
+
+
+def pin_refusals():
+    """Inputs the oracle refuses, each by name: a NaN or infinite router logit, an E4M3
+    NaN code (0x7F or 0xFF) in any block-scale tensor, a non-finite tensor scale, k > E,
+    d or f not a multiple of 32; MXFP8: an E4M3 NaN weight code, an E8M0 0xFF scale, K not
+    a multiple of 32. A valid input passes."""
+    inp = _small_layer(seed=11)
+    ex = moe.experts_dict(inp)
+    T, d, f, E, k = inp.T, inp.d, inp.f, inp.E, inp.k
+    moe.validate_moe(T, d, f, E, k, inp.x, inp.logits, ex)
+
+    def refused(fn, words):
+        try:
+            fn()
+        except moe.OracleRefusal as err:
+            assert all(wd in str(err) for wd in words), str(err)
+            return True
+        return False
+
+    for bad in (np.nan, np.inf):
+        lg = inp.logits.copy()
+        lg[1, 2] = bad
+        assert refused(lambda: moe.validate_moe(T, d, f, E, k, inp.x, lg, ex), ["logit"])
+        assert refused(lambda: moe.moe_layer(type(inp)(**{**inp.__dict__, "logits": lg})), ["logit"])
+    for nm in ("gate_s", "up_s", "down_s"):
+        for code in (0x7F, 0xFF):
+            ex2 = dict(ex)
+            ex2[nm] = ex[nm].copy()
+            ex2[nm].flat[5] = code
+            assert refused(lambda: moe.validate_moe(T, d, f, E, k, inp.x, inp.logits, ex2), ["NaN", nm])
+    for nm in ("gate_ts", "up_ts", "down_ts"):
+        ex2 = dict(ex)
+        ex2[nm] = ex[nm].copy()
+        ex2[nm][1] = np.inf
+        assert refused(lambda: moe.validate_moe(T, d, f, E, k, inp.x, inp.logits, ex2), ["tensor scale", nm])
+    assert refused(lambda: moe.validate_moe(T, d, f, 2, 3, inp.x, inp.logits[:, :2], ex), ["k > E"])
+    assert refused(lambda: moe.validate_moe(T, 48, f, E, k, inp.x, inp.logits, ex), ["multiples of 32"])
+    rng = np.random.default_rng(37)
+    w = rng.integers(0, 0x7F, size=(4, 64), dtype=np.uint8)
+    s = np.full((4, 2), 127, dtype=np.uint8)
+    x = F.bf16_rne_bits(rng.standard_normal((1, 64)))
+    mxfp8.mxfp8_gemm(x, w, s)
+    for code in (0x7F, 0xFF):
+        w2 = w.copy()
+        w2[2, 9] = code
+        assert refused(lambda: mxfp8.mxfp8_gemm(x, w2, s), ["NaN", "weight"])
+    s2 = s.copy()
+    s2[3, 1] = 0xFF
+    assert refused(lambda: mxfp8.mxfp8_gemm(x, w, s2), ["NaN", "E8M0"])
+    assert refused(lambda: mxfp8.validate(x[:, :48], w[:, :48], s[:, :1], 1, 4, 48), ["K % 32"])
 
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_") and callable(v)]

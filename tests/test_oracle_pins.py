@@ -109,6 +109,73 @@ MUTANTS = [
     ("mxfp8_block_16", "mxfp8.py",
      [("np.repeat(F.E8M0_TABLE[s], 32, axis=-1)", "np.repeat(F.E8M0_TABLE[s], 16, axis=-1)[..., : w.shape[-1]]")],
      ["pin_mxfp8_one_hot_and_scale", "pin_mxfp8_brute_force"]),
+    # ---- the acceptance rule and its slack terms
+    ("slack_h_x1024", "moe.py",
+     [("slack_h[sel] = td * ((amb * ulp) @ aWd.T)", "slack_h[sel] = 1024 * td * ((amb * ulp) @ aWd.T)")],
+     ["pin_slack_h_midpoint"]),
+    ("band_slack_x1024", "band.py",
+     [("bound = bound + np.asarray(slack)", "bound = bound + 1024 * np.asarray(slack)")] * 2,
+     ["pin_band_explained_by_hand"]),
+    ("amb_always_true", "moe.py",
+     [("amb = (h_exact - dh <= lo_mid) | (h_exact + dh >= hi_mid)", "amb = np.ones_like(H, dtype=bool)")],
+     ["pin_slack_h_midpoint", "pin_slack_h_window"]),
+    ("h_ulp_doubled", "moe.py",
+     [("ulp = F.bf16_ulp(H)", "ulp = 2 * F.bf16_ulp(H)")],
+     ["pin_slack_h_midpoint", "pin_slack_h_window"]),
+    ("acc_window_doubled", "moe.py",
+     [("ACC_REL = 2.0 ** -20", "ACC_REL = 2.0 ** -19")],
+     ["pin_slack_h_window"]),
+    ("gate_mass_signed", "moe.py",
+     [("mass_g = tg * (aX @ np.abs(Wg).T)", "mass_g = tg * (X @ Wg.T)")],
+     ["pin_slack_h_window"]),
+    ("mass_y_signed", "moe.py",
+     [("mass_y[sel] = td * (np.abs(H) @ aWd.T)", "mass_y[sel] = td * (H @ Wd.T)")],
+     ["pin_mass_y_brute_force"]),
+    ("mass_rel_2m10", "band.py",
+     [("MASS_REL = 2.0 ** -20", "MASS_REL = 2.0 ** -10")],
+     ["pin_band_explained_by_hand"]),
+    ("strict_open_interval", "band.py",
+     [("strict = diff <= strict_bound", "strict = diff < strict_bound")] * 2,
+     ["pin_band_strict_by_hand"]),
+    ("rtol_wider", "band.py",
+     [("RTOL = 2e-2", "RTOL = 2.1e-2")],
+     ["pin_band_strict_by_hand"]),
+    ("atol_wider", "band.py",
+     [("ATOL = 2e-3", "ATOL = 2.1e-3")],
+     ["pin_band_strict_by_hand"]),
+    ("nan_passes", "band.py",
+     [("diff = np.where(np.isnan(diff), np.inf, diff)", "diff = np.where(np.isnan(diff), 0.0, diff)")] * 2,
+     ["pin_band_strict_by_hand", "pin_band_explained_by_hand"]),
+    ("ulp_of_gpu_value", "band.py",
+     [("bound = strict_bound + F.bf16_ulp(r)", "bound = strict_bound + F.bf16_ulp(g)")],
+     ["pin_band_explained_by_hand"]),
+    ("ulp_term_on_f32_rows", "band.py",
+     [("bound = strict_bound.copy()", "bound = strict_bound + F.bf16_ulp(r)")],
+     ["pin_band_explained_by_hand"]),
+    ("bf16_ulp_subnormal_floor", "formats.py",
+     [("return np.ldexp(1.0, np.maximum(e, -125) - 8)", "return np.ldexp(1.0, np.maximum(e, -126) - 8)")],
+     ["pin_bf16_ulp_spacing"]),
+    ("bf16_ulp_doubled", "formats.py",
+     [("return np.ldexp(1.0, np.maximum(e, -125) - 8)", "return np.ldexp(2.0, np.maximum(e, -125) - 8)")],
+     ["pin_bf16_ulp_spacing", "pin_band_explained_by_hand"]),
+    ("gate_bound_without_d", "shared.py",
+     [("0.25 * (d + 8) * 2.0 ** -24", "0.25 * 2.0 ** -24")],
+     ["pin_shared_gate_bound"]),
+    ("mxfp8_mass_signed", "mxfp8.py",
+     [("mass = np.abs(X) @ np.abs(W).T", "mass = X @ W.T")],
+     ["pin_mxfp8_mass_brute_force"]),
+    ("refusal_nan_scale_code_dropped", "moe.py",
+     [("if np.any((s & 0x7F) == 0x7F):", "if False:")],
+     ["pin_refusals"]),
+    ("refusal_logit_check_dropped", "moe.py",
+     [("if not np.all(np.isfinite(logits)):", "if False:")],
+     ["pin_refusals"]),
+    ("refusal_tensor_scale_dropped", "moe.py",
+     [("if not np.all(np.isfinite(experts[nm])):", "if False:")],
+     ["pin_refusals"]),
+    ("refusal_e8m0_dropped", "mxfp8.py",
+     [("if np.any(s == 0xFF):", "if False:")],
+     ["pin_refusals"]),
 ]
 
 
@@ -130,6 +197,7 @@ def _exec_module(fname, edits, pkg_overrides):
 
 @pytest.mark.parametrize("name,fname,edits,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutant_is_caught(monkeypatch, name, fname, edits, pins):
+    import oracle.band as bandreal
     import oracle.formats as Freal
     import oracle.moe as moereal
     import oracle.mxfp8 as mxreal
@@ -137,12 +205,14 @@ def test_mutant_is_caught(monkeypatch, name, fname, edits, pins):
     import oracle.shared as shreal
     rtm = _exec_module("router.py", edits, {}) if fname == "router.py" else rtreal
     shm = _exec_module("shared.py", edits, {}) if fname == "shared.py" else shreal
-    if fname in ("router.py", "shared.py"):
+    bandm = _exec_module("band.py", edits, {}) if fname == "band.py" else bandreal
+    if fname in ("router.py", "shared.py", "band.py"):
         Fm, moem, mxm = Freal, moereal, mxreal
     elif fname == "formats.py":
         Fm = _exec_module("formats.py", edits, {})
         moem = _exec_module("moe.py", [], {"F": Fm})
         mxm = _exec_module("mxfp8.py", [], {"F": Fm})
+        bandm = _exec_module("band.py", [], {"F": Fm})
     elif fname == "moe.py":
         Fm = Freal
         moem = _exec_module("moe.py", edits, {})
@@ -155,6 +225,7 @@ def test_mutant_is_caught(monkeypatch, name, fname, edits, pins):
     monkeypatch.setattr(P, "mxfp8", mxm)
     monkeypatch.setattr(P, "router", rtm)
     monkeypatch.setattr(P, "shared", shm)
+    monkeypatch.setattr(P, "band", bandm)
     red = []
     for pn in pins:
         try:
