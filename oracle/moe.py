@@ -149,7 +149,7 @@ class FFNResult:
     rows: np.ndarray        # row-list positions p computed (int64)
     y_rows: np.ndarray      # float64 [len(rows), d]: ts_d * (H @ W_d^T), unrounded
     h_bits: np.ndarray      # uint16 [len(rows), f]: H = bf16_rne(silu(G) * U)
-    mass_y: np.ndarray      # float64 [len(rows), d]: ts_d * (|H| @ |W_d|^T)
+    mass_y: np.ndarray      # float64 [len(rows), d]: |ts_d| * (|H| @ |W_d|^T)
     slack_h: np.ndarray     # float64 [len(rows), d]: 1-ulp flips of ambiguous h elements
 
 
@@ -157,7 +157,7 @@ class FFNResult:
 ACC_REL = 2.0 ** -20
 
 
-def expert_ffn(x_bits, T, d, f, E, k, experts: dict, rl: RowLists, rows=None) -> FFNResult:
+def expert_ffn(x_bits, T, d, f, E, k, experts: dict, rl: RowLists, rows=None, map_fn=map) -> FFNResult:
     """Per routed row p (row-list order): with t = sorted_rows[p] // k and the
     expert e owning p,
 
@@ -167,6 +167,9 @@ def expert_ffn(x_bits, T, d, f, E, k, experts: dict, rl: RowLists, rows=None) ->
 
     ``rows`` restricts the computation to a subset of row-list positions (every
     row is independent of the others), for sampled checks at large sizes.
+    Experts are independent too: ``map_fn`` (default the builtin map; e.g. a
+    thread pool's map) applies the per-expert computation to the list of experts,
+    which changes nothing in the arithmetic.
     Also returns the slack terms used by the acceptance rule (see band.py).
     """
     offsets = rl.offsets.astype(np.int64)
@@ -179,7 +182,8 @@ def expert_ffn(x_bits, T, d, f, E, k, experts: dict, rl: RowLists, rows=None) ->
     slack_h = np.zeros((n, d))
     h_bits = np.zeros((n, f), dtype=np.uint16)
     owner = np.searchsorted(offsets, rows, side="right") - 1   # expert of each row
-    for e in np.unique(owner):
+
+    def one_expert(e):
         sel = np.nonzero(owner == e)[0]
         p = rows[sel]
         tok = rl.sorted_rows[p].astype(np.int64) // k
@@ -196,12 +200,12 @@ def expert_ffn(x_bits, T, d, f, E, k, experts: dict, rl: RowLists, rows=None) ->
         h_exact = sg * U
         H = F.bf16_rne(h_exact)
         O = td * (H @ Wd.T)
-        y_rows[sel] = O
-        h_bits[sel] = F.bf16_rne_bits(h_exact)
+        hb = F.bf16_rne_bits(h_exact)
         # ---- slack terms
+        # L1 masses: every factor taken by magnitude (tensor scales can be negative)
         aX = np.abs(X)
-        mass_g = tg * (aX @ np.abs(Wg).T)
-        mass_u = tu * (aX @ np.abs(Wu).T)
+        mass_g = abs(tg) * (aX @ np.abs(Wg).T)
+        mass_u = abs(tu) * (aX @ np.abs(Wu).T)
         # d silu / dg = s(g) * (1 + g * (1 - s(g))), s = logistic; h = silu(g) * u
         sig = np.where(G >= 0, 1.0 / (1.0 + np.exp(-np.abs(G))), np.exp(-np.abs(G)) / (1.0 + np.exp(-np.abs(G))))
         dsilu = sig * (1.0 + G * (1.0 - sig))
@@ -213,8 +217,15 @@ def expert_ffn(x_bits, T, d, f, E, k, experts: dict, rl: RowLists, rows=None) ->
         hi_mid = H + ulp / 2.0
         amb = (h_exact - dh <= lo_mid) | (h_exact + dh >= hi_mid)
         aWd = np.abs(Wd)
-        mass_y[sel] = td * (np.abs(H) @ aWd.T)
-        slack_h[sel] = td * ((amb * ulp) @ aWd.T)
+        my = abs(td) * (np.abs(H) @ aWd.T)
+        sh = abs(td) * ((amb * ulp) @ aWd.T)
+        return sel, O, hb, my, sh
+
+    for sel, O, hb, my, sh in map_fn(one_expert, list(np.unique(owner))):
+        y_rows[sel] = O
+        h_bits[sel] = hb
+        mass_y[sel] = my
+        slack_h[sel] = sh
     return FFNResult(rows=rows, y_rows=y_rows, h_bits=h_bits, mass_y=mass_y, slack_h=slack_h)
 
 
@@ -258,7 +269,7 @@ def moe_layer(inp) -> MoEResult:
     return MoEResult(ids, w, rl, ffn, y, out_bits, mass, slack)
 
 
-def moe_tokens(inp, tokens, ids=None, w=None, rl=None) -> MoEResult:
+def moe_tokens(inp, tokens, ids=None, w=None, rl=None, map_fn=map) -> MoEResult:
     """The layer's output for a subset of tokens only (each token's output needs
     only its own k rows), for sampled checks at sizes where the whole layer
     would take too long on the CPU. Routing is computed for every token (it is
@@ -272,7 +283,7 @@ def moe_tokens(inp, tokens, ids=None, w=None, rl=None) -> MoEResult:
     tokens = np.asarray(tokens, dtype=np.int64)
     assign = (tokens[:, None] * k + np.arange(k)[None, :]).reshape(-1)
     rows = rl.row_of[assign].astype(np.int64)
-    ffn = expert_ffn(inp.x, T, d, f, E, k, ex, rl, rows=rows)
+    ffn = expert_ffn(inp.x, T, d, f, E, k, ex, rl, rows=rows, map_fn=map_fn)
     nt = tokens.size
     yr = ffn.y_rows.reshape(nt, k, d)
     ws = w[tokens]

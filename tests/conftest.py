@@ -17,3 +17,15 @@ def pytest_configure(config):
 def gpu_available():
     import torch
     return torch.cuda.is_available()
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Write the band counts the GPU tests recorded (strict / explained / fail per case)."""
+    gu = sys.modules.get("gpu_util")
+    if gu is None or not getattr(gu, "RECORDS", None):
+        return
+    import json
+    out = os.path.join(ROOT, "gpurun_out")
+    os.makedirs(out, exist_ok=True)
+    with open(os.path.join(out, "parity_records.json"), "w") as fh:
+        json.dump({"exitstatus": int(exitstatus), "records": gu.RECORDS}, fh, indent=1)

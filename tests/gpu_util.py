@@ -16,6 +16,43 @@ def say(*a):
     sys.stdout.flush()
 
 
+# Every band check of a GPU test appends its counts here; the session writes them to
+# gpurun_out/parity_records.json (tests/conftest.py).
+RECORDS = []
+# "explained" elements (outside the strict band, inside the slack) must stay rare: the
+# slack covers bf16 rounding ties of h and fp32 sum-order effects, which touch well
+# under one element in two hundred of these workloads
+EXPLAINED_MAX = 0.005
+
+
+def check_band(rep, case, part="out"):
+    """Record a band report and assert FAIL = 0 and explained <= 0.5 % of the elements."""
+    RECORDS.append({"case": case, "part": part, "n": rep.n, "strict": rep.strict, "explained": rep.explained,
+                    "fail": rep.fail, "worst_excess": rep.worst_excess})
+    say(f"[{case}] {part}: {rep}")
+    assert rep.ok(), f"{case} {part}: {rep}"
+    assert rep.explained <= EXPLAINED_MAX * rep.n, f"{case} {part}: explained above 0.5 %: {rep}"
+    return rep
+
+
+def cover_tokens(offsets, sorted_rows, k, tile=128, skinny=16):
+    """Tokens whose routed rows cover every grouped-GEMM tile and every weight-streaming
+    expert of a prompt batch: for an expert with more than `skinny` rows, the first and
+    last row of each `tile`-row tile; for the others, their first and last row."""
+    off = np.asarray(offsets, dtype=np.int64)
+    rows = []
+    for e in range(off.size - 1):
+        a, b = int(off[e]), int(off[e + 1])
+        if b == a:
+            continue
+        if b - a > skinny:
+            for t0 in range(a, b, tile):
+                rows += [t0, min(t0 + tile, b) - 1]
+        else:
+            rows += [a, b - 1]
+    return np.unique(np.asarray(sorted_rows, dtype=np.int64)[np.asarray(rows)] // k)
+
+
 def upload_moe(inp, device="cuda"):
     x = torch.from_numpy(inp.x.view(np.int16)).to(device).view(torch.bfloat16)
     logits = torch.from_numpy(inp.logits).to(device)
@@ -64,25 +101,27 @@ def check_layer_full(inp, res, where=""):
     check_routing(inp, res, where)
     ref = moe.moe_layer(inp)
     assert not np.any(np.isnan(res["y_rows"])), f"{where}: unwritten expert rows (NaN canary)"
-    rep_rows = band.classify_f32(res["y_rows"], ref.ffn.y_rows, ref.ffn.mass_y, ref.ffn.slack_h)
-    rep_out = band.classify(res["out"], ref.out_bits, ref.mass, ref.slack)
-    say(f"[{where}] y_rows: {rep_rows}")
-    say(f"[{where}] out:    {rep_out}")
-    assert rep_rows.ok(), f"{where}: y_rows {rep_rows}"
-    assert rep_out.ok(), f"{where}: out {rep_out}"
-    return rep_out
+    check_band(band.classify_f32(res["y_rows"], ref.ffn.y_rows, ref.ffn.mass_y, ref.ffn.slack_h), where, "y_rows")
+    return check_band(band.classify(res["out"], ref.out_bits, ref.mass, ref.slack), where, "out")
 
 
-def check_layer_sampled(inp, res, tokens, where=""):
-    """Parity on sampled tokens (all of their k rows and d outputs)."""
+def check_layer_sampled(inp, res, tokens, where="", threads=8):
+    """Parity on sampled tokens (all of their k rows and d outputs). The oracle's experts
+    are independent and run on `threads` threads."""
+    from concurrent.futures import ThreadPoolExecutor
+
     ids, w, rl = check_routing(inp, res, where)
     assert not np.any(np.isnan(res["y_rows"])), f"{where}: unwritten expert rows (NaN canary)"
-    ref = moe.moe_tokens(inp, tokens, ids=ids, w=w, rl=rl)
+    say(f"[{where}] oracle for {len(tokens)} sampled tokens")
+    with ThreadPoolExecutor(threads) as ex:
+        def progress_map(fn, items):
+            for i, r in enumerate(ex.map(fn, items)):
+                if i % 16 == 15:
+                    say(f"[{where}] oracle: {i + 1} of {len(items)} experts")
+                yield r
+        ref = moe.moe_tokens(inp, tokens, ids=ids, w=w, rl=rl, map_fn=progress_map)
     rows = ref.ffn.rows
-    rep_rows = band.classify_f32(res["y_rows"][rows], ref.ffn.y_rows, ref.ffn.mass_y, ref.ffn.slack_h)
-    rep_out = band.classify(res["out"][np.asarray(tokens)], ref.out_bits, ref.mass, ref.slack)
-    say(f"[{where}] sampled {len(tokens)} tokens; y_rows: {rep_rows}")
-    say(f"[{where}] sampled out: {rep_out}")
-    assert rep_rows.ok(), f"{where}: y_rows {rep_rows}"
-    assert rep_out.ok(), f"{where}: out {rep_out}"
-    return rep_out
+    check_band(band.classify_f32(res["y_rows"][rows], ref.ffn.y_rows, ref.ffn.mass_y, ref.ffn.slack_h),
+               where, f"y_rows ({rows.size} sampled rows)")
+    return check_band(band.classify(res["out"][np.asarray(tokens)], ref.out_bits, ref.mass, ref.slack),
+                      where, f"out ({len(tokens)} sampled tokens)")

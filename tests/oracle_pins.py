@@ -940,7 +940,7 @@ def pin_slack_h_window():
 
 
 def pin_mass_y_brute_force():
-    """mass_y = ts_d * sum_i |H_i| |W_d[c, i]|, against scalar loops over the oracle's own
+    """mass_y = |ts_d| * sum_i |H_i| |W_d[c, i]|, against scalar loops over the oracle's own
     H bits and an independent scalar decode of W_d (a random single expert, d = 32, f = 16)."""
     for seed in (3, 4):
         d, f = 32, 16
@@ -948,7 +948,7 @@ def pin_mass_y_brute_force():
         rl = moe.row_lists(np.zeros((1, 1), np.int32), 1)
         res = moe.expert_ffn(x, 1, d, f, 1, 1, ex, rl)
         H = [abs(Fraction(bf16_bits_scalar(b))) for b in res.h_bits[0]]
-        td = Fraction(float(ex["down_ts"][0]))
+        td = abs(Fraction(float(ex["down_ts"][0])))
         for c in range(d):
             want = td * sum(H[i] * abs(_brute_nvfp4_row(ex["down_q"][0, c], ex["down_s"][0, c], i)) for i in range(f))
             assert abs(Fraction(res.mass_y[0, c]) - want) <= want * Fraction(1, 2 ** 48), (seed, c)
@@ -1069,5 +1069,33 @@ def pin_refusals():
     s2[3, 1] = 0xFF
     assert refused(lambda: mxfp8.mxfp8_gemm(x, w, s2), ["NaN", "E8M0"])
     assert refused(lambda: mxfp8.validate(x[:, :48], w[:, :48], s[:, :1], 1, 4, 48), ["K % 32"])
+
+
+def pin_masses_ignore_tensor_scale_signs():
+    """The masses and slacks are L1 quantities: negating ts_d negates every expert row
+    exactly and leaves mass_y and slack_h unchanged (never negative); negating ts_u negates
+    h (bfloat16 rounding is symmetric), hence the rows, and leaves the masses, the
+    ambiguity of each h and the slack unchanged."""
+    for seed in (6, 7):
+        d, f = 64, 32
+        x, ex = _single_expert_inputs(d, f, seed)
+        rl = moe.row_lists(np.zeros((1, 1), np.int32), 1)
+        a = moe.expert_ffn(x, 1, d, f, 1, 1, ex, rl)
+        assert np.all(a.mass_y > 0) and np.all(a.slack_h >= 0)
+        for nm in ("down_ts", "up_ts"):
+            ex2 = dict(ex)
+            ex2[nm] = -ex[nm]
+            b = moe.expert_ffn(x, 1, d, f, 1, 1, ex2, rl)
+            assert np.array_equal(b.y_rows, -a.y_rows), nm
+            assert np.array_equal(b.mass_y, a.mass_y) and np.array_equal(b.slack_h, a.slack_h), nm
+    # a row whose h sits on a midpoint keeps its slack under a negative ts_d
+    ex3 = _midpoint_expert(1 + 2.0 ** -8, td=-1.5)
+    res = _one_row(ex3, {0: 64.0})
+    assert res.slack_h[0, 0] == 48.0 and res.y_rows[0, 0] == -1.5 * 4096.0
+    # and the window keeps its width under a negative ts_u: h = -(4112 - 20/2048), 0.00977
+    # from the midpoint, inside the window 0.01176 (a signed up mass would make it 0.0039)
+    tg = float(np.float32(1 + 2.0 ** -8 - 20 * 2.0 ** -23))
+    res = _one_row(_midpoint_expert(tg, tu=-1.0), {0: 64.0})
+    assert bf16_bits_scalar(res.h_bits[0, 0]) == -4096.0 and res.slack_h[0, 0] == 32.0
 
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_") and callable(v)]

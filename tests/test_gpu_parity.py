@@ -9,7 +9,8 @@ import pytest
 import workloads
 from oracle import band, formats as F, moe, mxfp8 as omx
 
-from gpu_util import check_layer_full, check_layer_sampled, check_routing, run_moe, say, upload_moe
+from gpu_util import (check_band, check_layer_full, check_layer_sampled, check_routing, cover_tokens, run_moe, say,
+                      upload_moe)
 
 pytestmark = pytest.mark.gpu
 
@@ -96,20 +97,67 @@ def test_layer_small(T, d, f, E, k):
     check_layer_full(inp, run_moe(inp), f"T{T}d{d}f{f}E{E}k{k}")
 
 
+def _covering_sample(inp, extra, seed):
+    """Tokens covering every (expert, 128-row tile) of the grouped GEMM and every
+    weight-streaming expert (first and last row of each), plus `extra` random tokens."""
+    ids, _ = moe.route(inp.logits, inp.k)
+    rl = moe.row_lists(ids, inp.E)
+    toks = cover_tokens(rl.offsets, rl.sorted_rows, inp.k)
+    more = np.random.default_rng(seed).choice(inp.T, size=extra, replace=False)
+    return np.unique(np.concatenate([toks, more]))
+
+
+@pytest.mark.timeout(900)
 def test_layer_prompt_sampled():
     inp = workloads.moe_config("prompt")
-    say("layer prompt (T=512, d=3072, f=1536, E=128, k=8), sampled tokens")
+    toks = _covering_sample(inp, 16, 0)
+    say(f"layer prompt (T=512, d=3072, f=1536, E=128, k=8), {toks.size} tokens covering every tile")
     res = run_moe(inp)
-    toks = np.random.default_rng(0).choice(inp.T, size=24, replace=False)
-    check_layer_sampled(inp, res, np.sort(toks), "prompt")
+    check_layer_sampled(inp, res, toks, "prompt")
 
 
+@pytest.mark.timeout(900)
 def test_layer_long_prompt_sampled():
     inp = workloads.moe_config("long_prompt")
-    say("layer long_prompt (T=4096, d=7168, f=2048, E=256, k=8), sampled tokens")
+    toks = _covering_sample(inp, 8, 1)
+    say(f"layer long_prompt (T=4096, d=7168, f=2048, E=256, k=8), {toks.size} tokens covering every tile")
     res = run_moe(inp)
-    toks = np.random.default_rng(1).choice(inp.T, size=4, replace=False)
-    check_layer_sampled(inp, res, np.sort(toks), "long_prompt")
+    check_layer_sampled(inp, res, toks, "long_prompt")
+
+
+# E4M3 block scales over all 254 finite codes (zero, negative, subnormal, 448) and tensor
+# scales of both signs including 2^-8 and 2^8: the decode path (T <= 16), the routing
+# inside the FFN launch, the weight-streaming and grouped-GEMM prompt paths
+EDGE = [(4, 256, 128, 8, 2), (16, 512, 256, 16, 4), (60, 256, 128, 8, 2), (300, 512, 256, 4, 2)]
+
+
+@pytest.mark.parametrize("T,d,f,E,k", EDGE)
+def test_layer_edge_codes(T, d, f, E, k):
+    inp = workloads.make_moe(T, d, f, E, k, seed=5, config_id=64, zipf=True, scale_codes="finite",
+                             tensor_scales="edge")
+    say(f"layer edge codes T={T} d={d} f={f} E={E} k={k}")
+    check_layer_full(inp, run_moe(inp), f"edge T{T}d{d}f{f}E{E}k{k}")
+    if T <= 16:
+        import torch
+        import nvfp4_block_scaled_topk_amd as M
+        x, logits, ex = upload_moe(inp)
+        (ids, w, off, sr, ro), y = M.route_expert_ffn_nvfp4(logits, x, ex, k)
+        out = M.combine(y, ro, w)
+        torch.cuda.synchronize()
+        res = dict(ids=ids.cpu().numpy(), w=w.cpu().numpy(), offsets=off.cpu().numpy(),
+                   sorted_rows=sr.cpu().numpy(), row_of=ro.cpu().numpy(), y_rows=y.cpu().numpy(),
+                   out=out.view(torch.int16).cpu().numpy().view(np.uint16))
+        check_layer_full(inp, res, f"edge fused T{T}d{d}f{f}E{E}k{k}")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("T,d,f,E,k", [(4, 7168, 2048, 16, 8), (2, 4096, 2048, 8, 4)])
+def test_layer_few_tokens_wide(T, d, f, E, k):
+    """A few tokens with d > 4096 or f > 1024: past the one-launch few-token path, every
+    expert takes the weight-streaming kernels (and the grouped GEMM has no tile)."""
+    inp = workloads.make_moe(T, d, f, E, k, seed=6, config_id=65, zipf=True)
+    say(f"layer few tokens, wide T={T} d={d} f={f} E={E} k={k}")
+    check_layer_full(inp, run_moe(inp), f"wide T{T}d{d}f{f}E{E}k{k}")
 
 
 def test_layer_deterministic_and_permutation():
@@ -157,9 +205,7 @@ def test_decode_workspace_reuse():
         torch.cuda.synchronize()
         ref = omoe.moe_layer(inp)
         got = out.view(torch.int16).cpu().numpy().view(np.uint16)
-        rep = band.classify(got, ref.out_bits, ref.mass, ref.slack)
-        say(f"[reuse {i}] {rep}")
-        assert rep.ok(), f"call {i}: {rep}"
+        check_band(band.classify(got, ref.out_bits, ref.mass, ref.slack), f"workspace reuse call {i}")
 
 
 # ---------------------------------------------------------------- MXFP8
@@ -188,21 +234,34 @@ def test_mxfp8_small(M_, N, K):
     say(f"mxfp8 M={M_} N={N} K={K}")
     got = _run_mxfp8(inp)
     _, ref, mass = omx.mxfp8_gemm(inp.x, inp.w, inp.s)
-    rep = band.classify(got, ref, mass)
-    say(f"[mxfp8 {M_}x{N}x{K}] {rep}")
-    assert rep.ok(), str(rep)
+    check_band(band.classify(got, ref, mass), f"mxfp8 {M_}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M_,N,K", [(1, 200, 512), (3, 130, 4096), (10, 96, 1024), (40, 300, 2048), (200, 260, 512)])
+def test_mxfp8_wide_scales(M_, N, K):
+    """E8M0 block scales over codes 100..160 (2^-27 .. 2^33) with every finite E4M3 code:
+    each kernel (vector-ALU gemv, MFMA gemv, tiled GEMM) on the whole exponent spread."""
+    inp = workloads.make_mxfp8(M_, N, K, seed=3, config_id=71, e8m0=(100, 160))
+    say(f"mxfp8 wide scales M={M_} N={N} K={K}")
+    got = _run_mxfp8(inp)
+    _, ref, mass = omx.mxfp8_gemm(inp.x, inp.w, inp.s)
+    check_band(band.classify(got, ref, mass), f"mxfp8 wide scales {M_}x{N}x{K}")
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("M_", [1, 512])
 def test_mxfp8_config(M_):
     inp = workloads.mxfp8_config(M_)
     say(f"mxfp8 config M={M_} N={inp.N} K={inp.K}")
     got = _run_mxfp8(inp)
-    rows = np.arange(M_) if M_ == 1 else np.sort(np.random.default_rng(3).choice(M_, 6, replace=False))
+    if M_ == 1:
+        rows = np.arange(1)
+    else:
+        # the first and last row of every 128-row tile of the GEMM, and four more
+        tiles = [r for t0 in range(0, M_, 128) for r in (t0, min(t0 + 128, M_) - 1)]
+        rows = np.unique(np.concatenate([tiles, np.random.default_rng(3).choice(M_, 4, replace=False)]))
     _, ref, mass = omx.mxfp8_gemm(inp.x, inp.w, inp.s, rows=rows)
-    rep = band.classify(got[rows], ref, mass)
-    say(f"[mxfp8 config M={M_}] {rep}")
-    assert rep.ok(), str(rep)
+    check_band(band.classify(got[rows], ref, mass), f"mxfp8 config M={M_}", f"out ({rows.size} rows x {inp.N})")
 
 
 # ---------------------------------------------------------------- routing in the FFN launch

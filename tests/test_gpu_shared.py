@@ -8,7 +8,7 @@ import pytest
 import workloads
 from oracle import band, shared as oshared
 
-from gpu_util import say, upload_moe
+from gpu_util import check_band, say, upload_moe
 
 pytestmark = pytest.mark.gpu
 
@@ -63,9 +63,7 @@ def test_shared_layer_full(name, gated):
     say(f"shared layer {name} gated={gated}")
     got = _run(inp, sh, gated)
     ref = oshared.moe_layer_shared(inp, sh, gated=gated)
-    rep = band.classify(got, ref.out_bits, ref.mass, ref.slack)
-    say(f"[shared {name} gated={gated}] {rep}")
-    assert rep.ok(), str(rep)
+    check_band(band.classify(got, ref.out_bits, ref.mass, ref.slack), f"shared {name} gated={gated}")
 
 
 @pytest.mark.parametrize("name,ntok", [("prompt", 16), ("long_prompt", 3)])
@@ -76,9 +74,7 @@ def test_shared_layer_sampled(name, ntok):
     got = _run(inp, sh, True)
     toks = np.sort(np.random.default_rng(4).choice(inp.T, size=ntok, replace=False))
     ref = oshared.moe_tokens_shared(inp, sh, toks)
-    rep = band.classify(got[toks], ref.out_bits, ref.mass, ref.slack)
-    say(f"[shared {name}] {rep}")
-    assert rep.ok(), str(rep)
+    check_band(band.classify(got[toks], ref.out_bits, ref.mass, ref.slack), f"shared {name}", f"out ({ntok} sampled tokens)")
 
 
 @pytest.mark.parametrize("T,d,f,E,k", [(1, 64, 32, 4, 2), (17, 160, 96, 6, 3), (40, 256, 128, 8, 2)])
@@ -88,8 +84,7 @@ def test_shared_layer_small(T, d, f, E, k):
     say(f"shared small T={T} d={d} f={f} E={E} k={k}")
     got = _run(inp, sh, True)
     ref = oshared.moe_layer_shared(inp, sh)
-    rep = band.classify(got, ref.out_bits, ref.mass, ref.slack)
-    assert rep.ok(), str(rep)
+    check_band(band.classify(got, ref.out_bits, ref.mass, ref.slack), f"shared small T{T}d{d}f{f}E{E}k{k}")
 
 
 @pytest.mark.parametrize("name", ["prompt", "T40"])

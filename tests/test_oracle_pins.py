@@ -111,7 +111,7 @@ MUTANTS = [
      ["pin_mxfp8_one_hot_and_scale", "pin_mxfp8_brute_force"]),
     # ---- the acceptance rule and its slack terms
     ("slack_h_x1024", "moe.py",
-     [("slack_h[sel] = td * ((amb * ulp) @ aWd.T)", "slack_h[sel] = 1024 * td * ((amb * ulp) @ aWd.T)")],
+     [("sh = abs(td) * ((amb * ulp) @ aWd.T)", "sh = 1024 * abs(td) * ((amb * ulp) @ aWd.T)")],
      ["pin_slack_h_midpoint"]),
     ("band_slack_x1024", "band.py",
      [("bound = bound + np.asarray(slack)", "bound = bound + 1024 * np.asarray(slack)")] * 2,
@@ -126,11 +126,18 @@ MUTANTS = [
      [("ACC_REL = 2.0 ** -20", "ACC_REL = 2.0 ** -19")],
      ["pin_slack_h_window"]),
     ("gate_mass_signed", "moe.py",
-     [("mass_g = tg * (aX @ np.abs(Wg).T)", "mass_g = tg * (X @ Wg.T)")],
+     [("mass_g = abs(tg) * (aX @ np.abs(Wg).T)", "mass_g = abs(tg) * (X @ Wg.T)")],
      ["pin_slack_h_window"]),
     ("mass_y_signed", "moe.py",
-     [("mass_y[sel] = td * (np.abs(H) @ aWd.T)", "mass_y[sel] = td * (H @ Wd.T)")],
+     [("my = abs(td) * (np.abs(H) @ aWd.T)", "my = abs(td) * (H @ Wd.T)")],
      ["pin_mass_y_brute_force"]),
+    ("mass_y_signed_tensor_scale", "moe.py",
+     [("my = abs(td) * (np.abs(H) @ aWd.T)", "my = td * (np.abs(H) @ aWd.T)"),
+      ("sh = abs(td) * ((amb * ulp) @ aWd.T)", "sh = td * ((amb * ulp) @ aWd.T)")],
+     ["pin_masses_ignore_tensor_scale_signs"]),
+    ("mass_u_signed_tensor_scale", "moe.py",
+     [("mass_u = abs(tu) * (aX @ np.abs(Wu).T)", "mass_u = tu * (aX @ np.abs(Wu).T)")],
+     ["pin_masses_ignore_tensor_scale_signs"]),
     ("mass_rel_2m10", "band.py",
      [("MASS_REL = 2.0 ** -20", "MASS_REL = 2.0 ** -10")],
      ["pin_band_explained_by_hand"]),

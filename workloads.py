@@ -127,10 +127,25 @@ def make_logits(T: int, E: int, seed: int, config_id: int, zipf: bool) -> np.nda
     return logits
 
 
+# edge-case tensor scales: both signs, powers of two far from 1, and ordinary values
+EDGE_TENSOR_SCALES = np.array([2.0 ** -8, -(2.0 ** -8), 2.0 ** 8, -(2.0 ** 8), -1.0, 0.75, -1.375, 3.0],
+                              dtype=np.float32)
+
+
+def _finite_e4m3_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    """Uniform over the 254 finite E4M3 codes (0x7F and 0xFF, the NaN codes, excluded)."""
+    j = rng.integers(0, 254, size=shape, dtype=np.int32)
+    return np.where(j < 127, j, j + 1).astype(np.uint8)
+
+
 def make_moe(T: int, d: int, f: int, E: int, k: int, seed: int = 0, config_id: int = 99,
-             zipf: bool = False, name: str = "custom", experts: bool = True) -> MoEInputs:
+             zipf: bool = False, name: str = "custom", experts: bool = True,
+             scale_codes: str = "config", tensor_scales: str = "config") -> MoEInputs:
     """Draw one MoE layer's inputs. ``experts=False`` skips the weight draws
-    (zero-size placeholders), for routing-only cases."""
+    (zero-size placeholders), for routing-only cases. Edge cases:
+    ``scale_codes="finite"`` draws the E4M3 block scales uniformly over all 254 finite
+    codes (zero, negative and subnormal scales, 448 included) instead of 0x18..0x48;
+    ``tensor_scales="edge"`` draws each tensor scale from EDGE_TENSOR_SCALES."""
     if d % 32 or f % 32:
         raise ValueError("d and f must be multiples of 32")
     x = bf16_bits_from_normal(_rng(seed, config_id, _T_X), (T, d))
@@ -142,9 +157,13 @@ def make_moe(T: int, d: int, f: int, E: int, k: int, seed: int = 0, config_id: i
     def scales(tid, shape):
         if not experts:
             return np.zeros((0,), np.uint8)
+        if scale_codes == "finite":
+            return _finite_e4m3_codes(_rng(seed, config_id, tid), shape)
         return _rng(seed, config_id, tid).integers(0x18, 0x49, size=shape, dtype=np.uint8)
 
     def tscale(tid):
+        if tensor_scales == "edge":
+            return _rng(seed, config_id, tid).choice(EDGE_TENSOR_SCALES, size=(E,)).astype(np.float32)
         return _rng(seed, config_id, tid).uniform(0.5, 2.0, size=(E,)).astype(np.float32)
 
     return MoEInputs(
@@ -179,20 +198,19 @@ class MXFP8Inputs:
     name: str = "custom"
 
 
-def make_mxfp8_weights(N: int, K: int, seed: int = 0, config_id: int = 99):
+def make_mxfp8_weights(N: int, K: int, seed: int = 0, config_id: int = 99, e8m0=(121, 129)):
+    """E4M3 weights uniform over the 254 finite codes; E8M0 scales uniform over the codes
+    e8m0[0]..e8m0[1] (121..129: 2^-6 .. 2^2)."""
     if K % 32:
         raise ValueError("K must be a multiple of 32")
-    rng = _rng(seed, config_id, _T_MX_W)
-    # 254 finite codes: 0x00..0x7E and 0x80..0xFE
-    j = rng.integers(0, 254, size=(N, K), dtype=np.int32)
-    w = np.where(j < 127, j, j + 1).astype(np.uint8)
-    s = _rng(seed, config_id, _T_MX_S).integers(121, 130, size=(N, K // 32), dtype=np.uint8)
+    w = _finite_e4m3_codes(_rng(seed, config_id, _T_MX_W), (N, K))
+    s = _rng(seed, config_id, _T_MX_S).integers(e8m0[0], e8m0[1] + 1, size=(N, K // 32), dtype=np.uint8)
     return w, s
 
 
 def make_mxfp8(M: int, N: int, K: int, seed: int = 0, config_id: int = 99, name: str = "custom",
-               m_index: int = 0) -> MXFP8Inputs:
-    w, s = make_mxfp8_weights(N, K, seed, config_id)
+               m_index: int = 0, e8m0=(121, 129)) -> MXFP8Inputs:
+    w, s = make_mxfp8_weights(N, K, seed, config_id, e8m0)
     x = bf16_bits_from_normal(_rng(seed, config_id, _T_MX_X0 + m_index), (M, K))
     return MXFP8Inputs(M=M, N=N, K=K, x=x, w=w, s=s, name=name)
 
