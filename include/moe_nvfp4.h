@@ -25,8 +25,10 @@
  * Conventions for every entry point
  *   - Every data pointer is a DEVICE pointer, allocated and owned by the caller; the
  *     library never allocates, frees or retains memory. Its only global state is a
- *     per-process call counter (moe_expert_ffn_nvfp4 tags its workspace words with it)
- *     and cached device properties.
+ *     per-process call counter (moe_expert_ffn_nvfp4 tags its workspace words with it),
+ *     the wait limit and the per-device flag of moe_async_status, and device properties
+ *     cached per device (behind a lock: every entry point may be called from several
+ *     host threads).
  *   - `stream` is a hipStream_t (NULL = the default stream). A call only enqueues work
  *     on it; results are valid once the stream reaches the call.
  *   - Arguments are checked on the host before any HIP call; a call that returns a
@@ -63,7 +65,8 @@ enum {
   MOE_E_ALIGN = 3,     /* a pointer is not 16-byte aligned                             */
   MOE_E_WORKSPACE = 4, /* workspace NULL or smaller than the size query returns        */
   MOE_E_LAUNCH = 5,    /* a HIP launch failed; see moe_last_error()                    */
-  MOE_E_POLICY = 6     /* an unknown routing policy                                   */
+  MOE_E_POLICY = 6,    /* an unknown routing policy                                   */
+  MOE_E_WAIT_EXPIRED = 7 /* moe_async_status: a few-token launch gave up a wait          */
 };
 
 /* Routing normalization policies (moe_route_topk_policy). The pages make the router's
@@ -148,14 +151,17 @@ int moe_route_topk_policy(const float* logits, int T, int E, int k, int policy, 
  * device outputs of moe_route_topk for the same T, E, k.
  * Sizes: 1 <= T, d and f multiples of 32 (>= 32), 1 <= E <= 1024, 1 <= k <= min(E, 32).
  * Workspace: at least moe_expert_ffn_nvfp4_workspace(T, d, f, E, k) bytes (holds H; no
- * initial contents needed).
+ * initial contents needed). Calls that share a workspace must be ordered on one stream;
+ * calls with different workspaces may run concurrently on different streams.
  * Few tokens (T <= 16, d <= 4096, f <= 1024 and T * (max(d, f) + 8) * 2 <= 64 KiB) run as
- * one launch whose down-product workgroups wait, with a bounded spin, for the gate/up
- * workgroups of the same expert; the launch never has more workgroups than the GPU holds
- * at once. If
- * other work keeps some of them from becoming resident (for instance another such call
- * running concurrently on a second stream), a wait can expire: the affected rows of
- * y_rows are then NaN, and nothing hangs.
+ * one launch in which the down-product workgroups wait for the gate/up workgroups of the
+ * same expert. The launch has as many workgroups as the GPU holds at once, but the
+ * waits do not depend on them all being resident (work on other streams or processes
+ * can keep some from starting): a down-product workgroup that still misses some of its
+ * expert's H slices after a number of polls computes those gate/up items itself, with
+ * the same code, so the results are the same bits either way. As a last guard a wait
+ * gives up after a bound (moe_set_wait_limits): the affected y_rows are then NaN and
+ * moe_async_status reports MOE_E_WAIT_EXPIRED; that cannot happen with the defaults.
  */
 size_t moe_expert_ffn_nvfp4_workspace(int T, int d, int f, int E, int k);
 int moe_expert_ffn_nvfp4(const uint16_t* x, int T, int d, int f, int E, int k,
@@ -225,6 +231,29 @@ int moe_router_logits(const uint16_t* x, const uint16_t* w_r, int T, int d, int 
  */
 int mxfp8_gemm(const uint16_t* x, int M, int N, int K,
                const uint8_t* w, const uint8_t* s, uint16_t* y, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_async_status -- waits for `stream`, then reports whether any few-token launch on
+ * the current device gave up a wait since the last report (MOE_E_WAIT_EXPIRED; its
+ * affected y_rows are then NaN) or not (MOE_OK), and clears the flag. The flag is one
+ * per device and process. A HIP error while waiting returns MOE_E_LAUNCH. The pages
+ * refuse bad results by name rather than pass them on silently [#565 page, §9 Rules and
+ * related work, Accuracy]; this is the report for the one condition that only the
+ * device sees.
+ */
+int moe_async_status(void* stream);
+
+/* moe_set_wait_limits -- the polls of the few-token launch's waits, for the calls
+ * enqueued after it, process-wide: `steal_after` polls of a missing H slice before a
+ * down-product workgroup computes the missing gate/up items itself (default 256), and
+ * `give_up` polls of its full H read before it writes NaN rows and raises the flag of
+ * moe_async_status (default 1048576); each poll is followed by a short sleep. Stealing
+ * happens only when steal_after < give_up. Test hooks: (0, default) makes every
+ * down-product workgroup that finds H missing compute it itself (the results stay the
+ * same bits); (0, 0) gives up at once, forcing the guard's exit path without any fault.
+ * moe_get_wait_limits reads the current values (either pointer may be NULL). */
+void moe_set_wait_limits(uint32_t steal_after, uint32_t give_up);
+void moe_get_wait_limits(uint32_t* steal_after, uint32_t* give_up);
 
 /* Name of a status code ("MOE_OK", "MOE_E_SHAPE", ...); never NULL. */
 const char* moe_status_string(int status);

@@ -23,14 +23,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_nvfp4.so")
 
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_E_NULL", 2: "MOE_E_SHAPE", 3: "MOE_E_ALIGN",
-                4: "MOE_E_WORKSPACE", 5: "MOE_E_LAUNCH", 6: "MOE_E_POLICY"}
+                4: "MOE_E_WORKSPACE", 5: "MOE_E_LAUNCH", 6: "MOE_E_POLICY", 7: "MOE_E_WAIT_EXPIRED"}
 # routing normalization policies (MOE_ROUTE_* in the header)
 ROUTE_SOFTMAX_RENORM, ROUTE_SOFTMAX, ROUTE_SIGMOID_RENORM, ROUTE_SIGMOID = 0, 1, 2, 3
 
 EXPORTED_SYMBOLS = (
     "moe_route_topk_workspace", "moe_route_topk", "moe_route_topk_policy", "moe_expert_ffn_nvfp4_workspace",
     "moe_expert_ffn_nvfp4", "moe_route_expert_ffn_nvfp4", "moe_combine", "moe_combine_shared", "mxfp8_gemm", "moe_router_logits", "moe_status_string",
-    "moe_last_error",
+    "moe_last_error", "moe_async_status", "moe_set_wait_limits", "moe_get_wait_limits",
 )
 
 
@@ -83,6 +83,12 @@ def lib() -> ctypes.CDLL:
     L.mxfp8_gemm.restype = i32
     L.moe_router_logits.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     L.moe_router_logits.restype = i32
+    L.moe_async_status.argtypes = [vp]
+    L.moe_async_status.restype = i32
+    L.moe_set_wait_limits.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
+    L.moe_set_wait_limits.restype = None
+    L.moe_get_wait_limits.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32)]
+    L.moe_get_wait_limits.restype = None
     L.moe_status_string.argtypes = [i32]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_last_error.argtypes = []
@@ -95,6 +101,33 @@ def _check(status: int, where: str):
     if status != 0:
         detail = lib().moe_last_error().decode() if status == 5 else ""
         raise MoEError(status, where, detail)
+
+
+def async_status(device=None) -> int:
+    """Waits for torch's current stream and returns the library's asynchronous status
+    (0, or 7 = MOE_E_WAIT_EXPIRED: a few-token launch gave up a wait; the affected rows
+    are NaN), clearing it."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(dev):
+        st = lib().moe_async_status(torch.cuda.current_stream(dev).cuda_stream)
+    if st not in (0, 7):
+        _check(st, "moe_async_status")
+    return st
+
+
+def wait_limits() -> tuple:
+    """(steal_after, give_up): the polls of the few-token launch's waits."""
+    a, b = ctypes.c_uint32(), ctypes.c_uint32()
+    lib().moe_get_wait_limits(ctypes.byref(a), ctypes.byref(b))
+    return int(a.value), int(b.value)
+
+
+def set_wait_limits(steal_after: int, give_up: int) -> tuple:
+    """Sets the polls of the few-token launch's waits (see moe_set_wait_limits); returns
+    the previous (steal_after, give_up)."""
+    prev = wait_limits()
+    lib().moe_set_wait_limits(int(steal_after), int(give_up))
+    return prev
 
 
 def _stream(t: torch.Tensor) -> int:

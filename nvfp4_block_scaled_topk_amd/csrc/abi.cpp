@@ -46,7 +46,7 @@ size_t round_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 uint32_t next_call_tag() {
   static std::atomic<uint32_t> counter{static_cast<uint32_t>(std::random_device{}())};
   uint32_t t = counter.fetch_add(1, std::memory_order_relaxed) + 1u;
-  if (t == 0) t = counter.fetch_add(1, std::memory_order_relaxed) + 1u;
+  while (t == 0) t = counter.fetch_add(1, std::memory_order_relaxed) + 1u;
   return t;
 }
 
@@ -55,6 +55,10 @@ size_t h_bytes(int T, int d, int f, int k) {
   const size_t elem = moe::use_decode_path(T, d, f) ? 4 : 2;
   return round_up((size_t)T * k * f * elem);
 }
+
+// polls of the few-token launch's waits (moe_set_wait_limits)
+std::atomic<uint32_t> g_steal_after{moe::kDefaultStealAfter};
+std::atomic<uint32_t> g_give_up{moe::kDefaultGiveUp};
 
 }  // namespace
 
@@ -161,7 +165,8 @@ int moe_expert_ffn_nvfp4(const uint16_t* x, int T, int d, int f, int E, int k, c
   hipStream_t st = static_cast<hipStream_t>(stream);
   // a token routes to k distinct experts, so an expert has at most T rows: with
   // T <= 16 every expert's rows fit one decode tile
-  if (moe::use_decode_path(T, d, f)) return launch_status(moe::launch_ffn_decode(a, next_call_tag(), st));
+  if (moe::use_decode_path(T, d, f))
+    return launch_status(moe::launch_ffn_decode(a, next_call_tag(), g_steal_after.load(), g_give_up.load(), st));
   return launch_status(moe::launch_ffn_prompt(a, st));
 }
 
@@ -183,7 +188,8 @@ int moe_route_expert_ffn_nvfp4(const float* logits, const uint16_t* x, int T, in
   a.offsets_out = expert_offsets;
   a.sorted_rows_out = sorted_rows;
   a.row_of_out = row_of;
-  return launch_status(moe::launch_ffn_decode(a, next_call_tag(), static_cast<hipStream_t>(stream)));
+  return launch_status(
+      moe::launch_ffn_decode(a, next_call_tag(), g_steal_after.load(), g_give_up.load(), static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine(const float* y_rows, const int32_t* row_of, const float* topk_w, int T, int k, int d,
@@ -228,6 +234,24 @@ int mxfp8_gemm(const uint16_t* x, int M, int N, int K, const uint8_t* w, const u
   return launch_status(moe::launch_mxfp8(x, M, N, K, w, s, y, static_cast<hipStream_t>(stream)));
 }
 
+int moe_async_status(void* stream) {
+  hipError_t err = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  unsigned int flag = 0;
+  if (err == hipSuccess) err = moe::read_and_clear_async_status(flag);
+  if (err != hipSuccess) return launch_status(err);
+  return flag ? MOE_E_WAIT_EXPIRED : MOE_OK;
+}
+
+void moe_set_wait_limits(uint32_t steal_after, uint32_t give_up) {
+  g_steal_after.store(steal_after);
+  g_give_up.store(give_up);
+}
+
+void moe_get_wait_limits(uint32_t* steal_after, uint32_t* give_up) {
+  if (steal_after) *steal_after = g_steal_after.load();
+  if (give_up) *give_up = g_give_up.load();
+}
+
 const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "MOE_OK";
@@ -237,6 +261,7 @@ const char* moe_status_string(int status) {
     case MOE_E_WORKSPACE: return "MOE_E_WORKSPACE";
     case MOE_E_LAUNCH: return "MOE_E_LAUNCH";
     case MOE_E_POLICY: return "MOE_E_POLICY";
+    case MOE_E_WAIT_EXPIRED: return "MOE_E_WAIT_EXPIRED";
     default: return "MOE_E_UNKNOWN";
   }
 }

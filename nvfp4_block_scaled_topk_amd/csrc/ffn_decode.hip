@@ -39,10 +39,15 @@
 // waits for its stores and there are no separate completion flags. Every call writes
 // every H word it reads, so words left from earlier calls carry older tags.
 // Block b takes gate/up items b, b + G, ... and then down items G-1-b, 2G-1-b, ... (the
-// blocks without a gate/up item take the extra down items). Every block finishes its
-// gate/up items before it waits, and the grid never exceeds the number of blocks the
-// device holds at once, so every awaited H word belongs to a running block. A wait is
-// bounded: past kSpinLimit polls the block writes NaN rows instead of hanging.
+// blocks without a gate/up item take the extra down items); every block finishes its
+// gate/up items before it waits, and the grid is sized to what the device holds at once,
+// so normally every awaited H word belongs to a running block. Correctness does not rest
+// on that: a down item whose H slices are still missing after `steal_after` polls
+// computes the missing gate/up items of its expert itself (the same code on the same
+// inputs, so the same bits; a word written twice is written with the same value), so no
+// wait depends on a block that has not started (other work on the GPU, another stream).
+// As a last guard the full read gives up after `give_up` polls: the block then writes
+// NaN rows and raises the library's asynchronous status flag (moe_async_status).
 #include "device.hpp"
 #include "internal.hpp"
 #include "route_device.hpp"
@@ -57,8 +62,8 @@ constexpr int kDecMaxTouched = kDecMaxAssign;      // min(E, T * k)
 constexpr int kGUFeat = 32;                     // features of a gate/up item
 constexpr int kDCols = 16 * kDecWaves;          // columns of d in a down item
 constexpr int kDownPairs = 3;                   // W_down chunk pairs (2 x 128 K) a wave holds before its wait
-constexpr uint32_t kSpinLimit = 1u << 20;       // polls (each followed by s_sleep) before giving up
 constexpr int kScrWave = 4096;                  // LDS a wave uses to rearrange its weight codes
+constexpr int kDecMaxDeferred = 64;             // down items a block may take (the grid is sized for it)
 
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
@@ -89,6 +94,10 @@ __device__ __forceinline__ unsigned long long h_word(uint32_t lo, uint32_t hi, u
   return (unsigned long long)(lo | (hi << 16)) | ((unsigned long long)tag << 32);
 }
 
+// Set (atomic or, vector memory) when a wait of a few-token launch gives up; read and
+// cleared by moe_async_status.
+__device__ unsigned int g_async_status;
+
 struct DownPrefetch {
   u32x4 q[kDownPairs][2];  // [pair][rows 0-7 / 8-15], as loaded
   u32x4 sc;                // 16 bytes of the wave's 16 scale rows (f bytes, contiguous)
@@ -108,11 +117,278 @@ __host__ __device__ __forceinline__ size_t dec_row_region(int T, int d, int f) {
   return (r + 15) / 16 * 16;
 }
 
-__global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, uint32_t tag) {
+// Everything a gate/up item needs besides the kernel arguments: the block's LDS regions
+// and index lists, the H words and the call's tag.
+struct GateUpCtx {
+  unsigned char* s_dyn;      // the activation rows (row t at t * xstride)
+  unsigned char* s_scr;      // kScrWave bytes a wave
+  unsigned char* s_sc;       // the item's block scales
+  const int* s_tok;          // token of each routed row
+  const int* s_e;            // touched experts: id, first row, row count
+  const int* s_r0;
+  const int* s_n;
+  unsigned long long* hw;    // H as tagged words
+  uint32_t tag;
+};
+
+// One gate/up item (touched expert u = i / nfg, features 32 (i % nfg) ..): the block's
+// 8 waves compute the gate and up tiles, wave pairs of K quarters are summed in a fixed
+// order, and H = bf16_rne(silu(ts_g G) (ts_u U)) is stored as tagged words. Ends after
+// the H stores (the caller places the barrier). The kernel inlines it where a block does
+// its own items and where it computes a missing item of another block: the same code, so
+// the same bits.
+__device__ __forceinline__ void gate_up_item(const FFNArgs& a, const GateUpCtx& cx, int i) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int nfg = a.f / kGUFeat;
+  const int nchG = a.d / 128;
+  const int half = wave >> 2, kq = wave & 3;  // 16-feature half of the item, quarter of K
+  const int kc0 = nchG * kq / 4, kc1 = nchG * (kq + 1) / 4;
+  const bool gtail = kq == 3;
+  const int xstride = dec_xstride(a.d);
+  constexpr int kB = 4;  // chunks a wave loads at once
+  unsigned char* const s_dyn = cx.s_dyn;
+  unsigned char* const s_scr = cx.s_scr;
+  unsigned char* const s_sc = cx.s_sc;
+  const int* const s_tok = cx.s_tok;
+  const int* const s_e = cx.s_e;
+  const int* const s_r0 = cx.s_r0;
+  const int* const s_n = cx.s_n;
+  unsigned long long* const hw = cx.hw;
+  const uint32_t tag = cx.tag;
+  const int u = i / nfg, fg = i - u * nfg;
+  const int e = s_e[u], r0 = s_r0[u], ne = s_n[u];
+  // weight rows through buffer descriptors (expert slab base in scalar registers,
+  // a 32-bit row offset per lane)
+  const size_t slab = (size_t)a.f * (a.d / 2), sslab = (size_t)a.f * (a.d / 16);
+  const __amdgpu_buffer_rsrc_t qrs[2] = {dec_rsrc(a.gate_q + (size_t)e * slab, (uint32_t)slab),
+                                         dec_rsrc(a.up_q + (size_t)e * slab, (uint32_t)slab)};
+  const __amdgpu_buffer_rsrc_t srs[2] = {dec_rsrc(a.gate_s + (size_t)e * sslab, (uint32_t)sslab),
+                                         dec_rsrc(a.up_s + (size_t)e * sslab, (uint32_t)sslab)};
+  // MFMA layout: lane (grp, col) works on weight row `frow` of the item
+  const uint32_t frow = (uint32_t)(fg * kGUFeat + half * 16 + col);
+  // the item's scales in LDS: [gate / up][32 rows][d / 16 bytes]
+  const int srow = a.d / 16, sbytes = kGUFeat * srow;
+  const unsigned char* const my_sc = s_sc + (half * 16 + col) * srow;
+  // Code loads run along the rows instead: a load covers a pair of chunks (128 bytes,
+  // one cache line) of 8 rows -- lane group grp8 = lane / 8 takes row 8i + grp8 and
+  // lane lane % 8 its 16-byte segment -- rather than 64 bytes of 16 rows. The wave
+  // rearranges each pair into the MFMA layout through its LDS scratch.
+  const int grp8 = lane >> 3, seg8 = lane & 7;
+  const uint32_t qoff = (uint32_t)(fg * kGUFeat + half * 16 + grp8) * (uint32_t)(a.d / 2);
+  unsigned char* const scr = s_scr + wave * kScrWave;
+  floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  u32x4 lq[2][2][2];  // [pair][gate / up][rows 0-7 / 8-15], as loaded
+  // A batch always issues kB chunks of loads (a chunk past the wave's range repeats
+  // chunk c), so the number of loads in flight is a constant and every wait below is
+  // exact. Per pair: gate codes, then up.
+  auto load_batch = [&](int c) {
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const int lc = c + 2 * pr + (seg8 >> 2) < kc1 ? c + 2 * pr + (seg8 >> 2) : c;  // this lane's chunk
+      const int lb = (int)qoff + lc * 64 + 16 * (seg8 & 3);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(qrs[m], lb, i * 8 * (a.d / 2), kWeightAux);
+          lq[pr][m][i] = u32x4{v.x, v.y, v.z, v.w};
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // the item's scales (32 whole scale rows of gate and of up, contiguous in memory)
+  // and the activation rows of expert u by DMA first, then the first batch of
+  // weights; waiting for all but the weight loads leaves those in flight, and each
+  // pair of chunks is decoded as soon as its own loads have landed
+  for (int qi = (int)threadIdx.x; qi < 2 * sbytes / 16; qi += kDecThreads) {
+    const int m = qi >= sbytes / 16;
+    const uint32_t off = (uint32_t)(fg * kGUFeat) * (uint32_t)srow + (uint32_t)(qi * 16 - m * sbytes);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(srs[m], (lds_void_ptr)(s_sc + (qi - lane) * 16), 16, off, 0, 0, kWeightAux);
+  }
+  load_batch(kc0);
+  wait_vm<8>();  // the scale DMA has landed; the batch's 8 code loads may still be in flight
+  // a bare barrier: __syncthreads() would also wait for the weight loads
+  lds_barrier();
+  const bool valid = col < ne;
+  // Lanes of routed rows >= ne read whatever the LDS row holds: MFMA output column j
+  // depends only on operand column j, and those columns are never stored.
+  // the activation row of routed row col (rows >= ne: the expert's last row's token)
+  const unsigned char* xrow = s_dyn + s_tok[r0 + min(col, ne - 1)] * xstride;
+  auto xop = [&](int k0) -> bf16x8 { return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4v*>(xrow + k0 * 2)); };
+  // Rearrange a pair: piece (row r, 16-byte segment s) of matrix m sits at
+  // m * 2048 + r * 128 + ((s + r / 2) mod 8) * 16 in the wave's scratch, so the stores
+  // (two rows per 16 lanes) and the loads (a segment of 16 rows per 16 lanes) each hit
+  // 16 distinct 16-byte bank groups. LDS operations of one wave complete in order.
+  auto compute_pair = [&](int c, int pr) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 8 * i + grp8;
+        *reinterpret_cast<u32x4v*>(scr + m * 2048 + r * 128 + ((seg8 + (r >> 1)) & 7) * 16) =
+            u32x4v{lq[pr][m][i].x, lq[pr][m][i].y, lq[pr][m][i].z, lq[pr][m][i].w};
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    u32x4 q[2][2];  // [gate / up][chunk of the pair], MFMA layout
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        // chunk j of the pair, row col: segments 4j .. 4j + 3, lane group grp takes 4j + grp
+        const u32x4v v =
+            *reinterpret_cast<const u32x4v*>(scr + m * 2048 + col * 128 + ((4 * j + grp + (col >> 1)) & 7) * 16);
+        q[m][j] = u32x4{v.x, v.y, v.z, v.w};
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int h = 2 * pr + j;
+      if (c + h < kc1) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const uint32_t sc = *reinterpret_cast<const uint16_t*>(my_sc + m * sbytes + (c + h) * 8 + 2 * grp);
+          const E4M3Split s0 = e4m3_split_b<0>(sc);
+          const E4M3Split s1 = e4m3_split_b<1>(sc);
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            acc[m] = mfma16(nvfp4x8_to_bf16(word_of(q[m][j], s), s < 2 ? s0 : s1),
+                                xop((c + h) * 128 + 32 * grp + 8 * s), acc[m]);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto compute_batch = [&](int c) {
+    compute_pair(c, 0);
+    compute_pair(c, 1);
+  };
+  // the first batch straight after its loads (a separate copy keeps the compiler's
+  // per-load waits exact), then any further batches
+  compute_batch(kc0);
+  for (int c = kc0 + kB; c < kc1; c += kB) {
+    load_batch(c);
+    compute_batch(c);
+  }
+  if (gtail) {
+    // 32-element chunks past the last full 128: lane group g holds K0 + 8g .. K0 + 8g + 7
+    for (int K0 = nchG * 128; K0 < a.d; K0 += 32) {
+      const bf16x8 xv = xop(K0 + 8 * grp);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const uint32_t qq = __builtin_amdgcn_raw_buffer_load_b32(qrs[m], (int)(frow * (uint32_t)(a.d / 2) + 4 * grp),
+                                                               K0 / 2, kWeightAux);
+        const uint32_t sv = my_sc[m * sbytes + K0 / 16 + (grp >> 1)];
+        acc[m] = mfma16(nvfp4x8_to_bf16(qq, e4m3_split(sv)), xv, acc[m]);
+      }
+    }
+  }
+  // partial sums through the waves' scratch: [wave][gate / up][lane]
+  floatx4* const red = reinterpret_cast<floatx4*>(s_scr);
+  constexpr int kRedWave = kScrWave / (int)sizeof(floatx4);
+  red[wave * kRedWave + lane] = acc[0];
+  red[wave * kRedWave + 64 + lane] = acc[1];
+  __syncthreads();
+  if (kq == 0) {
+    if (valid) {
+      floatx4 Gs = red[wave * kRedWave + lane], Us = red[wave * kRedWave + 64 + lane];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        Gs += red[(wave + w) * kRedWave + lane];
+        Us += red[(wave + w) * kRedWave + 64 + lane];
+      }
+      const float tg = a.gate_ts[e], tu = a.up_ts[e];
+      uint32_t hb[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hb[r] = bf16_rne(silu_f32(tg * Gs[r]) * (tu * Us[r]));
+      // lane holds routed row `col`, features 4*grp .. 4*grp + 3 of the half
+      unsigned long long* dst = hw + ((size_t)(r0 + col) * a.f + fg * kGUFeat + half * 16 + 4 * grp) / 2;
+      __hip_atomic_store(dst, h_word(hb[0], hb[1], tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(dst + 1, h_word(hb[2], hb[3], tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// The same gate/up item with plain loads: every operand loaded in the MFMA layout
+// straight from memory (codes 16 bytes a lane, scales 2 bytes a lane) instead of whole
+// cache lines rearranged in LDS, no batching. Slower, and much lighter on registers; the
+// MFMA sequence, its operands and the reduction are those of gate_up_item, so the H bits
+// are the same. Used only by a down item that computes a missing item of another block.
+__device__ __forceinline__ void gate_up_item_plain(const FFNArgs& a, const GateUpCtx& cx, int i) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int nfg = a.f / kGUFeat;
+  const int nchG = a.d / 128;
+  const int half = wave >> 2, kq = wave & 3;
+  const int kc0 = nchG * kq / 4, kc1 = nchG * (kq + 1) / 4;
+  const int u = i / nfg, fg = i - u * nfg;
+  const int e = cx.s_e[u], r0 = cx.s_r0[u], ne = cx.s_n[u];
+  const int frow = fg * kGUFeat + half * 16 + col;  // this lane's weight row
+  const uint8_t* const q[2] = {a.gate_q + ((size_t)e * a.f + frow) * (a.d / 2),
+                               a.up_q + ((size_t)e * a.f + frow) * (a.d / 2)};
+  const uint8_t* const sc[2] = {a.gate_s + ((size_t)e * a.f + frow) * (a.d / 16),
+                                a.up_s + ((size_t)e * a.f + frow) * (a.d / 16)};
+  const unsigned char* xrow = cx.s_dyn + cx.s_tok[r0 + min(col, ne - 1)] * dec_xstride(a.d);
+  auto xop = [&](int k0) -> bf16x8 { return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4v*>(xrow + k0 * 2)); };
+  floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  for (int c = kc0; c < kc1; ++c) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const u32x4 w = ldg_u32x4(q[m] + c * 64 + 16 * grp);
+      const uint32_t s2 = *reinterpret_cast<const uint16_t*>(sc[m] + c * 8 + 2 * grp);
+      const E4M3Split s0 = e4m3_split_b<0>(s2);
+      const E4M3Split s1 = e4m3_split_b<1>(s2);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc[m] = mfma16(nvfp4x8_to_bf16(word_of(w, s), s < 2 ? s0 : s1), xop(c * 128 + 32 * grp + 8 * s), acc[m]);
+    }
+  }
+  if (kq == 3) {
+    for (int K0 = nchG * 128; K0 < a.d; K0 += 32) {
+      const bf16x8 xv = xop(K0 + 8 * grp);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const uint32_t qq = *reinterpret_cast<const uint32_t*>(q[m] + K0 / 2 + 4 * grp);
+        const uint32_t sv = sc[m][K0 / 16 + (grp >> 1)];
+        acc[m] = mfma16(nvfp4x8_to_bf16(qq, e4m3_split(sv)), xv, acc[m]);
+      }
+    }
+  }
+  floatx4* const red = reinterpret_cast<floatx4*>(cx.s_scr);
+  constexpr int kRedWave = kScrWave / (int)sizeof(floatx4);
+  red[wave * kRedWave + lane] = acc[0];
+  red[wave * kRedWave + 64 + lane] = acc[1];
+  __syncthreads();
+  if (kq == 0 && col < ne) {
+    floatx4 Gs = red[wave * kRedWave + lane], Us = red[wave * kRedWave + 64 + lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      Gs += red[(wave + w) * kRedWave + lane];
+      Us += red[(wave + w) * kRedWave + 64 + lane];
+    }
+    const float tg = a.gate_ts[e], tu = a.up_ts[e];
+    uint32_t hb[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) hb[r] = bf16_rne(silu_f32(tg * Gs[r]) * (tu * Us[r]));
+    unsigned long long* dst = cx.hw + ((size_t)(r0 + col) * a.f + fg * kGUFeat + half * 16 + 4 * grp) / 2;
+    __hip_atomic_store(dst, h_word(hb[0], hb[1], cx.tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(dst + 1, h_word(hb[2], hb[3], cx.tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, uint32_t tag, uint32_t steal_after,
+                                                                    uint32_t give_up) {
   extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
   __shared__ int s_tok[kDecMaxAssign];
   __shared__ int s_e[kDecMaxTouched], s_r0[kDecMaxTouched], s_n[kDecMaxTouched];
   __shared__ int s_U, s_timeout;
+  __shared__ uint32_t s_missing;   // a down item's H slices still missing (bit g: slice g)
+  __shared__ int s_def[kDecMaxDeferred];  // down items left for the end (their H not all there)
   unsigned char* const s_scr = s_dyn + dec_row_region(a.T, a.d, a.f);
   unsigned char* const s_sc = s_scr + kDecWaves * kScrWave;  // a gate/up item's block scales
   int* s_off = reinterpret_cast<int*>(s_scr);
@@ -127,19 +403,23 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
   // block's gate/up items), the touched experts and the token of every routed row: one
   // round trip
   const __amdgpu_buffer_rsrc_t xrs = dec_rsrc(a.x, (uint32_t)(a.T * a.d * 2));
-  {
-    // waves 0-3 load the routing inputs (or route the tokens: a 16-lane row a token) and
-    // waves 4-7 issue these copies, so that the loads the prologue waits on do not queue
-    // behind them (a wave's loads complete in order)
+  // the activation rows by buffer->LDS DMA, issued by waves first_wave.. (a 1 KB copy
+  // an instruction); the caller waits for them
+  auto copy_x_rows = [&](int first_wave) {
     const int xs = dec_xstride(a.d), ipr = (a.d * 2 + 1023) / 1024;  // 1 KB DMA instructions a row
-    for (int qi = wave - kDecWaves / 2; qi < a.T * ipr; qi += kDecWaves / 2) {
+    const int nw = kDecWaves - first_wave;
+    for (int qi = wave - first_wave; qi < a.T * ipr; qi += nw) {
       if (qi < 0) break;
       const int r = qi / ipr, jj = qi - r * ipr;
       const int within = jj * 1024 + lane * 16;
       const uint32_t voff = within < a.d * 2 ? (uint32_t)r * (uint32_t)(a.d * 2) + within : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void_ptr)(s_dyn + r * xs + jj * 1024), 16, voff, 0, 0, 0);
     }
-  }
+  };
+  // waves 0-3 load the routing inputs (or route the tokens: a 16-lane row a token) and
+  // waves 4-7 issue these copies, so that the loads the prologue waits on do not queue
+  // behind them (a wave's loads complete in order)
+  copy_x_rows(kDecWaves / 2);
   const int nA = a.T * a.k;
   if (a.logits) {
     // Route the tokens here (every block, redundantly: T <= 16 tokens of E <= 256 logits):
@@ -264,167 +544,9 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
   int j = G - 1 - (int)blockIdx.x;
 
   // ---- gate / up / SwiGLU items
-  const int nchG = a.d / 128;
-  const int half = wave >> 2, kq = wave & 3;  // 16-feature half of the item, quarter of K
-  const int kc0 = nchG * kq / 4, kc1 = nchG * (kq + 1) / 4;
-  const bool gtail = kq == 3;
-  const int xstride = dec_xstride(a.d);
-  constexpr int kB = 4;                     // chunks a wave loads at once
+  const GateUpCtx gcx = {s_dyn, s_scr, s_sc, s_tok, s_e, s_r0, s_n, hw, tag};
   auto gu_item = [&](int i, bool last) {
-    const int u = i / nfg, fg = i - u * nfg;
-    const int e = s_e[u], r0 = s_r0[u], ne = s_n[u];
-    // weight rows through buffer descriptors (expert slab base in scalar registers,
-    // a 32-bit row offset per lane)
-    const size_t slab = (size_t)a.f * (a.d / 2), sslab = (size_t)a.f * (a.d / 16);
-    const __amdgpu_buffer_rsrc_t qrs[2] = {dec_rsrc(a.gate_q + (size_t)e * slab, (uint32_t)slab),
-                                           dec_rsrc(a.up_q + (size_t)e * slab, (uint32_t)slab)};
-    const __amdgpu_buffer_rsrc_t srs[2] = {dec_rsrc(a.gate_s + (size_t)e * sslab, (uint32_t)sslab),
-                                           dec_rsrc(a.up_s + (size_t)e * sslab, (uint32_t)sslab)};
-    // MFMA layout: lane (grp, col) works on weight row `frow` of the item
-    const uint32_t frow = (uint32_t)(fg * kGUFeat + half * 16 + col);
-    // the item's scales in LDS: [gate / up][32 rows][d / 16 bytes]
-    const int srow = a.d / 16, sbytes = kGUFeat * srow;
-    const unsigned char* const my_sc = s_sc + (half * 16 + col) * srow;
-    // Code loads run along the rows instead: a load covers a pair of chunks (128 bytes,
-    // one cache line) of 8 rows -- lane group grp8 = lane / 8 takes row 8i + grp8 and
-    // lane lane % 8 its 16-byte segment -- rather than 64 bytes of 16 rows. The wave
-    // rearranges each pair into the MFMA layout through its LDS scratch.
-    const int grp8 = lane >> 3, seg8 = lane & 7;
-    const uint32_t qoff = (uint32_t)(fg * kGUFeat + half * 16 + grp8) * (uint32_t)(a.d / 2);
-    unsigned char* const scr = s_scr + wave * kScrWave;
-    floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    u32x4 lq[2][2][2];  // [pair][gate / up][rows 0-7 / 8-15], as loaded
-    // A batch always issues kB chunks of loads (a chunk past the wave's range repeats
-    // chunk c), so the number of loads in flight is a constant and every wait below is
-    // exact. Per pair: gate codes, then up.
-    auto load_batch = [&](int c) {
-#pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        const int lc = c + 2 * pr + (seg8 >> 2) < kc1 ? c + 2 * pr + (seg8 >> 2) : c;  // this lane's chunk
-        const int lb = (int)qoff + lc * 64 + 16 * (seg8 & 3);
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(qrs[m], lb, i * 8 * (a.d / 2), kWeightAux);
-            lq[pr][m][i] = u32x4{v.x, v.y, v.z, v.w};
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    // the item's scales (32 whole scale rows of gate and of up, contiguous in memory)
-    // and the activation rows of expert u by DMA first, then the first batch of
-    // weights; waiting for all but the weight loads leaves those in flight, and each
-    // pair of chunks is decoded as soon as its own loads have landed
-    for (int qi = (int)threadIdx.x; qi < 2 * sbytes / 16; qi += kDecThreads) {
-      const int m = qi >= sbytes / 16;
-      const uint32_t off = (uint32_t)(fg * kGUFeat) * (uint32_t)srow + (uint32_t)(qi * 16 - m * sbytes);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs[m], (lds_void_ptr)(s_sc + (qi - lane) * 16), 16, off, 0, 0, kWeightAux);
-    }
-    load_batch(kc0);
-    wait_vm<8>();  // the scale DMA has landed; the batch's 8 code loads may still be in flight
-    // a bare barrier: __syncthreads() would also wait for the weight loads
-    lds_barrier();
-    const bool valid = col < ne;
-    // Lanes of routed rows >= ne read whatever the LDS row holds: MFMA output column j
-    // depends only on operand column j, and those columns are never stored.
-    // the activation row of routed row col (rows >= ne: the expert's last row's token)
-    const unsigned char* xrow = s_dyn + s_tok[r0 + min(col, ne - 1)] * xstride;
-    auto xop = [&](int k0) -> bf16x8 { return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4v*>(xrow + k0 * 2)); };
-    // Rearrange a pair: piece (row r, 16-byte segment s) of matrix m sits at
-    // m * 2048 + r * 128 + ((s + r / 2) mod 8) * 16 in the wave's scratch, so the stores
-    // (two rows per 16 lanes) and the loads (a segment of 16 rows per 16 lanes) each hit
-    // 16 distinct 16-byte bank groups. LDS operations of one wave complete in order.
-    auto compute_pair = [&](int c, int pr) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int r = 8 * i + grp8;
-          *reinterpret_cast<u32x4v*>(scr + m * 2048 + r * 128 + ((seg8 + (r >> 1)) & 7) * 16) =
-              u32x4v{lq[pr][m][i].x, lq[pr][m][i].y, lq[pr][m][i].z, lq[pr][m][i].w};
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-      u32x4 q[2][2];  // [gate / up][chunk of the pair], MFMA layout
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          // chunk j of the pair, row col: segments 4j .. 4j + 3, lane group grp takes 4j + grp
-          const u32x4v v =
-              *reinterpret_cast<const u32x4v*>(scr + m * 2048 + col * 128 + ((4 * j + grp + (col >> 1)) & 7) * 16);
-          q[m][j] = u32x4{v.x, v.y, v.z, v.w};
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int h = 2 * pr + j;
-        if (c + h < kc1) {
-#pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            const uint32_t sc = *reinterpret_cast<const uint16_t*>(my_sc + m * sbytes + (c + h) * 8 + 2 * grp);
-            const E4M3Split s0 = e4m3_split_b<0>(sc);
-            const E4M3Split s1 = e4m3_split_b<1>(sc);
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-              acc[m] = mfma16(nvfp4x8_to_bf16(word_of(q[m][j], s), s < 2 ? s0 : s1),
-                                  xop((c + h) * 128 + 32 * grp + 8 * s), acc[m]);
-          }
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    auto compute_batch = [&](int c) {
-      compute_pair(c, 0);
-      compute_pair(c, 1);
-    };
-    // the first batch straight after its loads (a separate copy keeps the compiler's
-    // per-load waits exact), then any further batches
-    compute_batch(kc0);
-    for (int c = kc0 + kB; c < kc1; c += kB) {
-      load_batch(c);
-      compute_batch(c);
-    }
-    if (gtail) {
-      // 32-element chunks past the last full 128: lane group g holds K0 + 8g .. K0 + 8g + 7
-      for (int K0 = nchG * 128; K0 < a.d; K0 += 32) {
-        const bf16x8 xv = xop(K0 + 8 * grp);
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const uint32_t qq = __builtin_amdgcn_raw_buffer_load_b32(qrs[m], (int)(frow * (uint32_t)(a.d / 2) + 4 * grp),
-                                                                 K0 / 2, kWeightAux);
-          const uint32_t sv = my_sc[m * sbytes + K0 / 16 + (grp >> 1)];
-          acc[m] = mfma16(nvfp4x8_to_bf16(qq, e4m3_split(sv)), xv, acc[m]);
-        }
-      }
-    }
-    // partial sums through the waves' scratch: [wave][gate / up][lane]
-    floatx4* const red = reinterpret_cast<floatx4*>(s_scr);
-    constexpr int kRedWave = kScrWave / (int)sizeof(floatx4);
-    red[wave * kRedWave + lane] = acc[0];
-    red[wave * kRedWave + 64 + lane] = acc[1];
-    __syncthreads();
-    if (kq == 0) {
-      if (valid) {
-        floatx4 Gs = red[wave * kRedWave + lane], Us = red[wave * kRedWave + 64 + lane];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) {
-          Gs += red[(wave + w) * kRedWave + lane];
-          Us += red[(wave + w) * kRedWave + 64 + lane];
-        }
-        const float tg = a.gate_ts[e], tu = a.up_ts[e];
-        uint32_t hb[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hb[r] = bf16_rne(silu_f32(tg * Gs[r]) * (tu * Us[r]));
-        // lane holds routed row `col`, features 4*grp .. 4*grp + 3 of the half
-        unsigned long long* dst = hw + ((size_t)(r0 + col) * a.f + fg * kGUFeat + half * 16 + 4 * grp) / 2;
-        __hip_atomic_store(dst, h_word(hb[0], hb[1], tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(dst + 1, h_word(hb[2], hb[3], tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
+    gate_up_item(a, gcx, i);
     if (last && j < nD) prefetch(j);
     __syncthreads();
   };
@@ -442,31 +564,50 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
   // ---- down items
   const int hstride = a.f + 8;
   uint16_t* s_h = reinterpret_cast<uint16_t*>(s_dyn);
-  bool first = true;
-  for (; j < nD; j += G) {
-    if (!first) prefetch(j);
-    first = false;
+  const int nsl = a.f / 32;  // 32-feature slices of H = gate/up items an expert (slice g is item u * nfg + g)
+  // Probes: one word of each 32-feature slice of expert u's H rows (the last word the
+  // slice's gate/up item writes), polled up to `polls` times. missing_mask looks once at
+  // every probe of expert u and returns the slices still missing (bit g: slice g),
+  // block-uniform.
+  auto probe = [&](int r0, int r, int g, uint32_t polls) -> bool {
+    const unsigned long long* src = hw + ((size_t)(r0 + r) * a.f) / 2 + 16 * g + 15;
+    for (uint32_t it = 0;; ++it) {
+      const unsigned long long w0 = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((uint32_t)(w0 >> 32) == tag) return true;
+      if (it >= polls) return false;
+      __builtin_amdgcn_s_sleep(1);
+    }
+  };
+  auto missing_mask = [&](int u) -> uint32_t {
+    const int r0 = s_r0[u], ne = s_n[u];
+    if (threadIdx.x == 0) s_missing = 0;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < ne * nsl; idx += kDecThreads) {
+      const int r = idx / nsl, g = idx - r * nsl;
+      if (!probe(r0, r, g, 0)) atomicOr(&s_missing, 1u << g);  // LDS atomic
+    }
+    __syncthreads();
+    return s_missing;
+  };
+  // Down item j, its weights already in `pf`: H rows of its expert into LDS (bf16, row
+  // stride hstride) once every word carries this call's tag, then the products. With
+  // allow_defer, an item whose H slices are not all there after steal_after polls is
+  // left (returns true) for the block to finish after computing those slices itself.
+  auto down_item = [&](int j, bool allow_defer) -> bool {
     const int u = j / ndt;
     const int ct = (j - u * ndt) * kDecWaves + wave;
     const int e = s_e[u], r0 = s_r0[u], ne = s_n[u];
     // H rows of expert u -> LDS (bf16, row stride hstride), polling until every word
     // carries this call's tag
     const int npair = a.f / 4;  // pairs of H words (4 features) a row
+    // first wait on one word of each 32-feature slice of each row (the last word its
+    // gate/up item writes: 16x fewer device-scope loads while the producers finish, which
+    // eases the hot spot of many pollers on the same few KB); the full read below still
+    // validates every word
+    const bool may_defer = allow_defer && steal_after < give_up;
     {
-      // first wait on one word of each 32-feature slice of each row (one per gate/up
-      // item: 16x fewer device-scope loads while the producers finish, which eases the
-      // hot spot of many pollers on the same few KB); the full read below still
-      // validates every word. Each wait is bounded like the full poll.
-      const int nsl = a.f / 32;
-      for (int idx = threadIdx.x; idx < ne * nsl; idx += kDecThreads) {
-        const int r = idx / nsl, g = idx - r * nsl;
-        const unsigned long long* src = hw + ((size_t)(r0 + r) * a.f) / 2 + 16 * g + 15;
-        for (uint32_t it = 0; it < kSpinLimit; ++it) {
-          const unsigned long long w0 = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if ((uint32_t)(w0 >> 32) == tag) break;
-          __builtin_amdgcn_s_sleep(1);
-        }
-      }
+      const uint32_t polls = may_defer ? steal_after : give_up;
+      for (int idx = threadIdx.x; idx < ne * nsl; idx += kDecThreads) probe(r0, idx / nsl, idx % nsl, polls);
       __syncthreads();
     }
     for (uint32_t it = 0;; ++it) {
@@ -484,8 +625,13 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
         }
       }
       if (__syncthreads_or(bad) == 0) break;
-      if (it >= kSpinLimit) {
-        if (threadIdx.x == 0) s_timeout = 1;
+      // some producer has not written its slice yet: leave the item for later
+      if (may_defer && it >= steal_after) return true;
+      if (it >= give_up) {
+        if (threadIdx.x == 0) {
+          s_timeout = 1;
+          __hip_atomic_fetch_or(&g_async_status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         __syncthreads();
         break;
       }
@@ -561,32 +707,72 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
       }
     }
     __syncthreads();  // before the next item overwrites s_h
+    return false;
+  };
+  // The block's own down items (G - 1 - b, 2G - 1 - b, ...), then the ones it deferred.
+  // A deferred item's missing gate/up items are computed first (gate_up_item_plain: the
+  // same bits as their own blocks would give; a word written twice is written with the
+  // same value), on the activation rows copied into LDS again (H rows of down items
+  // replaced them); then the deferred items, whose waits now end. (Separate loops, and
+  // the plain item code: in one loop, or with the batched item code, the kernel spilled.)
+  int ndef = 0;  // deferred down items (their ids in s_def), block-uniform
+  bool first = true;
+  for (; j < nD; j += G) {
+    if (!first) prefetch(j);
+    first = false;
+    if (down_item(j, true)) {
+      if (threadIdx.x == 0) s_def[ndef] = j;
+      ++ndef;
+    }
+  }
+  if (ndef == 0) return;
+  __syncthreads();
+  for (int di = 0; di < ndef; ++di) {
+    const int u = s_def[di] / ndt;
+    const uint32_t missing = missing_mask(u);
+    if (missing != 0u) {
+      copy_x_rows(0);
+      __syncthreads();
+      for (int g = 0; g < nsl; ++g) {
+        if ((missing >> g) & 1u) {
+          gate_up_item_plain(a, gcx, u * nfg + g);
+          __syncthreads();
+        }
+      }
+    }
+  }
+  for (int di = 0; di < ndef; ++di) {
+    const int jd = s_def[di];
+    prefetch(jd);
+    down_item(jd, false);
   }
 }
 
 size_t ffn_decode_lds_bytes(int T, int d, int f) { return dec_row_region(T, d, f); }
 
-hipError_t launch_ffn_decode(const FFNArgs& a, uint32_t tag, hipStream_t stream) {
-  // co-resident blocks for this dynamic LDS size (cached per size)
-  static int cached_lds = -1, cached_capacity = 0;
+hipError_t launch_ffn_decode(const FFNArgs& a, uint32_t tag, uint32_t steal_after, uint32_t give_up,
+                             hipStream_t stream) {
   const int lds = (int)(dec_row_region(a.T, a.d, a.f) + (size_t)kDecWaves * kScrWave + (size_t)4 * a.d);
-  if (lds != cached_lds) {
-    int dev = 0, ncu = 0, per_cu = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err == hipSuccess) err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (err == hipSuccess)
-      err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&ffn_decode_kernel),
-                                                         kDecThreads, lds);
-    if (err != hipSuccess) return err;
-    if (ncu < 1 || per_cu < 1) return hipErrorInvalidConfiguration;
-    cached_capacity = ncu * per_cu;
-    cached_lds = lds;
-  }
+  // as many blocks as the device holds at once for this LDS size (so normally every
+  // block starts at once; the waits do not depend on it)
+  int capacity = 0;
+  hipError_t err = resident_blocks(reinterpret_cast<const void*>(&ffn_decode_kernel), kDecThreads, lds, capacity);
+  if (err != hipSuccess) return err;
   const long long touched = std::min<long long>(a.E, (long long)a.T * a.k);
-  const long long items = touched * std::max(a.f / kGUFeat, (a.d + kDCols - 1) / kDCols);
-  const int grid = (int)std::min<long long>(items, cached_capacity);
-  hipLaunchKernelGGL(ffn_decode_kernel, dim3(grid), dim3(kDecThreads), lds, stream, a, tag);
+  const long long down_items = touched * ((a.d + kDCols - 1) / kDCols);
+  const long long items = touched * std::max<long long>(a.f / kGUFeat, (a.d + kDCols - 1) / kDCols);
+  // no block may take more down items than it can defer
+  const long long grid_min = (down_items + kDecMaxDeferred - 1) / kDecMaxDeferred;
+  const int grid = (int)std::max<long long>(std::min<long long>(items, capacity), grid_min);
+  hipLaunchKernelGGL(ffn_decode_kernel, dim3(grid), dim3(kDecThreads), lds, stream, a, tag, steal_after, give_up);
   return hipGetLastError();
+}
+
+hipError_t read_and_clear_async_status(unsigned int& status) {
+  hipError_t err = hipMemcpyFromSymbol(&status, HIP_SYMBOL(g_async_status), sizeof(status), 0, hipMemcpyDeviceToHost);
+  if (err != hipSuccess || status == 0) return err;
+  const unsigned int zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_async_status), &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
 }
 
 }  // namespace moe

@@ -375,32 +375,18 @@ __global__ __launch_bounds__(kPromptThreads, 2) void ffn_prompt_kernel(FFNArgs a
   }
 }
 
-static int device_cu_count() {
-  int dev = 0, ncu = 256;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ncu = v;
-  }
-  return ncu;
-}
-
 hipError_t launch_ffn_prompt(const FFNArgs& a, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e0 = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_prompt_kernel<0>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, kPromptLdsBytes);
-    hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_prompt_kernel<1>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, kPromptLdsBytes);
-    if (e0 != hipSuccess) return e0;
-    if (e1 != hipSuccess) return e1;
-    attr_set = true;
-  }
+  hipError_t err = ensure_dynamic_lds(reinterpret_cast<const void*>(&ffn_prompt_kernel<0>), kPromptLdsBytes);
+  if (err == hipSuccess) err = ensure_dynamic_lds(reinterpret_cast<const void*>(&ffn_prompt_kernel<1>), kPromptLdsBytes);
+  if (err != hipSuccess) return err;
+  int ncu = 0;
+  err = device_cu_count(ncu);
+  if (err != hipSuccess) return err;
   const long long rows = (long long)a.T * a.k;
   const long long max_tiles = rows / kPromptRows + std::min<long long>(a.E, rows);
-  const int ncu = device_cu_count();
   const int ct_gu = (a.f + 127) / 128;
   const int grid_gu = (int)std::min<long long>(max_tiles * ct_gu, (long long)kPromptBlocksPerCu * ncu);
-  hipError_t err = launch_ffn_skinny_gateup(a, stream);
+  err = launch_ffn_skinny_gateup(a, stream);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(ffn_prompt_kernel<0>, dim3(grid_gu), dim3(kPromptThreads), kPromptLdsBytes, stream, a, ct_gu);
   err = hipGetLastError();

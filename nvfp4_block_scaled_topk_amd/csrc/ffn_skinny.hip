@@ -333,26 +333,19 @@ __global__ __launch_bounds__(kSkThreads) void ffn_skinny_down_kernel(FFNArgs a) 
   }
 }
 
-static int skinny_grid() {
-  static int grid = 0;
-  if (grid == 0) {
-    int dev = 0, ncu = 256;
-    if (hipGetDevice(&dev) == hipSuccess) {
-      int v = 0;
-      if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ncu = v;
-    }
-    grid = 8 * ncu;
-  }
-  return grid;
-}
-
 hipError_t launch_ffn_skinny_gateup(const FFNArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(ffn_skinny_gateup_kernel, dim3(skinny_grid()), dim3(kSkThreads), 0, stream, a);
+  int ncu = 0;
+  hipError_t err = device_cu_count(ncu);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(ffn_skinny_gateup_kernel, dim3(8 * ncu), dim3(kSkThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_ffn_skinny_down(const FFNArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(ffn_skinny_down_kernel, dim3(skinny_grid()), dim3(kSkThreads), 0, stream, a);
+  int ncu = 0;
+  hipError_t err = device_cu_count(ncu);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(ffn_skinny_down_kernel, dim3(8 * ncu), dim3(kSkThreads), 0, stream, a);
   return hipGetLastError();
 }
 

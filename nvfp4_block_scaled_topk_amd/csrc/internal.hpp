@@ -54,13 +54,26 @@ inline bool use_decode_path(int T, int d, int f) {
   return T <= kDecodeMaxRows && d <= kDecodeMaxD && f <= kDecodeMaxF &&
          ffn_decode_lds_bytes(T, d, f) <= kDecodeMaxLds;
 }
-hipError_t launch_ffn_decode(const FFNArgs& a, uint32_t tag, hipStream_t stream);
+// `steal_after`: polls of a missing H slice before a down item computes the missing
+// gate/up items itself; `give_up`: polls of the full H read before it writes NaN rows and
+// raises the asynchronous status flag (see ffn_decode.hip)
+hipError_t launch_ffn_decode(const FFNArgs& a, uint32_t tag, uint32_t steal_after, uint32_t give_up,
+                             hipStream_t stream);
+constexpr uint32_t kDefaultStealAfter = 256;
+constexpr uint32_t kDefaultGiveUp = 1u << 20;
+// the few-token launch's flag of a wait that gave up: read and cleared (synchronous)
+hipError_t read_and_clear_async_status(unsigned int& status);
 hipError_t launch_ffn_prompt(const FFNArgs& a, hipStream_t stream);
 // Prompt batches: experts with at most kSkinnyRows rows take the weight-streaming
 // kernels (ffn_skinny.hip); the grouped GEMM takes the others.
 constexpr int kSkinnyRows = 16;
 hipError_t launch_ffn_skinny_gateup(const FFNArgs& a, hipStream_t stream);
 hipError_t launch_ffn_skinny_down(const FFNArgs& a, hipStream_t stream);
+
+// device properties, cached per device (host_util.cpp; thread-safe)
+hipError_t device_cu_count(int& ncu);
+hipError_t resident_blocks(const void* kernel, int threads, int lds, int& blocks);
+hipError_t ensure_dynamic_lds(const void* kernel, int bytes);
 
 // combine
 hipError_t launch_combine(const float* y_rows, const int32_t* row_of, const float* w, int T,

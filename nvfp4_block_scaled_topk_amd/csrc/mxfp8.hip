@@ -416,16 +416,10 @@ hipError_t launch_mxfp8(const uint16_t* x, int M, int N, int K, const uint8_t* w
                        stream, x, M, N, K, w, s, y);
     return hipGetLastError();
   }
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mxfp8_gemm_kernel<true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes<true>());
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mxfp8_gemm_kernel<false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes<false>());
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&mxfp8_gemm_kernel<true>), gemm_lds_bytes<true>());
+  if (e == hipSuccess)
+    e = ensure_dynamic_lds(reinterpret_cast<const void*>(&mxfp8_gemm_kernel<false>), gemm_lds_bytes<false>());
+  if (e != hipSuccess) return e;
   const int mtiles = (M + kGM - 1) / kGM, ntiles = (N + kGN - 1) / kGN;
   if (K % 512 == 0 && K / 32 <= kGSRow)
     hipLaunchKernelGGL(mxfp8_gemm_kernel<true>, dim3(mtiles * ntiles), dim3(kGThreads), gemm_lds_bytes<true>(),

@@ -171,3 +171,13 @@ def test_route_ffn_refusals():
     assert call(w=A + 8) == ALIGN
     assert call(ws=None) == WS
 
+
+
+def test_wait_limits_round_trip():
+    """moe_set_wait_limits / moe_get_wait_limits (host state only, no GPU call)."""
+    L = M.lib()
+    prev = M.set_wait_limits(3, 7)
+    assert M.wait_limits() == (3, 7)
+    M.set_wait_limits(*prev)
+    assert M.wait_limits() == prev == (256, 1 << 20)
+    assert L.moe_status_string(7) == b"MOE_E_WAIT_EXPIRED"

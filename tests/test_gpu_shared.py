@@ -87,12 +87,12 @@ def test_shared_layer_small(T, d, f, E, k):
     check_band(band.classify(got, ref.out_bits, ref.mass, ref.slack), f"shared small T{T}d{d}f{f}E{E}k{k}")
 
 
-@pytest.mark.parametrize("name", ["prompt", "T40"])
+@pytest.mark.parametrize("name", ["prompt", "T40", "decode", "tiny"])
 def test_shared_side_stream_same_bits(name):
     """The shared expert on a side stream (joined by events) gives the same bits as on
-    the main stream. Prompt-path shapes only: the few-token path's single launch expects
-    every one of its workgroups to be resident at once, so its calls are not overlapped
-    with other work on a second stream."""
+    the main stream, on the prompt path and on the few-token path (whose single launch
+    then overlaps another few-token launch: its workgroups take work in ticket order, so
+    it does not need all of them resident at once)."""
     if name == "T40":
         inp = workloads.make_moe(40, 256, 128, 8, 2, seed=3, config_id=93, zipf=True)
         sh = workloads.make_shared(256, 128, seed=3, config_id=93)
