@@ -170,6 +170,25 @@ int moe_expert_ffn_nvfp4(const uint16_t* x, int T, int d, int f, int E, int k,
                          float* y_rows, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * moe_expert_ffn_nvfp4_scratch -- moe_expert_ffn_nvfp4 that allocates nothing and takes no
+ * workspace, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid it). H lives in a static device
+ * array of MOE_SCRATCH_BYTES that the library holds on every device it runs on for the
+ * life of the process. Arguments, results and refusals as moe_expert_ffn_nvfp4; a shape
+ * whose moe_expert_ffn_nvfp4_workspace exceeds MOE_SCRATCH_BYTES is refused with
+ * MOE_E_WORKSPACE (moe_last_error says how many bytes it needs). Every call on a device
+ * shares that device's array: calls that overlap on one device (different streams or
+ * host threads) race and must not be made; calls ordered on one stream are fine (the
+ * array keeps the last call's contents, which no call needs cleared). The first call on
+ * a device looks up the array's address (no allocation).
+ */
+#define MOE_SCRATCH_BYTES ((size_t)32 << 20)
+int moe_expert_ffn_nvfp4_scratch(const uint16_t* x, int T, int d, int f, int E, int k,
+                                 const moe_nvfp4_experts* w,
+                                 const int32_t* expert_offsets, const int32_t* sorted_rows,
+                                 float* y_rows, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * moe_route_expert_ffn_nvfp4 -- moe_route_topk (default policy, no bias) and
  * moe_expert_ffn_nvfp4 in one launch, for few tokens: the launch routes its tokens itself
  * (a whole batch routed in one run, "NVIDIA FP4-Local checkpoints on DGX Spark" page,

@@ -31,6 +31,7 @@ EXPORTED_SYMBOLS = (
     "moe_route_topk_workspace", "moe_route_topk", "moe_route_topk_policy", "moe_expert_ffn_nvfp4_workspace",
     "moe_expert_ffn_nvfp4", "moe_route_expert_ffn_nvfp4", "moe_combine", "moe_combine_shared", "mxfp8_gemm", "moe_router_logits", "moe_status_string",
     "moe_last_error", "moe_async_status", "moe_set_wait_limits", "moe_get_wait_limits",
+    "moe_expert_ffn_nvfp4_scratch",
 )
 
 
@@ -72,6 +73,9 @@ def lib() -> ctypes.CDLL:
     L.moe_expert_ffn_nvfp4.argtypes = [vp, i32, i32, i32, i32, i32, ctypes.POINTER(_Experts), vp, vp, vp,
                                        vp, sz, vp]
     L.moe_expert_ffn_nvfp4.restype = i32
+    L.moe_expert_ffn_nvfp4_scratch.argtypes = [vp, i32, i32, i32, i32, i32, ctypes.POINTER(_Experts), vp, vp, vp,
+                                               vp]
+    L.moe_expert_ffn_nvfp4_scratch.restype = i32
     L.moe_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
     L.moe_combine.restype = i32
     L.moe_route_expert_ffn_nvfp4.argtypes = [vp, vp, i32, i32, i32, i32, i32, ctypes.POINTER(_Experts),
@@ -264,6 +268,34 @@ def expert_ffn_nvfp4(x: torch.Tensor, experts: NVFP4Experts, offsets: torch.Tens
                                     _dev(out, torch.float32, "y_rows", (T * k, d)), workspace.data_ptr(),
                                     workspace.numel(), _stream(x))
     _check(st, "moe_expert_ffn_nvfp4")
+    return out
+
+
+# bytes of the static scratch behind expert_ffn_nvfp4_scratch (MOE_SCRATCH_BYTES)
+SCRATCH_BYTES = 32 << 20
+
+
+def expert_ffn_nvfp4_scratch(x: torch.Tensor, experts: NVFP4Experts, offsets: torch.Tensor,
+                             sorted_rows: torch.Tensor, k: int, out: torch.Tensor, check: bool = True):
+    """expert_ffn_nvfp4 through moe_expert_ffn_nvfp4_scratch: no workspace and no allocation
+    (the caller passes `out`, y_rows fp32 [T*k, d]); H lives in the library's static
+    scratch of SCRATCH_BYTES a device. Calls that overlap on one device race."""
+    if x.dtype in (torch.uint16, torch.int16):
+        x = x.view(torch.bfloat16)
+    T, d = x.shape
+    E, f = experts.E, experts.f
+    if experts.d != d:
+        raise ValueError(f"x has d={d}, experts have d={experts.d}")
+    if check:
+        experts.check()
+    ex = experts.c_struct()
+    st = lib().moe_expert_ffn_nvfp4_scratch(_dev(x, torch.bfloat16, "x"), T, d, f, E, k, ctypes.byref(ex),
+                                            _dev(offsets, torch.int32, "offsets", (E + 1,)),
+                                            _dev(sorted_rows, torch.int32, "sorted_rows", (T * k,)),
+                                            _dev(out, torch.float32, "y_rows", (T * k, d)), _stream(x))
+    if st == 4:
+        raise MoEError(st, "moe_expert_ffn_nvfp4_scratch", lib().moe_last_error().decode())
+    _check(st, "moe_expert_ffn_nvfp4_scratch")
     return out
 
 

@@ -7,6 +7,8 @@
 #include <atomic>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <random>
 
 #include "internal.hpp"
@@ -168,6 +170,61 @@ int moe_expert_ffn_nvfp4(const uint16_t* x, int T, int d, int f, int E, int k, c
   if (moe::use_decode_path(T, d, f))
     return launch_status(moe::launch_ffn_decode(a, next_call_tag(), g_steal_after.load(), g_give_up.load(), st));
   return launch_status(moe::launch_ffn_prompt(a, st));
+}
+
+}  // extern "C"
+
+namespace {
+
+// The scratch of moe_expert_ffn_nvfp4_scratch: H lives here instead of in a caller
+// workspace. One array per device (each device holds its own copy for the life of the
+// process); host code never uses the array's name as an address, only the device address
+// hipGetSymbolAddress gives for the current device, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[MOE_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;  // device -> address of its scratch
+
+hipError_t scratch_address(void*& ptr) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it != g_scratch_ptr.end()) {
+    ptr = it->second;
+    return hipSuccess;
+  }
+  void* p = nullptr;
+  err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (err != hipSuccess) return err;
+  if (p == nullptr) return hipErrorInvalidSymbol;
+  g_scratch_ptr[dev] = p;
+  ptr = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_expert_ffn_nvfp4_scratch(const uint16_t* x, int T, int d, int f, int E, int k, const moe_nvfp4_experts* w,
+                                 const int32_t* expert_offsets, const int32_t* sorted_rows, float* y_rows,
+                                 void* stream) {
+  const size_t need = moe_expert_ffn_nvfp4_workspace(T, d, f, E, k);
+  if (need > MOE_SCRATCH_BYTES) {
+    std::snprintf(g_last_error, sizeof(g_last_error),
+                  "moe_expert_ffn_nvfp4_scratch: H needs %zu bytes, the static scratch holds %zu", need,
+                  (size_t)MOE_SCRATCH_BYTES);
+    return MOE_E_WORKSPACE;
+  }
+  if (need == 0) return moe_expert_ffn_nvfp4(x, T, d, f, E, k, w, expert_offsets, sorted_rows, y_rows, nullptr, 0,
+                                             stream);  // a refused shape: named by the workspace entry point
+  void* ptr = nullptr;
+  const hipError_t err = scratch_address(ptr);
+  if (err != hipSuccess) return launch_status(err);
+  return moe_expert_ffn_nvfp4(x, T, d, f, E, k, w, expert_offsets, sorted_rows, y_rows, ptr, MOE_SCRATCH_BYTES,
+                              stream);
 }
 
 int moe_route_expert_ffn_nvfp4(const float* logits, const uint16_t* x, int T, int d, int f, int E, int k,

@@ -181,3 +181,19 @@ def test_wait_limits_round_trip():
     M.set_wait_limits(*prev)
     assert M.wait_limits() == prev == (256, 1 << 20)
     assert L.moe_status_string(7) == b"MOE_E_WAIT_EXPIRED"
+
+
+def test_no_alloc_entry_refuses_beyond_its_scratch():
+    """moe_expert_ffn_nvfp4_scratch refuses a shape whose H exceeds the static scratch
+    (the long-prompt configuration needs 128 MiB) before any HIP call, naming the sizes;
+    a refused shape is named as by the workspace entry point."""
+    L = M.lib()
+    ex = M._Experts(*([16] * 9))
+    fake = 256  # aligned, never dereferenced: the refusal comes first
+    st = L.moe_expert_ffn_nvfp4_scratch(fake, 4096, 7168, 2048, 256, 8, ctypes.byref(ex), fake, fake, fake, None)
+    assert M.STATUS_NAMES[st] == "MOE_E_WORKSPACE"
+    msg = L.moe_last_error().decode()
+    assert "static scratch holds 33554432" in msg and str(M.expert_ffn_workspace(4096, 7168, 2048, 256, 8)) in msg
+    assert M.expert_ffn_workspace(4096, 7168, 2048, 256, 8) > M.SCRATCH_BYTES
+    st = L.moe_expert_ffn_nvfp4_scratch(fake, 4, 48, 32, 8, 2, ctypes.byref(ex), fake, fake, fake, None)
+    assert M.STATUS_NAMES[st] == "MOE_E_SHAPE"
