@@ -23,10 +23,13 @@ Modules:
              dequantization, the expert FFN, the combine, slack terms.
   mxfp8    - the MXFP8 block-scaled projection.
   band     - the per-element acceptance rule (strict / explained / fail).
+  router   - the router projection and the routing policies.
+  shared   - the shared expert beside the routed ones and its gate.
+  block    - the block's output with the residual stream.
 
 Parity status: every function is pinned by the not-GPU tests (closed forms,
 brute force, library conversions, exact invariants). The end-to-end values at
 the large shapes rest on those pins plus the oracle's own consistency: the pages
 print no numeric example for this path.
 """
-from . import formats, moe, mxfp8, band  # noqa: F401
+from . import formats, moe, mxfp8, band, block  # noqa: F401

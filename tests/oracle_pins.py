@@ -18,7 +18,7 @@ import numpy as np
 
 import oracle
 from oracle import formats as F
-from oracle import band, moe, mxfp8, router, shared
+from oracle import band, block, moe, mxfp8, router, shared
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -1097,5 +1097,85 @@ def pin_masses_ignore_tensor_scale_signs():
     tg = float(np.float32(1 + 2.0 ** -8 - 20 * 2.0 ** -23))
     res = _one_row(_midpoint_expert(tg, tu=-1.0), {0: 64.0})
     assert bf16_bits_scalar(res.h_bits[0, 0]) == -4096.0 and res.slack_h[0, 0] == 32.0
+
+
+# ----------------------------------------------------------------------------- residual
+def pin_residual_zero_is_the_layer():
+    """A zero residual leaves the routed layer's bits (with and without the shared
+    expert); adding the residual only raises the mass, by |x|."""
+    import workloads
+    inp = _small_layer(seed=12)
+    base = moe.moe_layer(inp)
+    zero = np.zeros_like(inp.x)
+    r0 = block.add_residual(base, zero)
+    assert np.array_equal(r0.out_bits, base.out_bits) and np.array_equal(r0.mass, base.mass)
+    sh = workloads.make_shared(inp.d, inp.f, seed=12, config_id=80)
+    bs = shared.moe_layer_shared(inp, sh)
+    assert np.array_equal(block.add_residual(bs, zero).out_bits, bs.out_bits)
+    r1 = block.add_residual(base, inp.x)
+    assert np.array_equal(r1.mass - base.mass, np.abs(F.bf16_bits_to_f64(inp.x)))
+
+
+def pin_residual_closed_forms():
+    """All-zero expert codes: the block's output is the residual itself, bit for bit.
+    Identity experts (one expert, k = 1): out = bf16(x + bf16(silu(x) x)), each side exact
+    (by Fraction), rounded once."""
+    import workloads
+    inp = workloads.make_moe(5, 64, 32, 4, 2, seed=13, config_id=81)
+    for nm in ("gate_q", "up_q", "down_q"):
+        setattr(inp, nm, np.zeros_like(getattr(inp, nm)))
+    res = block.add_residual(moe.moe_layer(inp), inp.x)
+    assert np.array_equal(res.out_bits, inp.x)
+    d = 32
+    rng = np.random.default_rng(33)
+    T = 4
+    x = F.bf16_rne_bits(rng.standard_normal((T, d)) * 2)
+    ex = _identity_experts(d)
+    rl = moe.row_lists(np.zeros((T, 1), np.int32), 1)
+    ffn = moe.expert_ffn(x, T, d, d, 1, 1, ex, rl)
+    y, ob = moe.combine(ffn.y_rows, rl.row_of, np.ones((T, 1)), T, 1)
+    base = moe.MoEResult(None, None, rl, ffn, y, ob, ffn.mass_y, ffn.slack_h)
+    out = block.add_residual(base, x).out_bits
+    for t in range(T):
+        for i in range(d):
+            xv = bf16_bits_scalar(x[t, i])
+            sig = 1.0 / (1.0 + math.exp(-xv)) if xv >= 0 else math.exp(xv) / (1.0 + math.exp(xv))
+            h = frac_bf16_round(Fraction(xv * sig) * Fraction(xv))
+            assert Fraction(bf16_bits_scalar(out[t, i])) == frac_bf16_round(Fraction(xv) + h), (t, i)
+    # two scaled identity experts (k = 2, logits 1.0 and 0.5): the routed sum
+    # w0 H + w1 ts1 H is not a bfloat16 value; with the residual the output is
+    # bf16(x + w0 H + w1 ts1 H), one rounding of the exact sum
+    ex1 = _identity_experts(d)
+    ex2 = {nm: np.concatenate([v, v]) for nm, v in ex1.items()}
+    ts1 = np.float32(1.3)
+    ex2["down_ts"] = np.array([1.0, ts1], dtype=np.float32)
+    logits = np.tile(np.array([[1.0, 0.5]], dtype=np.float32), (T, 1))
+    ids, w = moe.route(logits, 2)
+    rl2 = moe.row_lists(ids, 2)
+    ffn2 = moe.expert_ffn(x, T, d, d, 2, 2, ex2, rl2)
+    y2, ob2 = moe.combine(ffn2.y_rows, rl2.row_of, w, T, 2)
+    base2 = moe.MoEResult(ids, w, rl2, ffn2, y2, ob2, np.zeros_like(y2), np.zeros_like(y2))
+    out2 = block.add_residual(base2, x).out_bits
+    w0 = 1.0 / (1.0 + math.exp(0.5 - 1.0))
+    for t in range(T):
+        for i in range(d):
+            xv = bf16_bits_scalar(x[t, i])
+            sig = 1.0 / (1.0 + math.exp(-xv)) if xv >= 0 else math.exp(xv) / (1.0 + math.exp(xv))
+            H = frac_bf16_round(Fraction(xv * sig) * Fraction(xv))
+            want = Fraction(xv) + Fraction(w0) * H + Fraction(1.0 - w0) * Fraction(float(ts1)) * H
+            got = Fraction(bf16_bits_scalar(out2[t, i]))
+            # the fp64 sum is within 2^-50 of `want`; a midpoint tie that close would be
+            # ambiguous, and none of these is
+            assert got == frac_bf16_round(want), (t, i)
+
+
+def pin_residual_sampled_tokens():
+    """The residual of sampled tokens is their own rows: the sampled path equals the whole
+    layer's rows for those tokens."""
+    inp = _small_layer(seed=14, T=9)
+    whole = block.add_residual(moe.moe_layer(inp), inp.x)
+    toks = [1, 4, 8]
+    part = block.add_residual(moe.moe_tokens(inp, toks), inp.x, toks)
+    assert np.array_equal(part.out_bits, whole.out_bits[toks])
 
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_") and callable(v)]

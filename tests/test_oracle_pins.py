@@ -109,6 +109,15 @@ MUTANTS = [
     ("mxfp8_block_16", "mxfp8.py",
      [("np.repeat(F.E8M0_TABLE[s], 32, axis=-1)", "np.repeat(F.E8M0_TABLE[s], 16, axis=-1)[..., : w.shape[-1]]")],
      ["pin_mxfp8_one_hot_and_scale", "pin_mxfp8_brute_force"]),
+    ("residual_added_twice", "block.py",
+     [("    y = res.y + x\n", "    y = res.y + 2 * x\n")],
+     ["pin_residual_closed_forms"]),
+    ("residual_rounded_first", "block.py",
+     [("    y = res.y + x\n", "    y = F.bf16_rne(res.y) + x\n")],
+     ["pin_residual_closed_forms"]),
+    ("residual_wrong_tokens", "block.py",
+     [("        x = x[np.asarray(tokens, dtype=np.int64)]\n", "        x = x[: len(tokens)]\n")],
+     ["pin_residual_sampled_tokens"]),
     # ---- the acceptance rule and its slack terms
     ("slack_h_x1024", "moe.py",
      [("sh = abs(td) * ((amb * ulp) @ aWd.T)", "sh = 1024 * abs(td) * ((amb * ulp) @ aWd.T)")],
@@ -205,6 +214,7 @@ def _exec_module(fname, edits, pkg_overrides):
 @pytest.mark.parametrize("name,fname,edits,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutant_is_caught(monkeypatch, name, fname, edits, pins):
     import oracle.band as bandreal
+    import oracle.block as blockreal
     import oracle.formats as Freal
     import oracle.moe as moereal
     import oracle.mxfp8 as mxreal
@@ -213,7 +223,8 @@ def test_mutant_is_caught(monkeypatch, name, fname, edits, pins):
     rtm = _exec_module("router.py", edits, {}) if fname == "router.py" else rtreal
     shm = _exec_module("shared.py", edits, {}) if fname == "shared.py" else shreal
     bandm = _exec_module("band.py", edits, {}) if fname == "band.py" else bandreal
-    if fname in ("router.py", "shared.py", "band.py"):
+    blockm = _exec_module("block.py", edits, {}) if fname == "block.py" else blockreal
+    if fname in ("router.py", "shared.py", "band.py", "block.py"):
         Fm, moem, mxm = Freal, moereal, mxreal
     elif fname == "formats.py":
         Fm = _exec_module("formats.py", edits, {})
@@ -233,6 +244,7 @@ def test_mutant_is_caught(monkeypatch, name, fname, edits, pins):
     monkeypatch.setattr(P, "router", rtm)
     monkeypatch.setattr(P, "shared", shm)
     monkeypatch.setattr(P, "band", bandm)
+    monkeypatch.setattr(P, "block", blockm)
     red = []
     for pn in pins:
         try:
