@@ -355,7 +355,7 @@ def bench_block(name, steps, warmup, timer, seed=0):
             M.expert_ffn_nvfp4(x, ex, off, srows, k, out=y_rows, workspace=fws, check=False)
         M.shared_expert_nvfp4(x, sx, out=s_rows, workspace=sws)
         M.router_logits(x, w_sg, out=glog)
-        M.combine(y_rows, rof, w, out=out, shared_rows=s_rows, shared_gate_logit=glog)
+        M.combine(y_rows, rof, w, out=out, shared_rows=s_rows, shared_gate_logit=glog, residual=x)
 
     for i in range(warmup):
         step(i)

@@ -14,7 +14,8 @@
  *                            scale per expert tensor (#489, #517, #545, #766);
  *   1+2. moe_route_expert_ffn_nvfp4  both in one launch for a few tokens;
  *   3. moe_combine           the router-weighted sum of each token's expert rows (#701);
- *                            moe_combine_shared adds a gated shared expert's rows (#686);
+ *                            moe_combine_shared adds a gated shared expert's rows (#686),
+ *                            moe_combine_residual also the block's residual stream;
  *   0. moe_router_logits     the router projection that produces the logits step 1 takes:
  *                            activations times the router matrix kept in its stored BF16
  *                            words, summed in fp32 (#732, #763);
@@ -227,6 +228,22 @@ int moe_combine(const float* y_rows, const int32_t* row_of, const float* topk_w,
 int moe_combine_shared(const float* y_rows, const int32_t* row_of, const float* topk_w,
                        int T, int k, int d, const float* shared_rows,
                        const float* shared_gate_logit, uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_combine_residual -- the block's output with its residual stream: the pages fold the
+ * adds that follow a producer into it ("NVIDIA FP4-Local checkpoints on DGX Spark" page,
+ * §4 remaining items; §4 Round 1, #701):
+ *   out[t][c] = bf16_rne( sum_j topk_w[t][j] * y_rows[row_of[t*k+j]][c]
+ *                         + g_t * shared_rows[t][c] + residual[t][c] ),
+ * the routed sum in j order, then the shared term (omitted when shared_rows is NULL; g_t as
+ * for moe_combine_shared), then the residual, in fp32, rounded once. residual bf16 [T][d]
+ * (the block's input activations). shared_gate_logit without shared_rows: MOE_E_NULL.
+ * Sizes and alignment as for moe_combine.
+ */
+int moe_combine_residual(const float* y_rows, const int32_t* row_of, const float* topk_w,
+                         int T, int k, int d, const float* shared_rows,
+                         const float* shared_gate_logit, const uint16_t* residual,
+                         uint16_t* out, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * moe_router_logits -- logits[t][e] = sum_i x[t][i] * w_r[e][i], fp32 accumulation

@@ -31,7 +31,7 @@ EXPORTED_SYMBOLS = (
     "moe_route_topk_workspace", "moe_route_topk", "moe_route_topk_policy", "moe_expert_ffn_nvfp4_workspace",
     "moe_expert_ffn_nvfp4", "moe_route_expert_ffn_nvfp4", "moe_combine", "moe_combine_shared", "mxfp8_gemm", "moe_router_logits", "moe_status_string",
     "moe_last_error", "moe_async_status", "moe_set_wait_limits", "moe_get_wait_limits",
-    "moe_expert_ffn_nvfp4_scratch",
+    "moe_expert_ffn_nvfp4_scratch", "moe_combine_residual",
 )
 
 
@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
     L.moe_route_expert_ffn_nvfp4.argtypes = [vp, vp, i32, i32, i32, i32, i32, ctypes.POINTER(_Experts),
                                              vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_route_expert_ffn_nvfp4.restype = i32
+    L.moe_combine_residual.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.moe_combine_residual.restype = i32
     L.moe_combine_shared.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]
     L.moe_combine_shared.restype = i32
     L.mxfp8_gemm.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
@@ -300,13 +302,28 @@ def expert_ffn_nvfp4_scratch(x: torch.Tensor, experts: NVFP4Experts, offsets: to
 
 
 def combine(y_rows: torch.Tensor, row_of: torch.Tensor, w: torch.Tensor, out=None,
-            shared_rows: torch.Tensor | None = None, shared_gate_logit: torch.Tensor | None = None):
+            shared_rows: torch.Tensor | None = None, shared_gate_logit: torch.Tensor | None = None,
+            residual: torch.Tensor | None = None):
     """out bf16 [T, d] = bf16_rne(sum_j w[t, j] * y_rows[row_of[t*k + j]] (+ g_t * shared_rows[t],
-    g_t = sigmoid(shared_gate_logit[t]) or 1))."""
+    g_t = sigmoid(shared_gate_logit[t]) or 1) (+ residual[t], bf16 [T, d]))."""
     T, k = w.shape
     d = y_rows.shape[1]
     if out is None:
         out = torch.empty((T, d), dtype=torch.bfloat16, device=y_rows.device)
+    if residual is not None:
+        if residual.dtype in (torch.uint16, torch.int16):
+            residual = residual.view(torch.bfloat16)
+        sp = _dev(shared_rows, torch.float32, "shared_rows", (T, d)) if shared_rows is not None else None
+        gp = None
+        if shared_gate_logit is not None:
+            gp = _dev(shared_gate_logit.reshape(T), torch.float32, "shared_gate_logit", (T,))
+        st = lib().moe_combine_residual(_dev(y_rows, torch.float32, "y_rows", (T * k, d)),
+                                        _dev(row_of, torch.int32, "row_of", (T * k,)),
+                                        _dev(w, torch.float32, "w", (T, k)), T, k, d, sp, gp,
+                                        _dev(residual, torch.bfloat16, "residual", (T, d)),
+                                        _dev(out, torch.bfloat16, "out", (T, d)), _stream(y_rows))
+        _check(st, "moe_combine_residual")
+        return out
     if shared_rows is not None:
         gp = None
         if shared_gate_logit is not None:

@@ -255,7 +255,8 @@ int moe_combine(const float* y_rows, const int32_t* row_of, const float* topk_w,
   if (T < 1 || k < 1 || k > 32 || d < 32 || d % 32 != 0 || (long long)T * k >= (1LL << 31)) return MOE_E_SHAPE;
   if (!aligned16(y_rows) || !aligned16(row_of) || !aligned16(topk_w) || !aligned16(out)) return MOE_E_ALIGN;
   return launch_status(
-      moe::launch_combine(y_rows, row_of, topk_w, T, k, d, nullptr, nullptr, out, static_cast<hipStream_t>(stream)));
+      moe::launch_combine(y_rows, row_of, topk_w, T, k, d, nullptr, nullptr, nullptr, out,
+                          static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine_shared(const float* y_rows, const int32_t* row_of, const float* topk_w, int T, int k, int d,
@@ -265,8 +266,21 @@ int moe_combine_shared(const float* y_rows, const int32_t* row_of, const float* 
   if (!aligned16(y_rows) || !aligned16(row_of) || !aligned16(topk_w) || !aligned16(shared_rows) ||
       (shared_gate_logit && !aligned16(shared_gate_logit)) || !aligned16(out))
     return MOE_E_ALIGN;
-  return launch_status(moe::launch_combine(y_rows, row_of, topk_w, T, k, d, shared_rows, shared_gate_logit, out,
-                                           static_cast<hipStream_t>(stream)));
+  return launch_status(moe::launch_combine(y_rows, row_of, topk_w, T, k, d, shared_rows, shared_gate_logit, nullptr,
+                                           out, static_cast<hipStream_t>(stream)));
+}
+
+int moe_combine_residual(const float* y_rows, const int32_t* row_of, const float* topk_w, int T, int k, int d,
+                         const float* shared_rows, const float* shared_gate_logit, const uint16_t* residual,
+                         uint16_t* out, void* stream) {
+  if (!y_rows || !row_of || !topk_w || !residual || !out) return MOE_E_NULL;
+  if (shared_gate_logit && !shared_rows) return MOE_E_NULL;
+  if (T < 1 || k < 1 || k > 32 || d < 32 || d % 32 != 0 || (long long)T * k >= (1LL << 31)) return MOE_E_SHAPE;
+  if (!aligned16(y_rows) || !aligned16(row_of) || !aligned16(topk_w) || (shared_rows && !aligned16(shared_rows)) ||
+      (shared_gate_logit && !aligned16(shared_gate_logit)) || !aligned16(residual) || !aligned16(out))
+    return MOE_E_ALIGN;
+  return launch_status(moe::launch_combine(y_rows, row_of, topk_w, T, k, d, shared_rows, shared_gate_logit, residual,
+                                           out, static_cast<hipStream_t>(stream)));
 }
 
 int moe_router_logits(const uint16_t* x, const uint16_t* w_r, int T, int d, int E, float* logits, void* stream) {

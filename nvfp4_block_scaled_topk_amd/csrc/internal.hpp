@@ -77,8 +77,8 @@ hipError_t ensure_dynamic_lds(const void* kernel, int bytes);
 
 // combine
 hipError_t launch_combine(const float* y_rows, const int32_t* row_of, const float* w, int T,
-                          int k, int d, const float* s_rows, const float* s_gate, uint16_t* out,
-                          hipStream_t stream);
+                          int k, int d, const float* s_rows, const float* s_gate, const uint16_t* resid,
+                          uint16_t* out, hipStream_t stream);
 
 // router projection
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_r, int T, int d, int E, float* logits,

@@ -197,3 +197,12 @@ def test_no_alloc_entry_refuses_beyond_its_scratch():
     assert M.expert_ffn_workspace(4096, 7168, 2048, 256, 8) > M.SCRATCH_BYTES
     st = L.moe_expert_ffn_nvfp4_scratch(fake, 4, 48, 32, 8, 2, ctypes.byref(ex), fake, fake, fake, None)
     assert M.STATUS_NAMES[st] == "MOE_E_SHAPE"
+
+
+def test_combine_residual_refusals():
+    L = M.lib()
+    p = 256
+    assert M.STATUS_NAMES[L.moe_combine_residual(p, p, p, 4, 2, 64, None, None, None, p, None)] == "MOE_E_NULL"
+    assert M.STATUS_NAMES[L.moe_combine_residual(p, p, p, 4, 2, 64, None, p, p, p, None)] == "MOE_E_NULL"
+    assert M.STATUS_NAMES[L.moe_combine_residual(p, p, p, 4, 2, 48, None, None, p, p, None)] == "MOE_E_SHAPE"
+    assert M.STATUS_NAMES[L.moe_combine_residual(p, p, p, 4, 2, 64, None, None, p + 8, p, None)] == "MOE_E_ALIGN"
