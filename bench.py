@@ -190,44 +190,82 @@ def bench_moe(name, steps, warmup, rotations, timer, seed=0):
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / steps
 
-    # the FFN inside the layer, in a separate loop with an event pair around every FFN
-    # call (the events add gaps to the layer, so this loop is not the timed region)
-    n_ev = min(steps, 50)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    # Per-step distribution: the same steps with an event between consecutive steps (the
+    # event records add small gaps, so this loop is not the timed region).
+    n_ev = min(steps, 100)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev + 1)]
     torch.cuda.synchronize()
     timer.queue_ahead(host_ms_per_step * n_ev * 1.5 + 20.0)
+    evs[0].record()
     for i in range(n_ev):
-        step(i, evs[i])
+        step(i)
+        evs[i + 1].record()
     torch.cuda.synchronize()
-    ffn_ms = [a.elapsed_time(b) for a, b in evs]
-    ffn_in_layer_ms = sum(ffn_ms) / len(ffn_ms)
+    step_us = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n_ev)])
+    p10, p50, p90 = (float(v) for v in np.percentile(step_us, [10, 50, 90]))
 
-    # The expert FFN alone, back to back (same routing, rotating weight copies), between
-    # one pair of events: its average duration per call, without per-call event overhead.
-    n_ffn = max(steps, 20)
-    a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    timer.queue_ahead(host_ms_per_step * n_ffn + 20.0)
-    a_ev.record()
-    for i in range(n_ffn):
-        M.expert_ffn_nvfp4(x, copies[i % rotations], off, srows, k, out=y_rows, workspace=fws, check=False)
-    b_ev.record()
-    torch.cuda.synchronize()
-    ffn_avg_ms = a_ev.elapsed_time(b_ev) / n_ffn
+    def back_to_back(call, n):
+        """Average duration of `call(i)` enqueued n times back to back between one pair of
+        events on the stream the kernels run on (torch's current stream)."""
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        timer.queue_ahead(host_ms_per_step * n + 20.0)
+        a_ev.record()
+        for i in range(n):
+            call(i)
+        b_ev.record()
+        torch.cuda.synchronize()
+        return a_ev.elapsed_time(b_ev) * 1e3 / n
+
+    n_b2b = max(steps, 50)
+    # the launch the layer runs for its expert FFN (with routing inside it for few tokens)
+    if fused:
+        launch_us = back_to_back(lambda i: M.route_expert_ffn_nvfp4(
+            logits, x, copies[i % rotations], k, route_out=rbufs, out=y_rows, workspace=fws, check=False), n_b2b)
+    else:
+        launch_us = back_to_back(lambda i: M.expert_ffn_nvfp4(
+            x, copies[i % rotations], off, srows, k, out=y_rows, workspace=fws, check=False), n_b2b)
+    # the expert FFN alone, routing lists given
+    ffn_us = back_to_back(lambda i: M.expert_ffn_nvfp4(
+        x, copies[i % rotations], off, srows, k, out=y_rows, workspace=fws, check=False), n_b2b)
 
     # algorithmic work (only what the method must move / compute)
     eb = expert_bytes(d, f)
+    counts = np.diff(off.cpu().numpy())
     ffn_bytes = U * eb + T * d * 2
+    launch_bytes = ffn_bytes + (T * E * 4 if fused else 0)
     layer_bytes = U * eb + T * d * 2 + T * E * 4 + T * d * 2
     flops = 2.0 * T * k * 3 * d * f
+
+    # Ceiling: a plain coalesced read (moe_read_ceiling) of the same bytes the expert
+    # kernels must read -- the touched experts' codes and scales, of the same rotating
+    # weight copies -- back to back.
+    touched = np.nonzero(counts > 0)[0]
+    names6 = ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")
+    tables = []
+    for c in copies:
+        rows = []
+        for nm in names6:
+            t = getattr(c, nm)
+            per = t[0].numel() * t.element_size()
+            for e in touched:
+                rows.append((t.data_ptr() + int(e) * per, per))
+        tables.append(torch.tensor(rows, dtype=torch.int64, device=dev))
+    read_bytes = sum(r[1] for r in rows)
+    sink = torch.zeros((4096,), dtype=torch.int32, device=dev)
+    ceiling_us = back_to_back(lambda i: M.read_ceiling(tables[i % rotations], read_bytes, sink), n_b2b)
+
     res = dict(
         name=name, T=T, d=d, f=f, E=E, k=k, touched_experts=U, rotations=rotations,
         ms_per_step=ms_per_step, tokens_per_s=T / (ms_per_step / 1e3),
-        ffn_avg_us=ffn_avg_ms * 1e3, ffn_in_layer_us=ffn_in_layer_ms * 1e3, ffn_min_in_layer_us=min(ffn_ms) * 1e3,
+        step_us_p10=p10, step_us_p50=p50, step_us_p90=p90,
+        launch_us=launch_us, launch_bytes=launch_bytes, ffn_avg_us=ffn_us,
         ffn_bytes=ffn_bytes, layer_bytes=layer_bytes, flops=flops,
+        ceiling_us=ceiling_us, ceiling_bytes=read_bytes, ceiling_gbps=read_bytes / (ceiling_us / 1e6) / 1e9,
         layer_hbm_gbps=layer_bytes / (ms_per_step / 1e3) / 1e9,
-        ffn_hbm_gbps=ffn_bytes / (ffn_avg_ms / 1e3) / 1e9,
-        ffn_tflops=flops / (ffn_avg_ms / 1e3) / 1e12,
+        launch_hbm_gbps=launch_bytes / (launch_us / 1e6) / 1e9,
+        ffn_hbm_gbps=ffn_bytes / (ffn_us / 1e6) / 1e9,
+        ffn_tflops=flops / (ffn_us / 1e6) / 1e12,
         layer_tflops=flops / (ms_per_step / 1e3) / 1e12,
         host_ms_per_step=host_ms_per_step, route_in_ffn_launch=fused,
     )
@@ -435,30 +473,91 @@ def bench_router(name, steps, warmup, timer, seed=0):
     return res
 
 
-def cpu_baseline(budget_s=12.0):
-    """The oracle (test infrastructure, untuned) on the host cores: whole decode
-    layers (route, dequantize, FFN, combine) on the same seeded input, repeated
-    until about `budget_s` of CPU time."""
+def host_cores():
+    """CPUs this process may run on, and how many physical cores they are (lscpu)."""
+    import subprocess
+    cpus = sorted(os.sched_getaffinity(0))
+    phys = None
+    try:
+        out = subprocess.run(["lscpu", "-p=CPU,CORE,SOCKET"], capture_output=True, text=True, timeout=10).stdout
+        cores = set()
+        for line in out.splitlines():
+            if line.startswith("#") or not line.strip():
+                continue
+            cpu, core, sock = (int(v) for v in line.split(",")[:3])
+            if cpu in cpus:
+                cores.add((sock, core))
+        phys = len(cores) or None
+    except Exception:  # lscpu missing: physical count unknown
+        phys = None
+    return len(cpus), phys
+
+
+def time_oracle(fn, threads, reps):
+    """Median wall-clock seconds of `fn` over `reps` runs with BLAS limited to `threads`."""
+    from threadpoolctl import threadpool_limits
+    ts = []
+    with threadpool_limits(limits=threads):
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+    ts.sort()
+    return ts[len(ts) // 2], ts
+
+
+def cpu_baseline():
+    """The oracle (test infrastructure, untuned) on the host cores: whole decode layers
+    (route, dequantize, FFN, combine) on the same seeded input as the GPU, median of 3
+    runs with BLAS on every CPU of the process's affinity set and on 1 thread."""
     import workloads
     from oracle import moe as omoe
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    logical, physical = host_cores()
     inp = workloads.moe_config("decode")
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        omoe.moe_layer(inp)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {"value": reps * inp.T / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} whole decode layers (T={inp.T}, d={inp.d}, f={inp.f}, E={inp.E}, k={inp.k}) "
-                      f"in {el:.1f} s; fp64 NumPy, BLAS matmuls on {threads} threads, the rest single-threaded"}
+    med_all, _ = time_oracle(lambda: omoe.moe_layer(inp), logical, 3)
+    med_one, _ = time_oracle(lambda: omoe.moe_layer(inp), 1, 3)
+    return {"value": inp.T / med_all, "unit": "tokens/s", "cores": logical, "kind": "oracle",
+            "physical_cores": physical, "one_thread_value": inp.T / med_one,
+            "sample": f"whole decode layers (T={inp.T}, d={inp.d}, f={inp.f}, E={inp.E}, k={inp.k}): median of 3 "
+                      f"runs, {med_all:.2f} s with BLAS on {logical} threads ({physical} physical cores), "
+                      f"{med_one:.2f} s on 1 thread; fp64 NumPy, elementwise work single-threaded"}
+
+
+def cpu_protocol(path):
+    """The oracle on every configuration (a report, not the bench line): tiny, decode,
+    prompt and the MXFP8 projection at M=1 and M=512 at 1 thread and all threads (median
+    of 3; prompt and M=512 once at 1 thread), the long prompt once at all threads."""
+    import workloads
+    from oracle import moe as omoe, mxfp8 as omx
+
+    logical, physical = host_cores()
+    rows = []
+
+    def run(name, unit_count, unit, fn, threads, reps):
+        log(f"[cpu] {name} threads={threads} reps={reps}")
+        med, ts = time_oracle(fn, threads, reps)
+        rows.append({"workload": name, "threads": threads, "runs": reps, "median_s": med, "all_s": ts,
+                     "value": unit_count / med, "unit": unit})
+
+    for name in ("tiny", "decode", "prompt"):
+        inp = workloads.moe_config(name)
+        for threads, reps in ((logical, 3), (1, 3 if name != "prompt" else 1)):
+            run(name, inp.T, "tokens/s", lambda inp=inp: omoe.moe_layer(inp), threads, reps)
+        del inp
+    for m in (1, 512):
+        inp = workloads.mxfp8_config(m)
+        for threads, reps in ((logical, 3), (1, 3 if m == 1 else 1)):
+            run(f"mxfp8_M{m}", m, "rows/s", lambda inp=inp: omx.mxfp8_gemm(inp.x, inp.w, inp.s), threads, reps)
+        del inp
+    inp = workloads.moe_config("long_prompt")
+    run("long_prompt", inp.T, "tokens/s", lambda: omoe.moe_layer(inp), logical, 1)
+    rep = {"logical_cpus": logical, "physical_cores": physical, "rows": rows,
+           "note": "fp64 NumPy oracle (test infrastructure, untuned); data generation excluded; BLAS threads "
+                   "limited with threadpoolctl"}
+    with open(path, "w") as fh:
+        json.dump(rep, fh, indent=1)
+    log(f"[cpu] wrote {path}")
 
 
 def main(argv=None):
@@ -474,7 +573,13 @@ def main(argv=None):
     ap.add_argument("--no-also", action="store_true", help="skip the prompt, long-prompt and MXFP8 measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--also-steps", type=int, default=20)
+    ap.add_argument("--cpu-protocol", default="",
+                    help="only time the CPU oracle on every configuration and write this JSON file")
     args = ap.parse_args(argv)
+
+    if args.cpu_protocol:
+        cpu_protocol(args.cpu_protocol)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU sharding is a design "
@@ -574,20 +679,30 @@ def main(argv=None):
         also["block_decode"] = bench_block("decode", max(args.also_steps, 50), 5, timer)
 
     decode_like = main_res["T"] <= 16
+    r = main_res
     if decode_like:
         files = DECODE_FILES
-        roof = {"bound": "hbm", "achieved": main_res["ffn_hbm_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": main_res["ffn_hbm_gbps"] / HBM_PEAK_GBPS, "traffic": load_traffic(args.workload, files),
-                "kernel": "moe_expert_ffn_nvfp4 decode (ffn_decode_kernel: gate/up/SwiGLU and down in one launch)",
-                "algorithmic_bytes": main_res["ffn_bytes"], "avg_us": main_res["ffn_avg_us"],
-                "avg_us_in_layer": main_res["ffn_in_layer_us"]}
+        roof = {"bound": "hbm", "achieved": r["launch_hbm_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": r["launch_hbm_gbps"] / HBM_PEAK_GBPS, "traffic": load_traffic(args.workload, files),
+                "kernel": ("ffn_decode_kernel as moe_route_expert_ffn_nvfp4 runs it (routing and the whole expert FFN "
+                           "in one launch: the launch each layer step runs)" if r["route_in_ffn_launch"] else
+                           "ffn_decode_kernel (moe_expert_ffn_nvfp4)"),
+                "algorithmic_bytes": r["launch_bytes"], "avg_us": r["launch_us"],
+                "layer_us": r["ms_per_step"] * 1e3, "layer_frac": r["layer_hbm_gbps"] / HBM_PEAK_GBPS,
+                "ffn_alone_us": r["ffn_avg_us"], "ffn_alone_frac": r["ffn_hbm_gbps"] / HBM_PEAK_GBPS,
+                "ceiling": {"kernel": "read_ranges_kernel (moe_read_ceiling: a plain coalesced read of the touched "
+                                      "experts' codes and scales, same weight rotation, nothing else)",
+                            "bytes": r["ceiling_bytes"], "avg_us": r["ceiling_us"], "gbps": r["ceiling_gbps"],
+                            "frac_of_peak": r["ceiling_gbps"] / HBM_PEAK_GBPS,
+                            "launch_frac_of_ceiling": r["launch_hbm_gbps"] / r["ceiling_gbps"]}}
     else:
         files = PROMPT_FILES
-        roof = {"bound": "mfma", "achieved": main_res["ffn_tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": main_res["ffn_tflops"] / BF16_PEAK_TFLOPS, "traffic": load_traffic(args.workload, files),
-                "kernel": PROMPT_KERNELS,
-                "algorithmic_flop": main_res["flops"], "avg_us": main_res["ffn_avg_us"],
-                "avg_us_in_layer": main_res["ffn_in_layer_us"]}
+        roof = {"bound": "mfma", "achieved": r["ffn_tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": r["ffn_tflops"] / BF16_PEAK_TFLOPS, "traffic": load_traffic(args.workload, files),
+                "kernel": PROMPT_KERNELS, "algorithmic_flop": r["flops"], "avg_us": r["ffn_avg_us"],
+                "layer_us": r["ms_per_step"] * 1e3,
+                "ceiling": {"kernel": "read_ranges_kernel (moe_read_ceiling: the touched experts' bytes)",
+                            "bytes": r["ceiling_bytes"], "avg_us": r["ceiling_us"], "gbps": r["ceiling_gbps"]}}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -615,6 +730,8 @@ def main(argv=None):
                    "layer_hbm_gbps": main_res["layer_hbm_gbps"]},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "step_us": {"p10": r["step_us_p10"], "p50": r["step_us_p50"], "p90": r["step_us_p90"],
+                    "note": "per-step durations from a second loop with an event between steps"},
     }
     if also:
         line["also"] = also

@@ -291,6 +291,19 @@ int moe_async_status(void* stream);
 void moe_set_wait_limits(uint32_t steal_after, uint32_t give_up);
 void moe_get_wait_limits(uint32_t* steal_after, uint32_t* give_up);
 
+/* ---------------------------------------------------------------------------------
+ * moe_read_ceiling -- a measurement helper, not a step of the layer: reads the given byte
+ * ranges once with plain coalesced 16-byte loads (the expert kernels' non-temporal hint)
+ * and nothing else, so that a benchmark can report the expert kernels against the rate
+ * this part reads the same bytes at (the pages measure against a baseline, "NVIDIA
+ * FP4-Local checkpoints on DGX Spark" page, §3 How results are measured).
+ * ranges: device memory, n pairs (device address, byte count), each a multiple of 16 and
+ * 16-byte aligned, total_bytes their sum; 1 <= n <= 1024. sink: device uint32 [sink_words]
+ * (one word a workgroup; at most sink_words workgroups). Contents of sink: unspecified.
+ */
+int moe_read_ceiling(const uint64_t* ranges, int n, uint64_t total_bytes, uint32_t* sink, int sink_words,
+                     void* stream);
+
 /* Name of a status code ("MOE_OK", "MOE_E_SHAPE", ...); never NULL. */
 const char* moe_status_string(int status);
 /* Text of the last HIP error seen by a call on this thread ("" if none). */

@@ -31,7 +31,7 @@ EXPORTED_SYMBOLS = (
     "moe_route_topk_workspace", "moe_route_topk", "moe_route_topk_policy", "moe_expert_ffn_nvfp4_workspace",
     "moe_expert_ffn_nvfp4", "moe_route_expert_ffn_nvfp4", "moe_combine", "moe_combine_shared", "mxfp8_gemm", "moe_router_logits", "moe_status_string",
     "moe_last_error", "moe_async_status", "moe_set_wait_limits", "moe_get_wait_limits",
-    "moe_expert_ffn_nvfp4_scratch", "moe_combine_residual",
+    "moe_expert_ffn_nvfp4_scratch", "moe_combine_residual", "moe_read_ceiling",
 )
 
 
@@ -95,6 +95,8 @@ def lib() -> ctypes.CDLL:
     L.moe_set_wait_limits.restype = None
     L.moe_get_wait_limits.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32)]
     L.moe_get_wait_limits.restype = None
+    L.moe_read_ceiling.argtypes = [vp, i32, ctypes.c_uint64, vp, i32, vp]
+    L.moe_read_ceiling.restype = i32
     L.moe_status_string.argtypes = [i32]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_last_error.argtypes = []
@@ -204,6 +206,15 @@ class NVFP4Experts:
             return torch.from_numpy(a).to(device)
         return cls(*[t(getattr(inp, n)) for n in
                      ("gate_q", "gate_s", "gate_ts", "up_q", "up_s", "up_ts", "down_q", "down_s", "down_ts")])
+
+
+def read_ceiling(ranges: torch.Tensor, total_bytes: int, sink: torch.Tensor):
+    """A plain streaming read of byte ranges (a measurement helper): `ranges` int64 device
+    tensor [n, 2] of (address, bytes), `sink` int32 device tensor (one word a workgroup)."""
+    n = ranges.shape[0]
+    st = lib().moe_read_ceiling(_dev(ranges, torch.int64, "ranges", (n, 2)), n, int(total_bytes),
+                                _dev(sink, torch.int32, "sink"), sink.numel(), _stream(ranges))
+    _check(st, "moe_read_ceiling")
 
 
 def route_topk_workspace(T: int, E: int, k: int) -> int:

@@ -323,6 +323,21 @@ void moe_get_wait_limits(uint32_t* steal_after, uint32_t* give_up) {
   if (give_up) *give_up = g_give_up.load();
 }
 
+int moe_read_ceiling(const uint64_t* ranges, int n, uint64_t total_bytes, uint32_t* sink, int sink_words,
+                     void* stream) {
+  if (!ranges || !sink) return MOE_E_NULL;
+  if (n < 1 || n > moe::read_ranges_max() || total_bytes == 0 || sink_words < 1) return MOE_E_SHAPE;
+  if (!aligned16(ranges) || !aligned16(sink)) return MOE_E_ALIGN;
+  int ncu = 0;
+  hipError_t err = moe::device_cu_count(ncu);
+  if (err != hipSuccess) return launch_status(err);
+  const long long pieces = (long long)((total_bytes + moe::read_piece_bytes() - 1) / moe::read_piece_bytes());
+  const int blocks = (int)std::min<long long>(std::min<long long>(pieces, 16LL * ncu), sink_words);
+  return launch_status(moe::launch_read_ranges(reinterpret_cast<const unsigned long long*>(ranges), n,
+                                               (unsigned long long)total_bytes, sink, blocks,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "MOE_OK";

@@ -84,6 +84,12 @@ hipError_t launch_combine(const float* y_rows, const int32_t* row_of, const floa
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_r, int T, int d, int E, float* logits,
                                 hipStream_t stream);
 
+// a plain streaming read of byte ranges (measure.hip): the benchmark's ceiling
+int read_ranges_max();
+int read_piece_bytes();
+hipError_t launch_read_ranges(const unsigned long long* table, int n, unsigned long long total, uint32_t* sink,
+                              int blocks, hipStream_t stream);
+
 // MXFP8
 hipError_t launch_mxfp8(const uint16_t* x, int M, int N, int K, const uint8_t* w,
                         const uint8_t* s, uint16_t* y, hipStream_t stream);
