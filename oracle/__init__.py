@@ -26,10 +26,11 @@ Modules:
   router   - the router projection and the routing policies.
   shared   - the shared expert beside the routed ones and its gate.
   block    - the block's output with the residual stream.
+  w8a8     - MXFP8 activations (OCP MX conversion) and the W8A8 MXFP8 projection.
 
 Parity status: every function is pinned by the not-GPU tests (closed forms,
 brute force, library conversions, exact invariants). The end-to-end values at
 the large shapes rest on those pins plus the oracle's own consistency: the pages
 print no numeric example for this path.
 """
-from . import formats, moe, mxfp8, band, block  # noqa: F401
+from . import formats, moe, mxfp8, band, block, w8a8  # noqa: F401

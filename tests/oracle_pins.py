@@ -18,7 +18,7 @@ import numpy as np
 
 import oracle
 from oracle import formats as F
-from oracle import band, block, moe, mxfp8, router, shared
+from oracle import band, block, moe, mxfp8, router, shared, w8a8
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -1177,5 +1177,98 @@ def pin_residual_sampled_tokens():
     toks = [1, 4, 8]
     part = block.add_residual(moe.moe_tokens(inp, toks), inp.x, toks)
     assert np.array_equal(part.out_bits, whole.out_bits[toks])
+
+
+# ----------------------------------------------------------------------------- MXFP8 activations (W8A8)
+def pin_e4m3_rounding_vs_torch():
+    """Nearest-even E4M3 of in-range values equals torch's float8_e4m3fn conversion (a
+    library routine) on random values over every binade, on every midpoint between
+    neighbouring codes and just off them; beyond 448 the value saturates to 448 (torch
+    gives NaN there, as the specification also allows; the reading here saturates)."""
+    import torch
+    rng = np.random.default_rng(91)
+    pos = F.E4M3_TABLE[:127]
+    mids = (pos[:-1] + pos[1:]) / 2
+    vals = np.concatenate([rng.uniform(-448, 448, 4000), rng.standard_normal(4000) * 2.0 ** rng.integers(-12, 9, 4000),
+                           mids, -mids, mids * (1 + 2 ** -20), mids * (1 - 2 ** -20), [0.0, -0.0, 448.0, -448.0]])
+    vals = vals[np.abs(vals) <= 448].astype(np.float32).astype(np.float64)
+    lib = torch.from_numpy(vals.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ours = w8a8.e4m3_rne_sat(vals)
+    assert np.array_equal(ours, lib), int(np.sum(ours != lib))
+    for v in (448.5, 464.0, 470.0, 511.9, 1e30):
+        assert w8a8.e4m3_rne_sat(np.array([v, -v])).tolist() == [0x7E, 0xFE]
+
+
+def pin_mx_scale_rule():
+    """The block scale is 2^(floor(log2 max|v|) - 8): a block whose largest magnitude is
+    exactly 2^e gets the code e - 8 + 127 and that element becomes 256 (code 0x78); any
+    block's largest scaled element lies in [256, 448] (saturated above); an all-zero block
+    gets code 0 and zeros; the code clamps at 0 (the top of bf16's range needs no clamp at
+    254)."""
+    rng = np.random.default_rng(93)
+    for e in (-20, -3, 0, 1, 7, 20):
+        blk = rng.uniform(-1, 1, 32) * 2.0 ** (e - 1)
+        blk[5] = -(2.0 ** e)
+        xb = F.bf16_rne_bits(blk[None, :])
+        assert F.bf16_bits_to_f64(xb)[0, 5] == -(2.0 ** e)
+        q, s = w8a8.quantize_mx(xb)
+        assert int(s[0, 0]) == e - 8 + 127 and int(q[0, 5]) == 0xF8
+    x = F.bf16_rne_bits(rng.standard_normal((6, 256)) * 2.0 ** rng.integers(-30, 30, (6, 1)))
+    q, s = w8a8.quantize_mx(x)
+    vals = np.abs(F.E4M3_TABLE[q]).reshape(6, 8, 32).max(axis=2)
+    assert np.all((vals >= 256) & (vals <= 448))
+    q0, s0 = w8a8.quantize_mx(np.zeros((1, 32), np.uint16))
+    assert int(s0[0, 0]) == 0 and np.all(F.E4M3_TABLE[q0] == 0)
+    big = F.bf16_rne_bits(np.full((1, 32), 2.0 ** 127))         # bf16's top binade: code 127 + 119
+    assert int(w8a8.quantize_mx(big)[1][0, 0]) == 246
+    tiny = np.full((1, 32), 0x0001, np.uint16)                  # the smallest bf16 subnormal, 2^-133
+    qt, st = w8a8.quantize_mx(tiny)                             # 2^-141 clamps to code 0; 2^-133 / 2^-127 = 2^-6
+    assert int(st[0, 0]) == 0 and np.all(F.E4M3_TABLE[qt] == 2.0 ** -6)
+
+
+def pin_mx_quantization_error_bound():
+    """Dequantized MXFP8 activations are within half an E4M3 step of the input (relative
+    2^-4 for normal elements, absolute 2^-10 times the scale for subnormal ones, the
+    saturated element within 64 times the scale); quantizing values that are already
+    MXFP8 with a block maximum in [256, 448] times the scale returns their own codes."""
+    rng = np.random.default_rng(95)
+    x = F.bf16_rne_bits(rng.standard_normal((8, 512)) * 3)
+    q, s = w8a8.quantize_mx(x)
+    xv = F.bf16_bits_to_f64(x)
+    xh = w8a8.dequant_mx(q, s)
+    sc = np.repeat(F.E8M0_TABLE[s], 32, axis=-1)
+    bound = np.maximum(np.abs(xv) * 2.0 ** -4, sc * 2.0 ** -10)
+    sat = np.abs(xv) / sc > 448
+    assert np.all((np.abs(xh - xv) <= bound) | (sat & (np.abs(xh - xv) <= 64 * sc)))
+    codes = rng.integers(0, 0x7F, size=(4, 64)).astype(np.uint8) | (rng.integers(0, 2, (4, 64)).astype(np.uint8) << 7)
+    codes[:, 0] = 0x7A                                          # 320: each block's maximum
+    codes[:, 32] = 0x7C                                         # 384
+    codes[(codes & 0x7F) > 0x7A] &= 0x80 | 0x79                 # others below 320
+    codes[:, 0], codes[:, 32] = 0x7A, 0x7C
+    sc = np.array([[120, 131]] * 4, dtype=np.uint8)
+    xb = F.bf16_rne_bits(w8a8.dequant_mx(codes, sc))
+    q2, s2 = w8a8.quantize_mx(xb)
+    assert np.array_equal(s2, sc)
+    same = (q2 == codes) | ((q2 & 0x7F) == 0) & ((codes & 0x7F) == 0)
+    assert np.all(same)
+
+
+def pin_w8a8_brute_force():
+    """The W8A8 projection on a tiny case against exact rationals over the dequantized
+    operands (each decoded by its own rule)."""
+    rng = np.random.default_rng(97)
+    M, N, K = 2, 3, 64
+    x = F.bf16_rne_bits(rng.standard_normal((M, K)))
+    xq, xs = w8a8.quantize_mx(x)
+    j = rng.integers(0, 254, size=(N, K))
+    w = np.where(j < 127, j, j + 1).astype(np.uint8)
+    s = rng.integers(121, 130, size=(N, K // 32), dtype=np.uint8)
+    y, ob, mass = w8a8.mxfp8_gemm_mx(xq, xs, w, s)
+    for m in range(M):
+        for n in range(N):
+            terms = [scalar_e4m3(int(xq[m, i])) * Fraction(2) ** (int(xs[m, i // 32]) - 127)
+                     * scalar_e4m3(int(w[n, i])) * Fraction(2) ** (int(s[n, i // 32]) - 127) for i in range(K)]
+            assert Fraction(bf16_bits_scalar(ob[m, n])) == frac_bf16_round(sum(terms))
+            assert abs(Fraction(mass[m, n]) - sum(abs(t) for t in terms)) <= sum(abs(t) for t in terms) * Fraction(1, 2 ** 48)
 
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_") and callable(v)]

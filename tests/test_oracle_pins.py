@@ -118,6 +118,19 @@ MUTANTS = [
     ("residual_wrong_tokens", "block.py",
      [("        x = x[np.asarray(tokens, dtype=np.int64)]\n", "        x = x[: len(tokens)]\n")],
      ["pin_residual_sampled_tokens"]),
+    ("e4m3_ties_away", "w8a8.py",
+     [("pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))", "pick_hi = (dhi <= dlo)")],
+     ["pin_e4m3_rounding_vs_torch"]),
+    ("mx_emax_7", "w8a8.py",
+     [("E4M3_EMAX = 8 ", "E4M3_EMAX = 7 ")],
+     ["pin_mx_scale_rule"]),
+    ("mx_overflow_to_nan", "w8a8.py",
+     [("    code = np.where(a == _POS_VALUES[hi], hi, code)           # exact values\n",
+       "    code = np.where(a == _POS_VALUES[hi], hi, code)\n    code = np.where(np.abs(v) > E4M3_MAX, 0x7F, code)\n")],
+     ["pin_e4m3_rounding_vs_torch", "pin_mx_scale_rule"]),
+    ("mx_scale_ceil", "w8a8.py",
+     [("shared = (e - 1) - E4M3_EMAX", "shared = e - E4M3_EMAX")],
+     ["pin_mx_scale_rule", "pin_mx_quantization_error_bound"]),
     # ---- the acceptance rule and its slack terms
     ("slack_h_x1024", "moe.py",
      [("sh = abs(td) * ((amb * ulp) @ aWd.T)", "sh = 1024 * abs(td) * ((amb * ulp) @ aWd.T)")],
@@ -215,6 +228,7 @@ def _exec_module(fname, edits, pkg_overrides):
 def test_mutant_is_caught(monkeypatch, name, fname, edits, pins):
     import oracle.band as bandreal
     import oracle.block as blockreal
+    import oracle.w8a8 as w8real
     import oracle.formats as Freal
     import oracle.moe as moereal
     import oracle.mxfp8 as mxreal
@@ -224,7 +238,8 @@ def test_mutant_is_caught(monkeypatch, name, fname, edits, pins):
     shm = _exec_module("shared.py", edits, {}) if fname == "shared.py" else shreal
     bandm = _exec_module("band.py", edits, {}) if fname == "band.py" else bandreal
     blockm = _exec_module("block.py", edits, {}) if fname == "block.py" else blockreal
-    if fname in ("router.py", "shared.py", "band.py", "block.py"):
+    w8m = _exec_module("w8a8.py", edits, {}) if fname == "w8a8.py" else w8real
+    if fname in ("router.py", "shared.py", "band.py", "block.py", "w8a8.py"):
         Fm, moem, mxm = Freal, moereal, mxreal
     elif fname == "formats.py":
         Fm = _exec_module("formats.py", edits, {})
@@ -245,6 +260,7 @@ def test_mutant_is_caught(monkeypatch, name, fname, edits, pins):
     monkeypatch.setattr(P, "shared", shm)
     monkeypatch.setattr(P, "band", bandm)
     monkeypatch.setattr(P, "block", blockm)
+    monkeypatch.setattr(P, "w8a8", w8m)
     red = []
     for pn in pins:
         try:
