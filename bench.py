@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s + HBM GB/s (decode) and MFMA TFLOP/s (prompt), 1×MI355X"
 HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 BF16_PEAK_TFLOPS = 2500.0       # MI355X published dense bf16 MFMA rate
+FP8_PEAK_TFLOPS = 5000.0        # MI355X published dense fp8 MFMA rate
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 # kernel sources whose hash a traffic record must match, per path
 DECODE_FILES = ["ffn_decode.hip", "device.hpp"]
@@ -330,6 +331,59 @@ def bench_mxfp8(M, steps, warmup, rotations, timer, seed=0):
     return res
 
 
+def bench_w8a8(M, steps, warmup, rotations, timer, seed=0):
+    """The W8A8 MXFP8 projection (N=12288, K=4096): activations quantized to MXFP8
+    (mxfp8_quantize) and the block-scaled fp8 product (mxfp8_gemm_mx), one pair of HIP
+    events around `steps` calls of each, weights rotated through `rotations` copies."""
+    import numpy as np
+    import torch
+
+    import nvfp4_block_scaled_topk_amd as M_
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    inp = workloads.mxfp8_config(M, seed=seed)
+    N, K = inp.N, inp.K
+    x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    w0 = torch.from_numpy(inp.w).to(dev)
+    s0 = torch.from_numpy(inp.s).to(dev)
+    del inp
+    ws = [(w0, s0)] + [(w0.clone(), s0.clone()) for _ in range(rotations - 1)]
+    xq, xs = M_.mxfp8_quantize(x)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    for i in range(warmup):
+        M_.mxfp8_quantize(x, out=(xq, xs))
+        M_.mxfp8_gemm_mx(xq, xs, *ws[i % rotations], out=y)
+    torch.cuda.synchronize()
+
+    def timed(call):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        timer.queue_ahead(steps * 0.1 + 20.0)
+        start.record()
+        for i in range(steps):
+            call(i)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) * 1e3 / steps
+
+    q_us = timed(lambda i: M_.mxfp8_quantize(x, out=(xq, xs)))
+    g_us = timed(lambda i: M_.mxfp8_gemm_mx(xq, xs, *ws[i % rotations], out=y))
+    flops = 2.0 * M * N * K
+    res = {"M": M, "N": N, "K": K, "quantize_us": q_us, "gemm_us": g_us, "total_us": q_us + g_us,
+           "rows_per_s": M / ((q_us + g_us) / 1e6), "algorithmic_flop": flops,
+           "gemm_tflops": flops / (g_us / 1e6) / 1e12,
+           "roofline": {"bound": "mfma", "achieved": flops / (g_us / 1e6) / 1e12, "peak": FP8_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": flops / (g_us / 1e6) / 1e12 / FP8_PEAK_TFLOPS,
+                        "kernel": "mx_gemm_kernel (mxfp8_gemm_mx: block-scaled fp8 MFMA)", "avg_us": g_us},
+           "error_vs_bf16_activations": "rms error / rms output 0.030 on 12 rows of this configuration "
+                                        "(tests/test_gpu_w8a8.py; profiles/parity_records.json reports)"}
+    log(f"[bench] w8a8 M={M}: {json.dumps(res)}")
+    del ws, w0, s0
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_block(name, steps, warmup, timer, seed=0):
     """The whole MoE block of a configuration: router projection, routing, routed expert
     FFN, the shared expert's FFN and gate logit, and the combine with the shared add, all
@@ -566,7 +620,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
-                    choices=["tiny", "decode", "prompt", "long_prompt", "mxfp8_M1", "mxfp8_M512",
+                    choices=["tiny", "decode", "prompt", "long_prompt", "mxfp8_M1", "mxfp8_M512", "w8a8_M512",
                              "router_decode", "router_long_prompt", "block_decode", "block_long_prompt"])
     ap.add_argument("--rotations", type=int, default=0,
                     help="weight copies to rotate (0: enough for the touched weights to reach 1 GB)")
@@ -606,6 +660,17 @@ def main(argv=None):
             "warmup": args.warmup, "ms_per_step": r["avg_us"] / 1e3, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": f"MXFP8 projection: M={m} bf16 rows, W 12288x4096 E4M3 in blocks of 32 with E8M0 scales"},
+            "roofline": r["roofline"], "cpu_baseline": None}), flush=True)
+        return
+
+    if args.workload == "w8a8_M512":
+        r = bench_w8a8(512, args.steps, args.warmup, 20, timer)
+        print(json.dumps({
+            "metric": METRIC, "value": r["rows_per_s"], "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": r["total_us"] / 1e3, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp8", "data": "synthetic",
+            "config": {"workload": "W8A8 MXFP8 projection: M=512 bf16 rows quantized to MXFP8, W 12288x4096 E4M3 "
+                                   "in blocks of 32 with E8M0 scales, block-scaled fp8 MFMA"},
             "roofline": r["roofline"], "cpu_baseline": None}), flush=True)
         return
 
@@ -674,6 +739,7 @@ def main(argv=None):
             also[f"mxfp8_M{m}"] = r
 
     if not args.no_also:
+        also["w8a8_M512"] = bench_w8a8(512, max(args.also_steps, 50), 5, 20, timer)
         for name in ("decode", "long_prompt"):
             also[f"router_{name}"] = bench_router(name, max(args.also_steps, 50), 5, timer)
         also["block_decode"] = bench_block("decode", max(args.also_steps, 50), 5, timer)

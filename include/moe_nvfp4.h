@@ -21,7 +21,8 @@
  *                            words, summed in fp32 (#732, #763);
  *   4. mxfp8_gemm            y = x . W^T for MXFP8 weights: E4M3 elements in blocks of 32
  *                            along K with one E8M0 scale a block, as a gemv (M = 1) and a
- *                            wide GEMM (#521).
+ *                            wide GEMM (#521); mxfp8_quantize + mxfp8_gemm_mx, the same
+ *                            product with MXFP8 activations (W8A8, #769).
  *
  * Conventions for every entry point
  *   - Every data pointer is a DEVICE pointer, allocated and owned by the caller; the
@@ -303,6 +304,30 @@ void moe_get_wait_limits(uint32_t* steal_after, uint32_t* give_up);
  */
 int moe_read_ceiling(const uint64_t* ranges, int n, uint64_t total_bytes, uint32_t* sink, int sink_words,
                      void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * mxfp8_quantize -- bf16 activations to MXFP8 (the W8A8 variant of the MXFP8 projection,
+ * "NVIDIA FP4-Local checkpoints on DGX Spark" page, §4 Round 1, #769), by the OCP MX v1.0
+ * conversion: per block of 32 along K, the E8M0 scale code is
+ * clamp(floor(log2 max|v|) - 8 + 127, 0, 254) (0 for an all-zero block) and each element
+ * is v / scale rounded to the nearest E4M3 value, ties to even, saturated to +-448 (the
+ * sign of zero kept).
+ * x bf16 [M][K] -> xq E4M3 [M][K], xs E8M0 [M][K/32]. Sizes: M >= 1, K a multiple of 32,
+ * M * K * 2 < 2^31. Unsafe contract: x finite.
+ */
+int mxfp8_quantize(const uint16_t* x, int M, int K, uint8_t* xq, uint8_t* xs, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * mxfp8_gemm_mx -- y[m][n] = bf16_rne( sum_i X[m][i] * W[n][i] ) with MXFP8 activations
+ * X = E4M3(xq) * 2^(xs - 127) (mxfp8_quantize) and MXFP8 weights as for mxfp8_gemm, both
+ * scales applied by gfx950's block-scaled matrix instruction, fp32 accumulation.
+ * xq [M][K], xs [M][K/32], w [N][K], s [N][K/32], y bf16 [M][N]. Sizes: M, N >= 1, K a
+ * multiple of 512, at most 4096; M * K and N * K < 2^31. The results differ from
+ * mxfp8_gemm's by the activation quantization (beyond the bf16 band); against the W8A8
+ * definition they are within it.
+ */
+int mxfp8_gemm_mx(const uint8_t* xq, const uint8_t* xs, int M, int N, int K,
+                  const uint8_t* w, const uint8_t* s, uint16_t* y, void* stream);
 
 /* Name of a status code ("MOE_OK", "MOE_E_SHAPE", ...); never NULL. */
 const char* moe_status_string(int status);

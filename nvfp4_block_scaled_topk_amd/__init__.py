@@ -31,7 +31,7 @@ EXPORTED_SYMBOLS = (
     "moe_route_topk_workspace", "moe_route_topk", "moe_route_topk_policy", "moe_expert_ffn_nvfp4_workspace",
     "moe_expert_ffn_nvfp4", "moe_route_expert_ffn_nvfp4", "moe_combine", "moe_combine_shared", "mxfp8_gemm", "moe_router_logits", "moe_status_string",
     "moe_last_error", "moe_async_status", "moe_set_wait_limits", "moe_get_wait_limits",
-    "moe_expert_ffn_nvfp4_scratch", "moe_combine_residual", "moe_read_ceiling",
+    "moe_expert_ffn_nvfp4_scratch", "moe_combine_residual", "moe_read_ceiling", "mxfp8_quantize", "mxfp8_gemm_mx",
 )
 
 
@@ -95,6 +95,10 @@ def lib() -> ctypes.CDLL:
     L.moe_set_wait_limits.restype = None
     L.moe_get_wait_limits.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32)]
     L.moe_get_wait_limits.restype = None
+    L.mxfp8_quantize.argtypes = [vp, i32, i32, vp, vp, vp]
+    L.mxfp8_quantize.restype = i32
+    L.mxfp8_gemm_mx.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp]
+    L.mxfp8_gemm_mx.restype = i32
     L.moe_read_ceiling.argtypes = [vp, i32, ctypes.c_uint64, vp, i32, vp]
     L.moe_read_ceiling.restype = i32
     L.moe_status_string.argtypes = [i32]
@@ -371,6 +375,35 @@ def mxfp8_gemm(x: torch.Tensor, w: torch.Tensor, s: torch.Tensor, out=None):
                           _dev(s, torch.uint8, "s", (N, K // 32)), _dev(out, torch.bfloat16, "y", (M, N)),
                           _stream(x))
     _check(st, "mxfp8_gemm")
+    return out
+
+
+def mxfp8_quantize(x: torch.Tensor, out=None):
+    """bf16 activations [M, K] -> (xq uint8 [M, K] E4M3 codes, xs uint8 [M, K/32] E8M0 scales),
+    the OCP MX conversion (W8A8 variant)."""
+    if x.dtype in (torch.uint16, torch.int16):
+        x = x.view(torch.bfloat16)
+    M, K = x.shape
+    if out is None:
+        out = (torch.empty((M, K), dtype=torch.uint8, device=x.device),
+               torch.empty((M, K // 32), dtype=torch.uint8, device=x.device))
+    xq, xs = out
+    st = lib().mxfp8_quantize(_dev(x, torch.bfloat16, "x"), M, K, _dev(xq, torch.uint8, "xq", (M, K)),
+                              _dev(xs, torch.uint8, "xs", (M, K // 32)), _stream(x))
+    _check(st, "mxfp8_quantize")
+    return xq, xs
+
+
+def mxfp8_gemm_mx(xq: torch.Tensor, xs: torch.Tensor, w: torch.Tensor, s: torch.Tensor, out=None):
+    """y bf16 [M, N] = X . W^T with MXFP8 activations (xq, xs) and MXFP8 weights (w, s)."""
+    M, K = xq.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    st = lib().mxfp8_gemm_mx(_dev(xq, torch.uint8, "xq", (M, K)), _dev(xs, torch.uint8, "xs", (M, K // 32)), M, N, K,
+                             _dev(w, torch.uint8, "w", (N, K)), _dev(s, torch.uint8, "s", (N, K // 32)),
+                             _dev(out, torch.bfloat16, "y", (M, N)), _stream(xq))
+    _check(st, "mxfp8_gemm_mx")
     return out
 
 

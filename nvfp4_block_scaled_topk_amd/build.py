@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libmoe_nvfp4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "host_util.cpp", "route.hip", "ffn_decode.hip", "ffn_prompt.hip", "ffn_skinny.hip", "combine.hip", "mxfp8.hip", "router.hip", "measure.hip"]
+SOURCES = ["abi.cpp", "host_util.cpp", "route.hip", "ffn_decode.hip", "ffn_prompt.hip", "ffn_skinny.hip", "combine.hip", "mxfp8.hip", "router.hip", "measure.hip", "mxfp8_w8a8.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -323,6 +323,24 @@ void moe_get_wait_limits(uint32_t* steal_after, uint32_t* give_up) {
   if (give_up) *give_up = g_give_up.load();
 }
 
+int mxfp8_quantize(const uint16_t* x, int M, int K, uint8_t* xq, uint8_t* xs, void* stream) {
+  if (!x || !xq || !xs) return MOE_E_NULL;
+  if (M < 1 || K < 32 || K % 32 != 0 || (long long)M * K * 2 >= (1LL << 31)) return MOE_E_SHAPE;
+  if (!aligned16(x) || !aligned16(xq) || !aligned16(xs)) return MOE_E_ALIGN;
+  return launch_status(moe::launch_mx_quantize(x, M, K, xq, xs, static_cast<hipStream_t>(stream)));
+}
+
+int mxfp8_gemm_mx(const uint8_t* xq, const uint8_t* xs, int M, int N, int K, const uint8_t* w, const uint8_t* s,
+                  uint16_t* y, void* stream) {
+  if (!xq || !xs || !w || !s || !y) return MOE_E_NULL;
+  // the tile's scale rows are loaded whole (K / 32 a multiple of 16, at most 128 bytes)
+  if (M < 1 || N < 1 || K < 512 || K % 512 != 0 || K > 4096 || (long long)M * K >= (1LL << 31) ||
+      (long long)N * K >= (1LL << 31))
+    return MOE_E_SHAPE;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(w) || !aligned16(s) || !aligned16(y)) return MOE_E_ALIGN;
+  return launch_status(moe::launch_mx_gemm(xq, xs, M, N, K, w, s, y, static_cast<hipStream_t>(stream)));
+}
+
 int moe_read_ceiling(const uint64_t* ranges, int n, uint64_t total_bytes, uint32_t* sink, int sink_words,
                      void* stream) {
   if (!ranges || !sink) return MOE_E_NULL;

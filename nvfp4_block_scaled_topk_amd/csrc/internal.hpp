@@ -94,4 +94,9 @@ hipError_t launch_read_ranges(const unsigned long long* table, int n, unsigned l
 hipError_t launch_mxfp8(const uint16_t* x, int M, int N, int K, const uint8_t* w,
                         const uint8_t* s, uint16_t* y, hipStream_t stream);
 
+// MXFP8 activations and the W8A8 projection (mxfp8_w8a8.hip)
+hipError_t launch_mx_quantize(const uint16_t* x, int M, int K, uint8_t* xq, uint8_t* xs, hipStream_t stream);
+hipError_t launch_mx_gemm(const uint8_t* xq, const uint8_t* xs, int M, int N, int K, const uint8_t* w,
+                          const uint8_t* s, uint16_t* y, hipStream_t stream);
+
 }  // namespace moe

@@ -22,10 +22,10 @@ def gpu_available():
 def pytest_sessionfinish(session, exitstatus):
     """Write the band counts the GPU tests recorded (strict / explained / fail per case)."""
     gu = sys.modules.get("gpu_util")
-    if gu is None or not getattr(gu, "RECORDS", None):
+    if gu is None or not (getattr(gu, "RECORDS", None) or getattr(gu, "REPORTS", None)):
         return
     import json
     out = os.path.join(ROOT, "gpurun_out")
     os.makedirs(out, exist_ok=True)
     with open(os.path.join(out, "parity_records.json"), "w") as fh:
-        json.dump({"exitstatus": int(exitstatus), "records": gu.RECORDS}, fh, indent=1)
+        json.dump({"exitstatus": int(exitstatus), "records": gu.RECORDS, "reports": gu.REPORTS}, fh, indent=1)

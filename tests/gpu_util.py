@@ -25,6 +25,11 @@ RECORDS = []
 EXPLAINED_MAX = 0.005
 
 
+# Measured errors that are reported, not bounded by the band (e.g. a lower-precision
+# variant against the exact path); written beside the band records.
+REPORTS = []
+
+
 def check_band(rep, case, part="out"):
     """Record a band report and assert FAIL = 0 and explained <= 0.5 % of the elements."""
     RECORDS.append({"case": case, "part": part, "n": rep.n, "strict": rep.strict, "explained": rep.explained,

@@ -1271,4 +1271,20 @@ def pin_w8a8_brute_force():
             assert Fraction(bf16_bits_scalar(ob[m, n])) == frac_bf16_round(sum(terms))
             assert abs(Fraction(mass[m, n]) - sum(abs(t) for t in terms)) <= sum(abs(t) for t in terms) * Fraction(1, 2 ** 48)
 
+
+def pin_band_mass_share_parameter():
+    """The mass share is a parameter of the bf16 check: at ref 100 (strict bound 2.002,
+    ulp 0.5) the value 103 is 0.498 beyond strict + ulp; with mass 400 it fails under the
+    2^-20 share (3.8e-4) and is explained under a share of 2^-9 (0.78); the directed-
+    rounding share is (K + 64) 2^-23 exactly."""
+    r = F.bf16_rne_bits(np.array([100.0]))[0]
+    assert bf16_bits_scalar(r) == 100.0
+    g = F.bf16_rne_bits(np.array([103.0]))[0]
+    assert bf16_bits_scalar(g) == 103.0
+    mass = np.array([400.0])
+    assert _band1(band.classify, g, r, mass=mass[0]) == (0, 0, 1)
+    assert _band1(lambda *a, **k: band.classify(*a, **k, mass_rel=2.0 ** -9), g, r, mass=mass[0]) == (0, 1, 0)
+    assert band.directed_sum_share(64) == 128 * 2.0 ** -23
+    assert band.directed_sum_share(4096) == 4160 * 2.0 ** -23
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_") and callable(v)]

@@ -160,6 +160,9 @@ MUTANTS = [
     ("mass_u_signed_tensor_scale", "moe.py",
      [("mass_u = abs(tu) * (aX @ np.abs(Wu).T)", "mass_u = tu * (aX @ np.abs(Wu).T)")],
      ["pin_masses_ignore_tensor_scale_signs"]),
+    ("mass_share_ignored", "band.py",
+     [("        bound = bound + mass_rel * np.asarray(mass)", "        bound = bound + MASS_REL * np.asarray(mass)")],
+     ["pin_band_mass_share_parameter"]),
     ("mass_rel_2m10", "band.py",
      [("MASS_REL = 2.0 ** -20", "MASS_REL = 2.0 ** -10")],
      ["pin_band_explained_by_hand"]),
