@@ -276,7 +276,7 @@ def bench_moe(name, steps, warmup, rotations, timer, seed=0):
     return res
 
 
-def bench_mxfp8(M, steps, warmup, rotations, timer, seed=0):
+def bench_mxfp8(M, steps, warmup, rotations, timer, seed=0, kernel_name=None):
     """MXFP8 projection y = x . W^T (N=12288, K=4096): `steps` calls queued behind a GPU
     sleep, bracketed by one pair of HIP events; weights rotate through `rotations`
     copies so repeats are not served from the Infinity Cache."""
@@ -319,7 +319,7 @@ def bench_mxfp8(M, steps, warmup, rotations, timer, seed=0):
     if M <= 16:
         res["roofline"] = {"bound": "hbm", "achieved": res["hbm_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": res["hbm_gbps"] / HBM_PEAK_GBPS,
-                           "kernel": "mxfp8_gemv_valu_kernel" if M <= 4 else "mxfp8_gemv_kernel",
+                           "kernel": kernel_name or ("mxfp8_gemv_valu_kernel" if M <= 4 else "mxfp8_gemv_kernel"),
                            "algorithmic_bytes": nbytes, "avg_us": res["avg_us"]}
     else:
         res["roofline"] = {"bound": "mfma", "achieved": res["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -382,6 +382,30 @@ def bench_w8a8(M, steps, warmup, rotations, timer, seed=0):
     del ws, w0, s0
     torch.cuda.empty_cache()
     return res
+
+
+def bench_mxfp8_columns(steps, timer, seed=0):
+    """The MXFP8 projection with a few activation rows: the per-card pick of the few-row
+    kernel (mxfp8_autotune over M = 1..16 at N=12288, K=4096), then 4 and 8 rows timed
+    with it."""
+    import numpy as np
+    import torch
+
+    import nvfp4_block_scaled_topk_amd as M_
+    import workloads
+
+    inp = workloads.mxfp8_config(16, seed=seed)
+    x = torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16)
+    picks, us = M_.mxfp8_autotune(x, torch.from_numpy(inp.w).cuda(), torch.from_numpy(inp.s).cuda(), reps=20)
+    del inp, x
+    torch.cuda.empty_cache()
+    out = {"picks": {str(m + 1): M_.MXFP8_KERNELS[p] for m, p in enumerate(picks)},
+           "autotune_us": {str(m + 1): dict(zip(M_.MXFP8_KERNELS, [None if v != v else round(v, 2) for v in t]))
+                           for m, t in enumerate(us)}}
+    for m in (4, 8):
+        out[f"M{m}"] = bench_mxfp8(m, steps, 5, 20, timer, seed=seed, kernel_name=M_.MXFP8_KERNELS[picks[m - 1]])
+    log(f"[bench] mxfp8 columns: picks {out['picks']}")
+    return out
 
 
 def bench_block(name, steps, warmup, timer, seed=0):
@@ -740,6 +764,7 @@ def main(argv=None):
 
     if not args.no_also:
         also["w8a8_M512"] = bench_w8a8(512, max(args.also_steps, 50), 5, 20, timer)
+        also["mxfp8_columns"] = bench_mxfp8_columns(max(args.also_steps, 50), timer)
         for name in ("decode", "long_prompt"):
             also[f"router_{name}"] = bench_router(name, max(args.also_steps, 50), 5, timer)
         also["block_decode"] = bench_block("decode", max(args.also_steps, 50), 5, timer)

@@ -264,7 +264,9 @@ int moe_router_logits(const uint16_t* x, const uint16_t* w_r, int T, int d, int 
  * W[n][i] = E4M3(w[n][i]) * 2^(s[n][i/32] - 127) (exact in bf16 for the scales in use).
  * x bf16 [M][K], w E4M3 [N][K], s E8M0 [N][K/32], y bf16 [M][N].
  * Sizes: M, N >= 1, K a multiple of 32 (>= 32), M * K * 2 < 2^31 and N * K < 2^31.
- * M <= 16 runs as a gemv, larger M as a tiled GEMM (128 x 256 output tiles).
+ * M > 16 runs as a tiled GEMM (128 x 192 output tiles). M <= 16 runs the kernel
+ * mxfp8_autotune picked for (this device, M, N, K), or without a pick the vector-ALU
+ * gemv for M <= 4 and the MFMA gemv up to 16.
  */
 int mxfp8_gemm(const uint16_t* x, int M, int N, int K,
                const uint8_t* w, const uint8_t* s, uint16_t* y, void* stream);
@@ -304,6 +306,27 @@ void moe_get_wait_limits(uint32_t* steal_after, uint32_t* give_up);
  */
 int moe_read_ceiling(const uint64_t* ranges, int n, uint64_t total_bytes, uint32_t* sink, int sink_words,
                      void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * mxfp8_autotune -- picks the fastest few-row MXFP8 kernel for this card: for every
+ * M = 1 .. M_max (<= 16) it times the vector-ALU gemv (M <= 8), the MFMA gemv and the
+ * tiled GEMM on the caller's operands (one warm-up and `reps` launches each on `stream`,
+ * HIP events; the call waits for them) and records the fastest for (current device, M,
+ * N, K); later mxfp8_gemm calls of that shape use it (the multi-column gemv picked per
+ * card, "bloomery 0.3.13" release notes, Also: an autotuned MXFP8 gemv at 4-8 columns).
+ * x bf16 [M_max][K], w [N][K], s [N][K/32], y bf16 [M_max][N] (overwritten). Optional
+ * outputs: picks int [M_max] (kernel ids: 0 vector-ALU gemv, 1 MFMA gemv, 2 tiled GEMM),
+ * us float [M_max][3] (microseconds a launch; entries of kernels not timed untouched).
+ * Every kernel gives results within the band of the same definition; the pick changes
+ * only the speed. Thread-safe; the records last for the process.
+ */
+int mxfp8_autotune(const uint16_t* x, int M_max, int N, int K, const uint8_t* w, const uint8_t* s,
+                   uint16_t* y, int reps, int* picks, float* us, void* stream);
+
+/* mxfp8_force_kernel -- a test hook: every later mxfp8_gemm call with M <= 16 runs the
+ * given kernel id (0, 1, 2 as above; 0 only for M <= 8, otherwise the MFMA gemv), or
+ * follows the records again with -1. Process-wide. Other values: MOE_E_SHAPE. */
+int mxfp8_force_kernel(int kernel);
 
 /* ---------------------------------------------------------------------------------
  * mxfp8_quantize -- bf16 activations to MXFP8 (the W8A8 variant of the MXFP8 projection,

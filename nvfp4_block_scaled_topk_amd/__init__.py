@@ -32,6 +32,7 @@ EXPORTED_SYMBOLS = (
     "moe_expert_ffn_nvfp4", "moe_route_expert_ffn_nvfp4", "moe_combine", "moe_combine_shared", "mxfp8_gemm", "moe_router_logits", "moe_status_string",
     "moe_last_error", "moe_async_status", "moe_set_wait_limits", "moe_get_wait_limits",
     "moe_expert_ffn_nvfp4_scratch", "moe_combine_residual", "moe_read_ceiling", "mxfp8_quantize", "mxfp8_gemm_mx",
+    "mxfp8_autotune", "mxfp8_force_kernel",
 )
 
 
@@ -95,6 +96,10 @@ def lib() -> ctypes.CDLL:
     L.moe_set_wait_limits.restype = None
     L.moe_get_wait_limits.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32)]
     L.moe_get_wait_limits.restype = None
+    L.mxfp8_autotune.argtypes = [vp, i32, i32, i32, vp, vp, vp, i32, vp, vp, vp]
+    L.mxfp8_autotune.restype = i32
+    L.mxfp8_force_kernel.argtypes = [i32]
+    L.mxfp8_force_kernel.restype = i32
     L.mxfp8_quantize.argtypes = [vp, i32, i32, vp, vp, vp]
     L.mxfp8_quantize.restype = i32
     L.mxfp8_gemm_mx.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp]
@@ -376,6 +381,32 @@ def mxfp8_gemm(x: torch.Tensor, w: torch.Tensor, s: torch.Tensor, out=None):
                           _stream(x))
     _check(st, "mxfp8_gemm")
     return out
+
+
+MXFP8_KERNELS = ("vector-ALU gemv", "MFMA gemv", "tiled GEMM")
+
+
+def mxfp8_autotune(x: torch.Tensor, w: torch.Tensor, s: torch.Tensor, reps: int = 20):
+    """Times the few-row MXFP8 kernels for M = 1 .. x.shape[0] (<= 16) on these operands
+    and records the fastest per (device, M, N, K). Returns (picks [M_max] kernel ids,
+    microseconds [M_max][3], NaN where a kernel was not timed)."""
+    if x.dtype in (torch.uint16, torch.int16):
+        x = x.view(torch.bfloat16)
+    M_max, K = x.shape
+    N = w.shape[0]
+    y = torch.empty((M_max, N), dtype=torch.bfloat16, device=x.device)
+    picks = (ctypes.c_int * M_max)()
+    us = (ctypes.c_float * (3 * M_max))(*([float("nan")] * (3 * M_max)))
+    st = lib().mxfp8_autotune(_dev(x, torch.bfloat16, "x"), M_max, N, K, _dev(w, torch.uint8, "w", (N, K)),
+                              _dev(s, torch.uint8, "s", (N, K // 32)), _dev(y, torch.bfloat16, "y", (M_max, N)),
+                              int(reps), picks, us, _stream(x))
+    _check(st, "mxfp8_autotune")
+    return list(picks), [list(us[3 * i:3 * i + 3]) for i in range(M_max)]
+
+
+def mxfp8_force_kernel(kernel: int):
+    """Test hook: run the given few-row MXFP8 kernel id for every M <= 16 (-1: the records)."""
+    _check(lib().mxfp8_force_kernel(int(kernel)), "mxfp8_force_kernel")
 
 
 def mxfp8_quantize(x: torch.Tensor, out=None):

@@ -323,6 +323,56 @@ void moe_get_wait_limits(uint32_t* steal_after, uint32_t* give_up) {
   if (give_up) *give_up = g_give_up.load();
 }
 
+int mxfp8_autotune(const uint16_t* x, int M_max, int N, int K, const uint8_t* w, const uint8_t* s, uint16_t* y,
+                   int reps, int* picks, float* us, void* stream) {
+  if (!x || !w || !s || !y) return MOE_E_NULL;
+  if (M_max < 1 || M_max > 16 || N < 1 || K < 32 || K % 32 != 0 || reps < 1 || (long long)M_max * K * 2 >= (1LL << 31) ||
+      (long long)N * K >= (1LL << 31))
+    return MOE_E_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(s) || !aligned16(y)) return MOE_E_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t ev[2];
+  hipError_t err = hipEventCreate(&ev[0]);
+  if (err != hipSuccess) return launch_status(err);
+  err = hipEventCreate(&ev[1]);
+  if (err != hipSuccess) {
+    (void)hipEventDestroy(ev[0]);
+    return launch_status(err);
+  }
+  for (int M = 1; M <= M_max && err == hipSuccess; ++M) {
+    float best = 0.f;
+    int pick = moe::mxfp8_default_kernel(M);
+    for (int kernel = moe::kMxValuGemv; kernel <= moe::kMxTiledGemm && err == hipSuccess; ++kernel) {
+      if (kernel == moe::kMxValuGemv && M > 8) continue;
+      err = moe::launch_mxfp8_kernel(kernel, x, M, N, K, w, s, y, st);  // warm-up
+      if (err == hipSuccess) err = hipEventRecord(ev[0], st);
+      for (int r = 0; r < reps && err == hipSuccess; ++r) err = moe::launch_mxfp8_kernel(kernel, x, M, N, K, w, s, y, st);
+      if (err == hipSuccess) err = hipEventRecord(ev[1], st);
+      if (err == hipSuccess) err = hipEventSynchronize(ev[1]);
+      float ms = 0.f;
+      if (err == hipSuccess) err = hipEventElapsedTime(&ms, ev[0], ev[1]);
+      if (err != hipSuccess) break;
+      const float t = ms * 1000.f / reps;
+      if (us) us[(M - 1) * 3 + kernel] = t;
+      if (best == 0.f || t < best) {
+        best = t;
+        pick = kernel;
+      }
+    }
+    if (err == hipSuccess) err = moe::mxfp8_record_kernel(M, N, K, pick);
+    if (picks) picks[M - 1] = pick;
+  }
+  (void)hipEventDestroy(ev[0]);
+  (void)hipEventDestroy(ev[1]);
+  return launch_status(err);
+}
+
+int mxfp8_force_kernel(int kernel) {
+  if (kernel < -1 || kernel > moe::kMxTiledGemm) return MOE_E_SHAPE;
+  moe::mxfp8_force_kernel(kernel);
+  return MOE_OK;
+}
+
 int mxfp8_quantize(const uint16_t* x, int M, int K, uint8_t* xq, uint8_t* xs, void* stream) {
   if (!x || !xq || !xs) return MOE_E_NULL;
   if (M < 1 || K < 32 || K % 32 != 0 || (long long)M * K * 2 >= (1LL << 31)) return MOE_E_SHAPE;

@@ -2,6 +2,7 @@
 // call from several host threads at once.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -15,7 +16,31 @@ std::mutex g_mu;
 std::map<int, int> g_cu;                                           // device -> compute units
 std::map<std::tuple<int, const void*, int, int>, int> g_resident;  // (device, kernel, threads, lds) -> blocks
 std::map<std::pair<int, const void*>, int> g_lds_attr;             // (device, kernel) -> bytes set
+std::map<std::tuple<int, int, int, int>, int> g_mx_pick;           // (device, M, N, K) -> MXFP8 kernel
+std::atomic<int> g_mx_forced{-1};
 }  // namespace
+
+int mxfp8_forced_kernel() { return g_mx_forced.load(); }
+void mxfp8_force_kernel(int kernel) { g_mx_forced.store(kernel); }
+
+hipError_t mxfp8_recorded_kernel(int M, int N, int K, int& kernel) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto it = g_mx_pick.find(std::make_tuple(dev, M, N, K));
+  kernel = it == g_mx_pick.end() ? -1 : it->second;
+  return hipSuccess;
+}
+
+hipError_t mxfp8_record_kernel(int M, int N, int K, int kernel) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_mx_pick[std::make_tuple(dev, M, N, K)] = kernel;
+  return hipSuccess;
+}
 
 hipError_t device_cu_count(int& ncu) {
   int dev = 0;

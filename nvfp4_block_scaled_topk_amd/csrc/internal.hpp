@@ -93,6 +93,17 @@ hipError_t launch_read_ranges(const unsigned long long* table, int n, unsigned l
 // MXFP8
 hipError_t launch_mxfp8(const uint16_t* x, int M, int N, int K, const uint8_t* w,
                         const uint8_t* s, uint16_t* y, hipStream_t stream);
+// the few-row MXFP8 kernels by id, and their pick per card (mxfp8_autotune)
+constexpr int kMxValuGemv = 0;   // M <= 8
+constexpr int kMxMfmaGemv = 1;   // M <= 16
+constexpr int kMxTiledGemm = 2;  // any M
+hipError_t launch_mxfp8_kernel(int kernel, const uint16_t* x, int M, int N, int K, const uint8_t* w,
+                               const uint8_t* s, uint16_t* y, hipStream_t stream);
+int mxfp8_default_kernel(int M);
+int mxfp8_forced_kernel();                                        // -1: none
+void mxfp8_force_kernel(int kernel);
+hipError_t mxfp8_recorded_kernel(int M, int N, int K, int& kernel);  // -1 when none is recorded
+hipError_t mxfp8_record_kernel(int M, int N, int K, int kernel);
 
 // MXFP8 activations and the W8A8 projection (mxfp8_w8a8.hip)
 hipError_t launch_mx_quantize(const uint16_t* x, int M, int K, uint8_t* xq, uint8_t* xs, hipStream_t stream);

@@ -399,19 +399,27 @@ __global__ __launch_bounds__(kGThreads, 1) void mxfp8_gemm_kernel(const uint16_t
   }
 }
 
-hipError_t launch_mxfp8(const uint16_t* x, int M, int N, int K, const uint8_t* w, const uint8_t* s,
-                        uint16_t* y, hipStream_t stream) {
-  if (M <= 4) {
+// The few-row kernels, by id: the vector-ALU gemv (M <= 8), the MFMA gemv (M <= 16) and
+// the tiled GEMM (any M). Which is fastest for M = 1..16 depends on the card (clocks, HBM,
+// cache sizes); mxfp8_autotune times them on the caller's operands and records the pick
+// per (device, M, N, K). Without a record: vector ALUs for M <= 4, the MFMA gemv up to 16.
+hipError_t launch_mxfp8_kernel(int kernel, const uint16_t* x, int M, int N, int K, const uint8_t* w, const uint8_t* s,
+                               uint16_t* y, hipStream_t stream) {
+  if (kernel == kMxValuGemv && M >= 1 && M <= 8) {
     const dim3 grid((N + kVRows * (kVThreads / 64) - 1) / (kVRows * (kVThreads / 64)));
     switch (M) {
       case 1: hipLaunchKernelGGL(mxfp8_gemv_valu_kernel<1>, grid, dim3(kVThreads), 0, stream, x, N, K, w, s, y); break;
       case 2: hipLaunchKernelGGL(mxfp8_gemv_valu_kernel<2>, grid, dim3(kVThreads), 0, stream, x, N, K, w, s, y); break;
       case 3: hipLaunchKernelGGL(mxfp8_gemv_valu_kernel<3>, grid, dim3(kVThreads), 0, stream, x, N, K, w, s, y); break;
-      default: hipLaunchKernelGGL(mxfp8_gemv_valu_kernel<4>, grid, dim3(kVThreads), 0, stream, x, N, K, w, s, y); break;
+      case 4: hipLaunchKernelGGL(mxfp8_gemv_valu_kernel<4>, grid, dim3(kVThreads), 0, stream, x, N, K, w, s, y); break;
+      case 5: hipLaunchKernelGGL(mxfp8_gemv_valu_kernel<5>, grid, dim3(kVThreads), 0, stream, x, N, K, w, s, y); break;
+      case 6: hipLaunchKernelGGL(mxfp8_gemv_valu_kernel<6>, grid, dim3(kVThreads), 0, stream, x, N, K, w, s, y); break;
+      case 7: hipLaunchKernelGGL(mxfp8_gemv_valu_kernel<7>, grid, dim3(kVThreads), 0, stream, x, N, K, w, s, y); break;
+      default: hipLaunchKernelGGL(mxfp8_gemv_valu_kernel<8>, grid, dim3(kVThreads), 0, stream, x, N, K, w, s, y); break;
     }
     return hipGetLastError();
   }
-  if (M <= 16) {
+  if (kernel == kMxMfmaGemv && M >= 1 && M <= 16) {
     hipLaunchKernelGGL(mxfp8_gemv_kernel<kMxGemvKsplit>, dim3((N + 15) / 16), dim3(64 * kMxGemvKsplit), 0,
                        stream, x, M, N, K, w, s, y);
     return hipGetLastError();
@@ -428,6 +436,20 @@ hipError_t launch_mxfp8(const uint16_t* x, int M, int N, int K, const uint8_t* w
     hipLaunchKernelGGL(mxfp8_gemm_kernel<false>, dim3(mtiles * ntiles), dim3(kGThreads), gemm_lds_bytes<false>(),
                        stream, x, M, N, K, w, s, y, mtiles);
   return hipGetLastError();
+}
+
+int mxfp8_default_kernel(int M) { return M <= 4 ? kMxValuGemv : M <= 16 ? kMxMfmaGemv : kMxTiledGemm; }
+
+hipError_t launch_mxfp8(const uint16_t* x, int M, int N, int K, const uint8_t* w, const uint8_t* s,
+                        uint16_t* y, hipStream_t stream) {
+  int kernel = mxfp8_default_kernel(M);
+  if (M <= 16) {
+    const int forced = mxfp8_forced_kernel();
+    int picked = -1;
+    if (forced >= 0) kernel = forced;
+    else if (mxfp8_recorded_kernel(M, N, K, picked) == hipSuccess && picked >= 0) kernel = picked;
+  }
+  return launch_mxfp8_kernel(kernel, x, M, N, K, w, s, y, stream);
 }
 
 }  // namespace moe

@@ -206,3 +206,13 @@ def test_combine_residual_refusals():
     assert M.STATUS_NAMES[L.moe_combine_residual(p, p, p, 4, 2, 64, None, p, p, p, None)] == "MOE_E_NULL"
     assert M.STATUS_NAMES[L.moe_combine_residual(p, p, p, 4, 2, 48, None, None, p, p, None)] == "MOE_E_SHAPE"
     assert M.STATUS_NAMES[L.moe_combine_residual(p, p, p, 4, 2, 64, None, None, p + 8, p, None)] == "MOE_E_ALIGN"
+
+
+def test_mxfp8_pick_refusals():
+    L = M.lib()
+    p = 256
+    assert M.STATUS_NAMES[L.mxfp8_autotune(p, 17, 64, 64, p, p, p, 5, None, None, None)] == "MOE_E_SHAPE"
+    assert M.STATUS_NAMES[L.mxfp8_autotune(p, 4, 64, 48, p, p, p, 5, None, None, None)] == "MOE_E_SHAPE"
+    assert M.STATUS_NAMES[L.mxfp8_autotune(None, 4, 64, 64, p, p, p, 5, None, None, None)] == "MOE_E_NULL"
+    assert M.STATUS_NAMES[L.mxfp8_force_kernel(3)] == "MOE_E_SHAPE"
+    assert L.mxfp8_force_kernel(-1) == 0

@@ -216,11 +216,14 @@ def make_mxfp8(M: int, N: int, K: int, seed: int = 0, config_id: int = 99, name:
 
 
 def mxfp8_config(M: int, seed: int = 0) -> MXFP8Inputs:
+    """The MXFP8 projection's weights (N=12288, K=4096) with M activation rows: M = 1 and
+    512 are the configuration's own; 2..16 (a few columns, for the per-card kernel pick)
+    draw their activations from streams of their own."""
     c = MXFP8_CONFIG
-    if M not in c["M"]:
-        raise ValueError(f"M must be one of {c['M']}")
-    return make_mxfp8(M, c["N"], c["K"], seed=seed, config_id=c["config_id"], name=f"mxfp8_M{M}",
-                      m_index=c["M"].index(M))
+    if M not in c["M"] and not 1 <= M <= 16:
+        raise ValueError(f"M must be one of {c['M']} or in 1..16")
+    m_index = c["M"].index(M) if M in c["M"] else 100 + M
+    return make_mxfp8(M, c["N"], c["K"], seed=seed, config_id=c["config_id"], name=f"mxfp8_M{M}", m_index=m_index)
 
 
 @dataclass
