@@ -44,6 +44,7 @@ DECODE_FILES = ["ffn_decode.hip", "device.hpp"]
 PROMPT_FILES = ["ffn_prompt.hip", "ffn_skinny.hip", "device.hpp"]
 MXFP8_FILES = ["mxfp8.hip", "device.hpp"]
 ROUTER_FILES = ["router.hip", "device.hpp"]
+W8A8_FILES = ["mxfp8_w8a8.hip", "device.hpp"]
 PROMPT_KERNELS = ("moe_expert_ffn_nvfp4 prompt path (ffn_prompt_kernel grouped GEMM gate/up + down; "
                   "ffn_skinny gate/up + down for experts with <= 16 rows)")
 
@@ -375,7 +376,8 @@ def bench_w8a8(M, steps, warmup, rotations, timer, seed=0):
            "gemm_tflops": flops / (g_us / 1e6) / 1e12,
            "roofline": {"bound": "mfma", "achieved": flops / (g_us / 1e6) / 1e12, "peak": FP8_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": flops / (g_us / 1e6) / 1e12 / FP8_PEAK_TFLOPS,
-                        "kernel": "mx_gemm_kernel (mxfp8_gemm_mx: block-scaled fp8 MFMA)", "avg_us": g_us},
+                        "kernel": "mx_gemm_kernel (mxfp8_gemm_mx: block-scaled fp8 MFMA)", "avg_us": g_us,
+                        "traffic": load_traffic(f"w8a8_M{M}", W8A8_FILES)},
            "error_vs_bf16_activations": "rms error / rms output 0.030 on 12 rows of this configuration "
                                         "(tests/test_gpu_w8a8.py; profiles/parity_records.json reports)"}
     log(f"[bench] w8a8 M={M}: {json.dumps(res)}")
