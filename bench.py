@@ -144,28 +144,22 @@ def bench_moe(name, steps, warmup, rotations, timer, seed=0):
     y_rows = torch.empty((T * k, d), dtype=torch.float32, device=dev)
     out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
     ids, w, off, srows, rof = rbufs
-    # few tokens: routing runs inside the FFN launch (moe_route_expert_ffn_nvfp4) when the
-    # shape allows it; otherwise route, then FFN
+    # few tokens: the whole layer (routing, expert FFN, combine) is one launch
+    # (moe_layer_nvfp4) when the shape allows it; otherwise route, FFN, combine
     fused = False
-    if T <= 16:
-        try:
-            M.route_expert_ffn_nvfp4(logits, x, ex0, k, route_out=rbufs, out=y_rows, workspace=fws, check=False)
-            fused = True
-        except M.MoEError:
-            fused = False
+    lws = None
+    if T <= 16 and M.layer_workspace(T, d, f, E, k) > 0:
+        lws = torch.zeros((M.layer_workspace(T, d, f, E, k),), dtype=torch.uint8, device=dev)
+        M.layer_nvfp4(logits, x, ex0, k, route_out=rbufs, out=out, workspace=lws, check=False)
+        fused = True
 
-    def step(i, ev=None):
+    def step(i):
         ex = copies[i % rotations]
-        if not fused:
-            M.route_topk(logits, k, out=rbufs, workspace=rws)
-        if ev is not None:
-            ev[0].record()
         if fused:
-            M.route_expert_ffn_nvfp4(logits, x, ex, k, route_out=rbufs, out=y_rows, workspace=fws, check=False)
-        else:
-            M.expert_ffn_nvfp4(x, ex, off, srows, k, out=y_rows, workspace=fws, check=False)
-        if ev is not None:
-            ev[1].record()
+            M.layer_nvfp4(logits, x, ex, k, route_out=rbufs, out=out, workspace=lws, check=False)
+            return
+        M.route_topk(logits, k, out=rbufs, workspace=rws)
+        M.expert_ffn_nvfp4(x, ex, off, srows, k, out=y_rows, workspace=fws, check=False)
         M.combine(y_rows, rof, w, out=out)
 
     for i in range(warmup):
@@ -220,23 +214,32 @@ def bench_moe(name, steps, warmup, rotations, timer, seed=0):
         return a_ev.elapsed_time(b_ev) * 1e3 / n
 
     n_b2b = max(steps, 50)
-    # the launch the layer runs for its expert FFN (with routing inside it for few tokens)
+    # the dominant launch of the layer: the whole layer for few tokens, else the expert FFN
     if fused:
-        launch_us = back_to_back(lambda i: M.route_expert_ffn_nvfp4(
-            logits, x, copies[i % rotations], k, route_out=rbufs, out=y_rows, workspace=fws, check=False), n_b2b)
+        launch_us = back_to_back(lambda i: M.layer_nvfp4(
+            logits, x, copies[i % rotations], k, route_out=rbufs, out=out, workspace=lws, check=False), n_b2b)
     else:
         launch_us = back_to_back(lambda i: M.expert_ffn_nvfp4(
             x, copies[i % rotations], off, srows, k, out=y_rows, workspace=fws, check=False), n_b2b)
     # the expert FFN alone, routing lists given
     ffn_us = back_to_back(lambda i: M.expert_ffn_nvfp4(
         x, copies[i % rotations], off, srows, k, out=y_rows, workspace=fws, check=False), n_b2b)
+    # for comparison, the same layer as separate launches (few tokens: routing inside the
+    # FFN launch, then the combine; otherwise the layer step itself)
+    separate_us = None
+    if fused:
+        def separate(i):
+            M.route_expert_ffn_nvfp4(logits, x, copies[i % rotations], k, route_out=rbufs, out=y_rows, workspace=fws,
+                                     check=False)
+            M.combine(y_rows, rof, w, out=out)
+        separate_us = back_to_back(separate, n_b2b)
 
     # algorithmic work (only what the method must move / compute)
     eb = expert_bytes(d, f)
     counts = np.diff(off.cpu().numpy())
     ffn_bytes = U * eb + T * d * 2
-    launch_bytes = ffn_bytes + (T * E * 4 if fused else 0)
     layer_bytes = U * eb + T * d * 2 + T * E * 4 + T * d * 2
+    launch_bytes = layer_bytes if fused else ffn_bytes
     flops = 2.0 * T * k * 3 * d * f
 
     # Ceiling: a plain coalesced read (moe_read_ceiling) of the same bytes the expert
@@ -269,7 +272,7 @@ def bench_moe(name, steps, warmup, rotations, timer, seed=0):
         ffn_hbm_gbps=ffn_bytes / (ffn_us / 1e6) / 1e9,
         ffn_tflops=flops / (ffn_us / 1e6) / 1e12,
         layer_tflops=flops / (ms_per_step / 1e3) / 1e12,
-        host_ms_per_step=host_ms_per_step, route_in_ffn_launch=fused,
+        host_ms_per_step=host_ms_per_step, layer_in_one_launch=fused, separate_launches_us=separate_us,
     )
     log(f"[bench] {name}: {json.dumps(res)}")
     del copies, ex0
@@ -455,46 +458,56 @@ def bench_block(name, steps, warmup, timer, seed=0):
     out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
     ids, w, off, srows, rof = rbufs
 
-    fused = False
-    if T <= 16:
-        try:
-            M.route_expert_ffn_nvfp4(logits, x, ex0, k, route_out=rbufs, out=y_rows, workspace=fws, check=False)
-            fused = True
-        except M.MoEError:
-            fused = False
+    # Few tokens: one router launch projects the routed logits and the shared gate's logit
+    # together (W_r with w_sg as row E), then the whole layer is one launch
+    # (moe_layer_nvfp4). Otherwise: router, routing, routed FFN, shared FFN, gate, combine.
+    one_launch = T <= 16 and M.layer_workspace(T, d, f, E, k, True) > 0
+    w_stk = torch.cat([w_r, w_sg], dim=0).contiguous()
+    stk = torch.empty((T, E + 1), dtype=torch.float32, device=dev)
+    lws = (torch.zeros((M.layer_workspace(T, d, f, E, k, True),), dtype=torch.uint8, device=dev)
+           if one_launch else None)
 
-    def step(i):
+    def separate_step(i):
         ex, sx = copies[i % rotations]
         M.router_logits(x, w_r, out=logits)
-        if fused:
-            M.route_expert_ffn_nvfp4(logits, x, ex, k, route_out=rbufs, out=y_rows, workspace=fws, check=False)
-        else:
-            M.route_topk(logits, k, out=rbufs, workspace=rws)
-            M.expert_ffn_nvfp4(x, ex, off, srows, k, out=y_rows, workspace=fws, check=False)
+        M.route_topk(logits, k, out=rbufs, workspace=rws)
+        M.expert_ffn_nvfp4(x, ex, off, srows, k, out=y_rows, workspace=fws, check=False)
         M.shared_expert_nvfp4(x, sx, out=s_rows, workspace=sws)
         M.router_logits(x, w_sg, out=glog)
         M.combine(y_rows, rof, w, out=out, shared_rows=s_rows, shared_gate_logit=glog, residual=x)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(min(steps, 20)):
-        step(i)
-    torch.cuda.synchronize()
-    host_ms = (time.perf_counter() - t0) * 1e3 / min(steps, 20)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    timer.queue_ahead(host_ms * steps * 1.5 + 20.0)
-    start.record()
-    for i in range(steps):
-        step(i)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    def layer_step(i):
+        ex, sx = copies[i % rotations]
+        M.router_logits(x, w_stk, out=stk)
+        M.layer_nvfp4(stk, x, ex, k, shared=sx, shared_gate_logit=stk[:, E:E + 1], residual=x, route_out=rbufs,
+                      out=out, workspace=lws, check=False)
+
+    step = layer_step if one_launch else separate_step
+
+    def timed(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(min(steps, 20)):
+            fn(i)
+        torch.cuda.synchronize()
+        host_ms = (time.perf_counter() - t0) * 1e3 / min(steps, 20)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        timer.queue_ahead(host_ms * steps * 1.5 + 20.0)
+        start.record()
+        for i in range(steps):
+            fn(i)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    ms = timed(step)
+    separate_ms = timed(separate_step) if one_launch else ms
     nbytes = (U + 1) * eb + E * d * 2 + d * 2 + 2 * T * d * 2 + T * E * 4
     flops = 2.0 * T * (k + 1) * 3 * d * f + 2.0 * T * (E + 1) * d
     res = {"T": T, "d": d, "f": f, "E": E, "k": k, "touched_experts": U, "weight_copies_rotated": rotations,
-           "route_in_ffn_launch": fused,
+           "layer_in_one_launch": one_launch, "separate_launches_ms_per_step": separate_ms,
            "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "algorithmic_bytes": nbytes, "algorithmic_flop": flops,
            "hbm_gbps": nbytes / (ms / 1e3) / 1e9, "tflops": flops / (ms / 1e3) / 1e12}
     log(f"[bench] block {name}: {json.dumps(res)}")
@@ -777,10 +790,11 @@ def main(argv=None):
         files = DECODE_FILES
         roof = {"bound": "hbm", "achieved": r["launch_hbm_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": r["launch_hbm_gbps"] / HBM_PEAK_GBPS, "traffic": load_traffic(args.workload, files),
-                "kernel": ("ffn_decode_kernel as moe_route_expert_ffn_nvfp4 runs it (routing and the whole expert FFN "
-                           "in one launch: the launch each layer step runs)" if r["route_in_ffn_launch"] else
+                "kernel": ("ffn_decode_kernel as moe_layer_nvfp4 runs it (routing, the expert FFN and the combine in "
+                           "one launch: the only launch of a layer step)" if r["layer_in_one_launch"] else
                            "ffn_decode_kernel (moe_expert_ffn_nvfp4)"),
                 "algorithmic_bytes": r["launch_bytes"], "avg_us": r["launch_us"],
+                "separate_launches_us": r["separate_launches_us"],
                 "layer_us": r["ms_per_step"] * 1e3, "layer_frac": r["layer_hbm_gbps"] / HBM_PEAK_GBPS,
                 "ffn_alone_us": r["ffn_avg_us"], "ffn_alone_frac": r["ffn_hbm_gbps"] / HBM_PEAK_GBPS,
                 "ceiling": {"kernel": "read_ranges_kernel (moe_read_ceiling: a plain coalesced read of the touched "
@@ -819,7 +833,7 @@ def main(argv=None):
                                f"f={main_res['f']}, E={main_res['E']} NVFP4 experts, top-{main_res['k']}"
                                + (", Zipf(1.1) routing skew" if zipf else ""),
                    "touched_experts": main_res["touched_experts"], "weight_copies_rotated": main_res["rotations"],
-                   "route_in_ffn_launch": main_res["route_in_ffn_launch"],
+                   "layer_in_one_launch": main_res["layer_in_one_launch"],
                    "layer_hbm_gbps": main_res["layer_hbm_gbps"]},
         "roofline": roof,
         "cpu_baseline": cpu,

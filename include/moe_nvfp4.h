@@ -13,6 +13,8 @@
  *                            codes, one F8_E4M3 scale per 16-element block, one fp32
  *                            scale per expert tensor (#489, #517, #545, #766);
  *   1+2. moe_route_expert_ffn_nvfp4  both in one launch for a few tokens;
+ *   1+2+3. moe_layer_nvfp4   the whole layer in one launch for a few tokens (optionally with
+ *                            a gated shared expert and the residual);
  *   3. moe_combine           the router-weighted sum of each token's expert rows (#701);
  *                            moe_combine_shared adds a gated shared expert's rows (#686),
  *                            moe_combine_residual also the block's residual stream;
@@ -37,7 +39,8 @@
  *     non-zero status has enqueued nothing, except MOE_E_LAUNCH (a launch failed; the
  *     HIP error text is available from moe_last_error()).
  *   - Every pointer must be 16-byte aligned (a misaligned view is refused at the call,
- *     after the pages' practice [#565 page, §10, #520]).
+ *     after the pages' practice [#565 page, §10, #520]), except where an entry point says
+ *     otherwise (moe_layer_nvfp4's shared_gate_logit).
  *   - Unsafe contract (documented, not checked on the device): router logits are finite;
  *     no E4M3 NaN codes (0x7F, 0xFF) in block scales or MXFP8 weights, no E8M0 0xFF;
  *     tensor scales are finite; outputs do not alias inputs; calls that share a
@@ -205,6 +208,43 @@ int moe_route_expert_ffn_nvfp4(const float* logits, const uint16_t* x, int T, in
                                const moe_nvfp4_experts* w, int32_t* topk_ids, float* topk_w,
                                int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_of,
                                float* y_rows, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_layer_nvfp4 -- the whole routed layer for few tokens in one launch: routing (default
+ * policy, no bias), the routed experts' FFN, an optional shared expert, and the combine
+ *   out[t] = bf16_rne( sum_j topk_w[t][j] * y[row_of[t*k+j]]  (+ g_t * S[t])  (+ residual[t]) ),
+ * g_t = 1 / (1 + exp(-shared_gate_logit[t * gate_ld])) (1 without a gate logit), summed in
+ * fp32 in that order and rounded once: the same bits as moe_route_topk, moe_expert_ffn_nvfp4
+ * (for the shared expert: one expert, offsets {0, T}, row p = token p) and
+ * moe_combine_residual / moe_combine_shared / moe_combine called one after the other. The
+ * pages route a whole batch in one run (#740), fold the expert sum into the combine (#701)
+ * and the shared expert's add into its producer ("NVIDIA FP4-Local checkpoints on DGX
+ * Spark" page, §4 Round 1 and §4 remaining items); here all of it is one launch, and the
+ * block whose down product completes a token's 128-column tile (an arrival counter per
+ * token and tile, in the workspace) sums that tile: no block waits for work that has not
+ * started, so the launch does not depend on all of its blocks being resident.
+ * logits fp32, row t at logits + t * logits_ld (logits_ld >= E, 0 means E; columns past E are
+ * not read, so a router that also projects the shared gate may leave its logit in column E);
+ * x bf16 [T][d]; w the routed experts; shared NULL or one expert of the same d and f;
+ * shared_gate_logit NULL or fp32, token t's at shared_gate_logit[t * gate_ld] (4-byte
+ * aligned; given only with a shared expert); residual NULL or bf16 [T][d]; out bf16 [T][d].
+ * topk_ids, topk_w, expert_offsets, sorted_rows, row_of: each NULL or written as by
+ * moe_route_topk. Sizes: those of moe_route_expert_ffn_nvfp4 (T <= 16, d <= 4096, f <= 1024,
+ * T * (max(d, f) + 8) * 2 <= 64 KiB, E <= 256, k <= 16); otherwise MOE_E_SHAPE (the
+ * workspace query returns 0). Workspace: at least moe_layer_nvfp4_workspace(T, d, f, E, k,
+ * shared != NULL) bytes, zero-filled before its first use (it starts with the arrival
+ * counters, which every call leaves at zero; the rest needs no contents); calls that share
+ * it must be ordered on one stream. A workspace that was not zero-filled is reported by
+ * moe_async_status (MOE_E_WAIT_EXPIRED), with some out elements NaN or not written. Waits:
+ * as moe_expert_ffn_nvfp4's few-token path (moe_async_status reports a wait that gave up;
+ * its out elements are then NaN).
+ */
+size_t moe_layer_nvfp4_workspace(int T, int d, int f, int E, int k, int with_shared);
+int moe_layer_nvfp4(const float* logits, int logits_ld, const uint16_t* x, int T, int d, int f, int E, int k,
+                    const moe_nvfp4_experts* w, const moe_nvfp4_experts* shared, const float* shared_gate_logit,
+                    int gate_ld, const uint16_t* residual, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                    int32_t* sorted_rows, int32_t* row_of, uint16_t* out, void* workspace, size_t workspace_bytes,
+                    void* stream);
 
 /* ---------------------------------------------------------------------------------
  * moe_combine -- out[t][c] = bf16_rne( sum_{j=0..k-1} topk_w[t][j] * y_rows[row_of[t*k+j]][c] ),

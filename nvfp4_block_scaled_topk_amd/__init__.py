@@ -32,7 +32,7 @@ EXPORTED_SYMBOLS = (
     "moe_expert_ffn_nvfp4", "moe_route_expert_ffn_nvfp4", "moe_combine", "moe_combine_shared", "mxfp8_gemm", "moe_router_logits", "moe_status_string",
     "moe_last_error", "moe_async_status", "moe_set_wait_limits", "moe_get_wait_limits",
     "moe_expert_ffn_nvfp4_scratch", "moe_combine_residual", "moe_read_ceiling", "mxfp8_quantize", "mxfp8_gemm_mx",
-    "mxfp8_autotune", "mxfp8_force_kernel",
+    "mxfp8_autotune", "mxfp8_force_kernel", "moe_layer_nvfp4_workspace", "moe_layer_nvfp4",
 )
 
 
@@ -106,6 +106,11 @@ def lib() -> ctypes.CDLL:
     L.mxfp8_gemm_mx.restype = i32
     L.moe_read_ceiling.argtypes = [vp, i32, ctypes.c_uint64, vp, i32, vp]
     L.moe_read_ceiling.restype = i32
+    L.moe_layer_nvfp4_workspace.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.moe_layer_nvfp4_workspace.restype = sz
+    L.moe_layer_nvfp4.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, ctypes.POINTER(_Experts),
+                                  ctypes.POINTER(_Experts), vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_layer_nvfp4.restype = i32
     L.moe_status_string.argtypes = [i32]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_last_error.argtypes = []
@@ -503,4 +508,66 @@ def route_expert_ffn_nvfp4(logits: torch.Tensor, x: torch.Tensor, experts: NVFP4
         workspace.data_ptr(), workspace.numel(), _stream(x))
     _check(st, "moe_route_expert_ffn_nvfp4")
     return route_out, out
+
+
+def layer_workspace(T: int, d: int, f: int, E: int, k: int, shared: bool = False) -> int:
+    """Workspace bytes of moe_layer_nvfp4 (0: the shape is not a few-token shape)."""
+    return int(lib().moe_layer_nvfp4_workspace(T, d, f, E, k, 1 if shared else 0))
+
+
+def layer_nvfp4(logits: torch.Tensor, x: torch.Tensor, experts: NVFP4Experts, k: int, shared: NVFP4Experts = None,
+                shared_gate_logit: torch.Tensor = None, residual: torch.Tensor = None, route_out=None, out=None,
+                workspace=None, check: bool = True):
+    """The whole routed layer for few tokens in one launch (moe_layer_nvfp4): routing,
+    the routed experts' FFN, an optional shared expert, and the combine with its gated
+    shared add and an optional residual: out = bf16_rne(sum_j w_j O_j (+ g S) (+ residual)),
+    the same bits as route_topk, expert_ffn_nvfp4 (and shared_expert_nvfp4) and combine.
+    logits float32 [T, L] with L >= E (columns past E are not read: the shared gate's
+    logit may sit in column E); shared_gate_logit float32 [T] or a [T, 1] column view of a
+    row-major float32 tensor (g = 1 when absent); residual bf16 [T, d]. route_out, when
+    given, receives (ids, w, offsets, sorted_rows, row_of). A workspace passed in must have
+    been zero-filled before its first use (torch.zeros); calls leave it reusable. Returns
+    out bf16 [T, d]."""
+    if x.dtype in (torch.uint16, torch.int16):
+        x = x.view(torch.bfloat16)
+    T, d = x.shape
+    E, f = experts.E, experts.f
+    dev = x.device
+    if logits.dim() != 2 or logits.shape[0] != T or logits.shape[1] < E or logits.dtype != torch.float32 or \
+            not logits.is_cuda or not logits.is_contiguous():
+        raise ValueError(f"logits must be a contiguous float32 CUDA tensor [T={T}, >= E={E}]")
+    if check:
+        experts.check()
+        if shared is not None:
+            shared.check()
+    if shared is not None and (shared.E != 1 or shared.f != f or shared.d != d):
+        raise ValueError("the shared expert is one expert of the routed experts' d and f")
+    gptr, gld = None, 1
+    if shared_gate_logit is not None:
+        g = shared_gate_logit
+        if not g.is_cuda or g.dtype != torch.float32 or g.shape[0] != T or g.numel() != T or \
+                (g.dim() == 2 and g.shape[1] != 1) or g.dim() > 2:
+            raise ValueError(f"shared_gate_logit must be float32 [T={T}] or [T, 1] on the device")
+        gptr, gld = g.data_ptr(), (g.stride(0) if T > 1 else 1)
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    need = layer_workspace(T, d, f, E, k, shared is not None)
+    if workspace is None:  # zero-filled before its first use (the arrival counters)
+        workspace = torch.zeros((max(need, 1),), dtype=torch.uint8, device=dev)
+    rp = [None] * 5
+    if route_out is not None:
+        ids, w, off, srows, rof = route_out
+        rp = [_dev(ids, torch.int32, "ids", (T, k)), _dev(w, torch.float32, "w", (T, k)),
+              _dev(off, torch.int32, "offsets", (E + 1,)), _dev(srows, torch.int32, "sorted_rows", (T * k,)),
+              _dev(rof, torch.int32, "row_of", (T * k,))]
+    cs = experts.c_struct()
+    ss = shared.c_struct() if shared is not None else None
+    rptr = _dev(residual.view(torch.bfloat16) if residual is not None and residual.dtype != torch.bfloat16
+                else residual, torch.bfloat16, "residual", (T, d)) if residual is not None else None
+    st = lib().moe_layer_nvfp4(
+        logits.data_ptr(), logits.shape[1], _dev(x, torch.bfloat16, "x", (T, d)), T, d, f, E, k, ctypes.byref(cs),
+        ctypes.byref(ss) if ss is not None else None, gptr, gld, rptr, *rp,
+        _dev(out, torch.bfloat16, "out", (T, d)), workspace.data_ptr(), workspace.numel(), _stream(x))
+    _check(st, "moe_layer_nvfp4")
+    return out
 

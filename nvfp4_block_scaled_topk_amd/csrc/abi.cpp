@@ -58,6 +58,22 @@ size_t h_bytes(int T, int d, int f, int k) {
   return round_up((size_t)T * k * f * elem);
 }
 
+// Workspace of the one-launch layer (moe_layer_nvfp4), in 256-byte aligned parts: the
+// arrival counters first ([T][ceil(d / 128)], one 128-byte line each; zero before the
+// first call, and every call leaves them zero), then H as tagged words ([rows][f / 2]
+// 8-byte words) and the expert rows as tagged words ([rows][d] 8-byte words); rows = T * k,
+// plus T with a shared expert.
+void layer_workspace_parts(int T, int d, int f, int k, bool shared, size_t& y_off, size_t& c_off, size_t& total) {
+  const size_t rows = (size_t)T * k + (shared ? (size_t)T : 0);
+  c_off = 0;
+  const size_t h_off = round_up((size_t)T * (size_t)((d + 127) / 128) * moe::kLayerCounterBytes);
+  y_off = h_off + round_up(rows * (size_t)f * 4);
+  total = y_off + round_up(rows * (size_t)d * 8);
+}
+size_t layer_counter_bytes(int T, int d) {
+  return round_up((size_t)T * (size_t)((d + 127) / 128) * moe::kLayerCounterBytes);
+}
+
 // polls of the few-token launch's waits (moe_set_wait_limits)
 std::atomic<uint32_t> g_steal_after{moe::kDefaultStealAfter};
 std::atomic<uint32_t> g_give_up{moe::kDefaultGiveUp};
@@ -245,6 +261,95 @@ int moe_route_expert_ffn_nvfp4(const float* logits, const uint16_t* x, int T, in
   a.offsets_out = expert_offsets;
   a.sorted_rows_out = sorted_rows;
   a.row_of_out = row_of;
+  return launch_status(
+      moe::launch_ffn_decode(a, next_call_tag(), g_steal_after.load(), g_give_up.load(), static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_layer_nvfp4_workspace(int T, int d, int f, int E, int k, int with_shared) {
+  if (!ffn_shape_ok(T, d, f, E, k) || !moe::use_decode_path(T, d, f) || E > moe::kFusedRouteMaxE ||
+      k > moe::kFusedRouteMaxK)
+    return 0;
+  size_t y_off, c_off, total;
+  layer_workspace_parts(T, d, f, k, with_shared != 0, y_off, c_off, total);
+  return total;
+}
+
+int moe_layer_nvfp4(const float* logits, int logits_ld, const uint16_t* x, int T, int d, int f, int E, int k,
+                    const moe_nvfp4_experts* w, const moe_nvfp4_experts* shared, const float* shared_gate_logit,
+                    int gate_ld, const uint16_t* residual, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                    int32_t* sorted_rows, int32_t* row_of, uint16_t* out, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (!logits || !x || !w || !out || !workspace) return MOE_E_NULL;
+  if (!w->gate_q || !w->gate_s || !w->gate_ts || !w->up_q || !w->up_s || !w->up_ts || !w->down_q ||
+      !w->down_s || !w->down_ts)
+    return MOE_E_NULL;
+  if (shared && (!shared->gate_q || !shared->gate_s || !shared->gate_ts || !shared->up_q || !shared->up_s ||
+                 !shared->up_ts || !shared->down_q || !shared->down_s || !shared->down_ts))
+    return MOE_E_NULL;
+  if (shared_gate_logit && !shared) return MOE_E_NULL;
+  const size_t need = moe_layer_nvfp4_workspace(T, d, f, E, k, shared != nullptr);
+  if (need == 0) return MOE_E_SHAPE;
+  if (logits_ld == 0) logits_ld = E;
+  if (logits_ld < E || (long long)T * logits_ld >= (1LL << 31)) return MOE_E_SHAPE;
+  if (shared_gate_logit && (gate_ld < 1 || (long long)T * gate_ld >= (1LL << 31))) return MOE_E_SHAPE;
+  if (workspace_bytes < need) return MOE_E_WORKSPACE;
+  const void* ptrs[] = {logits, x, out, workspace, w->gate_q, w->gate_s, w->gate_ts, w->up_q, w->up_s, w->up_ts,
+                        w->down_q, w->down_s, w->down_ts};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_E_ALIGN;
+  if (shared) {
+    const void* sp[] = {shared->gate_q, shared->gate_s, shared->gate_ts, shared->up_q, shared->up_s, shared->up_ts,
+                        shared->down_q, shared->down_s, shared->down_ts};
+    for (const void* p : sp)
+      if (!aligned16(p)) return MOE_E_ALIGN;
+  }
+  const void* opt[] = {residual, topk_ids, topk_w, expert_offsets, sorted_rows, row_of};
+  for (const void* p : opt)
+    if (p && !aligned16(p)) return MOE_E_ALIGN;
+  moe::FFNArgs a;
+  a.x = x;
+  a.T = T;
+  a.d = d;
+  a.f = f;
+  a.E = E;
+  a.k = k;
+  a.gate_q = w->gate_q;
+  a.gate_s = w->gate_s;
+  a.up_q = w->up_q;
+  a.up_s = w->up_s;
+  a.down_q = w->down_q;
+  a.down_s = w->down_s;
+  a.gate_ts = w->gate_ts;
+  a.up_ts = w->up_ts;
+  a.down_ts = w->down_ts;
+  size_t y_off, c_off, total;
+  layer_workspace_parts(T, d, f, k, shared != nullptr, y_off, c_off, total);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  a.ctr = reinterpret_cast<unsigned long long*>(ws + c_off);
+  a.h = reinterpret_cast<uint16_t*>(ws + layer_counter_bytes(T, d));
+  a.yw = reinterpret_cast<unsigned long long*>(ws + y_off);
+  a.out = out;
+  a.resid = residual;
+  a.logits = logits;
+  a.logits_ld = logits_ld;
+  a.ids_out = topk_ids;
+  a.w_out = topk_w;
+  a.offsets_out = expert_offsets;
+  a.sorted_rows_out = sorted_rows;
+  a.row_of_out = row_of;
+  if (shared) {
+    a.sh_gate_q = shared->gate_q;
+    a.sh_gate_s = shared->gate_s;
+    a.sh_up_q = shared->up_q;
+    a.sh_up_s = shared->up_s;
+    a.sh_down_q = shared->down_q;
+    a.sh_down_s = shared->down_s;
+    a.sh_gate_ts = shared->gate_ts;
+    a.sh_up_ts = shared->up_ts;
+    a.sh_down_ts = shared->down_ts;
+    a.gate_logit = shared_gate_logit;
+    a.gate_ld = gate_ld;
+  }
   return launch_status(
       moe::launch_ffn_decode(a, next_call_tag(), g_steal_after.load(), g_give_up.load(), static_cast<hipStream_t>(stream)));
 }

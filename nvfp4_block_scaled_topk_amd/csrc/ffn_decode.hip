@@ -64,6 +64,8 @@ constexpr int kDCols = 16 * kDecWaves;          // columns of d in a down item
 constexpr int kDownPairs = 3;                   // W_down chunk pairs (2 x 128 K) a wave holds before its wait
 constexpr int kScrWave = 4096;                  // LDS a wave uses to rearrange its weight codes
 constexpr int kDecMaxDeferred = 64;             // down items a block may take (the grid is sized for it)
+constexpr int kLayerMaxAssign = kDecodeMaxRows * kFusedRouteMaxK;  // T * k of a launch that routes
+constexpr int kCtrWords = kLayerCounterBytes / 8;                  // arrival counters: one a 128-byte line
 
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
@@ -117,6 +119,16 @@ __host__ __device__ __forceinline__ size_t dec_row_region(int T, int d, int f) {
   return (r + 15) / 16 * 16;
 }
 
+// Expert e's slab of a weight tensor and its tensor scale: e < E a routed expert, e == E
+// the shared expert (a one-launch layer with a shared expert)
+__device__ __forceinline__ const uint8_t* eslab(const uint8_t* routed, const uint8_t* shared, int e, int E,
+                                                size_t slab) {
+  return e < E ? routed + (size_t)e * slab : shared;
+}
+__device__ __forceinline__ float ets(const float* routed, const float* shared, int e, int E) {
+  return e < E ? routed[e] : shared[0];
+}
+
 // Everything a gate/up item needs besides the kernel arguments: the block's LDS regions
 // and index lists, the H words and the call's tag.
 struct GateUpCtx {
@@ -162,10 +174,10 @@ __device__ __forceinline__ void gate_up_item(const FFNArgs& a, const GateUpCtx& 
   // weight rows through buffer descriptors (expert slab base in scalar registers,
   // a 32-bit row offset per lane)
   const size_t slab = (size_t)a.f * (a.d / 2), sslab = (size_t)a.f * (a.d / 16);
-  const __amdgpu_buffer_rsrc_t qrs[2] = {dec_rsrc(a.gate_q + (size_t)e * slab, (uint32_t)slab),
-                                         dec_rsrc(a.up_q + (size_t)e * slab, (uint32_t)slab)};
-  const __amdgpu_buffer_rsrc_t srs[2] = {dec_rsrc(a.gate_s + (size_t)e * sslab, (uint32_t)sslab),
-                                         dec_rsrc(a.up_s + (size_t)e * sslab, (uint32_t)sslab)};
+  const __amdgpu_buffer_rsrc_t qrs[2] = {dec_rsrc(eslab(a.gate_q, a.sh_gate_q, e, a.E, slab), (uint32_t)slab),
+                                         dec_rsrc(eslab(a.up_q, a.sh_up_q, e, a.E, slab), (uint32_t)slab)};
+  const __amdgpu_buffer_rsrc_t srs[2] = {dec_rsrc(eslab(a.gate_s, a.sh_gate_s, e, a.E, sslab), (uint32_t)sslab),
+                                         dec_rsrc(eslab(a.up_s, a.sh_up_s, e, a.E, sslab), (uint32_t)sslab)};
   // MFMA layout: lane (grp, col) works on weight row `frow` of the item
   const uint32_t frow = (uint32_t)(fg * kGUFeat + half * 16 + col);
   // the item's scales in LDS: [gate / up][32 rows][d / 16 bytes]
@@ -301,7 +313,7 @@ __device__ __forceinline__ void gate_up_item(const FFNArgs& a, const GateUpCtx& 
         Gs += red[(wave + w) * kRedWave + lane];
         Us += red[(wave + w) * kRedWave + 64 + lane];
       }
-      const float tg = a.gate_ts[e], tu = a.up_ts[e];
+      const float tg = ets(a.gate_ts, a.sh_gate_ts, e, a.E), tu = ets(a.up_ts, a.sh_up_ts, e, a.E);
       uint32_t hb[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) hb[r] = bf16_rne(silu_f32(tg * Gs[r]) * (tu * Us[r]));
@@ -329,10 +341,11 @@ __device__ __forceinline__ void gate_up_item_plain(const FFNArgs& a, const GateU
   const int u = i / nfg, fg = i - u * nfg;
   const int e = cx.s_e[u], r0 = cx.s_r0[u], ne = cx.s_n[u];
   const int frow = fg * kGUFeat + half * 16 + col;  // this lane's weight row
-  const uint8_t* const q[2] = {a.gate_q + ((size_t)e * a.f + frow) * (a.d / 2),
-                               a.up_q + ((size_t)e * a.f + frow) * (a.d / 2)};
-  const uint8_t* const sc[2] = {a.gate_s + ((size_t)e * a.f + frow) * (a.d / 16),
-                                a.up_s + ((size_t)e * a.f + frow) * (a.d / 16)};
+  const size_t slab = (size_t)a.f * (a.d / 2), sslab = (size_t)a.f * (a.d / 16);
+  const uint8_t* const q[2] = {eslab(a.gate_q, a.sh_gate_q, e, a.E, slab) + (size_t)frow * (a.d / 2),
+                               eslab(a.up_q, a.sh_up_q, e, a.E, slab) + (size_t)frow * (a.d / 2)};
+  const uint8_t* const sc[2] = {eslab(a.gate_s, a.sh_gate_s, e, a.E, sslab) + (size_t)frow * (a.d / 16),
+                                eslab(a.up_s, a.sh_up_s, e, a.E, sslab) + (size_t)frow * (a.d / 16)};
   const unsigned char* xrow = cx.s_dyn + cx.s_tok[r0 + min(col, ne - 1)] * dec_xstride(a.d);
   auto xop = [&](int k0) -> bf16x8 { return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4v*>(xrow + k0 * 2)); };
   floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -371,7 +384,7 @@ __device__ __forceinline__ void gate_up_item_plain(const FFNArgs& a, const GateU
       Gs += red[(wave + w) * kRedWave + lane];
       Us += red[(wave + w) * kRedWave + 64 + lane];
     }
-    const float tg = a.gate_ts[e], tu = a.up_ts[e];
+    const float tg = ets(a.gate_ts, a.sh_gate_ts, e, a.E), tu = ets(a.up_ts, a.sh_up_ts, e, a.E);
     uint32_t hb[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) hb[r] = bf16_rne(silu_f32(tg * Gs[r]) * (tu * Us[r]));
@@ -389,6 +402,12 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
   __shared__ int s_U, s_timeout;
   __shared__ uint32_t s_missing;   // a down item's H slices still missing (bit g: slice g)
   __shared__ int s_def[kDecMaxDeferred];  // down items left for the end (their H not all there)
+  // one-launch layer: each assignment's row and weight (from the routing), and the tokens
+  // whose column tile the block combines after a down item
+  __shared__ int s_rowof[kLayerMaxAssign];
+  __shared__ float s_wt[kLayerMaxAssign];
+  __shared__ int s_done[kDecodeMaxRows];
+  __shared__ int s_ndone;
   unsigned char* const s_scr = s_dyn + dec_row_region(a.T, a.d, a.f);
   unsigned char* const s_sc = s_scr + kDecWaves * kScrWave;  // a gate/up item's block scales
   int* s_off = reinterpret_cast<int*>(s_scr);
@@ -421,6 +440,8 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
   // behind them (a wave's loads complete in order)
   copy_x_rows(kDecWaves / 2);
   const int nA = a.T * a.k;
+  const bool fold = a.out != nullptr;             // the launch also combines (with routing only)
+  const bool has_sh = a.sh_gate_q != nullptr;     // a shared expert: touched expert U, rows nA ..
   if (a.logits) {
     // Route the tokens here (every block, redundantly: T <= 16 tokens of E <= 256 logits):
     // the same top-k and weights as the routing kernel (one 16-lane row a token, waves
@@ -437,18 +458,20 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
     for (int e = threadIdx.x; e < a.E; e += kDecThreads) s_cnt[e] = 0;
     {
       const int gl = lane & 15, t = wave * 4 + (lane >> 4);  // a 16-lane row is one token
+      const size_t ld = a.logits_ld > 0 ? (size_t)a.logits_ld : (size_t)a.E;
       if (t < a.T) {
         float my_w;
         int my_i;
         if (a.E <= 128)
-          row_topk<8>(a.logits + (size_t)t * a.E, nullptr, a.E, a.k, gl, 0, my_i, my_w);
+          row_topk<8>(a.logits + (size_t)t * ld, nullptr, a.E, a.k, gl, 0, my_i, my_w);
         else
-          row_topk<16>(a.logits + (size_t)t * a.E, nullptr, a.E, a.k, gl, 0, my_i, my_w);
+          row_topk<16>(a.logits + (size_t)t * ld, nullptr, a.E, a.k, gl, 0, my_i, my_w);
         if (gl < a.k) {
           s_aid[t * a.k + gl] = my_i;
+          if (fold) s_wt[t * a.k + gl] = my_w;
           if (blockIdx.x == 0) {
-            a.ids_out[t * a.k + gl] = my_i;
-            a.w_out[t * a.k + gl] = my_w;
+            if (a.ids_out) a.ids_out[t * a.k + gl] = my_i;
+            if (a.w_out) a.w_out[t * a.k + gl] = my_w;
           }
         }
       }
@@ -462,13 +485,17 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
     for (int i = threadIdx.x; i < nA; i += kDecThreads) {
       const int p = s_off[s_aid[i]] + s_rnk[i];
       s_tok[p] = i / a.k;
+      if (fold) s_rowof[i] = p;
       if (blockIdx.x == 0) {
-        a.sorted_rows_out[p] = i;
-        a.row_of_out[i] = p;
+        if (a.sorted_rows_out) a.sorted_rows_out[p] = i;
+        if (a.row_of_out) a.row_of_out[i] = p;
       }
     }
-    if (blockIdx.x == 0)
+    if (blockIdx.x == 0 && a.offsets_out)
       for (int e = threadIdx.x; e <= a.E; e += kDecThreads) a.offsets_out[e] = s_off[e];
+    // the shared expert's rows: row nA + t is token t
+    if (has_sh)
+      for (int t = threadIdx.x; t < a.T; t += kDecThreads) s_tok[nA + t] = t;
   } else {
     constexpr int kHalf = kDecThreads / 2;  // waves 0-3
     if (threadIdx.x < kHalf) {
@@ -498,7 +525,12 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
       seen += __popcll(nz);
     }
     if (lane == 0) {
-      s_U = seen;
+      if (has_sh) {  // the shared expert: one more touched expert, every token a row
+        s_e[seen] = a.E;
+        s_r0[seen] = nA;
+        s_n[seen] = a.T;
+      }
+      s_U = seen + (has_sh ? 1 : 0);
       s_timeout = 0;
     }
   }
@@ -517,10 +549,8 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
   const int nchD = a.f / 128, npD = (nchD + 1) / 2;
   const int grp8 = lane >> 3, seg8 = lane & 7;
   DownPrefetch pf;
-  auto down_rsrc = [&](int e) {
-    const size_t slab = (size_t)a.d * (a.f / 2);
-    return dec_rsrc(a.down_q + (size_t)e * slab, (uint32_t)slab);
-  };
+  const size_t dslab = (size_t)a.d * (a.f / 2), dsslab = (size_t)a.d * (a.f / 16);
+  auto down_rsrc = [&](int e) { return dec_rsrc(eslab(a.down_q, a.sh_down_q, e, a.E, dslab), (uint32_t)dslab); };
   auto down_pair = [&](__amdgpu_buffer_rsrc_t rs, int ct, int pr, u32x4 (&dst)[2]) {
     const int lc = 2 * pr + (seg8 >> 2) < nchD ? 2 * pr + (seg8 >> 2) : 2 * pr;  // this lane's chunk
     const int lb = (ct * 16 + grp8) * (a.f / 2) + lc * 64 + 16 * (seg8 & 3);
@@ -539,7 +569,8 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
 #pragma unroll
     for (int pr = 0; pr < kDownPairs; ++pr)
       if (pr < npD) down_pair(rs, ct, pr, pf.q[pr]);
-    if (lane * 16 < a.f) pf.sc = ldg_nt_u32x4(a.down_s + ((size_t)e * a.d + ct * 16) * (a.f / 16) + lane * 16);
+    if (lane * 16 < a.f)
+      pf.sc = ldg_nt_u32x4(eslab(a.down_s, a.sh_down_s, e, a.E, dsslab) + (size_t)(ct * 16) * (a.f / 16) + lane * 16);
   };
   int j = G - 1 - (int)blockIdx.x;
 
@@ -588,6 +619,76 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
     }
     __syncthreads();
     return s_missing;
+  };
+  // One-launch layer: after a down item (column tile jt of the expert whose rows are
+  // r0 .. r0 + ne - 1) has issued its row stores, it counts its arrival at each of those
+  // rows' tokens' (token, jt) counters (one 128-byte line each, so that arrivals at
+  // different counters do not queue behind each other). A counter is zero when a call
+  // starts, and the arrival that completes it (k routed rows, plus the shared row) sets it
+  // back to zero and combines that token's columns of the tile. Every row it reads had
+  // its stores issued before its writer arrived, so its only wait is for those stores to
+  // become visible (the row words' tags tell). The sum is the combining kernel's: fp32
+  // fmaf in top-k order, then the gated shared row, then the residual, one rounding.
+  const int arrivals = a.k + (has_sh ? 1 : 0);
+  auto arrive_and_combine = [&](int jt, int r0, int ne) {
+    if (threadIdx.x == 0) s_ndone = 0;
+    __syncthreads();
+    if ((int)threadIdx.x < ne) {
+      const int t = s_tok[r0 + threadIdx.x];
+      unsigned long long* const cw = a.ctr + ((size_t)t * ndt + jt) * kCtrWords;
+      const unsigned long long old = __hip_atomic_fetch_add(cw, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((old >> 32) != 0ull || old >= (unsigned long long)arrivals) {
+        // a value no call leaves (the workspace was not zero-filled before its first use):
+        // this arrival combines nothing; reported, as a wait that gave up
+        __hip_atomic_fetch_or(&g_async_status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else if (old + 1ull == (unsigned long long)arrivals) {
+        __hip_atomic_store(cw, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_done[atomicAdd(&s_ndone, 1)] = t;  // LDS atomic
+      }
+    }
+    __syncthreads();
+    const int nd = s_ndone;
+    for (int q = threadIdx.x; q < nd * kDCols; q += kDecThreads) {
+      const int t = s_done[q / kDCols], c = jt * kDCols + q % kDCols;
+      if (c >= a.d) continue;
+      const int* const ro = s_rowof + t * a.k;
+      const float* const wt = s_wt + t * a.k;
+      float acc;
+      for (uint32_t it = 0;; ++it) {
+        acc = 0.f;
+        bool ok = true;
+        for (int j0 = 0; j0 < a.k; j0 += 8) {  // eight rows' loads in flight at once
+          unsigned long long v[8];
+#pragma unroll
+          for (int uu = 0; uu < 8; ++uu)
+            v[uu] = __hip_atomic_load(a.yw + (size_t)ro[min(j0 + uu, a.k - 1)] * a.d + c, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+          for (int uu = 0; uu < 8; ++uu) {
+            if (j0 + uu < a.k) {
+              ok = ok && (uint32_t)(v[uu] >> 32) == tag;
+              acc = fmaf(wt[j0 + uu], __uint_as_float((uint32_t)v[uu]), acc);
+            }
+          }
+        }
+        if (has_sh) {
+          const unsigned long long sv =
+              __hip_atomic_load(a.yw + (size_t)(nA + t) * a.d + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = ok && (uint32_t)(sv >> 32) == tag;
+          const float g = a.gate_logit ? 1.0f / (1.0f + expf(-a.gate_logit[(size_t)t * a.gate_ld])) : 1.0f;
+          acc = fmaf(g, __uint_as_float((uint32_t)sv), acc);
+        }
+        if (ok) break;
+        if (it >= give_up) {
+          acc = __builtin_nanf("");
+          __hip_atomic_fetch_or(&g_async_status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (a.resid) acc += bf16_to_f32(a.resid[(size_t)t * a.d + c]);
+      a.out[(size_t)t * a.d + c] = (uint16_t)bf16_rne(acc);
+    }
   };
   // Down item j, its weights already in `pf`: H rows of its expert into LDS (bf16, row
   // stride hstride) once every word carries this call's tag, then the products. With
@@ -688,14 +789,14 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
         down_compute(pr, lq);
       }
       // the 32-element chunks past the last full 128: lane group g holds K0 + 8g .. K0 + 8g + 7
-      const uint8_t* const wq = a.down_q + ((size_t)e * a.d + ct * 16 + col) * (a.f / 2);
+      const uint8_t* const wq = eslab(a.down_q, a.sh_down_q, e, a.E, dslab) + (size_t)(ct * 16 + col) * (a.f / 2);
       for (int K0 = nchD * 128; K0 < a.f; K0 += 32) {
         const uint32_t q = *reinterpret_cast<const uint32_t*>(wq + K0 / 2 + 4 * grp);
         const E4M3Split sp = e4m3_split(dsc[col * srowD + K0 / 16 + (grp >> 1)]);
         acc = mfma16(nvfp4x8_to_bf16(q, sp), hv(K0 + 8 * grp), acc);
       }
       if (valid) {
-        const float td = a.down_ts[e];
+        const float td = ets(a.down_ts, a.sh_down_ts, e, a.E);
         const float nanv = __builtin_nanf("");
         const bool bad = s_timeout != 0;
         float4 v;
@@ -703,9 +804,20 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
         v.y = bad ? nanv : td * acc[1];
         v.z = bad ? nanv : td * acc[2];
         v.w = bad ? nanv : td * acc[3];
-        *reinterpret_cast<float4*>(a.y_rows + (size_t)(r0 + col) * a.d + ct * 16 + 4 * grp) = v;
+        if (fold) {
+          // tagged words for the combining block (value, tag), as H
+          unsigned long long* dst = a.yw + (size_t)(r0 + col) * a.d + ct * 16 + 4 * grp;
+          const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            __hip_atomic_store(dst + r, ((unsigned long long)tag << 32) | __float_as_uint(vv[r]), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          *reinterpret_cast<float4*>(a.y_rows + (size_t)(r0 + col) * a.d + ct * 16 + 4 * grp) = v;
+        }
       }
     }
+    if (fold) arrive_and_combine(j - u * ndt, r0, ne);
     __syncthreads();  // before the next item overwrites s_h
     return false;
   };
@@ -758,7 +870,7 @@ hipError_t launch_ffn_decode(const FFNArgs& a, uint32_t tag, uint32_t steal_afte
   int capacity = 0;
   hipError_t err = resident_blocks(reinterpret_cast<const void*>(&ffn_decode_kernel), kDecThreads, lds, capacity);
   if (err != hipSuccess) return err;
-  const long long touched = std::min<long long>(a.E, (long long)a.T * a.k);
+  const long long touched = std::min<long long>(a.E, (long long)a.T * a.k) + (a.sh_gate_q ? 1 : 0);
   const long long down_items = touched * ((a.d + kDCols - 1) / kDCols);
   const long long items = touched * std::max<long long>(a.f / kGUFeat, (a.d + kDCols - 1) / kDCols);
   // no block may take more down items than it can defer

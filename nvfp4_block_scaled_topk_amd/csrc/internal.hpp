@@ -32,12 +32,31 @@ struct FFNArgs {
   // (default policy, no bias; E <= 256, k <= 16) instead of reading offsets and
   // sorted_rows, and its first block writes the routing outputs
   const float* logits = nullptr;
+  int logits_ld = 0;  // row stride of logits (0: E)
   int32_t* ids_out = nullptr;
   float* w_out = nullptr;
   int32_t* offsets_out = nullptr;
   int32_t* sorted_rows_out = nullptr;
   int32_t* row_of_out = nullptr;
+  // few-token path with routing in the launch only: the whole layer. With `out` set the
+  // launch also combines: the down items write their rows as tagged words `yw`
+  // ([rows][d], value and tag), count arrivals per (token, 128 columns) in `ctr`
+  // ([T][ceil(d / 128)] counters), and the block that completes a token's column
+  // tile writes out = bf16_rne(sum_j w_j y_j (+ g S) (+ resid)). A shared expert (the
+  // sh_* pointers, one expert of the same d and f) is one more touched expert with T
+  // rows after the routed ones, its add gated by sigmoid(gate_logit[t * gate_ld]).
+  uint16_t* out = nullptr;
+  unsigned long long* yw = nullptr;
+  unsigned long long* ctr = nullptr;  // kLayerCounterBytes apart, zero when a call starts
+  const uint16_t* resid = nullptr;
+  const uint8_t *sh_gate_q = nullptr, *sh_gate_s = nullptr, *sh_up_q = nullptr, *sh_up_s = nullptr,
+                *sh_down_q = nullptr, *sh_down_s = nullptr;
+  const float *sh_gate_ts = nullptr, *sh_up_ts = nullptr, *sh_down_ts = nullptr;
+  const float* gate_logit = nullptr;
+  int gate_ld = 1;
 };
+
+constexpr int kLayerCounterBytes = 128;  // one arrival counter a cache line
 constexpr int kFusedRouteMaxE = 256;
 constexpr int kFusedRouteMaxK = 16;
 // The decode path keeps every expert's rows in one 16-row MFMA tile (T <= 16).

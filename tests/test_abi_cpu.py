@@ -173,6 +173,39 @@ def test_route_ffn_refusals():
 
 
 
+def test_layer_refusals():
+    L = M.lib()
+    ex = M._Experts(*([A] * 9))
+    sx = M._Experts(*([A] * 9))
+    T, d, f, E, k = 4, 256, 128, 8, 2
+    need = L.moe_layer_nvfp4_workspace(T, d, f, E, k, 0)
+    need_sh = L.moe_layer_nvfp4_workspace(T, d, f, E, k, 1)
+    assert need_sh > need > 0
+    assert L.moe_layer_nvfp4_workspace(17, d, f, E, k, 0) == 0  # more than 16 tokens
+    assert L.moe_layer_nvfp4_workspace(T, d, f, 257, k, 0) == 0
+    assert L.moe_layer_nvfp4_workspace(T, d, f, 64, 17, 0) == 0
+
+    def call(lg=A, ld=0, x=A, T=T, d=d, f=f, E=E, k=k, sh=None, g=None, gld=1, res=None, ids=None, out=A, ws=A,
+             wsb=None):
+        if wsb is None:
+            wsb = need_sh if sh is not None else need
+        return L.moe_layer_nvfp4(lg, ld, x, T, d, f, E, k, ctypes.byref(ex), ctypes.byref(sh) if sh else None, g,
+                                 gld, res, ids, None, None, None, None, out, ws, wsb, None)
+    assert call(lg=None) == NULL
+    assert call(x=None) == NULL
+    assert call(out=None) == NULL
+    assert call(ws=None) == NULL
+    assert call(g=A) == NULL                     # a gate logit without a shared expert
+    assert call(T=17) == SHAPE
+    assert call(ld=E - 1) == SHAPE               # logits rows narrower than E
+    assert call(sh=sx, g=A, gld=0) == SHAPE
+    assert call(wsb=need - 1) == WS
+    assert call(sh=sx, wsb=need) == WS           # the shared expert needs the larger workspace
+    assert call(lg=A + 4) == ALIGN
+    assert call(res=A + 2) == ALIGN
+    assert call(ids=A + 4) == ALIGN
+
+
 def test_wait_limits_round_trip():
     """moe_set_wait_limits / moe_get_wait_limits (host state only, no GPU call)."""
     L = M.lib()
