@@ -17,10 +17,12 @@
 // experts, sigmoid renormalized over the selected, or sigmoid. Wave 0 then ranks every assignment among the block's
 // earlier assignments to the same expert, 64 at a time: ten ballots over the expert
 // index bits give each lane the mask of lanes with its expert, and a per-expert running
-// count in LDS carries across chunks. Kernel 2 (one block per token block): each block
-// sums the per-expert counts of the blocks before it and of all blocks, scans over
-// experts, and scatters p = offset[e] + (earlier blocks' count of e) + rank. No
-// atomics: the row lists are the same bits on every run. A batch of at most 16 tokens
+// count in LDS carries across chunks. Then p = offset[e] + (earlier blocks' count of e)
+// + rank for every assignment: up to 64 token blocks, one more kernel whose blocks each
+// sum the per-expert counts of the blocks before them and of all blocks, scan over
+// experts and scatter; beyond that two kernels, so that the work stays linear in the
+// batch: a scan over token blocks per expert, then the scan over experts and the scatter.
+// No atomics: the row lists are the same bits on every run. A batch of at most 16 tokens
 // runs as one launch (scan and scatter in the same block).
 #include "device.hpp"
 #include "internal.hpp"
@@ -32,6 +34,7 @@ constexpr int kRouteTokensPerBlock = 16;  // measured against 32 and 64: more bl
 constexpr int kRouteThreads = 256;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;
+constexpr int kRouteDirectScanMax = 64;  // token blocks up to which each scatter block sums the counts itself
 
 // PLAIN: the default policy without a bias, compiled with both as constants (the other
 // policies' code drops out)
@@ -167,12 +170,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   }
   const size_t a0 = (size_t)t_begin * k;
   for (int a = threadIdx.x; a < nas; a += kRouteThreads) ws_rank[a0 + a] = s_rank[a];
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) ws_counts[(size_t)blockIdx.x * E + e] = s_cnt[e];
+  // counts expert-major ([E][blocks]): the per-expert scan over blocks reads a contiguous row
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) ws_counts[(size_t)e * gridDim.x + blockIdx.x] = s_cnt[e];
 }
 
-// One block per token block: this block's base per expert (counts of the blocks before
-// it), every expert's total, the scan over experts, and the scatter of its own
-// assignments.
+// Few token blocks (nblocks <= kRouteDirectScanMax): one block per token block finds its
+// base per expert (the counts of the blocks before it) and every expert's total by
+// summing the counts itself, scans over experts, and scatters its own assignments. Each
+// block reads all nblocks * E counts, so this is only used while that is small; larger
+// batches take the two-level form below (route_block_scan_kernel, route_scatter_kernel),
+// whose work grows linearly with the batch.
 __global__ __launch_bounds__(kRouteThreads) void route_scan_scatter_kernel(
     const int32_t* __restrict__ topk_ids, int T, int E, int k, int nblocks,
     const int32_t* __restrict__ ws_rank, const int32_t* __restrict__ ws_counts,
@@ -189,7 +196,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_scatter_kernel(
     for (; j + 32 <= nblocks; j += 32) {
       int c[32];
 #pragma unroll
-      for (int u = 0; u < 32; ++u) c[u] = ws_counts[(size_t)(j + u) * E + e];
+      for (int u = 0; u < 32; ++u) c[u] = ws_counts[(size_t)e * nblocks + j + u];
 #pragma unroll
       for (int u = 0; u < 32; ++u) {
         before += (j + u < b) ? c[u] : 0;
@@ -197,7 +204,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_scatter_kernel(
       }
     }
     for (; j < nblocks; ++j) {
-      const int c = ws_counts[(size_t)j * E + e];
+      const int c = ws_counts[(size_t)e * nblocks + j];
       before += (j < b) ? c : 0;
       total += c;
     }
@@ -218,10 +225,58 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_scatter_kernel(
   }
 }
 
+// Many token blocks, first level: one block per expert turns the expert's row of counts
+// (one count a token block) into exclusive prefix sums in place (each token block's base
+// for the expert) and writes the expert's total. Integer sums: any grouping gives the same
+// values, so the row lists are those of the one-level form.
+__global__ __launch_bounds__(kRouteThreads) void route_block_scan_kernel(int nblocks, int32_t* __restrict__ ws_counts,
+                                                                         int32_t* __restrict__ ws_total) {
+  constexpr int kChunk = 1024;
+  __shared__ int s_in[kChunk];
+  __shared__ int s_out[kChunk + 1];
+  int32_t* const row = ws_counts + (size_t)blockIdx.x * nblocks;
+  int carry = 0;
+  for (int c0 = 0; c0 < nblocks; c0 += kChunk) {
+    const int n = min(kChunk, nblocks - c0);
+    for (int i = threadIdx.x; i < n; i += kRouteThreads) s_in[i] = row[c0 + i];
+    __syncthreads();
+    block_exclusive_scan(s_in, s_out, n);  // ends with a barrier
+    for (int i = threadIdx.x; i < n; i += kRouteThreads) row[c0 + i] = carry + s_out[i];
+    carry += s_out[n];
+    __syncthreads();  // before the next chunk overwrites s_in / s_out
+  }
+  if (threadIdx.x == 0) ws_total[blockIdx.x] = carry;
+}
+
+// Second level: one block per token block scans the E totals (the expert offsets; block 0
+// writes them) and scatters its own assignments to offset + its base + its rank.
+__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
+    const int32_t* __restrict__ topk_ids, int T, int E, int k, int nblocks, const int32_t* __restrict__ ws_rank,
+    const int32_t* __restrict__ ws_base, const int32_t* __restrict__ ws_total, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ sorted_rows, int32_t* __restrict__ row_of) {
+  __shared__ int s_tot[kMaxExperts];
+  __shared__ int s_off[kMaxExperts + 1];
+  const int b = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) s_tot[e] = ws_total[e];
+  __syncthreads();
+  block_exclusive_scan(s_tot, s_off, E);
+  if (b == 0)
+    for (int e = threadIdx.x; e <= E; e += kRouteThreads) expert_offsets[e] = s_off[e];
+  const int a_begin = b * kRouteTokensPerBlock * k;
+  const int a_end = min(T * k, a_begin + kRouteTokensPerBlock * k);
+  for (int a = a_begin + threadIdx.x; a < a_end; a += kRouteThreads) {
+    const int e = topk_ids[a];
+    const int p = s_off[e] + ws_base[(size_t)e * nblocks + b] + ws_rank[a];
+    sorted_rows[p] = a;
+    row_of[a] = p;
+  }
+}
+
 size_t route_workspace_bytes(int T, int E, int k) {
   const size_t nb = ((size_t)T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock;
   if (nb <= 1) return 0;
-  return ((size_t)T * k + nb * (size_t)E) * sizeof(int32_t);
+  // ranks [T * k], counts [E][nb], totals [E]
+  return ((size_t)T * k + nb * (size_t)E + (size_t)E) * sizeof(int32_t);
 }
 
 hipError_t launch_route(const float* logits, const float* bias, int policy, int T, int E, int k, int32_t* ids,
@@ -255,8 +310,17 @@ hipError_t launch_route(const float* logits, const float* bias, int policy, int 
 #undef MOE_ROUTE_LAUNCH
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nb <= 1) return err;
-  hipLaunchKernelGGL(route_scan_scatter_kernel, dim3(nb), dim3(kRouteThreads), 0, stream, ids, T, E, k, nb,
-                     ws_rank, ws_counts, offsets, sorted_rows, row_of);
+  if (nb <= kRouteDirectScanMax) {
+    hipLaunchKernelGGL(route_scan_scatter_kernel, dim3(nb), dim3(kRouteThreads), 0, stream, ids, T, E, k, nb,
+                       ws_rank, ws_counts, offsets, sorted_rows, row_of);
+    return hipGetLastError();
+  }
+  int32_t* const ws_total = ws_counts + (size_t)nb * E;
+  hipLaunchKernelGGL(route_block_scan_kernel, dim3(E), dim3(kRouteThreads), 0, stream, nb, ws_counts, ws_total);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(nb), dim3(kRouteThreads), 0, stream, ids, T, E, k, nb, ws_rank,
+                     ws_counts, ws_total, offsets, sorted_rows, row_of);
   return hipGetLastError();
 }
 

@@ -39,8 +39,12 @@ def test_route_configs(name):
     check_routing(inp, res, name)
 
 
+# 1024 and 1025 tokens: 64 and 65 blocks of 16, the two sides of the switch from the one-level
+# scan to the two-level one; 32768 tokens: 2048 blocks, more than one 1024-block chunk of
+# the per-expert scan
 ROUTE_EDGE = [(1, 1, 1), (1, 8, 8), (3, 64, 32), (16, 8, 2), (17, 8, 2), (33, 128, 8), (64, 7, 3), (65, 7, 3),
-              (130, 1024, 32), (200, 65, 1), (129, 128, 8), (1000, 256, 8), (37, 33, 32)]
+              (130, 1024, 32), (200, 65, 1), (129, 128, 8), (1000, 256, 8), (37, 33, 32), (1024, 256, 8),
+              (1025, 256, 8), (32768, 256, 8), (20000, 1024, 32)]
 
 
 @pytest.mark.parametrize("T,E,k", ROUTE_EDGE)
