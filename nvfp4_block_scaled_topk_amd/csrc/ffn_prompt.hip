@@ -21,8 +21,10 @@
 //             double-buffered blocks of 128 K elements (two activation stages), 64
 //             bytes of codes a weight row
 //
-// Work: one flat list of tiles (expert-major, column tile fastest) walked by a
-// persistent grid; each block derives the list from expert_offsets. Block b works on
+// Work: one flat list of tiles (row tiles that use all four 32-row fragments first, in
+// expert order, then experts' partly filled last tiles by fragments descending; column
+// tile fastest) walked by a persistent grid; each block derives the list from
+// expert_offsets. Block b works on
 // the list positions of "lane" (b mod 8) * (grid / 8) + b / 8, so the blocks a chip's
 // XCD receives (round-robin by block index) take consecutive tiles, which share
 // activation rows and weight columns in that XCD's L2.
@@ -83,17 +85,25 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// Per-block tile table: s_pref[e] = number of 256-row tiles of experts < e (experts with
-// at most kSkinnyRows rows have none).
-__device__ void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int* s_pref) {
+// Per-block tile table, heaviest row tiles first. A row tile's cost grows with the
+// 32-row activation fragments it uses (1..4); ordering the list by that, so that the
+// last, partly filled round of the persistent grid gets the lightest tiles, shortens the
+// longest block. Experts with at most kSkinnyRows rows have no tiles (they go to the
+// weight-streaming kernels).
+//   s_pref[e]: the four-fragment row tiles of experts < e (an expert's full 128-row
+//              tiles, and its last tile when it holds more than 96 rows), in expert order;
+//   s_part[i]: then the experts whose last tile has 1..96 rows, by fragments descending
+//              (3, 2, 1), each in expert order; returns their number.
+__device__ int build_tile_table(const int32_t* __restrict__ offsets, int E, int* s_pref, uint16_t* s_part) {
+  __shared__ int s_np;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int run = 0;
     for (int base = 0; base < E; base += 64) {
       const int e = base + lane;
       const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
-      // experts with few rows go to the weight-streaming kernels instead
-      const int v = cnt > kSkinnyRows ? (cnt + kPromptRows - 1) / kPromptRows : 0;
+      const int rem = cnt % kPromptRows;
+      const int v = cnt > kSkinnyRows ? cnt / kPromptRows + (rem > 3 * 32 ? 1 : 0) : 0;
       int incl = v;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -104,8 +114,22 @@ __device__ void build_tile_prefix(const int32_t* __restrict__ offsets, int E, in
       run += __shfl(incl, 63);
     }
     if (lane == 0) s_pref[E] = run;
+    int np = 0;
+    for (int frags = 3; frags >= 1; --frags) {
+      for (int base = 0; base < E; base += 64) {
+        const int e = base + lane;
+        const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+        const int rem = cnt % kPromptRows;
+        const bool pick = cnt > kSkinnyRows && rem > 0 && (rem + 31) / 32 == frags;
+        const uint64_t m = __ballot(pick);
+        if (pick) s_part[np + __popcll(m & ((1ull << lane) - 1ull))] = (uint16_t)e;
+        np += __popcll(m);
+      }
+    }
+    if (lane == 0) s_np = np;
   }
   __syncthreads();
+  return s_np;
 }
 
 // largest e with s_pref[e] <= t (s_pref non-decreasing, s_pref[0] = 0)
@@ -123,6 +147,7 @@ template <int MODE>  // 0: gate/up/SwiGLU -> H (bf16); 1: down -> y_rows (fp32)
 __global__ __launch_bounds__(kPromptThreads, 2) void ffn_prompt_kernel(FFNArgs a, int n_col_tiles) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int s_pref[kMaxE + 1];
+  __shared__ uint16_t s_part[kMaxE];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
@@ -138,16 +163,23 @@ __global__ __launch_bounds__(kPromptThreads, 2) void ffn_prompt_kernel(FFNArgs a
   const int dseg = (lane & 7) ^ (lane >> 3);
   const int wseg = (lane & 3) ^ ((lane >> 3) & 3);
 
-  build_tile_prefix(a.offsets, a.E, s_pref);
-  const int total_tiles = s_pref[a.E] * n_col_tiles;
+  const int n_part = build_tile_table(a.offsets, a.E, s_pref, s_part);
+  const int n_full = s_pref[a.E];
+  const int total_tiles = (n_full + n_part) * n_col_tiles;
   const int G = gridDim.x;
   const int lid = (G % kXcds == 0) ? (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds : blockIdx.x;
 
   for (int item = lid; item < total_tiles; item += G) {
     const int mt_all = item / n_col_tiles;
     const int ct = item - mt_all * n_col_tiles;
-    const int e = find_tile_expert(s_pref, a.E, mt_all);
-    const int mt = mt_all - s_pref[e];
+    int e, mt;
+    if (mt_all < n_full) {
+      e = find_tile_expert(s_pref, a.E, mt_all);
+      mt = mt_all - s_pref[e];
+    } else {  // an expert's last, partly filled tile
+      e = s_part[mt_all - n_full];
+      mt = (a.offsets[e + 1] - a.offsets[e]) / kPromptRows;
+    }
     const int p0 = a.offsets[e] + mt * kPromptRows;
     const int nrows = min(kPromptRows, a.offsets[e + 1] - p0);
     // 32-row activation fragments in use (0..4)
