@@ -114,9 +114,12 @@ __device__ __forceinline__ void w8_barrier() {
 }
 
 // LDS layout: a stage holds the activation codes (row r: 64 bytes = 4 slots of 16, logical
-// segment j in slot j ^ ((r >> 1) & 3)) then the weight codes (same layout); after the
-// stages a 1 KB sink, then the tile's scale rows (weights, then activations; row r's
-// logical 16-byte segment j in slot j ^ (r & 7) of its 128 bytes).
+// segment j in slot j ^ ((r >> 2) & 3): the 16 rows that 16 lanes of an operand read
+// then fall on 16 distinct 16-byte bank groups) then the weight codes (same layout); after
+// the stages a 1 KB sink, then the tile's scale rows (weights, then activations; row r's
+// logical 16-byte segment j in slot j ^ (r & 7) of its 128 bytes). A lane reads the
+// 16-byte segment of its rows' scales once per 8 stages (16 blocks) and takes a byte a
+// stage from registers.
 __global__ __launch_bounds__(kWThreads, 1) void mx_gemm_kernel(const uint8_t* __restrict__ xq,
                                                              const uint8_t* __restrict__ xs, int M, int N, int K,
                                                              const uint8_t* __restrict__ w,
@@ -143,13 +146,13 @@ __global__ __launch_bounds__(kWThreads, 1) void mx_gemm_kernel(const uint8_t* __
   // per-lane DMA sources: one activation instruction (16 rows x 64 bytes) and two weight
   // instructions a wave per stage; the stage's K offset goes in soffset
   const int xr = wave * 16 + (lane >> 2);
-  const int xseg = (lane & 3) ^ ((xr >> 1) & 3);
+  const int xseg = (lane & 3) ^ ((xr >> 2) & 3);
   const uint32_t xoff = (m0 + xr < M) ? (uint32_t)(m0 + xr) * (uint32_t)K + xseg * 16 : kWOOB;
   uint32_t woff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int wr = (wave * 2 + i) * 16 + (lane >> 2);  // weight row in the tile (past kWN: no row)
-    const int wseg = (lane & 3) ^ ((wr >> 1) & 3);
+    const int wseg = (lane & 3) ^ ((wr >> 2) & 3);
     woff[i] = (wr < kWN && n0 + wr < N) ? (uint32_t)(n0 + wr) * (uint32_t)K + wseg * 16 : kWOOB;
   }
   const int nst = K / kWK;
@@ -196,34 +199,56 @@ __global__ __launch_bounds__(kWThreads, 1) void mx_gemm_kernel(const uint8_t* __
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
 
   for (int c = 0; c < kWStages - 1 && c < nst; ++c) issue(c);
-  for (int c = 0; c < nst; ++c) {
-    // stage c's loads are the oldest in flight (the scale rows before them); later
-    // stages may still be outstanding
-    if (c + 2 < nst) w8_wait_vm<2 * kWOps>();
-    else if (c + 1 < nst) w8_wait_vm<kWOps>();
-    else w8_wait_vm<0>();
-    w8_barrier();  // every wave's part of stage c is in LDS; stage c - 1 is consumed
-    if (c + kWStages - 1 < nst) issue(c + kWStages - 1);
-
-    const unsigned char* st = smem + (c % kWStages) * kWStage;
-    const unsigned char* xsm = st;
-    const unsigned char* wsm = st + kWXBytes;
-    const int b = 2 * c + g;  // the scale block this lane supplies
-    // activation operand: row ma * 32 + l32; lane group g holds the stage's K elements
-    // 16g .. 16g + 15 (of scale block 2c) and 32 + 16g .. 32 + 16g + 15 (of block 2c + 1)
-    const int rx = ma * 32 + l32;
-    const w8u32x4 x0 = *reinterpret_cast<const w8u32x4*>(xsm + rx * 64 + ((g ^ ((rx >> 1) & 3)) * 16));
-    const w8u32x4 x1 = *reinterpret_cast<const w8u32x4*>(xsm + rx * 64 + (((g + 2) ^ ((rx >> 1) & 3)) * 16));
-    const i32x8 bop = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-    const int xsc = *(xscl + rx * kWSRow + (((b >> 4) ^ (rx & 7)) * 16) + (b & 15));
+  const int rx = ma * 32 + l32;  // this lane's activation row of the tile
+  int rw[3];                      // and its weight rows
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int r = nb * 96 + i * 32 + l32;
-      const w8u32x4 w0 = *reinterpret_cast<const w8u32x4*>(wsm + r * 64 + ((g ^ ((r >> 1) & 3)) * 16));
-      const w8u32x4 w1 = *reinterpret_cast<const w8u32x4*>(wsm + r * 64 + (((g + 2) ^ ((r >> 1) & 3)) * 16));
-      const i32x8 aop = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
-      const int wsc = *(wscl + r * kWSRow + (((b >> 4) ^ (r & 7)) * 16) + (b & 15));
-      acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc[i], 0, 0, 0, wsc, 0, xsc);
+  for (int i = 0; i < 3; ++i) rw[i] = nb * 96 + i * 32 + l32;
+  // stages in groups of 8 (nst is a multiple of 8: K % 512 == 0): the group's 16 scale
+  // blocks of each of the lane's rows are one 16-byte segment of the scale rows
+  for (int c8 = 0; c8 < nst; c8 += 8) {
+    const int seg = c8 >> 3;  // segment of blocks 16 seg .. 16 seg + 15
+    w8u32x4 xsv, wsv[3];
+#pragma unroll 1
+    for (int cc = 0; cc < 8; ++cc) {
+      const int c = c8 + cc;
+      // stage c's loads are the oldest in flight (the scale rows before them); later
+      // stages may still be outstanding
+      if (c + 2 < nst) w8_wait_vm<2 * kWOps>();
+      else if (c + 1 < nst) w8_wait_vm<kWOps>();
+      else w8_wait_vm<0>();
+      w8_barrier();  // every wave's part of stage c is in LDS; stage c - 1 is consumed
+      if (c + kWStages - 1 < nst) issue(c + kWStages - 1);
+      if (cc == 0) {
+        xsv = *reinterpret_cast<const w8u32x4*>(xscl + rx * kWSRow + ((seg ^ (rx & 7)) * 16));
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+          wsv[i] = *reinterpret_cast<const w8u32x4*>(wscl + rw[i] * kWSRow + ((seg ^ (rw[i] & 7)) * 16));
+      }
+      // the scale block this lane supplies: 2c + g, byte 2 cc + g of the segment, in
+      // dword cc / 2 at bit 8 (2 (cc % 2) + g)
+      const int sh = 8 * (2 * (cc & 1) + g);
+      auto pick = [&](const w8u32x4& v) -> int {
+        const uint32_t d = (cc >> 1) == 0 ? v.x : (cc >> 1) == 1 ? v.y : (cc >> 1) == 2 ? v.z : v.w;
+        return (int)((d >> sh) & 0xFFu);
+      };
+
+      const unsigned char* st = smem + (c % kWStages) * kWStage;
+      const unsigned char* xsm = st;
+      const unsigned char* wsm = st + kWXBytes;
+      // activation operand: row rx; lane group g holds the stage's K elements 16g .. 16g + 15
+      // (of scale block 2c) and 32 + 16g .. 32 + 16g + 15 (of block 2c + 1)
+      const w8u32x4 x0 = *reinterpret_cast<const w8u32x4*>(xsm + rx * 64 + ((g ^ ((rx >> 2) & 3)) * 16));
+      const w8u32x4 x1 = *reinterpret_cast<const w8u32x4*>(xsm + rx * 64 + (((g + 2) ^ ((rx >> 2) & 3)) * 16));
+      const i32x8 bop = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      const int xsc = pick(xsv);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int r = rw[i];
+        const w8u32x4 w0 = *reinterpret_cast<const w8u32x4*>(wsm + r * 64 + ((g ^ ((r >> 2) & 3)) * 16));
+        const w8u32x4 w1 = *reinterpret_cast<const w8u32x4*>(wsm + r * 64 + (((g + 2) ^ ((r >> 2) & 3)) * 16));
+        const i32x8 aop = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+        acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc[i], 0, 0, 0, pick(wsv[i]), 0, xsc);
+      }
     }
   }
 
