@@ -413,6 +413,32 @@ def bench_mxfp8_columns(steps, timer, seed=0):
     return out
 
 
+def bench_ffn_pick(seed=0):
+    """The few-token path of the NVFP4 expert FFN picked for this card (moe_ffn_autotune)
+    at the decode layer's shape (T=4, d=2048, f=768, E=128, k=8) and at its shared expert's
+    (one expert every token routes to: E=1, k=1): the pick and each path's time a call
+    (operands as the configuration's, no weight rotation)."""
+    import numpy as np
+    import torch
+
+    import nvfp4_block_scaled_topk_amd as M
+    import workloads
+
+    out = {}
+    for label, inp in (("decode", workloads.moe_config("decode", seed=seed)),
+                       ("shared_expert", workloads.make_moe(4, 2048, 768, 1, 1, seed=seed, config_id=98))):
+        x = torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16)
+        ex = M.NVFP4Experts.from_numpy(inp, "cuda")
+        _, _, off, srows, _ = M.route_topk(torch.from_numpy(inp.logits).cuda(), inp.k)
+        pick, us = M.ffn_autotune(x, ex, off, srows, inp.k, reps=50)
+        out[label] = {"pick": M.FFN_PATHS[pick],
+                      "us": {M.FFN_PATHS[i]: (None if v != v else round(v, 2)) for i, v in enumerate(us)}}
+        del ex, x
+    torch.cuda.empty_cache()
+    log(f"[bench] ffn pick: {json.dumps(out)}")
+    return out
+
+
 def bench_block(name, steps, warmup, timer, seed=0):
     """The whole MoE block of a configuration: router projection, routing, routed expert
     FFN, the shared expert's FFN and gate logit, and the combine with the shared add, all
@@ -780,6 +806,7 @@ def main(argv=None):
     if not args.no_also:
         also["w8a8_M512"] = bench_w8a8(512, max(args.also_steps, 50), 5, 20, timer)
         also["mxfp8_columns"] = bench_mxfp8_columns(max(args.also_steps, 50), timer)
+        also["ffn_pick"] = bench_ffn_pick()
         for name in ("decode", "long_prompt"):
             also[f"router_{name}"] = bench_router(name, max(args.also_steps, 50), 5, timer)
         also["block_decode"] = bench_block("decode", max(args.also_steps, 50), 5, timer)

@@ -369,6 +369,32 @@ int mxfp8_autotune(const uint16_t* x, int M_max, int N, int K, const uint8_t* w,
 int mxfp8_force_kernel(int kernel);
 
 /* ---------------------------------------------------------------------------------
+ * moe_ffn_autotune -- picks the faster few-token path of moe_expert_ffn_nvfp4 for this card
+ * and shape (the multi-column NVFP4 decode picked per card, "NVIDIA FP4-Local checkpoints
+ * on DGX Spark" page, §4 remaining items, and "bloomery 0.3.13" release notes, Also): for
+ * T <= 16 (every expert then has at most 16 rows) it times, on the caller's operands and
+ * routing, the one-launch decode kernel (path 0; only within its size limits, see
+ * moe_expert_ffn_nvfp4) and the two weight-streaming kernels (path 1), one warm-up and
+ * `reps` calls each on `stream` (HIP events; the call waits for them), and records the
+ * faster for (current device, T, d, f, E, k): later moe_expert_ffn_nvfp4 calls of that
+ * shape take it (without a record: path 0 where it applies, else path 1). Arguments as
+ * moe_expert_ffn_nvfp4 (y_rows and the workspace are overwritten), plus reps >= 1 and the
+ * optional outputs pick (the path recorded) and us float [2] (microseconds a call; the
+ * entry of a path not timed is untouched). Both paths give results within the band of the
+ * same definition (their fp32 sums run in different orders); the pick changes only the
+ * speed. Thread-safe; the records last for the process. T > 16: MOE_E_SHAPE.
+ */
+int moe_ffn_autotune(const uint16_t* x, int T, int d, int f, int E, int k, const moe_nvfp4_experts* w,
+                     const int32_t* expert_offsets, const int32_t* sorted_rows, float* y_rows, void* workspace,
+                     size_t workspace_bytes, int reps, int* pick, float* us, void* stream);
+
+/* moe_ffn_force_path -- a test hook: every later few-token moe_expert_ffn_nvfp4 call takes
+ * path 0 (the decode kernel, where its size limits allow it; otherwise path 1) or path 1
+ * (the streaming kernels), or follows the records again with -1. Process-wide. Other
+ * values: MOE_E_SHAPE. */
+int moe_ffn_force_path(int path);
+
+/* ---------------------------------------------------------------------------------
  * mxfp8_quantize -- bf16 activations to MXFP8 (the W8A8 variant of the MXFP8 projection,
  * "NVIDIA FP4-Local checkpoints on DGX Spark" page, §4 Round 1, #769), by the OCP MX v1.0
  * conversion: per block of 32 along K, the E8M0 scale code is

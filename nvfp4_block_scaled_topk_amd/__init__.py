@@ -32,7 +32,8 @@ EXPORTED_SYMBOLS = (
     "moe_expert_ffn_nvfp4", "moe_route_expert_ffn_nvfp4", "moe_combine", "moe_combine_shared", "mxfp8_gemm", "moe_router_logits", "moe_status_string",
     "moe_last_error", "moe_async_status", "moe_set_wait_limits", "moe_get_wait_limits",
     "moe_expert_ffn_nvfp4_scratch", "moe_combine_residual", "moe_read_ceiling", "mxfp8_quantize", "mxfp8_gemm_mx",
-    "mxfp8_autotune", "mxfp8_force_kernel", "moe_layer_nvfp4_workspace", "moe_layer_nvfp4",
+    "mxfp8_autotune", "mxfp8_force_kernel", "moe_layer_nvfp4_workspace", "moe_layer_nvfp4", "moe_ffn_autotune",
+    "moe_ffn_force_path",
 )
 
 
@@ -111,6 +112,11 @@ def lib() -> ctypes.CDLL:
     L.moe_layer_nvfp4.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, ctypes.POINTER(_Experts),
                                   ctypes.POINTER(_Experts), vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_layer_nvfp4.restype = i32
+    L.moe_ffn_autotune.argtypes = [vp, i32, i32, i32, i32, i32, ctypes.POINTER(_Experts), vp, vp, vp, vp, sz, i32,
+                                   vp, vp, vp]
+    L.moe_ffn_autotune.restype = i32
+    L.moe_ffn_force_path.argtypes = [i32]
+    L.moe_ffn_force_path.restype = i32
     L.moe_status_string.argtypes = [i32]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_last_error.argtypes = []
@@ -508,6 +514,39 @@ def route_expert_ffn_nvfp4(logits: torch.Tensor, x: torch.Tensor, experts: NVFP4
         workspace.data_ptr(), workspace.numel(), _stream(x))
     _check(st, "moe_route_expert_ffn_nvfp4")
     return route_out, out
+
+
+FFN_PATHS = ("decode launch", "streaming kernels")
+
+
+def ffn_autotune(x: torch.Tensor, experts: NVFP4Experts, expert_offsets: torch.Tensor, sorted_rows: torch.Tensor,
+                 k: int, reps: int = 20):
+    """Times the two few-token paths of expert_ffn_nvfp4 (T <= 16) on these operands and
+    routing and records the faster for this card and shape (moe_ffn_autotune). Returns
+    (pick, us): the path recorded and the microseconds a call of each path (NaN where a
+    path was not timed)."""
+    if x.dtype in (torch.uint16, torch.int16):
+        x = x.view(torch.bfloat16)
+    T, d = x.shape
+    E, f = experts.E, experts.f
+    y = torch.empty((T * k, d), dtype=torch.float32, device=x.device)
+    ws = torch.empty((max(expert_ffn_workspace(T, d, f, E, k), 1),), dtype=torch.uint8, device=x.device)
+    pick = ctypes.c_int(-1)
+    us = (ctypes.c_float * 2)(float("nan"), float("nan"))
+    cs = experts.c_struct()
+    st = lib().moe_ffn_autotune(
+        _dev(x, torch.bfloat16, "x", (T, d)), T, d, f, E, k, ctypes.byref(cs),
+        _dev(expert_offsets, torch.int32, "expert_offsets", (E + 1,)),
+        _dev(sorted_rows, torch.int32, "sorted_rows", (T * k,)), y.data_ptr(), ws.data_ptr(), ws.numel(), reps,
+        ctypes.byref(pick), us, _stream(x))
+    _check(st, "moe_ffn_autotune")
+    return pick.value, [us[0], us[1]]
+
+
+def ffn_force_path(path: int):
+    """Test hook: force the few-token path of expert_ffn_nvfp4 (0 decode launch, 1 streaming
+    kernels), or follow the records again (-1)."""
+    _check(lib().moe_ffn_force_path(path), "moe_ffn_force_path")
 
 
 def layer_workspace(T: int, d: int, f: int, E: int, k: int, shared: bool = False) -> int:

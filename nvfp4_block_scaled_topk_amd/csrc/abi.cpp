@@ -166,6 +166,31 @@ int ffn_setup(const uint16_t* x, int T, int d, int f, int E, int k, const moe_nv
   return MOE_OK;
 }
 
+// The path of a few-token call (a token routes to k distinct experts, so with T <= 16 an
+// expert has at most 16 rows: one decode or streaming tile): the forced one, else the
+// recorded pick, else the one-launch decode kernel when its size limits allow it.
+hipError_t few_token_path(int T, int d, int f, int E, int k, int& path) {
+  path = moe::ffn_forced_path();
+  if (path < 0) {
+    const hipError_t err = moe::ffn_recorded_path(T, d, f, E, k, path);
+    if (err != hipSuccess) return err;
+  }
+  if (path < 0) path = moe::kFfnDecodeLaunch;
+  if (path == moe::kFfnDecodeLaunch && !moe::use_decode_path(T, d, f)) path = moe::kFfnStreaming;
+  return hipSuccess;
+}
+
+// path: -1 for a batch (grouped GEMM and streaming kernels), else a few-token path
+hipError_t launch_ffn_path(const moe::FFNArgs& a, int path, hipStream_t st) {
+  if (path == moe::kFfnDecodeLaunch)
+    return moe::launch_ffn_decode(a, next_call_tag(), g_steal_after.load(), g_give_up.load(), st);
+  if (path == moe::kFfnStreaming) {
+    hipError_t err = moe::launch_ffn_skinny_gateup(a, st);
+    return err == hipSuccess ? moe::launch_ffn_skinny_down(a, st) : err;
+  }
+  return moe::launch_ffn_prompt(a, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,11 +206,12 @@ int moe_expert_ffn_nvfp4(const uint16_t* x, int T, int d, int f, int E, int k, c
   a.offsets = expert_offsets;
   a.sorted_rows = sorted_rows;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // a token routes to k distinct experts, so an expert has at most T rows: with
-  // T <= 16 every expert's rows fit one decode tile
-  if (moe::use_decode_path(T, d, f))
-    return launch_status(moe::launch_ffn_decode(a, next_call_tag(), g_steal_after.load(), g_give_up.load(), st));
-  return launch_status(moe::launch_ffn_prompt(a, st));
+  int path = -1;
+  if (T <= moe::kDecodeMaxRows) {
+    const hipError_t err = few_token_path(T, d, f, E, k, path);
+    if (err != hipSuccess) return launch_status(err);
+  }
+  return launch_status(launch_ffn_path(a, path, st));
 }
 
 }  // extern "C"
@@ -470,6 +496,58 @@ int mxfp8_autotune(const uint16_t* x, int M_max, int N, int K, const uint8_t* w,
   (void)hipEventDestroy(ev[0]);
   (void)hipEventDestroy(ev[1]);
   return launch_status(err);
+}
+
+int moe_ffn_autotune(const uint16_t* x, int T, int d, int f, int E, int k, const moe_nvfp4_experts* w,
+                     const int32_t* expert_offsets, const int32_t* sorted_rows, float* y_rows, void* workspace,
+                     size_t workspace_bytes, int reps, int* pick, float* us, void* stream) {
+  if (!expert_offsets || !sorted_rows) return MOE_E_NULL;
+  moe::FFNArgs a;
+  const int st0 = ffn_setup(x, T, d, f, E, k, w, y_rows, workspace, workspace_bytes, a);
+  if (st0 != MOE_OK) return st0;
+  if (T > moe::kDecodeMaxRows || reps < 1) return MOE_E_SHAPE;
+  if (!aligned16(expert_offsets) || !aligned16(sorted_rows)) return MOE_E_ALIGN;
+  a.offsets = expert_offsets;
+  a.sorted_rows = sorted_rows;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t ev[2];
+  hipError_t err = hipEventCreate(&ev[0]);
+  if (err != hipSuccess) return launch_status(err);
+  err = hipEventCreate(&ev[1]);
+  if (err != hipSuccess) {
+    (void)hipEventDestroy(ev[0]);
+    return launch_status(err);
+  }
+  float best = 0.f;
+  int choice = moe::kFfnStreaming;
+  for (int path = moe::kFfnDecodeLaunch; path <= moe::kFfnStreaming && err == hipSuccess; ++path) {
+    if (path == moe::kFfnDecodeLaunch && !moe::use_decode_path(T, d, f)) continue;
+    err = launch_ffn_path(a, path, st);  // warm-up
+    if (err == hipSuccess) err = hipEventRecord(ev[0], st);
+    for (int r = 0; r < reps && err == hipSuccess; ++r) err = launch_ffn_path(a, path, st);
+    if (err == hipSuccess) err = hipEventRecord(ev[1], st);
+    if (err == hipSuccess) err = hipEventSynchronize(ev[1]);
+    float ms = 0.f;
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, ev[0], ev[1]);
+    if (err != hipSuccess) break;
+    const float t = ms * 1000.f / reps;
+    if (us) us[path] = t;
+    if (best == 0.f || t < best) {
+      best = t;
+      choice = path;
+    }
+  }
+  if (err == hipSuccess) err = moe::ffn_record_path(T, d, f, E, k, choice);
+  if (pick) *pick = choice;
+  (void)hipEventDestroy(ev[0]);
+  (void)hipEventDestroy(ev[1]);
+  return launch_status(err);
+}
+
+int moe_ffn_force_path(int path) {
+  if (path < -1 || path > moe::kFfnStreaming) return MOE_E_SHAPE;
+  moe::ffn_force_path(path);
+  return MOE_OK;
 }
 
 int mxfp8_force_kernel(int kernel) {

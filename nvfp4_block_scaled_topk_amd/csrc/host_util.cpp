@@ -18,7 +18,31 @@ std::map<std::tuple<int, const void*, int, int>, int> g_resident;  // (device, k
 std::map<std::pair<int, const void*>, int> g_lds_attr;             // (device, kernel) -> bytes set
 std::map<std::tuple<int, int, int, int>, int> g_mx_pick;           // (device, M, N, K) -> MXFP8 kernel
 std::atomic<int> g_mx_forced{-1};
+std::map<std::tuple<int, int, int, int, int, int>, int> g_ffn_pick;  // (device, T, d, f, E, k) -> few-token path
+std::atomic<int> g_ffn_forced{-1};
 }  // namespace
+
+int ffn_forced_path() { return g_ffn_forced.load(); }
+void ffn_force_path(int path) { g_ffn_forced.store(path); }
+
+hipError_t ffn_recorded_path(int T, int d, int f, int E, int k, int& path) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto it = g_ffn_pick.find(std::make_tuple(dev, T, d, f, E, k));
+  path = it == g_ffn_pick.end() ? -1 : it->second;
+  return hipSuccess;
+}
+
+hipError_t ffn_record_path(int T, int d, int f, int E, int k, int path) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_ffn_pick[std::make_tuple(dev, T, d, f, E, k)] = path;
+  return hipSuccess;
+}
 
 int mxfp8_forced_kernel() { return g_mx_forced.load(); }
 void mxfp8_force_kernel(int kernel) { g_mx_forced.store(kernel); }

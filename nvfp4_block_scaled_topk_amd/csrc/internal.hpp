@@ -83,6 +83,16 @@ constexpr uint32_t kDefaultGiveUp = 1u << 20;
 // the few-token launch's flag of a wait that gave up: read and cleared (synchronous)
 hipError_t read_and_clear_async_status(unsigned int& status);
 hipError_t launch_ffn_prompt(const FFNArgs& a, hipStream_t stream);
+// The two paths of a few-token call (T <= kDecodeMaxRows: no expert has more rows than
+// one streaming tile): the one-launch decode kernel, or the two weight-streaming kernels
+// (no grouped-GEMM launch: it would have no tiles). Which is faster depends on the card
+// and the shape; moe_ffn_autotune records the pick per (device, T, d, f, E, k).
+constexpr int kFfnDecodeLaunch = 0;
+constexpr int kFfnStreaming = 1;
+int ffn_forced_path();  // -1: none
+void ffn_force_path(int path);
+hipError_t ffn_recorded_path(int T, int d, int f, int E, int k, int& path);  // -1 when none is recorded
+hipError_t ffn_record_path(int T, int d, int f, int E, int k, int path);
 // Prompt batches: experts with at most kSkinnyRows rows take the weight-streaming
 // kernels (ffn_skinny.hip); the grouped GEMM takes the others.
 constexpr int kSkinnyRows = 16;

@@ -206,6 +206,24 @@ def test_layer_refusals():
     assert call(ids=A + 4) == ALIGN
 
 
+def test_ffn_autotune_refusals():
+    L = M.lib()
+    ex = M._Experts(*([A] * 9))
+    T, d, f, E, k = 4, 256, 128, 8, 2
+    need = L.moe_expert_ffn_nvfp4_workspace(T, d, f, E, k)
+
+    def call(x=A, T=T, off=A, sr=A, reps=5, ws=A, wsb=need):
+        return L.moe_ffn_autotune(x, T, d, f, E, k, ctypes.byref(ex), off, sr, A, ws, wsb, reps, None, None, None)
+    assert call(off=None) == NULL
+    assert call(x=None) == NULL
+    assert call(T=17, wsb=L.moe_expert_ffn_nvfp4_workspace(17, d, f, E, k)) == SHAPE  # a batch: no pick
+    assert call(reps=0) == SHAPE
+    assert call(ws=None) == WS
+    assert call(off=A + 4) == ALIGN
+    assert M.STATUS_NAMES[L.moe_ffn_force_path(2)] == "MOE_E_SHAPE"
+    assert L.moe_ffn_force_path(-1) == 0
+
+
 def test_wait_limits_round_trip():
     """moe_set_wait_limits / moe_get_wait_limits (host state only, no GPU call)."""
     L = M.lib()
