@@ -35,6 +35,12 @@
  *     host threads).
  *   - `stream` is a hipStream_t (NULL = the default stream). A call only enqueues work
  *     on it; results are valid once the stream reaches the call.
+ *   - Calls may be captured in a HIP graph. A few-token FFN or layer call (T <= 16) tags the
+ *     words it hands between workgroups with a per-call value; a kernel argument would be
+ *     frozen in the graph, so under capture such a call also captures a one-thread kernel
+ *     that advances a word kept at the end of its workspace, and every replay reads its own
+ *     tag from there (the workspace queries include that word). Replays see the inputs as
+ *     they are when they run.
  *   - Arguments are checked on the host before any HIP call; a call that returns a
  *     non-zero status has enqueued nothing, except MOE_E_LAUNCH (a launch failed; the
  *     HIP error text is available from moe_last_error()).

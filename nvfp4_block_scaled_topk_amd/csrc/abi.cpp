@@ -45,17 +45,23 @@ size_t round_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 // Tags of the decode path's H words: a different value on every call, never 0 (freshly
 // cleared memory), starting from a random point so that words a workspace still holds
 // from earlier use cannot match.
+// Tags of calls made under graph capture come from the device and have the top bit set
+// (ffn_decode.hip); these have it clear.
 uint32_t next_call_tag() {
   static std::atomic<uint32_t> counter{static_cast<uint32_t>(std::random_device{}())};
-  uint32_t t = counter.fetch_add(1, std::memory_order_relaxed) + 1u;
-  while (t == 0) t = counter.fetch_add(1, std::memory_order_relaxed) + 1u;
+  uint32_t t = (counter.fetch_add(1, std::memory_order_relaxed) + 1u) & 0x7FFFFFFFu;
+  while (t == 0) t = (counter.fetch_add(1, std::memory_order_relaxed) + 1u) & 0x7FFFFFFFu;
   return t;
 }
 
-// H: bf16 for the prompt path, bf16 + tag (4 bytes an element) for the decode path
+// H: bf16 for the prompt path, bf16 + tag (4 bytes an element) for the decode path, which
+// also keeps its epoch word (graph capture) after H
 size_t h_bytes(int T, int d, int f, int k) {
-  const size_t elem = moe::use_decode_path(T, d, f) ? 4 : 2;
-  return round_up((size_t)T * k * f * elem);
+  const bool dec = moe::use_decode_path(T, d, f);
+  return round_up((size_t)T * k * f * (dec ? 4 : 2)) + (dec ? moe::kEpochBytes : 0);
+}
+uint32_t* epoch_word(void* workspace, int T, int d, int f, int k) {
+  return reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(workspace) + h_bytes(T, d, f, k) - moe::kEpochBytes);
 }
 
 // Workspace of the one-launch layer (moe_layer_nvfp4), in 256-byte aligned parts: the
@@ -68,7 +74,7 @@ void layer_workspace_parts(int T, int d, int f, int k, bool shared, size_t& y_of
   c_off = 0;
   const size_t h_off = round_up((size_t)T * (size_t)((d + 127) / 128) * moe::kLayerCounterBytes);
   y_off = h_off + round_up(rows * (size_t)f * 4);
-  total = y_off + round_up(rows * (size_t)d * 8);
+  total = y_off + round_up(rows * (size_t)d * 8) + moe::kEpochBytes;  // the epoch word last
 }
 size_t layer_counter_bytes(int T, int d) {
   return round_up((size_t)T * (size_t)((d + 127) / 128) * moe::kLayerCounterBytes);
@@ -163,6 +169,7 @@ int ffn_setup(const uint16_t* x, int T, int d, int f, int E, int k, const moe_nv
   a.down_ts = w->down_ts;
   a.y_rows = y_rows;
   a.h = static_cast<uint16_t*>(workspace);
+  if (moe::use_decode_path(T, d, f)) a.epoch = epoch_word(workspace, T, d, f, k);
   return MOE_OK;
 }
 
@@ -354,6 +361,7 @@ int moe_layer_nvfp4(const float* logits, int logits_ld, const uint16_t* x, int T
   a.ctr = reinterpret_cast<unsigned long long*>(ws + c_off);
   a.h = reinterpret_cast<uint16_t*>(ws + layer_counter_bytes(T, d));
   a.yw = reinterpret_cast<unsigned long long*>(ws + y_off);
+  a.epoch = reinterpret_cast<uint32_t*>(ws + total - moe::kEpochBytes);
   a.out = out;
   a.resid = residual;
   a.logits = logits;

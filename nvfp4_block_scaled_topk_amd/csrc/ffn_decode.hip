@@ -394,8 +394,25 @@ __device__ __forceinline__ void gate_up_item_plain(const FFNArgs& a, const GateU
   }
 }
 
-__global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, uint32_t tag, uint32_t steal_after,
+// Under HIP graph capture a kernel argument is frozen for every replay, so a captured
+// call takes its tag from the workspace instead: this one-thread kernel, captured just
+// before the FFN launch, advances the word there (tags of captured calls have the top bit
+// set, those of direct calls clear, so the two never meet; never 0).
+__global__ void advance_epoch_kernel(uint32_t* epoch) {
+  if (threadIdx.x == 0) {
+    const uint32_t e = __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t n = 0x80000000u | ((e + 1u) & 0x7FFFFFFFu);
+    if (n == 0x80000000u) n = 0x80000001u;
+    __hip_atomic_store(epoch, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, uint32_t tag_arg, uint32_t steal_after,
                                                                     uint32_t give_up) {
+  // this call's tag: the argument, or under graph capture the word the epoch kernel wrote
+  const uint32_t tag = a.epoch ? __builtin_amdgcn_readfirstlane(
+                                     __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                               : tag_arg;
   extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
   __shared__ int s_tok[kDecMaxAssign];
   __shared__ int s_e[kDecMaxTouched], s_r0[kDecMaxTouched], s_n[kDecMaxTouched];
@@ -876,7 +893,21 @@ hipError_t launch_ffn_decode(const FFNArgs& a, uint32_t tag, uint32_t steal_afte
   // no block may take more down items than it can defer
   const long long grid_min = (down_items + kDecMaxDeferred - 1) / kDecMaxDeferred;
   const int grid = (int)std::max<long long>(std::min<long long>(items, capacity), grid_min);
-  hipLaunchKernelGGL(ffn_decode_kernel, dim3(grid), dim3(kDecThreads), lds, stream, a, tag, steal_after, give_up);
+  // Under graph capture: a fresh tag for every replay from the workspace's epoch word
+  // (a direct call passes its own and leaves `epoch` unused).
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  err = hipStreamIsCapturing(stream, &cap);
+  if (err != hipSuccess) return err;
+  FFNArgs b = a;
+  b.epoch = nullptr;
+  if (cap == hipStreamCaptureStatusActive) {
+    if (a.epoch == nullptr) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(advance_epoch_kernel, dim3(1), dim3(64), 0, stream, a.epoch);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    b.epoch = a.epoch;
+  }
+  hipLaunchKernelGGL(ffn_decode_kernel, dim3(grid), dim3(kDecThreads), lds, stream, b, tag, steal_after, give_up);
   return hipGetLastError();
 }
 

@@ -54,7 +54,12 @@ struct FFNArgs {
   const float *sh_gate_ts = nullptr, *sh_up_ts = nullptr, *sh_down_ts = nullptr;
   const float* gate_logit = nullptr;
   int gate_ld = 1;
+  // few-token path: a 32-bit word in the workspace holding the tag of the latest call made
+  // under HIP graph capture (see launch_ffn_decode)
+  uint32_t* epoch = nullptr;
 };
+// Bytes a few-token workspace keeps for that word (at its end).
+constexpr size_t kEpochBytes = 256;
 
 constexpr int kLayerCounterBytes = 128;  // one arrival counter a cache line
 constexpr int kFusedRouteMaxE = 256;
