@@ -439,6 +439,94 @@ def bench_ffn_pick(seed=0):
     return out
 
 
+def bench_shards(steps, timer, seed=0):
+    """One GPU's share of the layer, as it would shard (the exchanges between GPUs are not
+    part of this build):
+    * EP = 8 at the long prompt: the FFN of a GPU's 256/8 experts on the rows routed to
+      them, gathered (k = 1 a row); rank 0 and the most loaded rank (routing skew);
+    * TP = 8 at decode: every expert's f/8 = 96 features; the partial layer (routing, FFN,
+      combine in one launch) an all-reduce would sum, weights rotated past the Infinity Cache."""
+    import numpy as np
+    import torch
+
+    import nvfp4_block_scaled_topk_amd as M
+    import workloads
+
+    names = ("gate_q", "gate_s", "gate_ts", "up_q", "up_s", "up_ts", "down_q", "down_s", "down_ts")
+    out = {}
+    inp = workloads.moe_config("long_prompt", seed=seed)
+    T, d, f, E, k = inp.T, inp.d, inp.f, inp.E, inp.k
+    x = torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16)
+    logits = torch.from_numpy(inp.logits).cuda()
+    ex = M.NVFP4Experts.from_numpy(inp, "cuda")
+    del inp
+    _, _, off, srows, _ = M.route_topk(logits, k)
+    offs = off.cpu().numpy()
+    per_rank = [int(offs[(r + 1) * E // 8] - offs[r * E // 8]) for r in range(8)]
+    for label, rank in (("ep8_rank0", 0), ("ep8_most_loaded", int(np.argmax(per_rank)))):
+        e0, e1 = rank * E // 8, (rank + 1) * E // 8
+        p0, p1 = int(offs[e0]), int(offs[e1])
+        x_loc = x.index_select(0, srows[p0:p1].long() // k).contiguous()
+        off_loc = (off[e0:e1 + 1] - p0).contiguous()
+        rows_loc = torch.arange(p1 - p0, dtype=torch.int32, device="cuda")
+        ex_loc = M.NVFP4Experts(*[getattr(ex, n)[e0:e1].contiguous() for n in names])
+        y = torch.empty((p1 - p0, d), dtype=torch.float32, device="cuda")
+        ws = torch.empty((max(M.expert_ffn_workspace(p1 - p0, d, f, e1 - e0, 1), 1),), dtype=torch.uint8, device="cuda")
+        call = lambda: M.expert_ffn_nvfp4(x_loc, ex_loc, off_loc, rows_loc, 1, out=y, workspace=ws, check=False)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        timer.queue_ahead(20.0)
+        a.record()
+        for _ in range(steps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / steps
+        flops = 2.0 * (p1 - p0) * 3 * d * f
+        out[label] = {"rank": rank, "experts": [e0, e1 - 1], "rows": p1 - p0, "rows_a_rank": per_rank,
+                      "ffn_us": us, "tflops": flops / (us / 1e6) / 1e12,
+                      "mfma_frac": flops / (us / 1e6) / 1e12 / BF16_PEAK_TFLOPS}
+        del x_loc, ex_loc, y, ws
+    del ex, x, logits
+    torch.cuda.empty_cache()
+
+    inp = workloads.tp_share(workloads.moe_config("decode", seed=seed), 8, 0)
+    T, d, f, E, k = inp.T, inp.d, inp.f, inp.E, inp.k
+    x = torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16)
+    logits = torch.from_numpy(inp.logits).cuda()
+    ex0 = M.NVFP4Experts.from_numpy(inp, "cuda")
+    del inp
+    _, _, off, _, _ = M.route_topk(logits, k)
+    U = int((off[1:] - off[:-1] > 0).sum().item())
+    eb = expert_bytes(d, f)
+    rot = max(1, -(-(1 << 30) // (U * eb)))
+    copies = [ex0] + [M.NVFP4Experts(*[getattr(ex0, n).clone() for n in names]) for _ in range(rot - 1)]
+    lws = torch.zeros((M.layer_workspace(T, d, f, E, k),), dtype=torch.uint8, device="cuda")
+    o = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    for i in range(5):
+        M.layer_nvfp4(logits, x, copies[i % rot], k, out=o, workspace=lws, check=False)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    timer.queue_ahead(20.0)
+    a.record()
+    for i in range(steps):
+        M.layer_nvfp4(logits, x, copies[i % rot], k, out=o, workspace=lws, check=False)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    nbytes = U * eb + T * d * 2 + T * E * 4 + T * d * 2
+    out["tp8_decode_rank0"] = {"f_local": f, "touched_experts": U, "weight_copies_rotated": rot,
+                               "layer_us": us, "algorithmic_bytes": nbytes,
+                               "hbm_gbps": nbytes / (us / 1e6) / 1e9,
+                               "hbm_frac": nbytes / (us / 1e6) / 1e9 / HBM_PEAK_GBPS}
+    del copies, ex0
+    torch.cuda.empty_cache()
+    log(f"[bench] shards: {json.dumps(out)}")
+    return out
+
+
 def bench_block(name, steps, warmup, timer, seed=0):
     """The whole MoE block of a configuration: router projection, routing, routed expert
     FFN, the shared expert's FFN and gate logit, and the combine with the shared add, all
@@ -807,6 +895,7 @@ def main(argv=None):
         also["w8a8_M512"] = bench_w8a8(512, max(args.also_steps, 50), 5, 20, timer)
         also["mxfp8_columns"] = bench_mxfp8_columns(max(args.also_steps, 50), timer)
         also["ffn_pick"] = bench_ffn_pick()
+        also["shards"] = bench_shards(max(args.also_steps, 50), timer)
         for name in ("decode", "long_prompt"):
             also[f"router_{name}"] = bench_router(name, max(args.also_steps, 50), 5, timer)
         also["block_decode"] = bench_block("decode", max(args.also_steps, 50), 5, timer)

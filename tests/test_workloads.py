@@ -38,3 +38,13 @@ def test_named_configs_shapes():
     d = workloads.moe_config("decode", experts=False)
     assert (d.T, d.d, d.f, d.E, d.k) == (4, 2048, 768, 128, 8)
     assert d.gate_q.size == 0
+
+
+def test_tp_share_slices_features():
+    """The TP share keeps features rank*f/tp .. of gate/up and the matching K range of down."""
+    inp = workloads.make_moe(2, 64, 256, 3, 2, seed=2, config_id=91)
+    sh = workloads.tp_share(inp, 8, 3)
+    assert sh.f == 32 and sh.gate_q.shape == (3, 32, 32) and sh.down_q.shape == (3, 64, 16)
+    assert np.array_equal(sh.gate_q, inp.gate_q[:, 96:128]) and np.array_equal(sh.up_s, inp.up_s[:, 96:128])
+    assert np.array_equal(sh.down_q, inp.down_q[:, :, 48:64]) and np.array_equal(sh.down_s, inp.down_s[:, :, 6:8])
+    assert sh.down_q.flags["C_CONTIGUOUS"] and sh.gate_ts is inp.gate_ts

@@ -175,6 +175,26 @@ def make_moe(T: int, d: int, f: int, E: int, k: int, seed: int = 0, config_id: i
     )
 
 
+def tp_share(inp: MoEInputs, tp: int, rank: int) -> MoEInputs:
+    """One GPU's share of a layer under tensor parallelism over f: features
+    rank * f/tp .. (rank + 1) * f/tp - 1 of every expert -- those rows of W_gate and W_up
+    (with their block scales) and those columns of W_down (its K range: codes f/tp/2 and
+    scales f/tp/16 of each row) -- and the same activations, logits and tensor scales.
+    Array slicing only; f/tp must stay a multiple of 32."""
+    fl = inp.f // tp
+    if inp.f % tp or fl % 32:
+        raise ValueError("f / tp must be a multiple of 32")
+    a, b = rank * fl, (rank + 1) * fl
+    return MoEInputs(
+        T=inp.T, d=inp.d, f=fl, E=inp.E, k=inp.k, x=inp.x, logits=inp.logits,
+        gate_q=np.ascontiguousarray(inp.gate_q[:, a:b]), gate_s=np.ascontiguousarray(inp.gate_s[:, a:b]),
+        gate_ts=inp.gate_ts,
+        up_q=np.ascontiguousarray(inp.up_q[:, a:b]), up_s=np.ascontiguousarray(inp.up_s[:, a:b]), up_ts=inp.up_ts,
+        down_q=np.ascontiguousarray(inp.down_q[:, :, a // 2:b // 2]),
+        down_s=np.ascontiguousarray(inp.down_s[:, :, a // 16:b // 16]), down_ts=inp.down_ts,
+        name=f"{inp.name}_tp{tp}_rank{rank}")
+
+
 def moe_config(name: str, seed: int = 0, experts: bool = True) -> MoEInputs:
     cid, T, d, f, E, k, zipf = MOE_CONFIGS[name]
     return make_moe(T, d, f, E, k, seed=seed, config_id=cid, zipf=zipf, name=name, experts=experts)
