@@ -373,7 +373,12 @@ def combine(y_rows: torch.Tensor, row_of: torch.Tensor, w: torch.Tensor, out=Non
 
 
 def moe_layer(x: torch.Tensor, logits: torch.Tensor, experts: NVFP4Experts, k: int):
-    """Route, expert FFN, combine: the whole routed MoE FFN. Returns out bf16 [T, d]."""
+    """Route, expert FFN, combine: the whole routed MoE FFN. Returns out bf16 [T, d]. For a
+    few tokens (the shapes moe_layer_nvfp4 takes) this is one launch, with the same bits as
+    the three calls it replaces."""
+    T, d = x.shape
+    if layer_workspace(T, d, experts.f, experts.E, k) > 0:
+        return layer_nvfp4(logits, x, experts, k)
     ids, w, off, srows, rof = route_topk(logits, k)
     y_rows = expert_ffn_nvfp4(x, experts, off, srows, k)
     return combine(y_rows, rof, w)

@@ -203,3 +203,19 @@ def test_layer_workspace_not_zero_filled_is_reported():
     torch.cuda.synchronize()
     assert M.async_status() == 0
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prompt_small"])
+def test_moe_layer_convenience(name):
+    """moe_layer (route, FFN, combine in one call): one launch where the shape allows, the
+    three entry points otherwise; the same bits as those entry points either way."""
+    import torch
+    import nvfp4_block_scaled_topk_amd as M
+    inp = (workloads.moe_config(name) if name != "prompt_small"
+           else workloads.make_moe(40, 256, 128, 16, 4, seed=6, config_id=94, zipf=True))
+    x, logits, ex, _, _ = _inputs(inp, None)
+    ref, _ = _separate(x, logits, ex, inp.k, None, None, None)
+    got = M.moe_layer(x, logits, ex, inp.k)
+    torch.cuda.synchronize()
+    assert M.async_status() == 0
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
