@@ -459,30 +459,40 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
   const int nA = a.T * a.k;
   const bool fold = a.out != nullptr;             // the launch also combines (with routing only)
   const bool has_sh = a.sh_gate_q != nullptr;     // a shared expert: touched expert U, rows nA ..
+  bool listed = false;  // the touched experts (s_e, s_r0, s_n, s_U) already listed; block-uniform
   if (a.logits) {
     // Route the tokens here (every block, redundantly: T <= 16 tokens of E <= 256 logits):
     // the same top-k and weights as the routing kernel (one 16-lane row a token, waves
-    // 0-3), then the stable row lists -- the rank of each assignment among the earlier
-    // ones of its expert (ballots, as the routing kernel), the per-expert counts and
-    // their exclusive scan. Block 0 writes
-    // the routing outputs. Work arrays live in the waves' scratch (free until the
-    // gate/up items start): offsets at 0, counts at 1028, experts of the assignments at
-    // 1288, ranks at 1800 (ints).
+    // 0-3), then the stable row lists. Block 0 writes the routing outputs. Work arrays
+    // live in the waves' scratch (free until the gate/up items start): offsets at 0,
+    // counts at 1028, experts of the assignments at 1288, ranks at 1800 (ints).
     int* const s_cnt = s_off + 1028;
     int* const s_aid = s_off + 1288;
     int* const s_rnk = s_off + 1800;
     static_assert(kDecWaves * kScrWave >= (int)sizeof(int) * (1800 + kDecMaxAssign), "routing arrays fit the scratch");
-    for (int e = threadIdx.x; e < a.E; e += kDecThreads) s_cnt[e] = 0;
+    const bool one_wave = nA <= 64;  // the row lists from one wave's ballots (below)
+    if (!one_wave)
+      for (int e = threadIdx.x; e < a.E; e += kDecThreads) s_cnt[e] = 0;
     {
-      const int gl = lane & 15, t = wave * 4 + (lane >> 4);  // a 16-lane row is one token
+      // up to 4 tokens: one wave a token (waves 0-3); more: a 16-lane row a token, four
+      // tokens a wave
+      const bool by_wave = a.T <= 4;
+      const int gl = by_wave ? lane : lane & 15;
+      const int t = by_wave ? wave : wave * 4 + (lane >> 4);
       const size_t ld = a.logits_ld > 0 ? (size_t)a.logits_ld : (size_t)a.E;
-      if (t < a.T) {
+      if (t < a.T && (!by_wave || wave < 4)) {
         float my_w;
         int my_i;
-        if (a.E <= 128)
-          row_topk<8>(a.logits + (size_t)t * ld, nullptr, a.E, a.k, gl, 0, my_i, my_w);
-        else
-          row_topk<16>(a.logits + (size_t)t * ld, nullptr, a.E, a.k, gl, 0, my_i, my_w);
+        const float* const lrow = a.logits + (size_t)t * ld;
+        if (by_wave) {
+          if (a.E <= 64) wave_topk<1>(lrow, a.E, a.k, lane, my_i, my_w);
+          else if (a.E <= 128) wave_topk<2>(lrow, a.E, a.k, lane, my_i, my_w);
+          else wave_topk<4>(lrow, a.E, a.k, lane, my_i, my_w);
+        } else if (a.E <= 128) {
+          row_topk<8>(lrow, nullptr, a.E, a.k, gl, 0, my_i, my_w);
+        } else {
+          row_topk<16>(lrow, nullptr, a.E, a.k, gl, 0, my_i, my_w);
+        }
         if (gl < a.k) {
           s_aid[t * a.k + gl] = my_i;
           if (fold) s_wt[t * a.k + gl] = my_w;
@@ -496,6 +506,70 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
     // LDS-only barriers inside the routing (the copies and the first block's stores are
     // covered by the full barrier that ends the prologue)
     lds_barrier();
+    if (one_wave) {
+      // At most 64 assignments: lane a of wave 0 holds assignment a (expert e) and finds,
+      // by one ballot per bit of the expert index from the top, the lanes holding the same
+      // expert and those holding a smaller one. Its row in the expert-grouped order is
+      // (assignments of smaller experts) + (earlier assignments of its own): the stable row
+      // lists. The first assignment of each expert lists it among the touched experts, at
+      // the number of distinct smaller experts.
+      if (wave == 0) {
+        const int e = lane < nA ? s_aid[lane] : -1;
+        const bool valid = e >= 0;
+        uint64_t same = __ballot(valid), less = 0ull;
+        const int nbits = 32 - __builtin_clz((unsigned)(a.E > 1 ? a.E - 1 : 1));
+        for (int bit = nbits - 1; bit >= 0; --bit) {
+          const bool one = valid && ((e >> bit) & 1);
+          const uint64_t b1 = __ballot(one);
+          if (one) {
+            less |= same & ~b1;
+            same &= b1;
+          } else {
+            same &= ~b1;
+          }
+        }
+        const int before = __popcll(same & ((1ull << lane) - 1ull));
+        const int nless = __popcll(less);
+        const int p = nless + before;
+        const bool first = valid && before == 0;
+        const uint64_t firsts = __ballot(first);
+        if (valid) {
+          s_tok[p] = lane / a.k;
+          if (fold) s_rowof[lane] = p;
+          if (blockIdx.x == 0) {
+            if (a.sorted_rows_out) a.sorted_rows_out[p] = lane;
+            if (a.row_of_out) a.row_of_out[lane] = p;
+          }
+        }
+        if (first) {
+          const int u = __popcll(firsts & less);
+          s_e[u] = e;
+          s_r0[u] = nless;
+          s_n[u] = __popcll(same);
+        }
+        const int U0 = __popcll(firsts);
+        if (has_sh)  // the shared expert: one more touched expert, every token a row (nA + t)
+          for (int t = lane; t < a.T; t += 64) s_tok[nA + t] = t;
+        if (lane == 0) {
+          if (has_sh) {
+            s_e[U0] = a.E;
+            s_r0[U0] = nA;
+            s_n[U0] = a.T;
+          }
+          s_U = U0 + (has_sh ? 1 : 0);
+          s_timeout = 0;
+        }
+      }
+      if (blockIdx.x == 0 && a.offsets_out)
+        for (int e2 = threadIdx.x; e2 <= a.E; e2 += kDecThreads) {
+          int c = 0;
+          for (int i = 0; i < nA; ++i) c += s_aid[i] < e2 ? 1 : 0;
+          a.offsets_out[e2] = c;
+        }
+      listed = true;
+    } else {
+    // the rank of each assignment among the earlier ones of its expert (ballots, as the
+    // routing kernel), the per-expert counts and their exclusive scan
     if (wave == 0) wave_rank_assignments(s_aid, nA, s_rnk, s_cnt, lane);
     lds_barrier();
     block_exclusive_scan(s_cnt, s_off, a.E);  // ends with a barrier
@@ -513,6 +587,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
     // the shared expert's rows: row nA + t is token t
     if (has_sh)
       for (int t = threadIdx.x; t < a.T; t += kDecThreads) s_tok[nA + t] = t;
+    }
   } else {
     constexpr int kHalf = kDecThreads / 2;  // waves 0-3
     if (threadIdx.x < kHalf) {
@@ -522,8 +597,8 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
   }
   // LDS only: the copies (and the first block's routing stores) are covered by the full
   // barrier that ends the prologue
-  lds_barrier();
-  if (wave == 0) {
+  if (!listed) lds_barrier();
+  if (wave == 0 && !listed) {
     int seen = 0;
     for (int base = 0; base < a.E; base += 64) {
       const int e = base + lane;
