@@ -495,6 +495,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
         }
         if (gl < a.k) {
           s_aid[t * a.k + gl] = my_i;
+          s_rnk[t * a.k + gl] = t;  // the assignment's token (the one-wave lists below; else overwritten)
           if (fold) s_wt[t * a.k + gl] = my_w;
           if (blockIdx.x == 0) {
             if (a.ids_out) a.ids_out[t * a.k + gl] = my_i;
@@ -515,18 +516,19 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
       // the number of distinct smaller experts.
       if (wave == 0) {
         const int e = lane < nA ? s_aid[lane] : -1;
+        const int tok = lane < nA ? s_rnk[lane] : 0;
         const bool valid = e >= 0;
+        // the ballots first (independent of each other), then each lane's masks from the
+        // top bit down (expert indices < 256 on this path: 8 bits)
+        uint64_t bal[8];
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) bal[bit] = __ballot(valid && ((e >> bit) & 1));
         uint64_t same = __ballot(valid), less = 0ull;
-        const int nbits = 32 - __builtin_clz((unsigned)(a.E > 1 ? a.E - 1 : 1));
-        for (int bit = nbits - 1; bit >= 0; --bit) {
+#pragma unroll
+        for (int bit = 7; bit >= 0; --bit) {
           const bool one = valid && ((e >> bit) & 1);
-          const uint64_t b1 = __ballot(one);
-          if (one) {
-            less |= same & ~b1;
-            same &= b1;
-          } else {
-            same &= ~b1;
-          }
+          less |= one ? (same & ~bal[bit]) : 0ull;
+          same &= one ? bal[bit] : ~bal[bit];
         }
         const int before = __popcll(same & ((1ull << lane) - 1ull));
         const int nless = __popcll(less);
@@ -534,7 +536,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void ffn_decode_kernel(FFNArgs a, u
         const bool first = valid && before == 0;
         const uint64_t firsts = __ballot(first);
         if (valid) {
-          s_tok[p] = lane / a.k;
+          s_tok[p] = tok;
           if (fold) s_rowof[lane] = p;
           if (blockIdx.x == 0) {
             if (a.sorted_rows_out) a.sorted_rows_out[p] = lane;
