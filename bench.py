@@ -40,7 +40,7 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X published dense bf16 MFMA rate
 FP8_PEAK_TFLOPS = 5000.0        # MI355X published dense fp8 MFMA rate
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 # kernel sources whose hash a traffic record must match, per path
-DECODE_FILES = ["ffn_decode.hip", "device.hpp"]
+DECODE_FILES = ["ffn_decode.hip", "route_device.hpp", "device.hpp"]
 PROMPT_FILES = ["ffn_prompt.hip", "ffn_skinny.hip", "device.hpp"]
 MXFP8_FILES = ["mxfp8.hip", "device.hpp"]
 ROUTER_FILES = ["router.hip", "device.hpp"]
