@@ -270,10 +270,15 @@ def test_mxfp8_config(M_):
 
 # ---------------------------------------------------------------- routing in the FFN launch
 @pytest.mark.parametrize("T,d,f,E,k", [(4, 2048, 768, 128, 8), (1, 32, 32, 1, 1), (3, 96, 64, 5, 2),
-                                       (16, 160, 96, 6, 3), (8, 512, 256, 256, 16), (16, 256, 128, 200, 4)])
+                                       (16, 160, 96, 6, 3), (8, 512, 256, 256, 16), (16, 256, 128, 200, 4),
+                                       (2, 256, 128, 256, 16), (4, 256, 128, 160, 16), (3, 128, 64, 64, 4),
+                                       (4, 128, 64, 65, 8), (5, 128, 64, 200, 13)])
 def test_route_ffn_fused(T, d, f, E, k):
     """moe_route_expert_ffn_nvfp4 against the oracle (routing bit-exact, whole layer in the
-    band) and against the separate moe_route_topk + moe_expert_ffn_nvfp4 calls (same bits)."""
+    band) and against the separate moe_route_topk + moe_expert_ffn_nvfp4 calls (same bits).
+    Shapes cover the launch's routing forms: one wave a token (T <= 4) with 1, 2 and 4 keys a
+    lane (E <= 64, <= 128, <= 256), a 16-lane row a token (T > 4), and the row lists from one
+    wave's ballots (T * k <= 64, 64 included) or from ranks, counts and a scan (T * k = 65)."""
     import torch
     import nvfp4_block_scaled_topk_amd as M
     inp = workloads.make_moe(T, d, f, E, k, seed=4, config_id=63, zipf=True)
