@@ -333,19 +333,21 @@ __global__ __launch_bounds__(kSkThreads) void ffn_skinny_down_kernel(FFNArgs a) 
   }
 }
 
+// The grid-stride loops run on as many blocks as the device holds at once (one round of
+// blocks: each reads the expert offsets once).
 hipError_t launch_ffn_skinny_gateup(const FFNArgs& a, hipStream_t stream) {
-  int ncu = 0;
-  hipError_t err = device_cu_count(ncu);
+  int blocks = 0;
+  hipError_t err = resident_blocks(reinterpret_cast<const void*>(&ffn_skinny_gateup_kernel), kSkThreads, 0, blocks);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(ffn_skinny_gateup_kernel, dim3(8 * ncu), dim3(kSkThreads), 0, stream, a);
+  hipLaunchKernelGGL(ffn_skinny_gateup_kernel, dim3(blocks), dim3(kSkThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_ffn_skinny_down(const FFNArgs& a, hipStream_t stream) {
-  int ncu = 0;
-  hipError_t err = device_cu_count(ncu);
+  int blocks = 0;
+  hipError_t err = resident_blocks(reinterpret_cast<const void*>(&ffn_skinny_down_kernel), kSkThreads, 0, blocks);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(ffn_skinny_down_kernel, dim3(8 * ncu), dim3(kSkThreads), 0, stream, a);
+  hipLaunchKernelGGL(ffn_skinny_down_kernel, dim3(blocks), dim3(kSkThreads), 0, stream, a);
   return hipGetLastError();
 }
 
