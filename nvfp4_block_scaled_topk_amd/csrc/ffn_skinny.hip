@@ -13,6 +13,8 @@
 // experts. Two launches, gate/up/SwiGLU (-> H, bf16) then down (-> fp32 rows), each a
 // grid-stride loop over (expert, 16 features or columns) items built on the device
 // from expert_offsets.
+#include <type_traits>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -22,6 +24,17 @@ constexpr int kSkThreads = 256;  // 4 waves split K
 constexpr int kSkWaves = 4;
 constexpr int kSkMaxE = 1024;
 constexpr int kSkScr = 2048;  // LDS a wave uses to rearrange a chunk pair of one tile
+
+constexpr uint32_t kSkOOB = 0x80000000u;  // a buffer offset past every record: reads zeros
+
+// 8 activation elements (bf16) at element `k` of a lane's row: the row starts at byte
+// offset aoff of the activation buffer; lanes of missing rows carry kSkOOB and read
+// zeros without a memory access.
+__device__ __forceinline__ u32x4 act_load(__amdgpu_buffer_rsrc_t ars, uint32_t aoff, int k) {
+  typedef uint32_t u32x4a __attribute__((ext_vector_type(4)));
+  const u32x4a v = __builtin_amdgcn_raw_buffer_load_b128(ars, (int)(aoff + (uint32_t)k * 2u), 0, 0);
+  return u32x4{v.x, v.y, v.z, v.w};
+}
 
 // Accumulates NW weight tiles of 16 rows (wq: row 0 of each tile, row stride wstride
 // bytes; wsc: the scale row of this lane's column) against one activation row per lane
@@ -36,13 +49,12 @@ constexpr int kSkScr = 2048;  // LDS a wave uses to rearrange a chunk pair of on
 template <int NW>
 __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW], size_t wstride,
                                                   const uint8_t* const (&wsc)[NW],
-                                                  const uint16_t* __restrict__ act, bool valid,
+                                                  __amdgpu_buffer_rsrc_t ars, uint32_t aoff,
                                                   int K, int c_begin, int c_end, bool tail,
                                                   floatx4 (&acc)[NW], unsigned char* scr) {
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, col = lane & 15;
   const int grp8 = lane >> 3, seg8 = lane & 7;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
   __amdgpu_buffer_rsrc_t rs[NW];
 #pragma unroll
@@ -50,32 +62,36 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
     rs[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wq[i]), 0, (int)(16 * wstride), 0x00020000);
   // pairs start at even chunks, so a pair is one aligned 128-byte line of each row; a
   // chunk of a pair outside [c_begin, c_end) reads nothing (an offset past the buffer)
-  for (int c = c_begin & ~1; c < c_end; c += 2) {
+  struct Pair {
+    u32x4 lq[NW][2];   // [tile][rows 0-7 / 8-15], as loaded
+    uint32_t sc[NW][2];
+    u32x4 xv[2][4];
+  };
+  auto load_pair = [&](int c, Pair& P) {
     const int mc = c + (seg8 >> 2);  // this lane's chunk
     const uint32_t lo = mc >= c_begin && mc < c_end ? (uint32_t)(grp8 * wstride) + (uint32_t)(c * 64 + 16 * seg8)
                                                     : 0x80000000u;
-    u32x4 lq[NW][2];
-    uint32_t sc[NW][2];
-    u32x4 xv[2][4];
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rs[i], (int)lo, (int)(8 * h * wstride), kWeightAux);
-        lq[i][h] = u32x4{v.x, v.y, v.z, v.w};
+        P.lq[i][h] = u32x4{v.x, v.y, v.z, v.w};
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int cc = c + j >= c_begin && c + j < c_end ? c + j : c_begin;
-        sc[i][j] = *reinterpret_cast<const uint16_t*>(wsc[i] + cc * 8 + 2 * grp);
+        P.sc[i][j] = *reinterpret_cast<const uint16_t*>(wsc[i] + cc * 8 + 2 * grp);
       }
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int cc = c + j >= c_begin && c + j < c_end ? c + j : c_begin;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) xv[j][s] = valid ? ldg_u32x4(act + cc * 128 + 32 * grp + 8 * s) : zero;
+      for (int s = 0; s < 4; ++s) P.xv[j][s] = act_load(ars, aoff, cc * 128 + 32 * grp + 8 * s);
     }
+  };
+  auto compute_pair = [&](int c, const Pair& P) {
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       // piece (row r, 16-byte segment s) at r * 128 + ((s + r / 2) mod 8) * 16: both the
@@ -84,7 +100,7 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
       for (int h = 0; h < 2; ++h) {
         const int r = 8 * h + grp8;
         *reinterpret_cast<u32x4v*>(scr + r * 128 + ((seg8 + (r >> 1)) & 7) * 16) =
-            u32x4v{lq[i][h].x, lq[i][h].y, lq[i][h].z, lq[i][h].w};
+            u32x4v{P.lq[i][h].x, P.lq[i][h].y, P.lq[i][h].z, P.lq[i][h].w};
       }
       __builtin_amdgcn_wave_barrier();
       u32x4 q[2];
@@ -94,24 +110,47 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
         q[j] = u32x4{v.x, v.y, v.z, v.w};
       }
       __builtin_amdgcn_wave_barrier();
+      // a chunk outside [c_begin, c_end) has zero codes (read past the buffer): its
+      // products are +-0 and leave the sums' bits unchanged
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        if (c + j >= c_begin && c + j < c_end) {
-          const E4M3Split s0 = e4m3_split_b<0>(sc[i][j]);
-          const E4M3Split s1 = e4m3_split_b<1>(sc[i][j]);
+        const E4M3Split s0 = e4m3_split_b<0>(P.sc[i][j]);
+        const E4M3Split s1 = e4m3_split_b<1>(P.sc[i][j]);
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const bf16x8 wv = nvfp4x8_to_bf16(word_of(q[j], s), s < 2 ? s0 : s1);
-            acc[i] = mfma16(wv, u32x4_as_bf16x8(xv[j][s]), acc[i]);
-          }
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 wv = nvfp4x8_to_bf16(word_of(q[j], s), s < 2 ? s0 : s1);
+          acc[i] = mfma16(wv, u32x4_as_bf16x8(P.xv[j][s]), acc[i]);
         }
       }
+    }
+  };
+  // Two pairs in flight: the next pair's loads are issued before the current pair is
+  // computed. Every path consumes each load it issues (no load past the last pair),
+  // so the loads outstanding at each wait are a fixed count.
+  const int c0 = c_begin & ~1;
+  const int np = c_end > c0 ? (c_end - c0 + 1) / 2 : 0;
+  if (np > 0) {
+    Pair P0, P1;
+    load_pair(c0, P0);
+    int p = 0;
+    for (; p + 2 < np; p += 2) {
+      load_pair(c0 + 2 * (p + 1), P1);
+      compute_pair(c0 + 2 * p, P0);
+      load_pair(c0 + 2 * (p + 2), P0);
+      compute_pair(c0 + 2 * (p + 1), P1);
+    }
+    if (p + 1 < np) {
+      load_pair(c0 + 2 * (p + 1), P1);
+      compute_pair(c0 + 2 * p, P0);
+      compute_pair(c0 + 2 * (p + 1), P1);
+    } else {
+      compute_pair(c0 + 2 * p, P0);
     }
   }
   if (tail) {
     // 32-element chunks: lane group g holds elements K0 + 8g .. K0 + 8g + 7 of row col
     for (int K0 = (K / 128) * 128; K0 < K; K0 += 32) {
-      const u32x4 xv = valid ? ldg_u32x4(act + K0 + 8 * grp) : zero;
+      const u32x4 xv = act_load(ars, aoff, K0 + 8 * grp);
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
         const uint32_t q = *reinterpret_cast<const uint32_t*>(wq[i] + (size_t)col * wstride + K0 / 2 + 4 * grp);
@@ -122,39 +161,51 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
   }
 }
 
-// Short K ranges (fewer than four chunks a wave): the same products with the codes
-// loaded straight in the operand layout (one weight row per lane column: wq / wsc) against one
-// activation row per lane column (act), over 128-element chunks [c_begin, c_end) and,
-// when `tail`, the 32-element chunks past the last full 128. Two chunks' loads are in
-// flight at a time. Lanes of missing rows (!valid) load no activations: with a few
-// rows an expert, that keeps the activation traffic far below the weight traffic.
+// Short K ranges (at most four chunks a wave): the same products with the codes loaded
+// straight in the operand layout (lane (grp, col): 16 bytes of weight row col; wq: row 0
+// of each tile, row stride wstride bytes; wsc: the scale row of this lane's column)
+// against one activation row per lane column (at byte offset aoff of the activation
+// buffer), over 128-element chunks [c_begin, c_end) and, when `tail`, the 32-element
+// chunks past the last full 128. The loads of up to four chunks are issued together
+// (slots past c_end load and compute nothing). Lanes
+// of missing rows (aoff past the buffer) load no activations: with a few rows an
+// expert, that keeps the activation traffic far below the weight traffic.
 template <int NW>
-__device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&wq)[NW],
+__device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&wq)[NW], size_t wstride,
                                                   const uint8_t* const (&wsc)[NW],
-                                                  const uint16_t* __restrict__ act, bool valid,
+                                                  __amdgpu_buffer_rsrc_t ars, uint32_t aoff,
                                                   int K, int c_begin, int c_end, bool tail,
                                                   floatx4 (&acc)[NW]) {
-  const int grp = (threadIdx.x & 63) >> 4;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  int c = c_begin;
-  // two chunks in flight per iteration
-  for (; c + 1 < c_end; c += 2) {
-    u32x4 q[2][NW];
-    uint32_t sc[2][NW];
-    u32x4 xv[2][4];
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4, col = lane & 15;
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  __amdgpu_buffer_rsrc_t rs[NW];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int K0 = (c + h) * 128;
+  for (int i = 0; i < NW; ++i)
+    rs[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wq[i]), 0, (int)(16 * wstride), 0x00020000);
+  const uint32_t wrow = (uint32_t)(col * wstride) + (uint32_t)(16 * grp);
+  // N chunks from cb: every load first, then the products (straight-line code for each
+  // count, so no load waits behind another chunk's products)
+  auto run = [&](int cb, auto n_const) {
+    constexpr int N = decltype(n_const)::value;
+    u32x4 q[N][NW];
+    uint32_t sc[N][NW];
+    u32x4 xv[N][4];
+#pragma unroll
+    for (int h = 0; h < N; ++h) {
+      const int K0 = (cb + h) * 128;
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
-        q[h][i] = ldg_nt_u32x4(wq[i] + K0 / 2 + 16 * grp);
+        const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rs[i], (int)(wrow + (uint32_t)(K0 / 2)), 0, kWeightAux);
+        q[h][i] = u32x4{v.x, v.y, v.z, v.w};
         sc[h][i] = *reinterpret_cast<const uint16_t*>(wsc[i] + K0 / 16 + 2 * grp);
       }
 #pragma unroll
-      for (int s = 0; s < 4; ++s) xv[h][s] = valid ? ldg_u32x4(act + K0 + 32 * grp + 8 * s) : zero;
+      for (int s = 0; s < 4; ++s) xv[h][s] = act_load(ars, aoff, K0 + 32 * grp + 8 * s);
     }
+    __builtin_amdgcn_sched_barrier(0);  // every load issued before the first product
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < N; ++h) {
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
         const E4M3Split s0 = e4m3_split_b<0>(sc[h][i]);
@@ -166,37 +217,22 @@ __device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&w
         }
       }
     }
-  }
-  for (; c < c_end; ++c) {
-    const int K0 = c * 128;
-    u32x4 q[NW];
-    uint32_t sc[NW];
-    u32x4 xv[4];
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      q[i] = ldg_nt_u32x4(wq[i] + K0 / 2 + 16 * grp);
-      sc[i] = *reinterpret_cast<const uint16_t*>(wsc[i] + K0 / 16 + 2 * grp);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) xv[s] = valid ? ldg_u32x4(act + K0 + 32 * grp + 8 * s) : zero;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      const E4M3Split s0 = e4m3_split_b<0>(sc[i]);
-      const E4M3Split s1 = e4m3_split_b<1>(sc[i]);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 wv = nvfp4x8_to_bf16(word_of(q[i], s), s < 2 ? s0 : s1);
-        acc[i] = mfma16(wv, u32x4_as_bf16x8(xv[s]), acc[i]);
-      }
-    }
+  };
+  int cb = c_begin;
+  for (; cb + 4 <= c_end; cb += 4) run(cb, std::integral_constant<int, 4>{});
+  switch (c_end - cb) {
+    case 3: run(cb, std::integral_constant<int, 3>{}); break;
+    case 2: run(cb, std::integral_constant<int, 2>{}); break;
+    case 1: run(cb, std::integral_constant<int, 1>{}); break;
+    default: break;
   }
   if (tail) {
     // 32-element chunks: lane group g holds elements K0 + 8g .. K0 + 8g + 7
     for (int K0 = (K / 128) * 128; K0 < K; K0 += 32) {
-      const u32x4 xv = valid ? ldg_u32x4(act + K0 + 8 * grp) : zero;
+      const u32x4 xv = act_load(ars, aoff, K0 + 8 * grp);
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
-        const uint32_t q = *reinterpret_cast<const uint32_t*>(wq[i] + K0 / 2 + 4 * grp);
+        const uint32_t q = *reinterpret_cast<const uint32_t*>(wq[i] + (size_t)col * wstride + K0 / 2 + 4 * grp);
         const E4M3Split s = e4m3_split(wsc[i][K0 / 16 + (grp >> 1)]);
         acc[i] = mfma16(nvfp4x8_to_bf16(q, s), u32x4_as_bf16x8(xv), acc[i]);
       }
@@ -235,45 +271,62 @@ __device__ int skinny_list(const int32_t* __restrict__ offsets, int E, int* s_of
   return *s_cnt;
 }
 
-__global__ __launch_bounds__(kSkThreads) void ffn_skinny_gateup_kernel(FFNArgs a) {
+__global__ __launch_bounds__(kSkThreads, 2) void ffn_skinny_gateup_kernel(FFNArgs a) {
   __shared__ int s_off[kSkMaxE + 1];
   __shared__ int s_e[kSkMaxE], s_r0[kSkMaxE], s_n[kSkMaxE];
   __shared__ int s_cnt;
-  __shared__ floatx4 red[kSkWaves][2][64];
+  __shared__ floatx4 red[2][kSkWaves][2][64];  // two items' partial sums, alternating
   __shared__ __attribute__((aligned(16))) unsigned char s_scr[kSkWaves][kSkScr];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int U = skinny_list(a.offsets, a.E, s_off, s_e, s_r0, s_n, &s_cnt);
+  // x as one buffer (T d 2 < 2^31 bytes, checked by the entry points)
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), 0, (int)((uint32_t)a.T * (uint32_t)a.d * 2u), 0x00020000);
   const int nft = a.f / 16;
   const int nch = a.d / 128;
-  for (int i = blockIdx.x; i < U * nft; i += gridDim.x) {
+  const int items = U * nft;
+  // the sorted_rows entry of routed row `col` of item `it` (rows past the expert's last
+  // repeat it), loaded one item ahead so that the activation loads need not wait for it
+  auto srow_of = [&](int it) {
+    const int uu = it / nft;
+    return a.sorted_rows[s_r0[uu] + min(col, s_n[uu] - 1)];
+  };
+  int srow = (int)blockIdx.x < items ? srow_of(blockIdx.x) : 0;
+  int buf = 0;
+  for (int i = blockIdx.x; i < items; i += gridDim.x, buf ^= 1) {
     const int u = i / nft, ft = i - u * nft;
     const int e = s_e[u], r0 = s_r0[u], ne = s_n[u];
     const size_t wrow0 = (size_t)e * a.f + ft * 16, wrow = wrow0 + col;
     const uint8_t* const wq[2] = {a.gate_q + wrow0 * (a.d / 2), a.up_q + wrow0 * (a.d / 2)};
     const uint8_t* const wsc[2] = {a.gate_s + wrow * (a.d / 16), a.up_s + wrow * (a.d / 16)};
     const bool valid = col < ne;
-    const uint16_t* act = a.x + (size_t)(a.sorted_rows[r0 + (valid ? col : 0)] / a.k) * a.d;
+    // the activation row of routed row `col` (x row sorted_rows[r0 + col] / k)
+    const uint32_t aoff = valid ? (uint32_t)(srow / a.k) * (uint32_t)(a.d * 2) : kSkOOB;
+    if (i + (int)gridDim.x < items) srow = srow_of(i + gridDim.x);
+    // the tensor scales, loaded with the weights (the epilogue needs them)
+    const float tg = a.gate_ts[e], tu = a.up_ts[e];
     floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     if (nch >= 4 * kSkWaves) {
-      decode_accumulate<2>(wq, a.d / 2, wsc, act, valid, a.d, nch * wave / kSkWaves, nch * (wave + 1) / kSkWaves,
+      decode_accumulate<2>(wq, a.d / 2, wsc, xrs, aoff, a.d, nch * wave / kSkWaves, nch * (wave + 1) / kSkWaves,
                            wave == kSkWaves - 1, acc, s_scr[wave]);
     } else {
-      const uint8_t* const wql[2] = {wq[0] + (size_t)col * (a.d / 2), wq[1] + (size_t)col * (a.d / 2)};
-      decode_accumulate_lanes<2>(wql, wsc, act, valid, a.d, nch * wave / kSkWaves, nch * (wave + 1) / kSkWaves,
+      decode_accumulate_lanes<2>(wq, a.d / 2, wsc, xrs, aoff, a.d, nch * wave / kSkWaves, nch * (wave + 1) / kSkWaves,
                                  wave == kSkWaves - 1, acc);
     }
-    red[wave][0][lane] = acc[0];
-    red[wave][1][lane] = acc[1];
+    red[buf][wave][0][lane] = acc[0];
+    red[buf][wave][1][lane] = acc[1];
+    // one barrier an item: the next item writes the other half of red, and the one
+    // after it is written only after this barrier's successor, which wave 0 reaches
+    // once its sums below are done
     __syncthreads();
     if (wave == 0 && valid) {
-      floatx4 G = red[0][0][lane], Uv = red[0][1][lane];
+      floatx4 G = red[buf][0][0][lane], Uv = red[buf][0][1][lane];
 #pragma unroll
       for (int w = 1; w < kSkWaves; ++w) {
-        G += red[w][0][lane];
-        Uv += red[w][1][lane];
+        G += red[buf][w][0][lane];
+        Uv += red[buf][w][1][lane];
       }
-      const float tg = a.gate_ts[e], tu = a.up_ts[e];
       uint32_t hb[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) hb[r] = bf16_rne(silu_f32(tg * G[r]) * (tu * Uv[r]));
@@ -283,45 +336,48 @@ __global__ __launch_bounds__(kSkThreads) void ffn_skinny_gateup_kernel(FFNArgs a
       v.y = hb[2] | (hb[3] << 16);
       *reinterpret_cast<uint2*>(a.h + (size_t)(r0 + col) * a.f + ft * 16 + 4 * grp) = v;
     }
-    __syncthreads();
   }
 }
 
-__global__ __launch_bounds__(kSkThreads) void ffn_skinny_down_kernel(FFNArgs a) {
+__global__ __launch_bounds__(kSkThreads, 3) void ffn_skinny_down_kernel(FFNArgs a) {
   __shared__ int s_off[kSkMaxE + 1];
   __shared__ int s_e[kSkMaxE], s_r0[kSkMaxE], s_n[kSkMaxE];
   __shared__ int s_cnt;
-  __shared__ floatx4 red[kSkWaves][64];
+  __shared__ floatx4 red[2][kSkWaves][64];  // two items' partial sums, alternating
   __shared__ __attribute__((aligned(16))) unsigned char s_scr[kSkWaves][kSkScr];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int U = skinny_list(a.offsets, a.E, s_off, s_e, s_r0, s_n, &s_cnt);
+  // H as one buffer (T k f 2 < 2^31 bytes, checked by the entry points)
+  const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
+      a.h, 0, (int)((uint32_t)a.T * (uint32_t)a.k * (uint32_t)a.f * 2u), 0x00020000);
   const int ndt = a.d / 16;
   const int nch = a.f / 128;
-  for (int i = blockIdx.x; i < U * ndt; i += gridDim.x) {
+  int buf = 0;
+  for (int i = blockIdx.x; i < U * ndt; i += gridDim.x, buf ^= 1) {
     const int u = i / ndt, dt = i - u * ndt;
     const int e = s_e[u], r0 = s_r0[u], ne = s_n[u];
     const size_t wrow0 = (size_t)e * a.d + dt * 16, wrow = wrow0 + col;
     const uint8_t* const wq[1] = {a.down_q + wrow0 * (a.f / 2)};
     const uint8_t* const wsc[1] = {a.down_s + wrow * (a.f / 16)};
     const bool valid = col < ne;
-    const uint16_t* act = a.h + (size_t)(r0 + (valid ? col : 0)) * a.f;
+    // H row r0 + col
+    const uint32_t aoff = valid ? (uint32_t)(r0 + col) * (uint32_t)(a.f * 2) : kSkOOB;
+    const float td = a.down_ts[e];  // loaded with the weights (the epilogue needs it)
     floatx4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
     if (nch >= 4 * kSkWaves) {
-      decode_accumulate<1>(wq, a.f / 2, wsc, act, valid, a.f, nch * wave / kSkWaves, nch * (wave + 1) / kSkWaves,
+      decode_accumulate<1>(wq, a.f / 2, wsc, hrs, aoff, a.f, nch * wave / kSkWaves, nch * (wave + 1) / kSkWaves,
                            wave == kSkWaves - 1, acc, s_scr[wave]);
     } else {
-      const uint8_t* const wql[1] = {wq[0] + (size_t)col * (a.f / 2)};
-      decode_accumulate_lanes<1>(wql, wsc, act, valid, a.f, nch * wave / kSkWaves, nch * (wave + 1) / kSkWaves,
+      decode_accumulate_lanes<1>(wq, a.f / 2, wsc, hrs, aoff, a.f, nch * wave / kSkWaves, nch * (wave + 1) / kSkWaves,
                                  wave == kSkWaves - 1, acc);
     }
-    red[wave][lane] = acc[0];
-    __syncthreads();
+    red[buf][wave][lane] = acc[0];
+    __syncthreads();  // one barrier an item (red alternates, as in the gate/up kernel)
     if (wave == 0 && valid) {
-      floatx4 O = red[0][lane];
+      floatx4 O = red[buf][0][lane];
 #pragma unroll
-      for (int w = 1; w < kSkWaves; ++w) O += red[w][lane];
-      const float td = a.down_ts[e];
+      for (int w = 1; w < kSkWaves; ++w) O += red[buf][w][lane];
       float4 v;
       v.x = td * O[0];
       v.y = td * O[1];
@@ -329,7 +385,6 @@ __global__ __launch_bounds__(kSkThreads) void ffn_skinny_down_kernel(FFNArgs a) 
       v.w = td * O[3];
       *reinterpret_cast<float4*>(a.y_rows + (size_t)(r0 + col) * a.d + dt * 16 + 4 * grp) = v;
     }
-    __syncthreads();
   }
 }
 

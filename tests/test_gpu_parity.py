@@ -91,6 +91,7 @@ SMALL = [
     (300, 512, 256, 6, 2),   # prompt path, d and f multiples of 256, ragged tiles
     (70, 256, 512, 3, 2),    # the same with f > d
     (150, 352, 320, 8, 2),   # prompt path, K stage counts 6 (half last stage) and 5
+    (40, 2336, 2208, 8, 2),  # streaming kernels' line loads: chunk ranges of odd bounds, K tails
 ]
 
 
