@@ -7,12 +7,14 @@
 // pages read each selected expert's weights once for all of its rows
 // [FP4-Local checkpoints on DGX Spark, §4 Round 1, #808]; so these experts (at most
 // kSkinnyRows rows each) take the weight-streaming form of the decode path instead:
-// one 16x16x32 bf16 MFMA tile covers all rows of an expert, each lane streams one
-// weight row's packed codes with 128-bit loads, decodes them in registers, and four
-// waves split K and add their sums in LDS in wave order. The grouped GEMM skips these
-// experts. Two launches, gate/up/SwiGLU (-> H, bf16) then down (-> fp32 rows), each a
-// grid-stride loop over (expert, 16 features or columns) items built on the device
-// from expert_offsets.
+// one 16x16x32 bf16 MFMA tile covers all rows of an expert, the codes stream in with
+// 128-bit loads and are decoded in registers, and four waves split K and add their
+// sums in LDS in wave order. The grouped GEMM skips these experts. Two launches,
+// gate/up/SwiGLU (-> H, bf16) then down (-> fp32 rows), each a grid-stride loop over
+// items built on the device from expert_offsets: (expert, 32 features) of gate and up,
+// (expert, 64 columns) of down, four 16-row weight tiles an item that share each
+// activation load (the activation operands, mostly lanes of missing rows, are what the
+// load data path carries most of).
 #include <type_traits>
 
 #include "device.hpp"
@@ -24,6 +26,8 @@ constexpr int kSkThreads = 256;  // 4 waves split K
 constexpr int kSkWaves = 4;
 constexpr int kSkMaxE = 1024;
 constexpr int kSkScr = 2048;  // LDS a wave uses to rearrange a chunk pair of one tile
+constexpr int kSkGuTiles = 2;  // 16-feature tiles of a gate/up item (each of gate and up)
+constexpr int kSkDnTiles = 4;  // 16-column tiles of a down item (one per wave in the sums)
 
 constexpr uint32_t kSkOOB = 0x80000000u;  // a buffer offset past every record: reads zeros
 
@@ -37,17 +41,18 @@ __device__ __forceinline__ u32x4 act_load(__amdgpu_buffer_rsrc_t ars, uint32_t a
 }
 
 // Accumulates NW weight tiles of 16 rows (wq: row 0 of each tile, row stride wstride
-// bytes; wsc: the scale row of this lane's column) against one activation row per lane
-// column (act), over 128-element chunks [c_begin, c_end) and, when `tail`, the
-// 32-element chunks past the last full 128. A pair of chunks is loaded at a time, along
-// the rows: load i of a tile gives lane group lane / 8 the 128 bytes (one cache line) of
-// row 8i + lane / 8, so a load touches 8 lines instead of 64 bytes of 16 rows; the wave
-// then rearranges the pair through its 2 KB LDS scratch `scr` into the MFMA operand
-// layout (lane group g: elements 32g .. 32g + 31 of each chunk). Lanes of missing rows
-// (!valid) load no activations: with a few rows an expert, that keeps the activation
-// traffic far below the weight traffic.
+// bytes; tiles nvalid.. are absent and read zeros; wsc: the scale row of this lane's
+// column) against one activation row per lane column (at byte offset aoff of the
+// activation buffer), over 128-element chunks [c_begin, c_end) and, when `tail`, the
+// 32-element chunks past the last full 128. The NW tiles share each activation load.
+// A pair of chunks is loaded at a time, along the rows: load i of a tile gives lane
+// group lane / 8 the 128 bytes (one cache line) of row 8i + lane / 8, so a load touches
+// 8 lines instead of 64 bytes of 16 rows; the wave then rearranges the pair through its
+// 2 KB LDS scratch `scr` into the MFMA operand layout (lane group g: elements
+// 32g .. 32g + 31 of each chunk). Lanes of missing rows (aoff past the buffer) load no
+// activations.
 template <int NW>
-__device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW], size_t wstride,
+__device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW], int nvalid, size_t wstride,
                                                   const uint8_t* const (&wsc)[NW],
                                                   __amdgpu_buffer_rsrc_t ars, uint32_t aoff,
                                                   int K, int c_begin, int c_end, bool tail,
@@ -59,7 +64,8 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
   __amdgpu_buffer_rsrc_t rs[NW];
 #pragma unroll
   for (int i = 0; i < NW; ++i)
-    rs[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wq[i]), 0, (int)(16 * wstride), 0x00020000);
+    rs[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wq[i]), 0, i < nvalid ? (int)(16 * wstride) : 0,
+                                              0x00020000);
   // pairs start at even chunks, so a pair is one aligned 128-byte line of each row; a
   // chunk of a pair outside [c_begin, c_end) reads nothing (an offset past the buffer)
   struct Pair {
@@ -163,15 +169,14 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
 
 // Short K ranges (at most four chunks a wave): the same products with the codes loaded
 // straight in the operand layout (lane (grp, col): 16 bytes of weight row col; wq: row 0
-// of each tile, row stride wstride bytes; wsc: the scale row of this lane's column)
-// against one activation row per lane column (at byte offset aoff of the activation
-// buffer), over 128-element chunks [c_begin, c_end) and, when `tail`, the 32-element
-// chunks past the last full 128. The loads of up to four chunks are issued together
-// (slots past c_end load and compute nothing). Lanes
-// of missing rows (aoff past the buffer) load no activations: with a few rows an
-// expert, that keeps the activation traffic far below the weight traffic.
+// of each tile, row stride wstride bytes, tiles nvalid.. absent; wsc: the scale row of
+// this lane's column) against one activation row per lane column (at byte offset aoff
+// of the activation buffer), over 128-element chunks [c_begin, c_end) and, when `tail`,
+// the 32-element chunks past the last full 128. The loads of up to four chunks are
+// issued together (slots past c_end load and compute nothing). Lanes of missing rows
+// (aoff past the buffer) load no activations.
 template <int NW>
-__device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&wq)[NW], size_t wstride,
+__device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&wq)[NW], int nvalid, size_t wstride,
                                                   const uint8_t* const (&wsc)[NW],
                                                   __amdgpu_buffer_rsrc_t ars, uint32_t aoff,
                                                   int K, int c_begin, int c_end, bool tail,
@@ -182,7 +187,8 @@ __device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&w
   __amdgpu_buffer_rsrc_t rs[NW];
 #pragma unroll
   for (int i = 0; i < NW; ++i)
-    rs[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wq[i]), 0, (int)(16 * wstride), 0x00020000);
+    rs[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wq[i]), 0, i < nvalid ? (int)(16 * wstride) : 0,
+                                              0x00020000);
   const uint32_t wrow = (uint32_t)(col * wstride) + (uint32_t)(16 * grp);
   // N chunks from cb: every load first, then the products (straight-line code for each
   // count, so no load waits behind another chunk's products)
@@ -275,7 +281,7 @@ __global__ __launch_bounds__(kSkThreads, 2) void ffn_skinny_gateup_kernel(FFNArg
   __shared__ int s_off[kSkMaxE + 1];
   __shared__ int s_e[kSkMaxE], s_r0[kSkMaxE], s_n[kSkMaxE];
   __shared__ int s_cnt;
-  __shared__ floatx4 red[2][kSkWaves][2][64];  // two items' partial sums, alternating
+  __shared__ floatx4 red[2][kSkWaves][2 * kSkGuTiles][64];  // two items' partial sums, alternating
   __shared__ __attribute__((aligned(16))) unsigned char s_scr[kSkWaves][kSkScr];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
@@ -283,67 +289,79 @@ __global__ __launch_bounds__(kSkThreads, 2) void ffn_skinny_gateup_kernel(FFNArg
   // x as one buffer (T d 2 < 2^31 bytes, checked by the entry points)
   const __amdgpu_buffer_rsrc_t xrs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), 0, (int)((uint32_t)a.T * (uint32_t)a.d * 2u), 0x00020000);
-  const int nft = a.f / 16;
+  const int nfg = a.f / (16 * kSkGuTiles);  // f is a multiple of 32
   const int nch = a.d / 128;
-  const int items = U * nft;
+  const int items = U * nfg;
   // the sorted_rows entry of routed row `col` of item `it` (rows past the expert's last
   // repeat it), loaded one item ahead so that the activation loads need not wait for it
   auto srow_of = [&](int it) {
-    const int uu = it / nft;
+    const int uu = it / nfg;
     return a.sorted_rows[s_r0[uu] + min(col, s_n[uu] - 1)];
   };
   int srow = (int)blockIdx.x < items ? srow_of(blockIdx.x) : 0;
   int buf = 0;
   for (int i = blockIdx.x; i < items; i += gridDim.x, buf ^= 1) {
-    const int u = i / nft, ft = i - u * nft;
+    const int u = i / nfg, fg = i - u * nfg;
     const int e = s_e[u], r0 = s_r0[u], ne = s_n[u];
-    const size_t wrow0 = (size_t)e * a.f + ft * 16, wrow = wrow0 + col;
-    const uint8_t* const wq[2] = {a.gate_q + wrow0 * (a.d / 2), a.up_q + wrow0 * (a.d / 2)};
-    const uint8_t* const wsc[2] = {a.gate_s + wrow * (a.d / 16), a.up_s + wrow * (a.d / 16)};
+    // tiles: gate features 16t.., t < kSkGuTiles, then up
+    const size_t wrow0 = (size_t)e * a.f + (size_t)fg * (16 * kSkGuTiles);
+    const uint8_t* wq[2 * kSkGuTiles];
+    const uint8_t* wsc[2 * kSkGuTiles];
+#pragma unroll
+    for (int t = 0; t < kSkGuTiles; ++t) {
+      wq[t] = a.gate_q + (wrow0 + 16 * t) * (a.d / 2);
+      wq[kSkGuTiles + t] = a.up_q + (wrow0 + 16 * t) * (a.d / 2);
+      wsc[t] = a.gate_s + (wrow0 + 16 * t + col) * (a.d / 16);
+      wsc[kSkGuTiles + t] = a.up_s + (wrow0 + 16 * t + col) * (a.d / 16);
+    }
     const bool valid = col < ne;
     // the activation row of routed row `col` (x row sorted_rows[r0 + col] / k)
     const uint32_t aoff = valid ? (uint32_t)(srow / a.k) * (uint32_t)(a.d * 2) : kSkOOB;
     if (i + (int)gridDim.x < items) srow = srow_of(i + gridDim.x);
     // the tensor scales, loaded with the weights (the epilogue needs them)
     const float tg = a.gate_ts[e], tu = a.up_ts[e];
-    floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    floatx4 acc[2 * kSkGuTiles];
+#pragma unroll
+    for (int t = 0; t < 2 * kSkGuTiles; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (nch >= 4 * kSkWaves) {
-      decode_accumulate<2>(wq, a.d / 2, wsc, xrs, aoff, a.d, nch * wave / kSkWaves, nch * (wave + 1) / kSkWaves,
-                           wave == kSkWaves - 1, acc, s_scr[wave]);
+      decode_accumulate<2 * kSkGuTiles>(wq, 2 * kSkGuTiles, a.d / 2, wsc, xrs, aoff, a.d, nch * wave / kSkWaves,
+                                        nch * (wave + 1) / kSkWaves, wave == kSkWaves - 1, acc, s_scr[wave]);
     } else {
-      decode_accumulate_lanes<2>(wq, a.d / 2, wsc, xrs, aoff, a.d, nch * wave / kSkWaves, nch * (wave + 1) / kSkWaves,
-                                 wave == kSkWaves - 1, acc);
+      decode_accumulate_lanes<2 * kSkGuTiles>(wq, 2 * kSkGuTiles, a.d / 2, wsc, xrs, aoff, a.d, nch * wave / kSkWaves,
+                                              nch * (wave + 1) / kSkWaves, wave == kSkWaves - 1, acc);
     }
-    red[buf][wave][0][lane] = acc[0];
-    red[buf][wave][1][lane] = acc[1];
+#pragma unroll
+    for (int t = 0; t < 2 * kSkGuTiles; ++t) red[buf][wave][t][lane] = acc[t];
     // one barrier an item: the next item writes the other half of red, and the one
-    // after it is written only after this barrier's successor, which wave 0 reaches
-    // once its sums below are done
+    // after it is written only after this barrier's successor, which the summing
+    // waves reach once their sums below are done
     __syncthreads();
-    if (wave == 0 && valid) {
-      floatx4 G = red[buf][0][0][lane], Uv = red[buf][0][1][lane];
+    if (wave < kSkGuTiles && valid) {
+      // wave t sums feature tile t: gate partials [t], up partials [kSkGuTiles + t]
+      const int t = wave;
+      floatx4 G = red[buf][0][t][lane], Uv = red[buf][0][kSkGuTiles + t][lane];
 #pragma unroll
       for (int w = 1; w < kSkWaves; ++w) {
-        G += red[buf][w][0][lane];
-        Uv += red[buf][w][1][lane];
+        G += red[buf][w][t][lane];
+        Uv += red[buf][w][kSkGuTiles + t][lane];
       }
       uint32_t hb[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) hb[r] = bf16_rne(silu_f32(tg * G[r]) * (tu * Uv[r]));
-      // lane holds routed row `col`, features 4*grp .. 4*grp + 3 of the tile
+      // lane holds routed row `col`, features 4*grp .. 4*grp + 3 of tile t
       uint2 v;
       v.x = hb[0] | (hb[1] << 16);
       v.y = hb[2] | (hb[3] << 16);
-      *reinterpret_cast<uint2*>(a.h + (size_t)(r0 + col) * a.f + ft * 16 + 4 * grp) = v;
+      *reinterpret_cast<uint2*>(a.h + (size_t)(r0 + col) * a.f + (size_t)fg * (16 * kSkGuTiles) + 16 * t + 4 * grp) = v;
     }
   }
 }
 
-__global__ __launch_bounds__(kSkThreads, 3) void ffn_skinny_down_kernel(FFNArgs a) {
+__global__ __launch_bounds__(kSkThreads, 2) void ffn_skinny_down_kernel(FFNArgs a) {
   __shared__ int s_off[kSkMaxE + 1];
   __shared__ int s_e[kSkMaxE], s_r0[kSkMaxE], s_n[kSkMaxE];
   __shared__ int s_cnt;
-  __shared__ floatx4 red[2][kSkWaves][64];  // two items' partial sums, alternating
+  __shared__ floatx4 red[2][kSkWaves][kSkDnTiles][64];  // two items' partial sums, alternating
   __shared__ __attribute__((aligned(16))) unsigned char s_scr[kSkWaves][kSkScr];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
@@ -352,38 +370,51 @@ __global__ __launch_bounds__(kSkThreads, 3) void ffn_skinny_down_kernel(FFNArgs 
   const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
       a.h, 0, (int)((uint32_t)a.T * (uint32_t)a.k * (uint32_t)a.f * 2u), 0x00020000);
   const int ndt = a.d / 16;
+  const int ndg = (ndt + kSkDnTiles - 1) / kSkDnTiles;  // column groups (the last may be short)
   const int nch = a.f / 128;
   int buf = 0;
-  for (int i = blockIdx.x; i < U * ndt; i += gridDim.x, buf ^= 1) {
-    const int u = i / ndt, dt = i - u * ndt;
+  for (int i = blockIdx.x; i < U * ndg; i += gridDim.x, buf ^= 1) {
+    const int u = i / ndg, dg = i - u * ndg;
     const int e = s_e[u], r0 = s_r0[u], ne = s_n[u];
-    const size_t wrow0 = (size_t)e * a.d + dt * 16, wrow = wrow0 + col;
-    const uint8_t* const wq[1] = {a.down_q + wrow0 * (a.f / 2)};
-    const uint8_t* const wsc[1] = {a.down_s + wrow * (a.f / 16)};
+    const int nt = min(kSkDnTiles, ndt - dg * kSkDnTiles);  // tiles of this group
+    const uint8_t* wq[kSkDnTiles];
+    const uint8_t* wsc[kSkDnTiles];
+#pragma unroll
+    for (int t = 0; t < kSkDnTiles; ++t) {
+      // absent tiles (t >= nt) point at tile 0 and read zeros
+      const size_t wrow0 = (size_t)e * a.d + (size_t)(dg * kSkDnTiles + (t < nt ? t : 0)) * 16;
+      wq[t] = a.down_q + wrow0 * (a.f / 2);
+      wsc[t] = a.down_s + (wrow0 + col) * (a.f / 16);
+    }
     const bool valid = col < ne;
     // H row r0 + col
     const uint32_t aoff = valid ? (uint32_t)(r0 + col) * (uint32_t)(a.f * 2) : kSkOOB;
     const float td = a.down_ts[e];  // loaded with the weights (the epilogue needs it)
-    floatx4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
-    if (nch >= 4 * kSkWaves) {
-      decode_accumulate<1>(wq, a.f / 2, wsc, hrs, aoff, a.f, nch * wave / kSkWaves, nch * (wave + 1) / kSkWaves,
-                           wave == kSkWaves - 1, acc, s_scr[wave]);
-    } else {
-      decode_accumulate_lanes<1>(wq, a.f / 2, wsc, hrs, aoff, a.f, nch * wave / kSkWaves, nch * (wave + 1) / kSkWaves,
-                                 wave == kSkWaves - 1, acc);
-    }
-    red[buf][wave][lane] = acc[0];
-    __syncthreads();  // one barrier an item (red alternates, as in the gate/up kernel)
-    if (wave == 0 && valid) {
-      floatx4 O = red[buf][0][lane];
+    floatx4 acc[kSkDnTiles];
 #pragma unroll
-      for (int w = 1; w < kSkWaves; ++w) O += red[buf][w][lane];
+    for (int t = 0; t < kSkDnTiles; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (nch >= 4 * kSkWaves) {
+      decode_accumulate<kSkDnTiles>(wq, nt, a.f / 2, wsc, hrs, aoff, a.f, nch * wave / kSkWaves,
+                                    nch * (wave + 1) / kSkWaves, wave == kSkWaves - 1, acc, s_scr[wave]);
+    } else {
+      decode_accumulate_lanes<kSkDnTiles>(wq, nt, a.f / 2, wsc, hrs, aoff, a.f, nch * wave / kSkWaves,
+                                          nch * (wave + 1) / kSkWaves, wave == kSkWaves - 1, acc);
+    }
+#pragma unroll
+    for (int t = 0; t < kSkDnTiles; ++t) red[buf][wave][t][lane] = acc[t];
+    __syncthreads();  // one barrier an item (red alternates, as in the gate/up kernel)
+    if (wave < nt && valid) {
+      // wave t sums column tile t
+      const int t = wave;
+      floatx4 O = red[buf][0][t][lane];
+#pragma unroll
+      for (int w = 1; w < kSkWaves; ++w) O += red[buf][w][t][lane];
       float4 v;
       v.x = td * O[0];
       v.y = td * O[1];
       v.z = td * O[2];
       v.w = td * O[3];
-      *reinterpret_cast<float4*>(a.y_rows + (size_t)(r0 + col) * a.d + dt * 16 + 4 * grp) = v;
+      *reinterpret_cast<float4*>(a.y_rows + (size_t)(r0 + col) * a.d + (size_t)(dg * kSkDnTiles + t) * 16 + 4 * grp) = v;
     }
   }
 }
