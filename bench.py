@@ -41,12 +41,12 @@ FP8_PEAK_TFLOPS = 5000.0        # MI355X published dense fp8 MFMA rate
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 # kernel sources whose hash a traffic record must match, per path
 DECODE_FILES = ["ffn_decode.hip", "route_device.hpp", "device.hpp"]
-PROMPT_FILES = ["ffn_prompt.hip", "ffn_skinny.hip", "device.hpp"]
+PROMPT_FILES = ["ffn_prompt.hip", "skinny_device.hpp", "device.hpp"]
 MXFP8_FILES = ["mxfp8.hip", "device.hpp"]
 ROUTER_FILES = ["router.hip", "device.hpp"]
 W8A8_FILES = ["mxfp8_w8a8.hip", "device.hpp"]
-PROMPT_KERNELS = ("moe_expert_ffn_nvfp4 prompt path (ffn_prompt_kernel grouped GEMM gate/up + down; "
-                  "ffn_skinny gate/up + down for experts with <= 16 rows)")
+PROMPT_KERNELS = ("moe_expert_ffn_nvfp4 prompt path (ffn_prompt_kernel gate/up, then down: the grouped GEMM's "
+                  "tiles, then the weight-streaming items of the experts with <= 32 rows)")
 
 
 def log(*a):

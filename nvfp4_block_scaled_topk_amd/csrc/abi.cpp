@@ -54,11 +54,12 @@ uint32_t next_call_tag() {
   return t;
 }
 
-// H: bf16 for the prompt path, bf16 + tag (4 bytes an element) for the decode path, which
-// also keeps its epoch word (graph capture) after H
+// H: bf16 for the prompt path, bf16 + tag (4 bytes an element) for the decode path; after
+// H the decode path keeps its epoch word (graph capture), the prompt path its two work
+// counters (kEpochBytes either way)
 size_t h_bytes(int T, int d, int f, int k) {
   const bool dec = moe::use_decode_path(T, d, f);
-  return round_up((size_t)T * k * f * (dec ? 4 : 2)) + (dec ? moe::kEpochBytes : 0);
+  return round_up((size_t)T * k * f * (dec ? 4 : 2)) + moe::kEpochBytes;
 }
 uint32_t* epoch_word(void* workspace, int T, int d, int f, int k) {
   return reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(workspace) + h_bytes(T, d, f, k) - moe::kEpochBytes);
@@ -170,6 +171,7 @@ int ffn_setup(const uint16_t* x, int T, int d, int f, int E, int k, const moe_nv
   a.y_rows = y_rows;
   a.h = static_cast<uint16_t*>(workspace);
   if (moe::use_decode_path(T, d, f)) a.epoch = epoch_word(workspace, T, d, f, k);
+  else a.work_ctr = epoch_word(workspace, T, d, f, k);  // the same slot after H
   return MOE_OK;
 }
 

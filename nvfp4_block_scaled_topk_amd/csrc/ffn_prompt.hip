@@ -30,6 +30,7 @@
 // activation rows and weight columns in that XCD's L2.
 #include "device.hpp"
 #include "internal.hpp"
+#include "skinny_device.hpp"
 
 #include <type_traits>
 
@@ -405,6 +406,16 @@ __global__ __launch_bounds__(kPromptThreads, 2) void ffn_prompt_kernel(FFNArgs a
       }
     }
   }
+  // Then the weight-streaming items of the experts with at most kSkinnyRows rows, from
+  // the launch's counter: a block that runs out of tiles early (the last round of
+  // tiles is partly filled) starts on them at once. The LDS is theirs once every wave
+  // is done with the last tile.
+  __syncthreads();
+  skinny_phase<MODE>(a, smem, a.work_ctr + MODE);
+}
+
+__global__ void zero_words_kernel(uint32_t* w, int n) {
+  if ((int)threadIdx.x < n) w[threadIdx.x] = 0u;
 }
 
 hipError_t launch_ffn_prompt(const FFNArgs& a, hipStream_t stream) {
@@ -414,20 +425,17 @@ hipError_t launch_ffn_prompt(const FFNArgs& a, hipStream_t stream) {
   int ncu = 0;
   err = device_cu_count(ncu);
   if (err != hipSuccess) return err;
-  const long long rows = (long long)a.T * a.k;
-  const long long max_tiles = rows / kPromptRows + std::min<long long>(a.E, rows);
+  // a persistent grid of two blocks a CU: tiles first, then the streaming items
+  const int grid = kPromptBlocksPerCu * ncu;
   const int ct_gu = (a.f + 127) / 128;
-  const int grid_gu = (int)std::min<long long>(max_tiles * ct_gu, (long long)kPromptBlocksPerCu * ncu);
-  err = launch_ffn_skinny_gateup(a, stream);
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(ffn_prompt_kernel<0>, dim3(grid_gu), dim3(kPromptThreads), kPromptLdsBytes, stream, a, ct_gu);
+  const int ct_dn = (a.d + 255) / 256;
+  hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, stream, a.work_ctr, 2);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  err = launch_ffn_skinny_down(a, stream);
+  hipLaunchKernelGGL(ffn_prompt_kernel<0>, dim3(grid), dim3(kPromptThreads), kPromptLdsBytes, stream, a, ct_gu);
+  err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int ct_dn = (a.d + 255) / 256;
-  const int grid_dn = (int)std::min<long long>(max_tiles * ct_dn, (long long)kPromptBlocksPerCu * ncu);
-  hipLaunchKernelGGL(ffn_prompt_kernel<1>, dim3(grid_dn), dim3(kPromptThreads), kPromptLdsBytes, stream, a, ct_dn);
+  hipLaunchKernelGGL(ffn_prompt_kernel<1>, dim3(grid), dim3(kPromptThreads), kPromptLdsBytes, stream, a, ct_dn);
   return hipGetLastError();
 }
 

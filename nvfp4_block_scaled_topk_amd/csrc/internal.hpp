@@ -57,6 +57,9 @@ struct FFNArgs {
   // few-token path: a 32-bit word in the workspace holding the tag of the latest call made
   // under HIP graph capture (see launch_ffn_decode)
   uint32_t* epoch = nullptr;
+  // prompt path: two 32-bit work counters in the workspace (gate/up, down), zeroed by
+  // the launch itself before its kernels take items from them
+  uint32_t* work_ctr = nullptr;
 };
 // Bytes a few-token workspace keeps for that word (at its end).
 constexpr size_t kEpochBytes = 256;
@@ -99,8 +102,9 @@ void ffn_force_path(int path);
 hipError_t ffn_recorded_path(int T, int d, int f, int E, int k, int& path);  // -1 when none is recorded
 hipError_t ffn_record_path(int T, int d, int f, int E, int k, int path);
 // Prompt batches: experts with at most kSkinnyRows rows take the weight-streaming
-// kernels (ffn_skinny.hip); the grouped GEMM takes the others.
-constexpr int kSkinnyRows = 16;
+// kernels (ffn_skinny.hip: 1..16 rows as one 16-row set, 17..32 as two); the grouped
+// GEMM takes the others.
+constexpr int kSkinnyRows = 32;
 hipError_t launch_ffn_skinny_gateup(const FFNArgs& a, hipStream_t stream);
 hipError_t launch_ffn_skinny_down(const FFNArgs& a, hipStream_t stream);
 

@@ -40,21 +40,20 @@ def check_band(rep, case, part="out"):
     return rep
 
 
-def cover_tokens(offsets, sorted_rows, k, tile=128, skinny=16):
+def cover_tokens(offsets, sorted_rows, k, tile=128, skinny=32, rowset=16):
     """Tokens whose routed rows cover every grouped-GEMM tile and every weight-streaming
     expert of a prompt batch: for an expert with more than `skinny` rows, the first and
-    last row of each `tile`-row tile; for the others, their first and last row."""
+    last row of each `tile`-row tile; for the others, the first and last row of each of
+    their `rowset`-row sets."""
     off = np.asarray(offsets, dtype=np.int64)
     rows = []
     for e in range(off.size - 1):
         a, b = int(off[e]), int(off[e + 1])
         if b == a:
             continue
-        if b - a > skinny:
-            for t0 in range(a, b, tile):
-                rows += [t0, min(t0 + tile, b) - 1]
-        else:
-            rows += [a, b - 1]
+        step = tile if b - a > skinny else rowset
+        for t0 in range(a, b, step):
+            rows += [t0, min(t0 + step, b) - 1]
     return np.unique(np.asarray(sorted_rows, dtype=np.int64)[np.asarray(rows)] // k)
 
 
