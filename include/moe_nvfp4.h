@@ -161,8 +161,8 @@ int moe_route_topk_policy(const float* logits, int T, int E, int k, int policy, 
  * x is bf16 [T][d]; y_rows is fp32 [T*k][d]. expert_offsets / sorted_rows are the
  * device outputs of moe_route_topk for the same T, E, k.
  * Sizes: 1 <= T, d and f multiples of 32 (>= 32), 1 <= E <= 1024, 1 <= k <= min(E, 32).
- * Workspace: at least moe_expert_ffn_nvfp4_workspace(T, d, f, E, k) bytes (holds H; no
- * initial contents needed). Calls that share a workspace must be ordered on one stream;
+ * Workspace: at least moe_expert_ffn_nvfp4_workspace(T, d, f, E, k) bytes (holds H and, for
+ * batches, two work counters that each call clears itself; no initial contents needed). Calls that share a workspace must be ordered on one stream;
  * calls with different workspaces may run concurrently on different streams.
  * Few tokens (T <= 16, d <= 4096, f <= 1024 and T * (max(d, f) + 8) * 2 <= 64 KiB) run as
  * one launch in which the down-product workgroups wait for the gate/up workgroups of the
