@@ -30,7 +30,8 @@ namespace moe {
 constexpr int kSkThreads = 256;  // 4 waves split K
 constexpr int kSkWaves = 4;
 constexpr int kSkMaxE = 1024;
-constexpr int kSkScr = 2048;  // LDS a wave uses to rearrange a chunk pair of one tile
+constexpr int kSkScrScale = 1024;          // the part of it that regroups a pair's block scales
+constexpr int kSkScr = 2048 + kSkScrScale;  // LDS a wave uses to rearrange a chunk pair of one tile
 
 constexpr uint32_t kSkOOB = 0x80000000u;  // a buffer offset past every record: reads zeros
 
@@ -54,13 +55,16 @@ __device__ __forceinline__ u32x4 act_load(__amdgpu_buffer_rsrc_t ars, uint32_t a
 // 8 lines instead of 64 bytes of 16 rows; the wave then rearranges the pair through its
 // 2 KB LDS scratch `scr` into the MFMA operand layout (lane group g: elements
 // 32g .. 32g + 31 of each chunk). Lanes of missing rows (aoff past the buffer) load no
-// activations.
+// activations. Block scales: K is a multiple of 256, so a scale row holds whole 16-byte
+// pairs, and one 16-byte load a lane brings a pair's scales of all NW tiles (lane l:
+// tile (l / 16) mod NW, row l mod 16, through the per-lane pointer wsl to that row's
+// scales), which the wave regroups through the last kSkScrScale bytes of its scratch.
 template <int NW, int RS>
 __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW], int nvalid, size_t wstride,
-                                                  const uint8_t* const (&wsc)[NW],
+                                                  const uint8_t* wsl,
                                                   __amdgpu_buffer_rsrc_t ars, const uint32_t (&aoff)[RS],
-                                                  int K, int c_begin, int c_end, bool tail,
-                                                  floatx4 (&acc)[NW][RS], unsigned char* scr) {
+                                                  int c_begin, int c_end, floatx4 (&acc)[NW][RS],
+                                                  unsigned char* scr) {
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, col = lane & 15;
   const int grp8 = lane >> 3, seg8 = lane & 7;
@@ -74,7 +78,7 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
   // chunk of a pair outside [c_begin, c_end) reads nothing (an offset past the buffer)
   struct Pair {
     u32x4 lq[NW][2];   // [tile][rows 0-7 / 8-15], as loaded
-    uint32_t sc[NW][2];
+    u32x4 scq;         // this lane's 16 scale bytes of the pair (tile, row as above)
     u32x4 xv[RS][2][4];
   };
   auto load_pair = [&](int c, Pair& P) {
@@ -88,12 +92,10 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
         const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rs[i], (int)lo, (int)(8 * h * wstride), kWeightAux);
         P.lq[i][h] = u32x4{v.x, v.y, v.z, v.w};
       }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int cc = c + j >= c_begin && c + j < c_end ? c + j : c_begin;
-        P.sc[i][j] = *reinterpret_cast<const uint16_t*>(wsc[i] + cc * 8 + 2 * grp);
-      }
     }
+    // a chunk of the pair outside [c_begin, c_end) gets its own scales (its codes are
+    // zero, so they scale nothing)
+    P.scq = *reinterpret_cast<const u32x4*>(wsl + c * 8);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int cc = c + j >= c_begin && c + j < c_end ? c + j : c_begin;
@@ -104,6 +106,20 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
     }
   };
   auto compute_pair = [&](int c, const Pair& P) {
+    // lane l's bytes (chunk c: x, y; chunk c + 1: z, w) regrouped as four dwords, dword g
+    // holding what lane group g of the lane's row needs, then read back per tile:
+    // scw[i] = [chunk c: bytes 2 grp, 2 grp + 1 | chunk c + 1: the same] of tile i, row col
+    uint32_t scw[NW];
+    {
+      unsigned char* const ss = scr + kSkScr - kSkScrScale;
+      *reinterpret_cast<u32x4v*>(ss + lane * 16) =
+          u32x4v{__builtin_amdgcn_perm(P.scq.z, P.scq.x, 0x05040100u), __builtin_amdgcn_perm(P.scq.z, P.scq.x, 0x07060302u),
+                 __builtin_amdgcn_perm(P.scq.w, P.scq.y, 0x05040100u), __builtin_amdgcn_perm(P.scq.w, P.scq.y, 0x07060302u)};
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < NW; ++i) scw[i] = *reinterpret_cast<const uint32_t*>(ss + (i * 16 + col) * 16 + grp * 4);
+      __builtin_amdgcn_wave_barrier();
+    }
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       // piece (row r, 16-byte segment s) at r * 128 + ((s + r / 2) mod 8) * 16: both the
@@ -126,8 +142,8 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
       // products are +-0 and leave the sums' bits unchanged
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const E4M3Split s0 = e4m3_split_b<0>(P.sc[i][j]);
-        const E4M3Split s1 = e4m3_split_b<1>(P.sc[i][j]);
+        const E4M3Split s0 = j == 0 ? e4m3_split_b<0>(scw[i]) : e4m3_split_b<2>(scw[i]);
+        const E4M3Split s1 = j == 0 ? e4m3_split_b<1>(scw[i]) : e4m3_split_b<3>(scw[i]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const bf16x8 wv = nvfp4x8_to_bf16(word_of(q[j], s), s < 2 ? s0 : s1);
@@ -168,38 +184,25 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
       compute_pair(c0 + 2 * p, P0);
     }
   }
-  if (tail) {
-    // 32-element chunks: lane group g holds elements K0 + 8g .. K0 + 8g + 7 of row col
-    for (int K0 = (K / 128) * 128; K0 < K; K0 += 32) {
-      u32x4 xv[RS];
-#pragma unroll
-      for (int r = 0; r < RS; ++r) xv[r] = act_load(ars, aoff[r], K0 + 8 * grp);
-#pragma unroll
-      for (int i = 0; i < NW; ++i) {
-        const uint32_t q = *reinterpret_cast<const uint32_t*>(wq[i] + (size_t)col * wstride + K0 / 2 + 4 * grp);
-        const E4M3Split s = e4m3_split(wsc[i][K0 / 16 + (grp >> 1)]);
-        const bf16x8 wv = nvfp4x8_to_bf16(q, s);
-#pragma unroll
-        for (int r = 0; r < RS; ++r) acc[i][r] = mfma16(wv, u32x4_as_bf16x8(xv[r]), acc[i][r]);
-      }
-    }
-  }
 }
 
-// Short K ranges (at most four chunks a wave): the same products with the codes loaded
+// Short K ranges (at most four chunks a wave), and any K range when K is not a multiple
+// of 256 (in rounds of four chunks): the same products with the codes loaded
 // straight in the operand layout (lane (grp, col): 16 bytes of weight row col; wq: row 0
 // of each tile, row stride wstride bytes, tiles nvalid.. absent; wsc: the scale row of
 // this lane's column) against RS sets of 16 activation rows (row col of set r at byte
 // offset aoff[r] of the activation buffer), over 128-element chunks [c_begin, c_end)
 // and, when `tail`, the 32-element chunks past the last full 128. The loads of up to
-// four chunks (two with two row sets) are issued together. Lanes
-// of missing rows (aoff past the buffer) load no activations.
-template <int NW, int RS>
+// four chunks (two with two row sets) are issued together. Lanes of missing rows (aoff
+// past the buffer) load no activations. With SCQ (K a multiple of 256) the block scales
+// come as in decode_accumulate, a 16-byte load a lane for each chunk pair (through
+// wsl), regrouped through the wave's scratch `scr`.
+template <int NW, int RS, bool SCQ>
 __device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&wq)[NW], int nvalid, size_t wstride,
-                                                  const uint8_t* const (&wsc)[NW],
+                                                  const uint8_t* const (&wsc)[NW], const uint8_t* wsl,
                                                   __amdgpu_buffer_rsrc_t ars, const uint32_t (&aoff)[RS],
                                                   int K, int c_begin, int c_end, bool tail,
-                                                  floatx4 (&acc)[NW][RS]) {
+                                                  floatx4 (&acc)[NW][RS], unsigned char* scr) {
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, col = lane & 15;
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
@@ -213,9 +216,16 @@ __device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&w
   // count, so no load waits behind another chunk's products)
   auto run = [&](int cb, auto n_const) {
     constexpr int N = decltype(n_const)::value;
+    constexpr int NPM = N / 2 + 1;  // chunk pairs that can hold N chunks
     u32x4 q[N][NW];
     uint32_t sc[N][NW];
+    u32x4 scq[SCQ ? NPM : 1];
     u32x4 xv[N][RS][4];
+    const int pf = cb >> 1, pl = (cb + N - 1) >> 1;  // SCQ: first and last pair of the chunks
+    if constexpr (SCQ) {
+#pragma unroll
+      for (int p = 0; p < NPM; ++p) scq[p] = *reinterpret_cast<const u32x4*>(wsl + min(pf + p, pl) * 16);
+    }
 #pragma unroll
     for (int h = 0; h < N; ++h) {
       const int K0 = (cb + h) * 128;
@@ -223,7 +233,7 @@ __device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&w
       for (int i = 0; i < NW; ++i) {
         const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rs[i], (int)(wrow + (uint32_t)(K0 / 2)), 0, kWeightAux);
         q[h][i] = u32x4{v.x, v.y, v.z, v.w};
-        sc[h][i] = *reinterpret_cast<const uint16_t*>(wsc[i] + K0 / 16 + 2 * grp);
+        if constexpr (!SCQ) sc[h][i] = *reinterpret_cast<const uint16_t*>(wsc[i] + K0 / 16 + 2 * grp);
       }
 #pragma unroll
       for (int r = 0; r < RS; ++r)
@@ -231,6 +241,23 @@ __device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&w
         for (int s = 0; s < 4; ++s) xv[h][r][s] = act_load(ars, aoff[r], K0 + 32 * grp + 8 * s);
     }
     __builtin_amdgcn_sched_barrier(0);  // every load issued before the first product
+    if constexpr (SCQ) {
+      // pair p's bytes regrouped as in decode_accumulate (1 KB a pair), then chunk h's two
+      // bytes of tile i, row col, lane group grp read back
+#pragma unroll
+      for (int p = 0; p < NPM; ++p)
+        *reinterpret_cast<u32x4v*>(scr + p * 1024 + lane * 16) =
+            u32x4v{__builtin_amdgcn_perm(scq[p].z, scq[p].x, 0x05040100u), __builtin_amdgcn_perm(scq[p].z, scq[p].x, 0x07060302u),
+                   __builtin_amdgcn_perm(scq[p].w, scq[p].y, 0x05040100u), __builtin_amdgcn_perm(scq[p].w, scq[p].y, 0x07060302u)};
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int h = 0; h < N; ++h)
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+          sc[h][i] = *reinterpret_cast<const uint16_t*>(scr + (((cb + h) >> 1) - pf) * 1024 + (i * 16 + col) * 16 +
+                                                        grp * 4 + ((cb + h) & 1) * 2);
+      __builtin_amdgcn_wave_barrier();
+    }
 #pragma unroll
     for (int h = 0; h < N; ++h) {
 #pragma unroll
@@ -399,12 +426,16 @@ __device__ __forceinline__ void skinny_gateup_item(const FFNArgs& a, __amdgpu_bu
 #pragma unroll
     for (int r = 0; r < RS; ++r) acc[t][r] = floatx4{0.f, 0.f, 0.f, 0.f};
   unsigned char* const scr = L.scr + wave * kSkScr;
-  if (nch >= 4 * kSkWaves) {
-    decode_accumulate<NW, RS>(wq, NW, a.d / 2, wsc, xrs, aoff, a.d, nch * wave / kSkWaves,
-                              nch * (wave + 1) / kSkWaves, wave == kSkWaves - 1, acc, scr);
+  // the scale-load role of this lane (16-byte scale loads): tile (lane / 16) mod NW, row lane mod 16
+  const int lt = (lane >> 4) % NW, lr = lane & 15;
+  const uint8_t* wsl = (lt < FT ? a.gate_s : a.up_s) + (wrow0 + 16 * (lt % FT) + lr) * (a.d / 16);
+  const int c_begin = nch * wave / kSkWaves, c_end = nch * (wave + 1) / kSkWaves;
+  if (a.d % 256 == 0) {
+    if (nch >= 4 * kSkWaves) decode_accumulate<NW, RS>(wq, NW, a.d / 2, wsl, xrs, aoff, c_begin, c_end, acc, scr);
+    else decode_accumulate_lanes<NW, RS, true>(wq, NW, a.d / 2, wsc, wsl, xrs, aoff, a.d, c_begin, c_end, false, acc, scr);
   } else {
-    decode_accumulate_lanes<NW, RS>(wq, NW, a.d / 2, wsc, xrs, aoff, a.d, nch * wave / kSkWaves,
-                                    nch * (wave + 1) / kSkWaves, wave == kSkWaves - 1, acc);
+    decode_accumulate_lanes<NW, RS, false>(wq, NW, a.d / 2, wsc, wsl, xrs, aoff, a.d, c_begin, c_end,
+                                           wave == kSkWaves - 1, acc, scr);
   }
 #pragma unroll
   for (int t = 0; t < NW; ++t)
@@ -468,12 +499,17 @@ __device__ __forceinline__ void skinny_down_item(const FFNArgs& a, __amdgpu_buff
 #pragma unroll
     for (int r = 0; r < RS; ++r) acc[t][r] = floatx4{0.f, 0.f, 0.f, 0.f};
   unsigned char* const scr = L.scr + wave * kSkScr;
-  if (nch >= 4 * kSkWaves) {
-    decode_accumulate<NW, RS>(wq, nt, a.f / 2, wsc, hrs, aoff, a.f, nch * wave / kSkWaves,
-                              nch * (wave + 1) / kSkWaves, wave == kSkWaves - 1, acc, scr);
+  // the scale-load role of this lane (16-byte scale loads): tile (lane / 16) mod NW
+  // (absent tiles: tile 0), row lane mod 16
+  const int lt = (lane >> 4) % NW, lr = lane & 15;
+  const uint8_t* wsl = a.down_s + ((size_t)e * a.d + (size_t)(dg * NW + (lt < nt ? lt : 0)) * 16 + lr) * (a.f / 16);
+  const int c_begin = nch * wave / kSkWaves, c_end = nch * (wave + 1) / kSkWaves;
+  if (a.f % 256 == 0) {
+    if (nch >= 4 * kSkWaves) decode_accumulate<NW, RS>(wq, nt, a.f / 2, wsl, hrs, aoff, c_begin, c_end, acc, scr);
+    else decode_accumulate_lanes<NW, RS, true>(wq, nt, a.f / 2, wsc, wsl, hrs, aoff, a.f, c_begin, c_end, false, acc, scr);
   } else {
-    decode_accumulate_lanes<NW, RS>(wq, nt, a.f / 2, wsc, hrs, aoff, a.f, nch * wave / kSkWaves,
-                                    nch * (wave + 1) / kSkWaves, wave == kSkWaves - 1, acc);
+    decode_accumulate_lanes<NW, RS, false>(wq, nt, a.f / 2, wsc, wsl, hrs, aoff, a.f, c_begin, c_end,
+                                           wave == kSkWaves - 1, acc, scr);
   }
 #pragma unroll
   for (int t = 0; t < NW; ++t)
