@@ -227,23 +227,37 @@ __global__ __launch_bounds__(kPromptThreads, 2) void ffn_prompt_kernel(FFNArgs a
         woff[i] = soff[i] = kOOB;
       }
     }
+    // A stage or block that lies wholly inside K (a wave-uniform test) copies with the
+    // lanes' offsets as they are; only a last, half stage (K % 64 == 32) selects per lane.
     auto issue_x = [&](int c) {
       const int K0 = c * kPromptKC;
       unsigned char* buf = smem + kXOff + (c & 1) * kXStageBytes + wave * 32 * 128;
-      const bool tail = K0 + 8 * dseg >= K;  // only in a last, half stage (K % 64 == 32)
+      if (K0 + kPromptKC <= K) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma16(xrs, buf + i * 1024, tail ? kOOB : xoff[i], K0 * 2);
+        for (int i = 0; i < 4; ++i) dma16(xrs, buf + i * 1024, xoff[i], K0 * 2);
+      } else {
+        const bool tail = K0 + 8 * dseg >= K;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(xrs, buf + i * 1024, tail ? kOOB : xoff[i], K0 * 2);
+      }
     };
     auto issue_ws = [&](int b) {
       const int K0 = b * kBlockStages * kPromptKC;
       unsigned char* wbuf = smem + kWOff + (b & 1) * kWBlockBytes + wave * 64 * kWRowBytes;
       unsigned char* sbuf = smem + kSOff + (b & 1) * kSBlockBytes + wave * 64 * kSRowBytes;
-      const bool wtail = K0 + 32 * wseg >= K;
-      const bool stail = K0 + 32 * (lane & 3) >= K;
+      if (K0 + kBlockStages * kPromptKC <= K) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma16(wrs, wbuf + i * 1024, wtail ? kOOB : woff[i], K0 / 2);
+        for (int i = 0; i < 4; ++i) dma16(wrs, wbuf + i * 1024, woff[i], K0 / 2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma2(srs, sbuf + i * 256, stail ? kOOB : soff[i], K0 / 16);
+        for (int i = 0; i < 4; ++i) dma2(srs, sbuf + i * 256, soff[i], K0 / 16);
+      } else {
+        const bool wtail = K0 + 32 * wseg >= K;
+        const bool stail = K0 + 32 * (lane & 3) >= K;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(wrs, wbuf + i * 1024, wtail ? kOOB : woff[i], K0 / 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma2(srs, sbuf + i * 256, stail ? kOOB : soff[i], K0 / 16);
+      }
     };
 
     floatx16 acc[2][4];
