@@ -235,14 +235,15 @@ __device__ __forceinline__ void gemm_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// LDS layout of a stage:
-//   x: row r (128 bytes = 8 slots of 16 bytes), logical segment j in slot j ^ (r & 7);
-//   W: row r (64 bytes = 4 slots), logical segment j in slot j ^ ((r >> 1) & 3);
+// LDS layout of a stage (the slot patterns give the 16 rows that 16 lanes read 16
+// distinct 16-byte bank groups):
+//   x: row r (128 bytes = 8 slots of 16 bytes), logical segment j in slot j ^ ((r >> 1) & 7);
+//   W: row r (64 bytes = 4 slots), logical segment j in slot j ^ ((r >> 2) & 3);
 //   scales: wave w's region holds rows 32w .. 32w + 31, (row, block b) in dword slot
 //   2 * (row & 31) + b -- or, when K is a multiple of 512 and at most 4096, all of the
 //   tile's scale rows come in once before the K loop, in whole 128-byte rows (a DMA
 //   instruction reads 8 full cache lines instead of one byte of 32 rows every stage):
-//   row r's logical 16-byte segment j in slot j ^ (r & 7) of its 128 bytes.
+//   row r's logical 16-byte segment j in slot j ^ ((r >> 1) & 7) of its 128 bytes.
 // MFMA K order within a stage (a permutation of K applied to both operands): lane group
 // g (lane / 32) at step 2p + h takes W bytes 8h .. 8h + 7 of segment 2p + g, i.e. K
 // elements 16 * (2p + g) + 8h .. + 7, which are activation segment 4p + 2g + h.
@@ -275,10 +276,10 @@ __global__ __launch_bounds__(kGThreads, 1) void mxfp8_gemm_kernel(const uint16_t
   for (int i = 0; i < 2; ++i) {
     const int ins = wave * 2 + i;
     const int xr = ins * 8 + (lane >> 3);           // activation row in the tile
-    xseg[i] = (lane & 7) ^ (lane >> 3);              // logical segment this lane fetches
+    xseg[i] = (lane & 7) ^ ((xr >> 1) & 7);          // logical segment this lane fetches
     xoff[i] = (m0 + xr < M) ? (uint32_t)(m0 + xr) * (uint32_t)(K * 2) + xseg[i] * 16 : kGOOB;
     const int wr = ins * 16 + (lane >> 2);           // weight row in the tile (past kGN: no row)
-    wseg[i] = (lane & 3) ^ ((lane >> 3) & 3);
+    wseg[i] = (lane & 3) ^ ((wr >> 2) & 3);
     woff[i] = (wr < kGN && n0 + wr < N) ? (uint32_t)(n0 + wr) * (uint32_t)K + wseg[i] * 16 : kGOOB;
   }
   const int srow = wave * 32 + (lane >> 1), sblk = lane & 1;
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(kGThreads, 1) void mxfp8_gemm_kernel(const uint16_t
     for (int j = 0; j < 3; ++j) {
       const int ins = wave * 3 + j;
       const int r = ins * 8 + (lane >> 3);
-      const int seg = (lane & 7) ^ (r & 7);
+      const int seg = (lane & 7) ^ ((r >> 1) & 7);
       const uint32_t off = (n0 + r < N && seg * 16 < K / 32) ? (uint32_t)(n0 + r) * (uint32_t)(K / 32) + seg * 16 : kGOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (gemm_lds_ptr)(scl + ins * 1024), 16, off, 0, 0, 0);
     }
@@ -353,12 +354,12 @@ __global__ __launch_bounds__(kGThreads, 1) void mxfp8_gemm_kernel(const uint16_t
 #pragma unroll
       for (int i = 0; i < 3; ++i) {
         const int r = nb * 96 + i * 32 + l32;
-        const int slot = (2 * p + g) ^ ((r >> 1) & 3);
+        const int slot = (2 * p + g) ^ ((r >> 2) & 3);
         wv[i] = *reinterpret_cast<const gu32x4v*>(ws + r * 64 + slot * 16);
         uint32_t code;
         if (PRE) {
           const int b = 2 * c + p;  // scale block of this half stage
-          code = *(scl + r * kGSRow + (((b >> 4) ^ (r & 7)) * 16) + (b & 15));
+          code = *(scl + r * kGSRow + (((b >> 4) ^ ((r >> 1) & 7)) * 16) + (b & 15));
         } else {
           code = *(ss + (r >> 5) * 256 + ((r & 31) * 2 + p) * 4);
         }
@@ -371,7 +372,7 @@ __global__ __launch_bounds__(kGThreads, 1) void mxfp8_gemm_kernel(const uint16_t
         for (int i = 0; i < 3; ++i) a[i] = mxfp8x8_to_bf16(wv[i][2 * h], wv[i][2 * h + 1], p2[i]);
         const int r = ma * 32 + l32;
         const int j = 4 * p + 2 * g + h;
-        const gu32x4v bv = *reinterpret_cast<const gu32x4v*>(xs + r * 128 + ((j ^ (r & 7)) * 16));
+        const gu32x4v bv = *reinterpret_cast<const gu32x4v*>(xs + r * 128 + ((j ^ ((r >> 1) & 7)) * 16));
         const bf16x8 b = __builtin_bit_cast(bf16x8, bv);
 #pragma unroll
         for (int i = 0; i < 3; ++i) acc[i] = mx_mfma32(a[i], b, acc[i]);
