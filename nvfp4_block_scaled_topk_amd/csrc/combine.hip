@@ -20,75 +20,99 @@ namespace moe {
 
 constexpr int kCombineThreads = 256;
 
-template <bool SHARED, bool RESID>
+// The rows are read once: non-temporal loads.
+__device__ __forceinline__ float4 ldnt_f4(const float* p) {
+  typedef float f4v __attribute__((ext_vector_type(4)));
+  const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
+// Tokens TT*blockIdx.x .. + TT - 1, columns (blockIdx.y * kCombineThreads + thread) * 4 ..
+// + 3 of each. With k <= 8 every row load of the block's tokens is issued before the
+// first sum (a row slot past k repeats row k - 1 and adds nothing); larger k sums eight
+// rows at a time.
+template <bool SHARED, bool RESID, int TT>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const float* __restrict__ y_rows, const int32_t* __restrict__ row_of,
     const float* __restrict__ w, int T, int k, int d, const float* __restrict__ s_rows,
     const float* __restrict__ s_gate, const uint16_t* __restrict__ resid, uint16_t* __restrict__ out) {
-  // the token's row positions and weights are the same for the whole block: scalar loads
-  const int t = blockIdx.x;
-  const int32_t* const ro = row_of + (size_t)t * k;
-  const float* const wt = w + (size_t)t * k;
   const int c = (blockIdx.y * kCombineThreads + threadIdx.x) * 4;
   if (c >= d) return;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float4 sv;
-  if constexpr (SHARED) sv = *reinterpret_cast<const float4*>(s_rows + (size_t)t * d + c);
-  uint2 xr;
-  if constexpr (RESID) xr = *reinterpret_cast<const uint2*>(resid + (size_t)t * d + c);
-  // eight rows' loads in flight at once (a group past k repeats row k-1 and adds
-  // nothing), then the sums in top-k order
+  float4 acc[TT];
+  float4 v[TT][8];
+#pragma unroll
+  for (int q = 0; q < TT; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j0 = 0; j0 < k; j0 += 8) {
-    float4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      v[u] = *reinterpret_cast<const float4*>(y_rows + (size_t)ro[min(j0 + u, k - 1)] * d + c);
+    for (int q = 0; q < TT; ++q) {
+      const int t = min((int)blockIdx.x * TT + q, T - 1);
+      // the token's row positions are the same for the whole block: scalar loads
+      const int32_t* const ro = row_of + (size_t)t * k;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (j0 + u < k) {
-        const float wj = wt[j0 + u];
-        acc.x = fmaf(wj, v[u].x, acc.x);
-        acc.y = fmaf(wj, v[u].y, acc.y);
-        acc.z = fmaf(wj, v[u].z, acc.z);
-        acc.w = fmaf(wj, v[u].w, acc.w);
+      for (int u = 0; u < 8; ++u) v[q][u] = ldnt_f4(y_rows + (size_t)ro[min(j0 + u, k - 1)] * d + c);
+    }
+#pragma unroll
+    for (int q = 0; q < TT; ++q) {
+      const int t = min((int)blockIdx.x * TT + q, T - 1);
+      const float* const wt = w + (size_t)t * k;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u < k) {
+          const float wj = wt[j0 + u];
+          acc[q].x = fmaf(wj, v[q][u].x, acc[q].x);
+          acc[q].y = fmaf(wj, v[q][u].y, acc[q].y);
+          acc[q].z = fmaf(wj, v[q][u].z, acc[q].z);
+          acc[q].w = fmaf(wj, v[q][u].w, acc[q].w);
+        }
       }
     }
   }
-  if constexpr (SHARED) {
-    const float g = s_gate ? 1.0f / (1.0f + expf(-s_gate[t])) : 1.0f;
-    acc.x = fmaf(g, sv.x, acc.x);
-    acc.y = fmaf(g, sv.y, acc.y);
-    acc.z = fmaf(g, sv.z, acc.z);
-    acc.w = fmaf(g, sv.w, acc.w);
+#pragma unroll
+  for (int q = 0; q < TT; ++q) {
+    const int t = (int)blockIdx.x * TT + q;
+    if (t >= T) break;
+    float4 a4 = acc[q];
+    if constexpr (SHARED) {
+      const float4 sv = *reinterpret_cast<const float4*>(s_rows + (size_t)t * d + c);
+      const float g = s_gate ? 1.0f / (1.0f + expf(-s_gate[t])) : 1.0f;
+      a4.x = fmaf(g, sv.x, a4.x);
+      a4.y = fmaf(g, sv.y, a4.y);
+      a4.z = fmaf(g, sv.z, a4.z);
+      a4.w = fmaf(g, sv.w, a4.w);
+    }
+    if constexpr (RESID) {
+      const uint2 xr = *reinterpret_cast<const uint2*>(resid + (size_t)t * d + c);
+      a4.x += bf16_to_f32((uint16_t)(xr.x & 0xFFFFu));
+      a4.y += bf16_to_f32((uint16_t)(xr.x >> 16));
+      a4.z += bf16_to_f32((uint16_t)(xr.y & 0xFFFFu));
+      a4.w += bf16_to_f32((uint16_t)(xr.y >> 16));
+    }
+    uint2 o;
+    o.x = (uint32_t)bf16_rne(a4.x) | ((uint32_t)bf16_rne(a4.y) << 16);
+    o.y = (uint32_t)bf16_rne(a4.z) | ((uint32_t)bf16_rne(a4.w) << 16);
+    *reinterpret_cast<uint2*>(out + (size_t)t * d + c) = o;
   }
-  if constexpr (RESID) {
-    acc.x += bf16_to_f32((uint16_t)(xr.x & 0xFFFFu));
-    acc.y += bf16_to_f32((uint16_t)(xr.x >> 16));
-    acc.z += bf16_to_f32((uint16_t)(xr.y & 0xFFFFu));
-    acc.w += bf16_to_f32((uint16_t)(xr.y >> 16));
-  }
-  uint2 o;
-  o.x = (uint32_t)bf16_rne(acc.x) | ((uint32_t)bf16_rne(acc.y) << 16);
-  o.y = (uint32_t)bf16_rne(acc.z) | ((uint32_t)bf16_rne(acc.w) << 16);
-  *reinterpret_cast<uint2*>(out + (size_t)t * d + c) = o;
 }
+
+constexpr int kCombineTokens = 1;  // tokens a block (2 and 4 measured no faster)
 
 hipError_t launch_combine(const float* y_rows, const int32_t* row_of, const float* w, int T, int k,
                           int d, const float* s_rows, const float* s_gate, const uint16_t* resid, uint16_t* out,
                           hipStream_t stream) {
-  dim3 grid(T, (d / 4 + kCombineThreads - 1) / kCombineThreads);
+  constexpr int TT = kCombineTokens;
+  dim3 grid((T + TT - 1) / TT, (d / 4 + kCombineThreads - 1) / kCombineThreads);
   if (s_rows && resid)
-    hipLaunchKernelGGL((combine_kernel<true, true>), grid, dim3(kCombineThreads), 0, stream, y_rows, row_of, w, T, k,
-                       d, s_rows, s_gate, resid, out);
+    hipLaunchKernelGGL((combine_kernel<true, true, TT>), grid, dim3(kCombineThreads), 0, stream, y_rows, row_of, w,
+                       T, k, d, s_rows, s_gate, resid, out);
   else if (s_rows)
-    hipLaunchKernelGGL((combine_kernel<true, false>), grid, dim3(kCombineThreads), 0, stream, y_rows, row_of, w, T, k,
-                       d, s_rows, s_gate, nullptr, out);
+    hipLaunchKernelGGL((combine_kernel<true, false, TT>), grid, dim3(kCombineThreads), 0, stream, y_rows, row_of, w,
+                       T, k, d, s_rows, s_gate, nullptr, out);
   else if (resid)
-    hipLaunchKernelGGL((combine_kernel<false, true>), grid, dim3(kCombineThreads), 0, stream, y_rows, row_of, w, T, k,
-                       d, nullptr, nullptr, resid, out);
+    hipLaunchKernelGGL((combine_kernel<false, true, TT>), grid, dim3(kCombineThreads), 0, stream, y_rows, row_of, w,
+                       T, k, d, nullptr, nullptr, resid, out);
   else
-    hipLaunchKernelGGL((combine_kernel<false, false>), grid, dim3(kCombineThreads), 0, stream, y_rows, row_of, w, T,
-                       k, d, nullptr, nullptr, nullptr, out);
+    hipLaunchKernelGGL((combine_kernel<false, false, TT>), grid, dim3(kCombineThreads), 0, stream, y_rows, row_of, w,
+                       T, k, d, nullptr, nullptr, nullptr, out);
   return hipGetLastError();
 }
 
