@@ -42,7 +42,9 @@ constexpr int kBlockStages = 2;         // weight / scale block = 2 stages = 128
 constexpr int kXStageBytes = 128 * 128;     // 16 KB: 128 rows x 64 bf16
 constexpr int kWRowBytes = 64;              // a weight row's codes in one block
 constexpr int kWBlockBytes = 256 * kWRowBytes;  // 16 KB: 256 weight rows x 128 codes
-constexpr int kSRowBytes = 16;              // a weight row's 4 scale pairs in one block (dword slots)
+// a weight row's block scales in LDS: the 4 scale pairs of one weight block in dword slots, or
+// (16-byte scale copies) the 16 scale bytes of 256 K elements, four stages
+constexpr int kSRowBytes = 16;
 constexpr int kSBlockBytes = 256 * kSRowBytes;  // 4 KB
 constexpr int kXOff = 0;
 constexpr int kWOff = 2 * kXStageBytes;
@@ -52,6 +54,7 @@ constexpr int kPromptThreads = 256;     // 4 waves, one per SIMD (two workgroups
 constexpr int kPromptBlocksPerCu = 2;
 constexpr int kXDma = 4;                // activation DMA instructions per wave per stage
 constexpr int kWSDma = 8;               // weight + scale DMA instructions per wave per block
+constexpr int kWDma = 4;                // weight DMA instructions per wave per block
 constexpr int kMaxE = 1024;
 constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every record: reads zeros
 constexpr int kXcds = 8;
@@ -170,6 +173,15 @@ __global__ __launch_bounds__(kPromptThreads, 2) void ffn_prompt_kernel(FFNArgs a
   const int G = gridDim.x;
   const int lid = (G % kXcds == 0) ? (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds : blockIdx.x;
 
+  // Block scales copied 16 bytes a lane (one DMA instruction a wave brings 256 K elements'
+  // scales of 64 weight rows, in place of eight 2-byte copies over the same four stages)
+  // when K is a multiple of 256 and the scale tensors are 16-byte aligned (then so is
+  // every row's 256-K piece).
+  const bool sc16 =
+      K % 256 == 0 &&
+      ((MODE == 0 ? (reinterpret_cast<uintptr_t>(a.gate_s) | reinterpret_cast<uintptr_t>(a.up_s))
+                  : reinterpret_cast<uintptr_t>(a.down_s)) & 15) == 0;
+
   for (int item = lid; item < total_tiles; item += G) {
     const int mt_all = item / n_col_tiles;
     const int ct = item - mt_all * n_col_tiles;
@@ -227,6 +239,13 @@ __global__ __launch_bounds__(kPromptThreads, 2) void ffn_prompt_kernel(FFNArgs a
         woff[i] = soff[i] = kOOB;
       }
     }
+    // 16-byte scale copies: lane l of wave w copies tile row 64w + l
+    uint32_t soff16;
+    {
+      const int r = wave * 64 + lane;
+      const int n = MODE == 0 ? ct * 128 + (r & 127) : ct * 256 + r;
+      soff16 = n < N ? (uint32_t)n * (uint32_t)(K / 16) : kOOB;
+    }
     // A stage or block that lies wholly inside K (a wave-uniform test) copies with the
     // lanes' offsets as they are; only a last, half stage (K % 64 == 32) selects per lane.
     auto issue_x = [&](int c) {
@@ -248,9 +267,15 @@ __global__ __launch_bounds__(kPromptThreads, 2) void ffn_prompt_kernel(FFNArgs a
       if (K0 + kBlockStages * kPromptKC <= K) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16(wrs, wbuf + i * 1024, woff[i], K0 / 2);
+        if (sc16) {
+          // with the first weight block of each pair: the scales of stages 2b .. 2b + 3
+          if ((b & 1) == 0)
+            dma16(srs, smem + kSOff + ((b >> 1) & 1) * kSBlockBytes + wave * 64 * kSRowBytes, soff16, K0 / 16);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma2(srs, sbuf + i * 256, soff[i], K0 / 16);
-      } else {
+          for (int i = 0; i < 4; ++i) dma2(srs, sbuf + i * 256, soff[i], K0 / 16);
+        }
+      } else {  // K is not a multiple of 256 here, so no 16-byte scale copies
         const bool wtail = K0 + 32 * wseg >= K;
         const bool stail = K0 + 32 * (lane & 3) >= K;
 #pragma unroll
@@ -300,8 +325,14 @@ __global__ __launch_bounds__(kPromptThreads, 2) void ffn_prompt_kernel(FFNArgs a
       for (int c = 0; c < nch; ++c) {
         // loads issued after stage c's activations: the block issued in stage c - 1
         const bool blk_after = c >= 1 && ((c - 1) % kBlockStages) == 0 && (c - 1) / kBlockStages + 1 < nblk;
-        if (blk_after) wait_vm<kWSDma>();
-        else wait_vm<0>();
+        // (the block issued then, (c - 1) / 2 + 1, brought 16-byte scale copies if even)
+        if (blk_after) {
+          if (!sc16) wait_vm<kWSDma>();
+          else if ((((c - 1) / kBlockStages + 1) & 1) == 0) wait_vm<kWDma + 1>();
+          else wait_vm<kWDma>();
+        } else {
+          wait_vm<0>();
+        }
         wait_lgkm0();
         __builtin_amdgcn_s_barrier();
         if (c + 1 < nch) issue_x(c + 1);
@@ -312,7 +343,10 @@ __global__ __launch_bounds__(kPromptThreads, 2) void ffn_prompt_kernel(FFNArgs a
         const int cs = c % kBlockStages;
         const int blk = (c / kBlockStages) & 1;
         const unsigned char* wb = smem + kWOff + blk * kWBlockBytes;
-        const unsigned char* sb = smem + kSOff + blk * kSBlockBytes;
+        // this stage's two scale bytes of lane group g: dword slot 2cs + g of the block's
+        // scale pairs, or bytes 4 (c mod 4) + 2g of the 16-byte scale copy
+        const unsigned char* sb = smem + kSOff + (sc16 ? ((c >> 2) & 1) : blk) * kSBlockBytes +
+                                  (sc16 ? 4 * (c & 3) + 2 * g : (2 * cs + g) * 4);
         // weights of this stage: logical 16-byte segment 2cs + g of the row's 64 bytes
         u32x4 q[2];
         uint32_t sc[2];
@@ -320,7 +354,7 @@ __global__ __launch_bounds__(kPromptThreads, 2) void ffn_prompt_kernel(FFNArgs a
         for (int i = 0; i < 2; ++i) {
           const int r = wrow[i];
           q[i] = *reinterpret_cast<const u32x4*>(wb + r * kWRowBytes + (((2 * cs + g) ^ ((r >> 1) & 3)) * 16));
-          sc[i] = *reinterpret_cast<const uint32_t*>(sb + r * kSRowBytes + (2 * cs + g) * 4);
+          sc[i] = *reinterpret_cast<const uint16_t*>(sb + r * kSRowBytes);
         }
         // activation fragment t of MFMA step s: row 32t + l32, logical segment 4g + s
         constexpr int NB = NTF > 0 ? NTF : 1;

@@ -44,6 +44,41 @@ __device__ __forceinline__ u32x4 act_load(__amdgpu_buffer_rsrc_t ars, uint32_t a
   return u32x4{v.x, v.y, v.z, v.w};
 }
 
+// Lane col of each 16-lane row takes the 16 bytes of lane col + SH (a DPP row shift;
+// lanes whose source lies past their row take zeros).
+template <int SH>
+__device__ __forceinline__ u32x4 rows_shl(const u32x4& v) {
+  if constexpr (SH == 0) {
+    return v;
+  } else {
+    return u32x4{(uint32_t)__builtin_amdgcn_mov_dpp((int)v.x, 0x100 + SH, 0xF, 0xF, true),
+                 (uint32_t)__builtin_amdgcn_mov_dpp((int)v.y, 0x100 + SH, 0xF, 0xF, true),
+                 (uint32_t)__builtin_amdgcn_mov_dpp((int)v.z, 0x100 + SH, 0xF, 0xF, true),
+                 (uint32_t)__builtin_amdgcn_mov_dpp((int)v.w, 0x100 + SH, 0xF, 0xF, true)};
+  }
+}
+
+// Activation rows packed PK to a lane row (PK = 1, 2, 4), for one row set of at most
+// 16 / PK rows: lane col holds row col mod (16 / PK), and its 16-byte load q brings the
+// 8-element group act_group(q, col) of the four (s = 0..3) its lane group needs from a
+// 128-element chunk, so a chunk takes 4 / PK loads instead of four. The operand of group
+// s is then load s / PK shifted down by (s mod PK) (16 / PK) lanes; lanes past the rows
+// hold other groups' elements, which feed only the products of missing rows.
+template <int PK>
+__device__ __forceinline__ int act_group(int q, int col) {
+  return q * PK + col / (16 / PK);
+}
+template <int PK>
+__device__ __forceinline__ u32x4 act_operand(const u32x4 (&v)[4 / PK], int s) {
+  if constexpr (PK == 1) {
+    return v[s];
+  } else if constexpr (PK == 2) {
+    return (s & 1) ? rows_shl<8>(v[s >> 1]) : v[s >> 1];
+  } else {
+    return s == 0 ? v[0] : s == 1 ? rows_shl<4>(v[0]) : s == 2 ? rows_shl<8>(v[0]) : rows_shl<12>(v[0]);
+  }
+}
+
 // Accumulates NW weight tiles of 16 rows (wq: row 0 of each tile, row stride wstride
 // bytes; tiles nvalid.. are absent and read zeros; wsc: the scale row of this lane's
 // column) against RS sets of 16 activation rows, one row per lane column in each (at
@@ -59,7 +94,8 @@ __device__ __forceinline__ u32x4 act_load(__amdgpu_buffer_rsrc_t ars, uint32_t a
 // pairs, and one 16-byte load a lane brings a pair's scales of all NW tiles (lane l:
 // tile (l / 16) mod NW, row l mod 16, through the per-lane pointer wsl to that row's
 // scales), which the wave regroups through the last kSkScrScale bytes of its scratch.
-template <int NW, int RS>
+// PK > 1 (one row set): activation rows packed PK to a lane row (act_operand).
+template <int NW, int RS, int PK = 1>
 __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW], int nvalid, size_t wstride,
                                                   const uint8_t* wsl,
                                                   __amdgpu_buffer_rsrc_t ars, const uint32_t (&aoff)[RS],
@@ -79,7 +115,7 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
   struct Pair {
     u32x4 lq[NW][2];   // [tile][rows 0-7 / 8-15], as loaded
     u32x4 scq;         // this lane's 16 scale bytes of the pair (tile, row as above)
-    u32x4 xv[RS][2][4];
+    u32x4 xv[RS][2][4 / PK];
   };
   auto load_pair = [&](int c, Pair& P) {
     const int mc = c + (seg8 >> 2);  // this lane's chunk
@@ -102,7 +138,8 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
 #pragma unroll
       for (int r = 0; r < RS; ++r)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) P.xv[r][j][s] = act_load(ars, aoff[r], cc * 128 + 32 * grp + 8 * s);
+        for (int q = 0; q < 4 / PK; ++q)
+          P.xv[r][j][q] = act_load(ars, aoff[r], cc * 128 + 32 * grp + 8 * act_group<PK>(q, col));
     }
   };
   auto compute_pair = [&](int c, const Pair& P) {
@@ -120,6 +157,13 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
       for (int i = 0; i < NW; ++i) scw[i] = *reinterpret_cast<const uint32_t*>(ss + (i * 16 + col) * 16 + grp * 4);
       __builtin_amdgcn_wave_barrier();
     }
+    u32x4 xo[RS][2][4];  // the activation operands, shared by the NW tiles
+#pragma unroll
+    for (int r = 0; r < RS; ++r)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xo[r][j][s] = act_operand<PK>(P.xv[r][j], s);
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       // piece (row r, 16-byte segment s) at r * 128 + ((s + r / 2) mod 8) * 16: both the
@@ -148,7 +192,7 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
         for (int s = 0; s < 4; ++s) {
           const bf16x8 wv = nvfp4x8_to_bf16(word_of(q[j], s), s < 2 ? s0 : s1);
 #pragma unroll
-          for (int r = 0; r < RS; ++r) acc[i][r] = mfma16(wv, u32x4_as_bf16x8(P.xv[r][j][s]), acc[i][r]);
+          for (int r = 0; r < RS; ++r) acc[i][r] = mfma16(wv, u32x4_as_bf16x8(xo[r][j][s]), acc[i][r]);
         }
       }
     }
@@ -197,7 +241,7 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
 // past the buffer) load no activations. With SCQ (K a multiple of 256) the block scales
 // come as in decode_accumulate, a 16-byte load a lane for each chunk pair (through
 // wsl), regrouped through the wave's scratch `scr`.
-template <int NW, int RS, bool SCQ>
+template <int NW, int RS, bool SCQ, int PK = 1>
 __device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&wq)[NW], int nvalid, size_t wstride,
                                                   const uint8_t* const (&wsc)[NW], const uint8_t* wsl,
                                                   __amdgpu_buffer_rsrc_t ars, const uint32_t (&aoff)[RS],
@@ -220,7 +264,7 @@ __device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&w
     u32x4 q[N][NW];
     uint32_t sc[N][NW];
     u32x4 scq[SCQ ? NPM : 1];
-    u32x4 xv[N][RS][4];
+    u32x4 xv[N][RS][4 / PK];
     const int pf = cb >> 1, pl = (cb + N - 1) >> 1;  // SCQ: first and last pair of the chunks
     if constexpr (SCQ) {
 #pragma unroll
@@ -238,7 +282,7 @@ __device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&w
 #pragma unroll
       for (int r = 0; r < RS; ++r)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) xv[h][r][s] = act_load(ars, aoff[r], K0 + 32 * grp + 8 * s);
+        for (int q = 0; q < 4 / PK; ++q) xv[h][r][q] = act_load(ars, aoff[r], K0 + 32 * grp + 8 * act_group<PK>(q, col));
     }
     __builtin_amdgcn_sched_barrier(0);  // every load issued before the first product
     if constexpr (SCQ) {
@@ -260,6 +304,11 @@ __device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&w
     }
 #pragma unroll
     for (int h = 0; h < N; ++h) {
+      u32x4 xo[RS][4];  // chunk h's activation operands, shared by the NW tiles
+#pragma unroll
+      for (int r = 0; r < RS; ++r)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xo[r][s] = act_operand<PK>(xv[h][r], s);
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
         const E4M3Split s0 = e4m3_split_b<0>(sc[h][i]);
@@ -268,7 +317,7 @@ __device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&w
         for (int s = 0; s < 4; ++s) {
           const bf16x8 wv = nvfp4x8_to_bf16(word_of(q[h][i], s), s < 2 ? s0 : s1);
 #pragma unroll
-          for (int r = 0; r < RS; ++r) acc[i][r] = mfma16(wv, u32x4_as_bf16x8(xv[h][r][s]), acc[i][r]);
+          for (int r = 0; r < RS; ++r) acc[i][r] = mfma16(wv, u32x4_as_bf16x8(xo[r][s]), acc[i][r]);
         }
       }
     }
@@ -411,11 +460,14 @@ __device__ __forceinline__ void skinny_gateup_item(const FFNArgs& a, __amdgpu_bu
     wsc[t] = a.gate_s + (wrow0 + 16 * t + col) * (a.d / 16);
     wsc[FT + t] = a.up_s + (wrow0 + 16 * t + col) * (a.d / 16);
   }
-  // the activation rows of routed rows 16 r + col (x row sorted_rows[..] / k)
+  // one row set of at most 8 (4) rows, K a multiple of 256: rows packed 2 (4) to a lane row
+  const int pk = RS == 1 && a.d % 256 == 0 ? (ne <= 4 ? 4 : ne <= 8 ? 2 : 1) : 1;
+  // the activation rows of routed rows 16 r + col (x row sorted_rows[..] / k); packed:
+  // row col mod (16 / pk)
   uint32_t aoff[RS];
 #pragma unroll
   for (int r = 0; r < RS; ++r) {
-    const int row = 16 * r + col;
+    const int row = 16 * r + (col & (16 / pk - 1));
     aoff[r] = row < ne ? (uint32_t)(a.sorted_rows[r0 + row] / a.k) * (uint32_t)(a.d * 2) : kSkOOB;
   }
   // the tensor scales, loaded with the weights (the epilogue needs them)
@@ -430,9 +482,19 @@ __device__ __forceinline__ void skinny_gateup_item(const FFNArgs& a, __amdgpu_bu
   const int lt = (lane >> 4) % NW, lr = lane & 15;
   const uint8_t* wsl = (lt < FT ? a.gate_s : a.up_s) + (wrow0 + 16 * (lt % FT) + lr) * (a.d / 16);
   const int c_begin = nch * wave / kSkWaves, c_end = nch * (wave + 1) / kSkWaves;
+  auto stream = [&](auto pk_c) {
+    constexpr int PK = decltype(pk_c)::value;
+    if (nch >= 4 * kSkWaves) decode_accumulate<NW, RS, PK>(wq, NW, a.d / 2, wsl, xrs, aoff, c_begin, c_end, acc, scr);
+    else decode_accumulate_lanes<NW, RS, true, PK>(wq, NW, a.d / 2, wsc, wsl, xrs, aoff, a.d, c_begin, c_end, false, acc, scr);
+  };
   if (a.d % 256 == 0) {
-    if (nch >= 4 * kSkWaves) decode_accumulate<NW, RS>(wq, NW, a.d / 2, wsl, xrs, aoff, c_begin, c_end, acc, scr);
-    else decode_accumulate_lanes<NW, RS, true>(wq, NW, a.d / 2, wsc, wsl, xrs, aoff, a.d, c_begin, c_end, false, acc, scr);
+    if constexpr (RS == 1) {
+      if (pk == 4) stream(std::integral_constant<int, 4>{});
+      else if (pk == 2) stream(std::integral_constant<int, 2>{});
+      else stream(std::integral_constant<int, 1>{});
+    } else {
+      stream(std::integral_constant<int, 1>{});
+    }
   } else {
     decode_accumulate_lanes<NW, RS, false>(wq, NW, a.d / 2, wsc, wsl, xrs, aoff, a.d, c_begin, c_end,
                                            wave == kSkWaves - 1, acc, scr);
@@ -488,10 +550,15 @@ __device__ __forceinline__ void skinny_down_item(const FFNArgs& a, __amdgpu_buff
     wq[t] = a.down_q + wrow0 * (a.f / 2);
     wsc[t] = a.down_s + (wrow0 + col) * (a.f / 16);
   }
-  // H rows r0 + 16 r + col
+  // one row set of at most 8 (4) rows, K a multiple of 256: rows packed 2 (4) to a lane row
+  const int pk = RS == 1 && a.f % 256 == 0 ? (ne <= 4 ? 4 : ne <= 8 ? 2 : 1) : 1;
+  // H rows r0 + 16 r + col; packed: row col mod (16 / pk)
   uint32_t aoff[RS];
 #pragma unroll
-  for (int r = 0; r < RS; ++r) aoff[r] = 16 * r + col < ne ? (uint32_t)(r0 + 16 * r + col) * (uint32_t)(a.f * 2) : kSkOOB;
+  for (int r = 0; r < RS; ++r) {
+    const int row = 16 * r + (col & (16 / pk - 1));
+    aoff[r] = row < ne ? (uint32_t)(r0 + row) * (uint32_t)(a.f * 2) : kSkOOB;
+  }
   const float td = a.down_ts[e];  // loaded with the weights (the epilogue needs it)
   floatx4 acc[NW][RS];
 #pragma unroll
@@ -504,9 +571,19 @@ __device__ __forceinline__ void skinny_down_item(const FFNArgs& a, __amdgpu_buff
   const int lt = (lane >> 4) % NW, lr = lane & 15;
   const uint8_t* wsl = a.down_s + ((size_t)e * a.d + (size_t)(dg * NW + (lt < nt ? lt : 0)) * 16 + lr) * (a.f / 16);
   const int c_begin = nch * wave / kSkWaves, c_end = nch * (wave + 1) / kSkWaves;
+  auto stream = [&](auto pk_c) {
+    constexpr int PK = decltype(pk_c)::value;
+    if (nch >= 4 * kSkWaves) decode_accumulate<NW, RS, PK>(wq, nt, a.f / 2, wsl, hrs, aoff, c_begin, c_end, acc, scr);
+    else decode_accumulate_lanes<NW, RS, true, PK>(wq, nt, a.f / 2, wsc, wsl, hrs, aoff, a.f, c_begin, c_end, false, acc, scr);
+  };
   if (a.f % 256 == 0) {
-    if (nch >= 4 * kSkWaves) decode_accumulate<NW, RS>(wq, nt, a.f / 2, wsl, hrs, aoff, c_begin, c_end, acc, scr);
-    else decode_accumulate_lanes<NW, RS, true>(wq, nt, a.f / 2, wsc, wsl, hrs, aoff, a.f, c_begin, c_end, false, acc, scr);
+    if constexpr (RS == 1) {
+      if (pk == 4) stream(std::integral_constant<int, 4>{});
+      else if (pk == 2) stream(std::integral_constant<int, 2>{});
+      else stream(std::integral_constant<int, 1>{});
+    } else {
+      stream(std::integral_constant<int, 1>{});
+    }
   } else {
     decode_accumulate_lanes<NW, RS, false>(wq, nt, a.f / 2, wsc, wsl, hrs, aoff, a.f, c_begin, c_end,
                                            wave == kSkWaves - 1, acc, scr);
