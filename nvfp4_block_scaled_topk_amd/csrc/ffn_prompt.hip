@@ -17,9 +17,10 @@
 //   MFMA    = v_mfma_f32_32x32x16_bf16, weights as the A operand, activations as B
 //   staging = buffer->LDS DMA only (no register staging; out-of-range lanes read zeros,
 //             which also pads ragged rows and K tails): activations in double-buffered
-//             stages of 64 K elements; packed weight codes and block scales in
-//             double-buffered blocks of 128 K elements (two activation stages), 64
-//             bytes of codes a weight row
+//             stages of 64 K elements; packed weight codes in double-buffered
+//             blocks of 128 K elements (two activation stages), 64 bytes of codes a
+//             weight row; block scales with them (2 bytes a lane), or, when K is a
+//             multiple of 256, 16 bytes a lane for 256 K elements (four stages)
 //
 // Work: one flat list of tiles (row tiles that use all four 32-row fragments first, in
 // expert order, then experts' partly filled last tiles by fragments descending; column
