@@ -460,6 +460,7 @@ __global__ __launch_bounds__(kPromptThreads, 2) void ffn_prompt_kernel(FFNArgs a
   // tiles is partly filled) starts on them at once. The LDS is theirs once every wave
   // is done with the last tile.
   __syncthreads();
+  static_assert(kSkLdsBytes <= kPromptLdsBytes, "the streaming items reuse the tiles' LDS");
   skinny_phase<MODE>(a, smem, a.work_ctr + MODE);
 }
 

@@ -30,7 +30,7 @@ namespace moe {
 constexpr int kSkThreads = 256;  // 4 waves split K
 constexpr int kSkWaves = 4;
 constexpr int kSkMaxE = 1024;
-constexpr int kSkScrScale = 1024;          // the part of it that regroups a pair's block scales
+constexpr int kSkScrScale = 2048;          // the part of it that regroups two pairs' block scales
 constexpr int kSkScr = 2048 + kSkScrScale;  // LDS a wave uses to rearrange a chunk pair of one tile
 
 constexpr uint32_t kSkOOB = 0x80000000u;  // a buffer offset past every record: reads zeros
@@ -91,13 +91,15 @@ __device__ __forceinline__ u32x4 act_operand(const u32x4 (&v)[4 / PK], int s) {
 // 2 KB LDS scratch `scr` into the MFMA operand layout (lane group g: elements
 // 32g .. 32g + 31 of each chunk). Lanes of missing rows (aoff past the buffer) load no
 // activations. Block scales: K is a multiple of 256, so a scale row holds whole 16-byte
-// pairs, and one 16-byte load a lane brings a pair's scales of all NW tiles (lane l:
-// tile (l / 16) mod NW, row l mod 16, through the per-lane pointer wsl to that row's
-// scales), which the wave regroups through the last kSkScrScale bytes of its scratch.
+// pairs; the loads of every other pair bring the scales of that pair and the next one
+// for all NW tiles' rows, 16 bytes a lane, two lanes a row (lane l: row 32h + l / 2 of
+// the NW * 16, through the per-lane pointer wsl2[h], pair l mod 2), so a load touches 32
+// rows' lines instead of 64; the wave regroups both pairs through the last kSkScrScale
+// bytes of its scratch (1 KB a pair).
 // PK > 1 (one row set): activation rows packed PK to a lane row (act_operand).
 template <int NW, int RS, int PK = 1>
 __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW], int nvalid, size_t wstride,
-                                                  const uint8_t* wsl,
+                                                  const uint8_t* const (&wsl2)[NW / 2],
                                                   __amdgpu_buffer_rsrc_t ars, const uint32_t (&aoff)[RS],
                                                   int c_begin, int c_end, floatx4 (&acc)[NW][RS],
                                                   unsigned char* scr) {
@@ -112,9 +114,14 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
                                               0x00020000);
   // pairs start at even chunks, so a pair is one aligned 128-byte line of each row; a
   // chunk of a pair outside [c_begin, c_end) reads nothing (an offset past the buffer)
+  // pairs start at c0 (even); the scale loads of a pair p even also cover pair p + 1
+  // (the last pair's scales where there is none)
+  const int c0 = c_begin & ~1;
+  const int np = c_end > c0 ? (c_end - c0 + 1) / 2 : 0;
+  const int c_last = c0 + 2 * (np - 1);
   struct Pair {
     u32x4 lq[NW][2];   // [tile][rows 0-7 / 8-15], as loaded
-    u32x4 scq;         // this lane's 16 scale bytes of the pair (tile, row as above)
+    u32x4 scq[NW / 2];  // even pairs: this lane's 16 scale bytes of its row and pair
     u32x4 xv[RS][2][4 / PK];
   };
   auto load_pair = [&](int c, Pair& P) {
@@ -129,9 +136,13 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
         P.lq[i][h] = u32x4{v.x, v.y, v.z, v.w};
       }
     }
-    // a chunk of the pair outside [c_begin, c_end) gets its own scales (its codes are
+    // a chunk of a pair outside [c_begin, c_end) gets its own scales (its codes are
     // zero, so they scale nothing)
-    P.scq = *reinterpret_cast<const u32x4*>(wsl + c * 8);
+    if (((c - c0) & 2) == 0) {
+      const int cq = min(c + 2 * (lane & 1), c_last);
+#pragma unroll
+      for (int h = 0; h < NW / 2; ++h) P.scq[h] = *reinterpret_cast<const u32x4*>(wsl2[h] + cq * 8);
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int cc = c + j >= c_begin && c + j < c_end ? c + j : c_begin;
@@ -146,15 +157,25 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
     // lane l's bytes (chunk c: x, y; chunk c + 1: z, w) regrouped as four dwords, dword g
     // holding what lane group g of the lane's row needs, then read back per tile:
     // scw[i] = [chunk c: bytes 2 grp, 2 grp + 1 | chunk c + 1: the same] of tile i, row col
+    // (even pairs first write both pairs' regrouped scales: pair p + j at j KB, row
+    // 32h + l / 2 at 16 (32h + l / 2))
     uint32_t scw[NW];
     {
       unsigned char* const ss = scr + kSkScr - kSkScrScale;
-      *reinterpret_cast<u32x4v*>(ss + lane * 16) =
-          u32x4v{__builtin_amdgcn_perm(P.scq.z, P.scq.x, 0x05040100u), __builtin_amdgcn_perm(P.scq.z, P.scq.x, 0x07060302u),
-                 __builtin_amdgcn_perm(P.scq.w, P.scq.y, 0x05040100u), __builtin_amdgcn_perm(P.scq.w, P.scq.y, 0x07060302u)};
-      __builtin_amdgcn_wave_barrier();
+      const bool even = ((c - c0) & 2) == 0;
+      if (even) {
 #pragma unroll
-      for (int i = 0; i < NW; ++i) scw[i] = *reinterpret_cast<const uint32_t*>(ss + (i * 16 + col) * 16 + grp * 4);
+        for (int h = 0; h < NW / 2; ++h)
+          *reinterpret_cast<u32x4v*>(ss + (lane & 1) * 1024 + (32 * h + (lane >> 1)) * 16) =
+              u32x4v{__builtin_amdgcn_perm(P.scq[h].z, P.scq[h].x, 0x05040100u),
+                     __builtin_amdgcn_perm(P.scq[h].z, P.scq[h].x, 0x07060302u),
+                     __builtin_amdgcn_perm(P.scq[h].w, P.scq[h].y, 0x05040100u),
+                     __builtin_amdgcn_perm(P.scq[h].w, P.scq[h].y, 0x07060302u)};
+        __builtin_amdgcn_wave_barrier();
+      }
+#pragma unroll
+      for (int i = 0; i < NW; ++i)
+        scw[i] = *reinterpret_cast<const uint32_t*>(ss + (even ? 0 : 1024) + (i * 16 + col) * 16 + grp * 4);
       __builtin_amdgcn_wave_barrier();
     }
     u32x4 xo[RS][2][4];  // the activation operands, shared by the NW tiles
@@ -200,8 +221,6 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
   // One row set: two pairs in flight (the next pair's loads are issued before the
   // current pair is computed). Every path consumes each load it issues (no load past
   // the last pair), so the loads outstanding at each wait are a fixed count.
-  const int c0 = c_begin & ~1;
-  const int np = c_end > c0 ? (c_end - c0 + 1) / 2 : 0;
   if constexpr (RS > 1) {
     // two row sets: one pair at a time (a second pair's activation operands would not
     // fit in the registers)
@@ -361,7 +380,7 @@ __device__ __forceinline__ void decode_accumulate_lanes(const uint8_t* const (&w
 constexpr int kSkRedBytes = 2 * kSkWaves * 4 * 64 * 16;
 constexpr int kSkScrOff = kSkRedBytes;
 constexpr int kSkListOff = kSkScrOff + kSkWaves * kSkScr;
-constexpr int kSkSlotOff = kSkListOff + 2 * 3 * kSkMaxE * 4;
+constexpr int kSkSlotOff = kSkListOff + 2 * kSkMaxE * (4 + 4 + 2);  // row counts 16-bit
 constexpr int kSkLdsBytes = kSkSlotOff + 64;
 
 struct SkLds {
@@ -369,17 +388,18 @@ struct SkLds {
   unsigned char* scr;
   int* e[2];
   int* r0[2];
-  int* n[2];
+  uint16_t* n[2];
   int* slot;  // [0..1] item slots, [2..3] list lengths
   __device__ explicit SkLds(unsigned char* base) {
     red = reinterpret_cast<floatx4*>(base);
     scr = base + kSkScrOff;
     int* l = reinterpret_cast<int*>(base + kSkListOff);
+    uint16_t* ln = reinterpret_cast<uint16_t*>(base + kSkListOff + 2 * 2 * kSkMaxE * 4);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      e[s] = l + (3 * s + 0) * kSkMaxE;
-      r0[s] = l + (3 * s + 1) * kSkMaxE;
-      n[s] = l + (3 * s + 2) * kSkMaxE;
+      e[s] = l + (2 * s + 0) * kSkMaxE;
+      r0[s] = l + (2 * s + 1) * kSkMaxE;
+      n[s] = ln + s * kSkMaxE;
     }
     slot = reinterpret_cast<int*>(base + kSkSlotOff);
   }
@@ -406,7 +426,7 @@ __device__ __forceinline__ void skinny_lists(const int32_t* __restrict__ offsets
           const int r = seen[s] + __popcll(m & ((1ull << lane) - 1ull));
           L.e[s][r] = e;
           L.r0[s][r] = o0;
-          L.n[s][r] = c;
+          L.n[s][r] = (uint16_t)c;
         }
         seen[s] += __popcll(m);
       }
@@ -481,10 +501,17 @@ __device__ __forceinline__ void skinny_gateup_item(const FFNArgs& a, __amdgpu_bu
   // the scale-load role of this lane (16-byte scale loads): tile (lane / 16) mod NW, row lane mod 16
   const int lt = (lane >> 4) % NW, lr = lane & 15;
   const uint8_t* wsl = (lt < FT ? a.gate_s : a.up_s) + (wrow0 + 16 * (lt % FT) + lr) * (a.d / 16);
+  // the two-pair scale loads of the line path: row 32h + lane / 2 of the NW tiles
+  const uint8_t* wsl2[NW / 2];
+#pragma unroll
+  for (int h = 0; h < NW / 2; ++h) {
+    const int t = (32 * h + (lane >> 1)) >> 4, rr = (lane >> 1) & 15;
+    wsl2[h] = (t < FT ? a.gate_s : a.up_s) + (wrow0 + 16 * (t % FT) + rr) * (a.d / 16);
+  }
   const int c_begin = nch * wave / kSkWaves, c_end = nch * (wave + 1) / kSkWaves;
   auto stream = [&](auto pk_c) {
     constexpr int PK = decltype(pk_c)::value;
-    if (nch >= 4 * kSkWaves) decode_accumulate<NW, RS, PK>(wq, NW, a.d / 2, wsl, xrs, aoff, c_begin, c_end, acc, scr);
+    if (nch >= 4 * kSkWaves) decode_accumulate<NW, RS, PK>(wq, NW, a.d / 2, wsl2, xrs, aoff, c_begin, c_end, acc, scr);
     else decode_accumulate_lanes<NW, RS, true, PK>(wq, NW, a.d / 2, wsc, wsl, xrs, aoff, a.d, c_begin, c_end, false, acc, scr);
   };
   if (a.d % 256 == 0) {
@@ -570,10 +597,17 @@ __device__ __forceinline__ void skinny_down_item(const FFNArgs& a, __amdgpu_buff
   // (absent tiles: tile 0), row lane mod 16
   const int lt = (lane >> 4) % NW, lr = lane & 15;
   const uint8_t* wsl = a.down_s + ((size_t)e * a.d + (size_t)(dg * NW + (lt < nt ? lt : 0)) * 16 + lr) * (a.f / 16);
+  // the two-pair scale loads of the line path: row 32h + lane / 2 of the NW tiles
+  const uint8_t* wsl2[NW / 2];
+#pragma unroll
+  for (int h = 0; h < NW / 2; ++h) {
+    const int t = (32 * h + (lane >> 1)) >> 4, rr = (lane >> 1) & 15;
+    wsl2[h] = a.down_s + ((size_t)e * a.d + (size_t)(dg * NW + (t < nt ? t : 0)) * 16 + rr) * (a.f / 16);
+  }
   const int c_begin = nch * wave / kSkWaves, c_end = nch * (wave + 1) / kSkWaves;
   auto stream = [&](auto pk_c) {
     constexpr int PK = decltype(pk_c)::value;
-    if (nch >= 4 * kSkWaves) decode_accumulate<NW, RS, PK>(wq, nt, a.f / 2, wsl, hrs, aoff, c_begin, c_end, acc, scr);
+    if (nch >= 4 * kSkWaves) decode_accumulate<NW, RS, PK>(wq, nt, a.f / 2, wsl2, hrs, aoff, c_begin, c_end, acc, scr);
     else decode_accumulate_lanes<NW, RS, true, PK>(wq, nt, a.f / 2, wsc, wsl, hrs, aoff, a.f, c_begin, c_end, false, acc, scr);
   };
   if (a.f % 256 == 0) {
