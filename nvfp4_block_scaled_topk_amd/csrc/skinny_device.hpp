@@ -112,10 +112,10 @@ __device__ __forceinline__ void decode_accumulate(const uint8_t* const (&wq)[NW]
   for (int i = 0; i < NW; ++i)
     rs[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wq[i]), 0, i < nvalid ? (int)(16 * wstride) : 0,
                                               0x00020000);
-  // pairs start at even chunks, so a pair is one aligned 128-byte line of each row; a
-  // chunk of a pair outside [c_begin, c_end) reads nothing (an offset past the buffer)
-  // pairs start at c0 (even); the scale loads of a pair p even also cover pair p + 1
-  // (the last pair's scales where there is none)
+  // pairs start at even chunks (c0, c0 + 2, ...), so a pair is one aligned 128-byte line
+  // of each row; a chunk of a pair outside [c_begin, c_end) reads nothing (an offset past
+  // the buffer). The scale loads of an even pair p also bring pair p + 1's scales (the
+  // last pair's again where p is the last).
   const int c0 = c_begin & ~1;
   const int np = c_end > c0 ? (c_end - c0 + 1) / 2 : 0;
   const int c_last = c0 + 2 * (np - 1);
