@@ -25,7 +25,8 @@ def pytest_sessionfinish(session, exitstatus):
     if gu is None or not (getattr(gu, "RECORDS", None) or getattr(gu, "REPORTS", None)):
         return
     import json
-    out = os.path.join(ROOT, "gpurun_out")
-    os.makedirs(out, exist_ok=True)
-    with open(os.path.join(out, "parity_records.json"), "w") as fh:
+    # MOE_PARITY_RECORDS names the file (default: parity_out/parity_records.json)
+    path = os.environ.get("MOE_PARITY_RECORDS") or os.path.join(ROOT, "parity_out", "parity_records.json")
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "w") as fh:
         json.dump({"exitstatus": int(exitstatus), "records": gu.RECORDS, "reports": gu.REPORTS}, fh, indent=1)

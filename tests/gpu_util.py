@@ -16,8 +16,8 @@ def say(*a):
     sys.stdout.flush()
 
 
-# Every band check of a GPU test appends its counts here; the session writes them to
-# gpurun_out/parity_records.json (tests/conftest.py).
+# Every band check of a GPU test appends its counts here; the session writes them to a
+# JSON file at its end (tests/conftest.py, MOE_PARITY_RECORDS).
 RECORDS = []
 # "explained" elements (outside the strict band, inside the slack) must stay rare: the
 # slack covers bf16 rounding ties of h and fp32 sum-order effects, which touch well
