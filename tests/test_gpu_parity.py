@@ -92,6 +92,8 @@ SMALL = [
     (70, 256, 512, 3, 2),    # the same with f > d
     (150, 352, 320, 8, 2),   # prompt path, K stage counts 6 (half last stage) and 5
     (40, 2336, 2208, 8, 2),  # streaming kernels' line loads: chunk ranges of odd bounds, K tails
+    (40, 2304, 2560, 8, 2),  # the same with K multiples of 256 (18 and 20 chunks): whole-line path
+                             # with two-pair scale loads, waves' ranges starting on odd chunks
 ]
 
 
