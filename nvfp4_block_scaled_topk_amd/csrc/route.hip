@@ -30,7 +30,7 @@
 
 namespace moe {
 
-constexpr int kRouteTokensPerBlock = 16;  // measured against 32 and 64: more blocks, shorter chains
+constexpr int kRouteTokensPerBlock = 16;  // measured against 8, 32 and 64 (8: no faster at 512 tokens)
 constexpr int kRouteThreads = 256;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;
