@@ -104,6 +104,15 @@ def test_layer_small(T, d, f, E, k):
     check_layer_full(inp, run_moe(inp), f"T{T}d{d}f{f}E{E}k{k}")
 
 
+def test_layer_streaming_packing():
+    """Experts of 4, 5..8 and 9..12 rows (uniform routing) on the whole-line streaming path
+    (K multiples of 256, 18 and 20 chunks, waves' ranges starting on odd chunks): activation
+    rows packed 4, 2 and 1 to a lane row; full outputs against the oracle."""
+    inp = workloads.make_moe(40, 2304, 2560, 12, 2, seed=1, config_id=62, zipf=False)
+    say("layer streaming packing T=40 d=2304 f=2560 E=12 k=2 (uniform routing)")
+    check_layer_full(inp, run_moe(inp), "streaming packing T40d2304f2560E12k2")
+
+
 def _covering_sample(inp, extra, seed):
     """Tokens covering every (expert, 128-row tile) of the grouped GEMM and every
     weight-streaming expert (first and last row of each), plus `extra` random tokens."""
